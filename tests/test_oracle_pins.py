@@ -1,0 +1,385 @@
+"""Pins of the CPU oracle against things other than itself: brute force on
+tiny inputs, a library convolution, closed forms, invariants, and hand-worked
+tile plans.  CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+import synthetic as S
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- rounding
+def test_f16_rounding_closed_forms():
+    # IEEE binary16 round-to-nearest-even: ulp(1) = 2^-10, max finite 65504,
+    # smallest subnormal 2^-24.
+    cases = [
+        (1.0 + 2.0 ** -11, 1.0),                  # exact tie -> even (mantissa 0)
+        (1.0 + 3 * 2.0 ** -11, 1.0 + 2.0 ** -9),  # tie between odd and even -> even
+        (1.0 + 2.0 ** -11 + 2.0 ** -20, 1.0 + 2.0 ** -10),  # above the tie -> up
+        (65504.0, 65504.0),
+        (65519.0, 65504.0),
+        (65520.0, math.inf),                      # tie at the top rounds to overflow
+        (2.0 ** -24, 2.0 ** -24),                 # subnormals kept
+        (2.0 ** -25, 0.0),                        # tie -> even (zero)
+        (3 * 2.0 ** -26, 2.0 ** -24),
+        (-2.5 * 2.0 ** -10 - 1.0, -(1.0 + 2.0 ** -9)),
+    ]
+    for value, expected in cases:
+        got = float(O.round_to(np.array([value]), "f16")[0])
+        assert got == expected, (value, got, expected)
+
+
+# ------------------------------------------------------------- conv pins
+def brute_conv(x, cin, w, b, relu):
+    """Six nested loops, float64, taps outside the image skipped."""
+    h, wd = x.shape[:2]
+    cout = w.shape[0]
+    out = np.zeros((h, wd, cout))
+    for y in range(h):
+        for xx in range(wd):
+            for o in range(cout):
+                acc = float(b[o])
+                for ky in range(3):
+                    for kx in range(3):
+                        sy, sx = y + ky - 1, xx + kx - 1
+                        if 0 <= sy < h and 0 <= sx < wd:
+                            for i in range(cin):
+                                acc += float(w[o, ky, kx, i]) * float(x[sy, sx, i])
+                out[y, xx, o] = max(acc, 0.0) if relu else acc
+    return out
+
+
+@pytest.mark.parametrize("h,w,cin,cout,relu", [(5, 7, 5, 6, True), (4, 4, 3, 3, False),
+                                                (3, 6, 9, 13, True), (1, 1, 4, 5, False)])
+@pytest.mark.parametrize("precision", ["f32", "f16"])
+def test_conv_matches_brute_force(h, w, cin, cout, relu, precision):
+    r = np.random.default_rng(h * 100 + cin)
+    x = np.zeros((h, w, O.stored(cin)), np.float32)
+    x[..., :cin] = r.standard_normal((h, w, cin))
+    x = O.round_to(x, precision)
+    wt = r.standard_normal((cout, 3, 3, cin)).astype(np.float32)
+    b = r.standard_normal(cout).astype(np.float32)
+    got = O.conv3x3(x, cin, wt, b, relu, precision)
+    assert got.shape == (h, w, O.stored(cout))
+    assert np.all(got[..., cout:] == 0)
+    wq = O.round_to(wt, precision).astype(np.float64)
+    ref = O.round_to(brute_conv(x.astype(np.float64), cin, wq, b, relu), precision)
+    # float64 sums in a different order can move the rounded value by one ulp
+    ulp = np.spacing(np.abs(ref.astype(np.float32)).astype(ref.dtype)).astype(np.float64)
+    assert np.all(np.abs(got[..., :cout].astype(np.float64) - ref.astype(np.float64)) <= ulp)
+
+
+def test_conv_matches_torch_conv2d():
+    torch = pytest.importorskip("torch")
+    r = np.random.default_rng(7)
+    h, w, cin, cout = 16, 12, 13, 7
+    x = np.zeros((h, w, 16), np.float32)
+    x[..., :cin] = r.standard_normal((h, w, cin))
+    wt = r.standard_normal((cout, 3, 3, cin)).astype(np.float32)
+    b = r.standard_normal(cout).astype(np.float32)
+    got = O.conv3x3(x, cin, wt, b, False, "f32")
+    tx = torch.from_numpy(x[..., :cin].astype(np.float64)).permute(2, 0, 1)[None]
+    tw = torch.from_numpy(wt.astype(np.float64)).permute(0, 3, 1, 2)
+    ref = torch.nn.functional.conv2d(tx, tw, torch.from_numpy(b.astype(np.float64)), padding=1)
+    ref = ref[0].permute(1, 2, 0).numpy().astype(np.float32)
+    np.testing.assert_allclose(got[..., :cout], ref, rtol=2e-6, atol=2e-6)
+
+
+@pytest.mark.parametrize("precision", ["f32", "f16"])
+def test_conv_delta_kernel_passes_input_through(precision):
+    r = np.random.default_rng(1)
+    c = 12
+    x = O.round_to(np.abs(r.standard_normal((9, 11, c))), precision)
+    w = np.zeros((c, 3, 3, c), np.float32)
+    w[np.arange(c), 1, 1, np.arange(c)] = 1.0
+    got = O.conv3x3(x, c, w, np.zeros(c, np.float32), True, precision)
+    assert got.dtype == x.dtype
+    assert np.array_equal(got, x)
+
+
+def test_conv_linear_before_relu():
+    r = np.random.default_rng(2)
+    cin, cout = 7, 5
+    x = r.standard_normal((6, 8, 8)).astype(np.float32)
+    y = r.standard_normal((6, 8, 8)).astype(np.float32)
+    w = r.standard_normal((cout, 3, 3, cin)).astype(np.float32)
+    zero = np.zeros(cout, np.float32)
+    cx = O.conv3x3(x, cin, w, zero, False, "f32")
+    # scaling by a power of two commutes with every rounding: bit-exact
+    assert np.array_equal(O.conv3x3(x * 8, cin, w, zero, False, "f32"), cx * 8)
+    cy = O.conv3x3(y, cin, w, zero, False, "f32")
+    cxy = O.conv3x3(x + y, cin, w, zero, False, "f32")
+    np.testing.assert_allclose(cxy, cx + cy, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("precision", ["f32", "f16"])
+def test_conv_zero_padding_counts_valid_taps(precision):
+    cin, cout = 12, 4
+    h, w = 5, 6
+    x = O.round_to(np.ones((h, w, cin)), precision)
+    wt = np.ones((cout, 3, 3, cin), np.float32)
+    got = O.conv3x3(x, cin, wt, np.zeros(cout, np.float32), False, precision).astype(np.float64)
+    rows = np.array([2] + [3] * (h - 2) + [2])
+    cols = np.array([2] + [3] * (w - 2) + [2])
+    expected = np.outer(rows, cols) * cin
+    for o in range(cout):
+        assert np.array_equal(got[..., o], expected)
+
+
+# ----------------------------------------------------- pool / upsample-concat
+def test_pool_closed_form_on_ramp():
+    h, w, c = 8, 10, 4
+    y, x, ch = np.meshgrid(np.arange(h), np.arange(w), np.arange(c), indexing="ij")
+    ramp = (y * w + x + ch * 0.001).astype(np.float32)
+    got = O.pool2x2(ramp)
+    yy, xx, cc = np.meshgrid(np.arange(h // 2), np.arange(w // 2), np.arange(c), indexing="ij")
+    expected = ramp[2 * yy + 1, 2 * xx + 1, cc]
+    assert np.array_equal(got, expected)
+
+
+def test_pool_matches_four_way_max():
+    r = np.random.default_rng(3)
+    x = r.standard_normal((6, 4, 8)).astype(np.float16)
+    got = O.pool2x2(x)
+    for y in range(3):
+        for xx in range(2):
+            for c in range(8):
+                m = max(x[2 * y, 2 * xx, c], x[2 * y, 2 * xx + 1, c],
+                        x[2 * y + 1, 2 * xx, c], x[2 * y + 1, 2 * xx + 1, c])
+                assert got[y, xx, c] == m
+    with pytest.raises(ValueError):
+        O.pool2x2(np.zeros((3, 4, 4)))
+
+
+def test_upsample_concat_closed_form():
+    r = np.random.default_rng(4)
+    low = r.standard_normal((3, 5, 8)).astype(np.float16)
+    skip = np.zeros((6, 10, 12), np.float16)
+    skip[..., :9] = r.standard_normal((6, 10, 9))
+    z = O.upsample_concat(low, 8, skip, 9)
+    assert z.shape == (6, 10, 20)
+    for y in range(6):
+        for x in range(10):
+            assert np.array_equal(z[y, x, :8], low[y // 2, x // 2])
+            assert np.array_equal(z[y, x, 8:], skip[y, x])
+    with pytest.raises(ValueError):
+        O.upsample_concat(np.zeros((3, 5, 8)), 6, skip, 9)
+
+
+# ------------------------------------------------------------ pack / unpack
+def _tiny_images():
+    h, w = 3, 4
+    color = np.zeros((h, w, 4), np.float32)
+    albedo = np.zeros((h, w, 4), np.float32)
+    normal = np.zeros((h, w, 4), np.float32)
+    for y in range(h):
+        for x in range(w):
+            base = (y * w + x) / 16.0
+            color[y, x] = [base, base + 0.25, base + 0.5, 0.125 * x]
+            albedo[y, x] = [0.5 * base, 0.25, 0.75, 9.0]
+            normal[y, x] = [-1.0, 0.0, 0.5, 7.0]
+    return color, albedo, normal
+
+
+def test_pack_lane_layout_ldr():
+    color, albedo, normal = _tiny_images()
+    p = O.pack_input(color, albedo, normal, 0, 0, 4, 3, False, 1.0, "f32")
+    assert p.shape == (3, 4, 12) and p.dtype == np.float32
+    for y in range(3):
+        for x in range(4):
+            c = np.clip(color[y, x, :3], 0, 1)
+            a = albedo[y, x, :3]
+            expected = [*c, *a, 0.0, 0.5, 0.75, 0.0, 0.0, 0.0]
+            assert np.array_equal(p[y, x], np.array(expected, np.float32))
+    p3 = O.pack_input(color, None, None, 0, 0, 4, 3, False, 1.0, "f16")
+    assert p3.shape == (3, 4, 4) and np.all(p3[..., 3] == 0)
+    p6 = O.pack_input(color, albedo, None, 0, 0, 4, 3, False, 1.0, "f16")
+    assert p6.shape == (3, 4, 8) and np.all(p6[..., 6:] == 0)
+    assert np.array_equal(p6[..., 3:6], albedo[..., :3].astype(np.float16))
+
+
+def test_pack_clamp_to_edge_and_special_values():
+    color, albedo, normal = _tiny_images()
+    p = O.pack_input(color, albedo, normal, -2, -1, 8, 5, False, 1.0, "f32")
+    for ty in range(5):
+        for tx in range(8):
+            sy = min(max(ty - 1, 0), 2)
+            sx = min(max(tx - 2, 0), 3)
+            assert np.array_equal(p[ty, tx, :3], np.clip(color[sy, sx, :3], 0, 1))
+    inf = np.float32(np.inf)
+    color = np.array([[[np.nan, -1.0, inf, 1.0]]], np.float32)
+    albedo = np.array([[[np.nan, 2.0, -3.0, 1.0]]], np.float32)
+    normal = np.array([[[np.nan, -5.0, 5.0, 0.0]]], np.float32)
+    p = O.pack_input(color, albedo, normal, 0, 0, 1, 1, True, 1.0, "f32")[0, 0]
+    assert p[0] == 0.0 and p[1] == 0.0                       # NaN -> 0, negative -> 0
+    assert p[2] == np.float32(math.log1p(O.FLT_MAX))         # +inf -> F(FLT_MAX)
+    assert list(p[3:6]) == [0.0, 1.0, 0.0]
+    assert list(p[6:9]) == [0.5, 0.0, 1.0]                   # NaN -> 0 -> 0.5
+
+
+def test_hdr_transfer_round_trip_and_fixed_point():
+    assert O.hdr_forward(0.0) == 0.0 and O.hdr_inverse(0.0) == 0.0
+    x = np.exp(np.linspace(-20, 20, 101))
+    np.testing.assert_allclose(O.hdr_inverse(O.hdr_forward(x)), x, rtol=1e-12)
+    assert np.all(np.diff(O.hdr_forward(x)) > 0)
+
+
+def test_unpack_inverts_pack_and_copies_alpha():
+    r = S.rng(5)
+    color, albedo, normal = S.images(r, 20, 12)
+    scale = 0.75
+    packed = O.pack_input(color, None, None, 0, 0, 20, 12, True, scale, "f32")
+    net = np.zeros((12, 20, 4), np.float32)
+    net[..., :3] = packed[..., :3]
+    out = np.full((12, 20, 4), np.nan, np.float32)
+    O.unpack_output(net, 0, 0, color, 0, 0, 20, 12, True, scale, out)
+    np.testing.assert_allclose(out[..., :3], color[..., :3], rtol=2e-6)
+    assert np.array_equal(out[..., 3], color[..., 3])
+
+
+def test_unpack_writes_exactly_its_rectangle():
+    r = S.rng(6)
+    color, _, _ = S.images(r, 16, 16)
+    net = r.standard_normal((32, 32, 4)).astype(np.float32)
+    out = np.full((16, 16, 4), np.nan, np.float32)
+    O.unpack_output(net, 5, 3, color, 2, 4, 7, 9, False, 1.0, out)
+    written = ~np.isnan(out[..., 0])
+    expected = np.zeros((16, 16), bool)
+    expected[4:13, 2:9] = True
+    assert np.array_equal(written, expected)
+    assert np.array_equal(out[4:13, 2:9, :3], np.clip(net[3:12, 5:12, :3], 0, 1))
+
+
+# --------------------------------------------------------------- tile plan
+def _check_plan(w, h, t, o, tiles):
+    limit = t if t > 0 else O.align_up(max(w, h))
+    cover = np.zeros((h, w), np.int32)
+    for (ix, iy, iw, ih, ox, oy, ow, oh) in tiles:
+        for v in (ix, iy, iw, ih):
+            assert v % 16 == 0
+        assert iw <= limit and ih <= limit and ow > 0 and oh > 0
+        assert 0 <= ix and ix + iw <= O.align_up(w) and 0 <= iy and iy + ih <= O.align_up(h)
+        assert ix <= ox and ox + ow <= ix + iw and iy <= oy and oy + oh <= iy + ih
+        # at least `o` pixels of context on every side, unless the input span
+        # already reaches the edge of the untiled (16-aligned) input
+        assert ix == 0 or ox - ix >= o
+        assert ix + iw == O.align_up(w) or ix + iw - (ox + ow) >= o
+        assert iy == 0 or oy - iy >= o
+        assert iy + ih == O.align_up(h) or iy + ih - (oy + oh) >= o
+        cover[oy:oy + oh, ox:ox + ow] += 1
+    assert np.all(cover == 1)
+
+
+def test_tile_plan_matches_hand_worked_cases():
+    with open(os.path.join(GOLDEN, "tile_plan_3840x2160.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        tiles = O.plan_tiles(case["width"], case["height"], case["max_tile"], case["overlap"])
+        expected = [(x[0], y[0], x[1], y[1], x[2], y[2], x[3], y[3])
+                    for y in case["y_spans"] for x in case["x_spans"]]
+        assert tiles == expected
+        _check_plan(case["width"], case["height"], case["max_tile"], case["overlap"], tiles)
+
+
+def test_tile_plan_invariants_random():
+    r = np.random.default_rng(8)
+    for _ in range(300):
+        w, h = int(r.integers(1, 3000)), int(r.integers(1, 3000))
+        o = 16 * int(r.integers(0, 7))
+        t = 16 * int(r.integers(2 * o // 16 + 1, 2 * o // 16 + 80))
+        if r.random() < 0.1:
+            t = 0
+        _check_plan(w, h, t, o, O.plan_tiles(w, h, t, o))
+
+
+def test_tile_plan_rejects_bad_arguments():
+    for args in [(0, 5, 0, 0), (5, -1, 0, 0), (100, 100, 40, 0), (100, 100, 64, 8),
+                 (1000, 100, 64, 32)]:
+        with pytest.raises(ValueError):
+            O.plan_tiles(*args)
+
+
+# ------------------------------------------------------------- network
+def test_network_work_per_pixel():
+    # 2 * 9 * sum(cin * cout / 4^level), worked by hand per level:
+    #   L0: 9*32 + 32*32 + 73*64 + 64*32 + 32*3        = 8128
+    #   L1: (32*48 + 128*64 + 64*64) / 4                = 3456
+    #   L2: (48*64 + 160*96 + 96*96) / 16               = 1728
+    #   L3: (64*80 + 160*112 + 112*112) / 64            = 556
+    #   L4: (80*96 + 96*96) / 256                       = 66
+    #   18 * (8128 + 3456 + 1728 + 556 + 66)            = 250812
+    assert O.unet_flops_per_pixel(9) == 250812
+    assert [c for c, _ in O.unet_layer_shapes(9)] == [9, 32, 32, 48, 64, 80, 96, 160, 112,
+                                                      160, 96, 128, 64, 73, 64, 32]
+
+
+def _reach_intervals():
+    """Input interval of every level-0 output column x in [0, 16), by interval
+    propagation through the layer table (conv widens by 1 at its level, pool
+    maps [a, b] -> [2a, 2b + 1], nearest upsample maps [a, b] -> [a >> 1, b >> 1])."""
+    producers = {}
+    level_of = {"input": 0}
+    level = 0
+    for (name, src, skip, cout, pool, relu) in O.UNET_LAYERS:
+        if skip is not None:
+            level -= 1
+        producers[name] = (src, skip, pool, level)
+        level_of[name] = level + (1 if pool else 0)
+        if pool:
+            level += 1
+
+    def deps(value, a, b):
+        if value == "input":
+            return a, b
+        src, skip, pool, conv_level = producers[value]
+        if pool:
+            a, b = 2 * a, 2 * b + 1
+        a, b = a - 1, b + 1
+        lo, hi = (deps(src, a >> 1, b >> 1) if skip is not None else deps(src, a, b))
+        if skip is not None:
+            slo, shi = deps(skip, a, b)
+            lo, hi = min(lo, slo), max(hi, shi)
+        return lo, hi
+
+    return [deps(O.UNET_LAYERS[-1][0], x, x) for x in range(16)]
+
+
+def test_default_overlap_covers_receptive_reach():
+    reach = max(max(x - lo, hi - x) for x, (lo, hi) in enumerate(_reach_intervals()))
+    assert O.align_up(reach) == O.DEFAULT_OVERLAP
+    assert reach > 80
+
+
+@pytest.fixture(scope="module")
+def small_unet():
+    r = S.rng(0)
+    color, albedo, normal = S.images(r, 400, 64)
+    ws, bs = S.layer_params(r, O.unet_layer_shapes(9))
+    return color, albedo, normal, ws, bs
+
+
+def test_tiled_equals_untiled_at_default_overlap(small_unet):
+    color, albedo, normal, ws, bs = small_unet
+    untiled = O.unet_forward(ws, bs, color, albedo, normal, True, 1.0, 0, 96, "f32")
+    tiles = O.plan_tiles(400, 64, 304, 96)
+    assert len(tiles) == 4
+    tiled = O.unet_forward(ws, bs, color, albedo, normal, True, 1.0, 304, 96, "f32")
+    assert not np.any(np.isnan(tiled)) and not np.any(np.isnan(untiled))
+    assert O.max_rel_error(tiled, untiled) <= 1e-6
+
+
+def test_f16_storage_stays_within_tolerance_of_f32(small_unet):
+    color, albedo, normal, ws, bs = small_unet
+    p32 = O.pack_input(color, albedo, normal, 0, 0, 400, 64, True, 1.0, "f32")
+    p16 = O.pack_input(color, albedo, normal, 0, 0, 400, 64, True, 1.0, "f16")
+    n32 = O.unet_forward_packed(ws, bs, p32, 9, "f32")
+    n16 = O.unet_forward_packed(ws, bs, p16, 9, "f16")
+    assert n16.dtype == np.float32 and np.all(n32[..., 3] == 0)
+    err = O.max_rel_error(n16, n32)
+    assert 0 < err < 2e-2
