@@ -1,0 +1,237 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, its
+host-only logic (tile planner, layer table, weight packing, workspace plan)
+matches the oracle or the documented layout, and every argument error is
+rejected before any device work.  No GPU is touched."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import unet_x3_convolution_amd as U
+from oracle import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    if not os.path.exists(U.LIB_PATH):
+        from unet_x3_convolution_amd import build
+        build.build(verbose=False)
+    U.lib()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "oidn_mi355x.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(oidn_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 20
+    lib = U.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(U.EXPORTS) == names
+    assert U.lib().oidn_version() >= 100
+
+
+def test_tile_planner_matches_oracle():
+    r = np.random.default_rng(11)
+    cases = [(3840, 2160, 1024, 32), (3840, 2160, 1024, 96), (1920, 1080, 0, 32), (1920, 1080, 0, -1),
+             (17, 5, 0, 0), (1, 1, 16, 0), (400, 64, 304, 96)]
+    for _ in range(400):
+        o = 16 * int(r.integers(0, 7))
+        t = 16 * int(r.integers(2 * o // 16 + 1, 2 * o // 16 + 70))
+        cases.append((int(r.integers(1, 5000)), int(r.integers(1, 5000)), 0 if r.random() < 0.1 else t, o))
+    for w, h, t, o in cases:
+        assert U.oidn_plan_tiles(w, h, t, o) == O.plan_tiles(w, h, t, o), (w, h, t, o)
+
+
+def test_tile_planner_errors():
+    for args in [(0, 5, 0, 0), (5, -1, 0, 0), (100, 100, 40, 0), (100, 100, 64, 8), (1000, 100, 64, 32)]:
+        with pytest.raises(U.OidnError) as e:
+            U.oidn_plan_tiles(*args)
+        assert e.value.code == U.OIDN_E_INVALID
+        with pytest.raises(ValueError):
+            O.plan_tiles(*args)
+    # capacity too small
+    import ctypes
+    count = ctypes.c_int()
+    arr = (U.oidn_tile * 2)()
+    rc = U.lib().oidn_plan_tiles(3840, 2160, 1024, 32, arr, 2, ctypes.byref(count))
+    assert rc == U.OIDN_E_WORKSPACE and count.value == 12
+
+
+@pytest.mark.parametrize("in_channels", [3, 6, 9])
+def test_layer_table_matches_oracle(in_channels):
+    assert U.oidn_unet_layer_count() == len(O.UNET_LAYERS)
+    assert U.unet_layer_shapes(in_channels) == O.unet_layer_shapes(in_channels)
+    for i, (name, _src, skip, cout, pool, relu) in enumerate(O.UNET_LAYERS):
+        n, c0, c1, co, level, flags = U.oidn_unet_layer_info(in_channels, i)
+        assert n == name and co == cout
+        assert (c1 > 0) == (skip is not None)
+        assert bool(flags & U.OIDN_POOL2X2) == pool and bool(flags & U.OIDN_RELU) == relu
+
+
+def _decode_f16(packed, cin0, cin1, cout):
+    """Decode the fp16 fragment layout from its documented description:
+    bias (16 * nf floats, 256-aligned), then per chunk (<= 32 stored channels
+    of one source; sources in order), per K step, per output fragment q, a
+    1 KB fragment of 64 lanes x 8 halves; lane l holds row r = l % 16 (output
+    channel 4 * nf * (r // 4) + 4 * q + r % 4) and K group kg = 4 * step + l // 16
+    of the chunk, kg = tap * cg + group, channels coff + 8 * group + j."""
+    cs = [O.stored(cin0), O.stored(cin1) if cin1 else 0]
+    nf = -(-O.stored(cout) // 16)
+    bias_bytes = -(-(4 * 16 * nf) // 256) * 256
+    bias = packed[:4 * cout].view(np.float32)
+    frags = packed[bias_bytes:].view(np.float16).reshape(-1, 64, 8)
+    w = np.full((cout, 9, cin0 + cin1), np.nan, np.float32)
+    f = 0
+    for s_idx in range(2):
+        for off in range(0, cs[s_idx], 32):
+            cg = -(-min(32, cs[s_idx] - off) // 8)
+            steps = -(-9 * cg // 4)
+            for st in range(steps):
+                for q in range(nf):
+                    frag = frags[f]
+                    f += 1
+                    for lane in range(64):
+                        r, kg = lane % 16, 4 * st + lane // 16
+                        o = 4 * nf * (r // 4) + 4 * q + r % 4
+                        vals = frag[lane].astype(np.float32)
+                        if o >= cout or kg >= 9 * cg:
+                            assert np.all(vals == 0)
+                            continue
+                        tap, grp = divmod(kg, cg)
+                        for j in range(8):
+                            c = off + 8 * grp + j
+                            logical = c if s_idx == 0 else cin0 + c
+                            limit = cin0 if s_idx == 0 else cin1
+                            if c < limit:
+                                w[o, tap, logical] = vals[j]
+                            else:
+                                assert vals[j] == 0
+    assert f == frags.shape[0]
+    return w.reshape(cout, 3, 3, cin0 + cin1), bias
+
+
+@pytest.mark.parametrize("cin0,cin1,cout", [(9, 0, 32), (32, 0, 48), (64, 9, 64), (96, 64, 112),
+                                            (5, 0, 3), (36, 0, 20)])
+def test_f16_weight_layout_round_trip(cin0, cin1, cout):
+    r = np.random.default_rng(cin0 + cout)
+    w = r.standard_normal((cout, 3, 3, cin0 + cin1)).astype(np.float32)
+    b = r.standard_normal(cout).astype(np.float32)
+    packed = U.oidn_conv3x3_pack_weights_host(w, b, cin0, cin1, cout, U.OIDN_F16)
+    wd, bd = _decode_f16(packed, cin0, cin1, cout)
+    assert not np.any(np.isnan(wd))
+    assert np.array_equal(wd, w.astype(np.float16).astype(np.float32))
+    assert np.array_equal(bd, b)
+
+
+def test_f32_weight_layout_round_trip():
+    cin0, cin1, cout = 64, 9, 6
+    r = np.random.default_rng(3)
+    w = r.standard_normal((cout, 3, 3, cin0 + cin1)).astype(np.float32)
+    b = r.standard_normal(cout).astype(np.float32)
+    packed = U.oidn_conv3x3_pack_weights_host(w, b, cin0, cin1, cout, U.OIDN_F32).view(np.float32)
+    cs, cst = O.stored(cout), O.stored(cin0) + O.stored(cin1)
+    assert np.array_equal(packed[:cout], b) and np.all(packed[cout:cs] == 0)
+    wt = packed[64:].reshape(cs // 4, 9, cst, 4)
+    for o in range(cs):
+        for tap in range(9):
+            for c in range(cst):
+                li = c if c < cin0 else (cin0 + c - O.stored(cin0) if c - O.stored(cin0) < cin1 else -1)
+                expected = w[o, tap // 3, tap % 3, li] if (o < cout and li >= 0) else 0.0
+                assert wt[o // 4, tap, c, o % 4] == expected
+
+
+def test_workspace_plan_is_liveness_bounded():
+    es = 2
+    tw, th = 512, 512
+    ws = U.oidn_unet_packed_workspace_bytes(9, tw, th, U.OIDN_F16)
+    px = tw * th
+    # lower bound: dec_conv1a's operands alive together (upsampled 64ch at /2, output 64ch)
+    # plus the three pooled skips, which are all alive at that point or earlier
+    lower = px * 64 * es + px // 4 * 64 * es
+    # upper bound: every value in its own buffer
+    sizes = [px * 32, px // 4 * 32, px // 16 * 48, px // 64 * 64, px // 256 * 80, px // 256 * 96,
+             px // 256 * 96, px // 64 * 112, px // 64 * 112, px // 16 * 96, px // 16 * 96,
+             px // 4 * 64, px // 4 * 64, px * 64, px * 32]
+    upper = sum(s * es for s in sizes) + 256 * 20
+    assert lower <= ws <= upper
+    full = U.oidn_unet_workspace_bytes(9, 1920, 1080, 0, 32, U.OIDN_F16)
+    assert full >= 1920 * 1088 * (12 * 2 + 16)
+
+
+def test_weight_bytes_sum_per_layer():
+    for dtype in (U.OIDN_F16, U.OIDN_F32):
+        total = U.oidn_unet_weights_bytes(9, dtype)
+        per = sum(-(-U.oidn_conv3x3_weights_bytes(U.oidn_unet_layer_info(9, i)[1],
+                                                   U.oidn_unet_layer_info(9, i)[2],
+                                                   U.oidn_unet_layer_info(9, i)[3], dtype) // 256) * 256
+                  for i in range(16))
+        assert total == per
+
+
+# ---- argument errors: rejected before any device work (no GPU involved) ----
+FAKE = 1 << 20   # a 16-byte aligned fake device address, never dereferenced
+
+
+def _code(fn, *args):
+    with pytest.raises(U.OidnError) as e:
+        fn(*args)
+    return e.value.code
+
+
+def test_conv_argument_errors():
+    E, N = U.OIDN_E_INVALID, U.OIDN_E_UNSUPPORTED
+    c = U.oidn_conv3x3
+    assert _code(c, 0, 8, 8, 12, FAKE, FAKE, 32, U.OIDN_F16, U.OIDN_F16, 1, 0) == E       # null x
+    assert _code(c, FAKE, 0, 8, 12, FAKE, FAKE, 32, U.OIDN_F16, U.OIDN_F16, 1, 0) == E    # h = 0
+    assert _code(c, FAKE, 7, 8, 12, FAKE, FAKE, 32, U.OIDN_F16, U.OIDN_F16, 3, 0) == E    # odd pool
+    assert _code(c, FAKE, 8, 8, 12, FAKE, FAKE, 32, U.OIDN_F32, U.OIDN_F16, 1, 0) == N    # f32 -> f16
+    assert _code(c, FAKE, 8, 8, 12, FAKE, FAKE, 32, U.OIDN_BF16, U.OIDN_BF16, 1, 0) == N  # bf16
+    assert _code(c, FAKE, 8, 8, 12, FAKE, FAKE, 32, 7, U.OIDN_F16, 1, 0) == E             # dtype
+    assert _code(c, FAKE, 8, 8, 12, FAKE, FAKE, 32, U.OIDN_F16, U.OIDN_F16, 8, 0) == E    # flags
+    assert _code(c, FAKE, 8, 8, 300, FAKE, FAKE, 32, U.OIDN_F16, U.OIDN_F16, 1, 0) == N   # cin
+    assert _code(c, FAKE + 4, 8, 8, 12, FAKE, FAKE, 32, U.OIDN_F16, U.OIDN_F16, 1, 0) == E  # align
+    u = U.oidn_conv3x3_upcat
+    assert _code(u, FAKE, 6, FAKE, 9, 8, 8, FAKE, FAKE, 32, U.OIDN_F16, U.OIDN_F16, 1, 0) == E  # c_low%4
+    assert _code(u, FAKE, 8, FAKE, 9, 7, 8, FAKE, FAKE, 32, U.OIDN_F16, U.OIDN_F16, 1, 0) == E  # odd h
+    assert _code(U.oidn_conv3x3_weights_bytes, 6, 9, 32, U.OIDN_F16) == E
+    assert _code(U.oidn_conv3x3_weights_bytes, 8, 0, 0, U.OIDN_F16) == E
+
+
+def test_elementwise_argument_errors():
+    E, N = U.OIDN_E_INVALID, U.OIDN_E_UNSUPPORTED
+    assert _code(U.oidn_pool2x2, FAKE, 7, 8, 12, FAKE, U.OIDN_F16, 0) == E
+    assert _code(U.oidn_pool2x2, 0, 8, 8, 12, FAKE, U.OIDN_F16, 0) == E
+    assert _code(U.oidn_upsample_concat, FAKE, 5, FAKE, 4, 8, 8, FAKE, U.OIDN_F16, 0) == E
+    p = U.oidn_pack_input
+    assert _code(p, FAKE, None, FAKE, 8, 8, 0, 0, 8, 8, 1, 1, 1.0, FAKE, U.OIDN_F16, 0) == E  # normal w/o albedo
+    assert _code(p, FAKE, None, None, 8, 8, 0, 0, 8, 8, 1, 0, 1.0, FAKE, U.OIDN_F16, 0) == N  # pu transfer
+    assert _code(p, FAKE, None, None, 8, 8, 0, 0, 8, 8, 1, 1, 0.0, FAKE, U.OIDN_F16, 0) == E  # scale 0
+    assert _code(p, FAKE, None, None, 0, 8, 0, 0, 8, 8, 1, 1, 1.0, FAKE, U.OIDN_F16, 0) == E
+    q = U.oidn_unpack_output
+    assert _code(q, FAKE, 16, 16, 8, 0, FAKE, 32, 32, 0, 0, 16, 16, 1, 1, 1.0, FAKE, 0) == E  # reads past tile
+    assert _code(q, FAKE, 16, 16, 0, 0, FAKE, 8, 8, 0, 0, 16, 16, 1, 1, 1.0, FAKE, 0) == E    # past image
+
+
+def test_unet_argument_errors():
+    E, W = U.OIDN_E_INVALID, U.OIDN_E_WORKSPACE
+    f = U.oidn_unet_forward_packed
+    assert _code(f, FAKE, 9, FAKE, 72, 64, FAKE, 1 << 40, FAKE, U.OIDN_F16, 0) == E   # tw % 16
+    assert _code(f, FAKE, 7, FAKE, 64, 64, FAKE, 1 << 40, FAKE, U.OIDN_F16, 0) == E   # channels
+    assert _code(f, FAKE, 9, FAKE, 64, 64, FAKE, 1000, FAKE, U.OIDN_F16, 0) == W      # workspace
+    g = U.oidn_unet_forward
+    assert _code(g, FAKE, 9, FAKE, FAKE, None, 64, 64, 1, 1, 1.0, 0, 32, FAKE, 1 << 40, FAKE,
+                 U.OIDN_F16, 0) == E                                                    # 2 images for 9 ch
+    assert _code(g, FAKE, 3, FAKE, None, None, 64, 64, 1, 1, 1.0, 40, 32, FAKE, 1 << 40, FAKE,
+                 U.OIDN_F16, 0) == E                                                    # max_tile % 16
+    assert _code(g, FAKE, 3, FAKE, None, None, 64, 64, 1, 1, 1.0, 0, 32, FAKE, 10, FAKE,
+                 U.OIDN_F16, 0) == W
+    assert _code(U.oidn_unet_layer_info, 9, 16) == E
+    assert "layer 16" in U.last_error()

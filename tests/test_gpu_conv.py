@@ -1,0 +1,169 @@
+"""GPU parity of the 3x3 conv kernels (fp32 VALU and fp16 MFMA) against the
+CPU oracle, through the C ABI, plus the conv invariants on the GPU."""
+import numpy as np
+import pytest
+
+import synthetic as S
+import unet_x3_convolution_amd as U
+from helpers import DT, TOL, dev, empty, host, packed_conv, rel_err, say, ulp_diff_f16
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def run_conv(x_np, cin, w, b, cout, precision, flags, out_precision=None):
+    out_precision = out_precision or precision
+    h, wd = x_np.shape[:2]
+    pk = packed_conv(w, b, cin, 0, cout, precision)
+    oh, ow = (h // 2, wd // 2) if flags & U.OIDN_POOL2X2 else (h, wd)
+    y = empty((oh, ow, O.stored(cout)), O.np_storage(out_precision), fill=float("nan"))
+    U.oidn_conv3x3(dev(x_np), h, wd, cin, pk, y, cout, DT[precision], DT[out_precision], flags)
+    return host(y)
+
+
+def oracle_conv(x_np, cin, w, b, cout, precision, flags, out_precision=None):
+    y = O.conv3x3(x_np, cin, w, b, bool(flags & U.OIDN_RELU), precision, out_precision)
+    return O.pool2x2(y) if flags & U.OIDN_POOL2X2 else y
+
+
+def check(got, ref, cout, precision, label):
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert not np.any(np.isnan(got)), f"{label}: unwritten outputs"
+    assert np.all(got[..., cout:] == 0), f"{label}: pad lanes not zero"
+    err = rel_err(got[..., :cout], ref[..., :cout])
+    extra = ""
+    if got.dtype == np.float16:
+        extra = f" max_ulp={int(ulp_diff_f16(got, ref).max())}"
+    say(f"{label}: max_rel_err={err:.3e}{extra}")
+    assert err <= TOL[precision], (label, err)
+
+
+def test_config1_single_conv_fp32():
+    """64x64, 9 (12 stored) -> 32 channels, fp32, He-normal weights, seed 0."""
+    r = S.rng(0)
+    x = S.uniform_activation(r, 64, 64, 9, 12)
+    w = S.he_normal(r, 32, 9)
+    b = S.bias(r, 32)
+    got = run_conv(x, 9, w, b, 32, "f32", U.OIDN_RELU)
+    check(got, oracle_conv(x, 9, w, b, 32, "f32", U.OIDN_RELU), 32, "f32", "config1")
+
+
+F16_CASES = [
+    # h, w, cin, cout, flags, out precision
+    (64, 64, 9, 32, U.OIDN_RELU, "f16"),
+    (37, 23, 12, 3, 0, "f32"),                       # ragged tile edges, final-layer shape
+    (16, 16, 32, 32, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),
+    (50, 34, 48, 80, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),
+    (18, 30, 76, 64, U.OIDN_RELU, "f16"),
+    (33, 17, 5, 20, U.OIDN_RELU, "f16"),             # cout not a multiple of 16
+    (24, 20, 160, 112, U.OIDN_RELU, "f16"),          # five K chunks, 7 output fragments
+    (8, 8, 256, 128, U.OIDN_RELU, "f16"),            # channel limits
+    (1, 1, 4, 4, 0, "f16"),
+    (2, 2, 8, 16, U.OIDN_RELU | U.OIDN_POOL2X2, "f32"),
+    (70, 3, 96, 96, U.OIDN_RELU, "f16"),
+]
+
+
+@pytest.mark.parametrize("h,w,cin,cout,flags,outp", F16_CASES)
+def test_conv_f16_matches_oracle(h, w, cin, cout, flags, outp):
+    r = np.random.default_rng(1000 + h * 7 + cin)
+    x = O.round_to(S.relu_normal_activation(r, h, w, cin, O.stored(cin)), "f16")
+    wt = S.he_normal(r, cout, cin)
+    b = S.bias(r, cout)
+    got = run_conv(x, cin, wt, b, cout, "f16", flags, outp)
+    check(got, oracle_conv(x, cin, wt, b, cout, "f16", flags, outp), cout, "f16",
+          f"conv f16 {h}x{w} {cin}->{cout} flags={flags} out={outp}")
+
+
+@pytest.mark.parametrize("h,w,cin,cout,flags", [(20, 18, 12, 8, U.OIDN_RELU),
+                                                (10, 14, 40, 20, U.OIDN_RELU | U.OIDN_POOL2X2),
+                                                (9, 5, 3, 3, 0)])
+def test_conv_f32_matches_oracle(h, w, cin, cout, flags):
+    r = np.random.default_rng(h + cin)
+    x = S.relu_normal_activation(r, h, w, cin, O.stored(cin))
+    wt = S.he_normal(r, cout, cin)
+    b = S.bias(r, cout)
+    got = run_conv(x, cin, wt, b, cout, "f32", flags)
+    check(got, oracle_conv(x, cin, wt, b, cout, "f32", flags), cout, "f32",
+          f"conv f32 {h}x{w} {cin}->{cout} flags={flags}")
+
+
+@pytest.mark.parametrize("precision", ["f16", "f32"])
+def test_conv_delta_kernel_is_identity_on_gpu(precision):
+    r = np.random.default_rng(5)
+    c = 48
+    x = O.round_to(np.abs(r.standard_normal((21, 19, c))), precision)
+    w = np.zeros((c, 3, 3, c), np.float32)
+    w[np.arange(c), 1, 1, np.arange(c)] = 1.0
+    got = run_conv(x, c, w, np.zeros(c, np.float32), c, precision, U.OIDN_RELU)
+    assert np.array_equal(got, x)
+
+
+def test_conv_zero_padding_counts_on_gpu():
+    cin, cout = 32, 16
+    h, w = 19, 35
+    x = np.ones((h, w, cin), np.float16)
+    got = run_conv(x, cin, np.ones((cout, 3, 3, cin), np.float32), np.zeros(cout, np.float32),
+                   cout, "f16", 0).astype(np.float64)
+    rows = np.array([2] + [3] * (h - 2) + [2])
+    cols = np.array([2] + [3] * (w - 2) + [2])
+    expected = np.outer(rows, cols) * cin
+    for o in range(cout):
+        assert np.array_equal(got[..., o], expected)
+
+
+def test_fused_pool_equals_conv_then_pool_bit_exact():
+    r = np.random.default_rng(6)
+    h, w, cin, cout = 34, 46, 32, 48
+    x = O.round_to(S.relu_normal_activation(r, h, w, cin, cin), "f16")
+    wt = S.he_normal(r, cout, cin)
+    b = S.bias(r, cout)
+    fused = run_conv(x, cin, wt, b, cout, "f16", U.OIDN_RELU | U.OIDN_POOL2X2)
+    full = run_conv(x, cin, wt, b, cout, "f16", U.OIDN_RELU)
+    y = empty((h // 2, w // 2, cout), np.float16)
+    U.oidn_pool2x2(dev(full), h, w, cout, y, U.OIDN_F16)
+    assert np.array_equal(fused, host(y))
+
+
+UPCAT_CASES = [
+    # h, w (output), c_low, c_skip, cout, precision
+    (16, 16, 96, 64, 112, "f16"),
+    (32, 48, 64, 9, 64, "f16"),
+    (20, 12, 8, 5, 16, "f16"),
+    (18, 26, 112, 48, 96, "f16"),
+    (12, 10, 16, 9, 8, "f32"),
+]
+
+
+@pytest.mark.parametrize("h,w,c_low,c_skip,cout,precision", UPCAT_CASES)
+def test_decoder_conv_matches_oracle(h, w, c_low, c_skip, cout, precision):
+    r = np.random.default_rng(h * w + c_low)
+    low = O.round_to(S.relu_normal_activation(r, h // 2, w // 2, c_low, c_low), precision)
+    skip = O.round_to(S.relu_normal_activation(r, h, w, c_skip, O.stored(c_skip)), precision)
+    wt = S.he_normal(r, cout, c_low + c_skip)
+    b = S.bias(r, cout)
+    pk = packed_conv(wt, b, c_low, c_skip, cout, precision)
+    y = empty((h, w, O.stored(cout)), O.np_storage(precision), fill=float("nan"))
+    U.oidn_conv3x3_upcat(dev(low), c_low, dev(skip), c_skip, h, w, pk, y, cout, DT[precision],
+                         DT[precision], U.OIDN_RELU)
+    got = host(y)
+    z = O.upsample_concat(low, c_low, skip, c_skip)
+    ref = O.conv3x3(z, c_low + c_skip, wt, b, True, precision)
+    check(got, ref, cout, precision, f"upcat conv {precision} {h}x{w} [{c_low}|{c_skip}]->{cout}")
+
+
+def test_conv_ladder_config2():
+    """256x256 fp16: 32->48->64->80->96->96, conv+ReLU then 2x2 pool per stage;
+    each stage is checked against the oracle on the GPU's own stage input."""
+    r = S.rng(0)
+    x = O.round_to(S.relu_normal_activation(r, 256, 256, 32, 32), "f16")
+    chans = [32, 48, 64, 80, 96, 96]
+    flags = U.OIDN_RELU | U.OIDN_POOL2X2
+    for i in range(5):
+        cin, cout = chans[i], chans[i + 1]
+        wt = S.he_normal(r, cout, cin)
+        b = S.bias(r, cout)
+        got = run_conv(x, cin, wt, b, cout, "f16", flags)
+        check(got, oracle_conv(x, cin, wt, b, cout, "f16", flags), cout, "f16",
+              f"ladder stage {i} {x.shape[0]}^2 {cin}->{cout}")
+        x = got

@@ -1,0 +1,165 @@
+"""GPU parity of the whole UNet denoise against the CPU oracle: the network on
+packed tiles, the end-to-end tiled path, the 1080p and 4K workloads on
+sampled output rectangles, and tiled == untiled."""
+import numpy as np
+import pytest
+
+import synthetic as S
+import unet_x3_convolution_amd as U
+from helpers import DT, TOL, dev, empty, host, packed_unet, rel_err, say
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def make_case(width, height, in_channels=9, seed=0):
+    r = S.rng(seed)
+    color, albedo, normal = S.images(r, width, height)
+    ws, bs = S.layer_params(r, U.unet_layer_shapes(in_channels))
+    if in_channels < 9:
+        normal = None
+    if in_channels < 6:
+        albedo = None
+    return color, albedo, normal, ws, bs
+
+
+def gpu_forward_packed(ws, bs, packed, in_channels, precision):
+    th, tw = packed.shape[:2]
+    wd = packed_unet(ws, bs, in_channels, precision)
+    nbytes = U.oidn_unet_packed_workspace_bytes(in_channels, tw, th, DT[precision])
+    work = empty((nbytes,), np.uint8)
+    out = empty((th, tw, 4), np.float32, fill=float("nan"))
+    U.oidn_unet_forward_packed(wd, in_channels, dev(packed), tw, th, work, nbytes, out, DT[precision])
+    return host(out)
+
+
+def gpu_denoise(ws, bs, color, albedo, normal, precision, max_tile, overlap, hdr=True, scale=1.0):
+    img_h, img_w = color.shape[:2]
+    in_channels = 3 * (1 + (albedo is not None) + (normal is not None))
+    wd = packed_unet(ws, bs, in_channels, precision)
+    nbytes = U.oidn_unet_workspace_bytes(in_channels, img_w, img_h, max_tile, overlap, DT[precision])
+    work = empty((nbytes,), np.uint8)
+    out = empty((img_h, img_w, 4), np.float32, fill=float("nan"))
+    U.oidn_unet_forward(wd, in_channels, dev(color), None if albedo is None else dev(albedo),
+                        None if normal is None else dev(normal), img_w, img_h, hdr,
+                        U.OIDN_TRANSFER_LOG, scale, max_tile, overlap, work, nbytes, out,
+                        DT[precision])
+    return host(out)
+
+
+@pytest.mark.parametrize("tw,th,in_channels,precision", [(64, 48, 9, "f16"), (80, 32, 3, "f16"),
+                                                         (48, 64, 6, "f16"), (64, 64, 9, "f32")])
+def test_network_on_packed_tile(tw, th, in_channels, precision):
+    color, albedo, normal, ws, bs = make_case(tw, th, in_channels, seed=tw + th)
+    packed = O.pack_input(color, albedo, normal, 0, 0, tw, th, True, 1.0, precision)
+    got = gpu_forward_packed(ws, bs, packed, in_channels, precision)
+    ref = O.unet_forward_packed(ws, bs, packed, in_channels, precision)
+    err = rel_err(got, ref)
+    say(f"network {precision} {tw}x{th} in={in_channels}: max_rel_err={err:.3e}")
+    assert np.all(got[..., 3] == 0)
+    assert err <= TOL[precision]
+
+
+def test_config3_network_512_fp16():
+    """512x512 fp16: HDR log pack of seeded colour/albedo/normal, then the network."""
+    color, albedo, normal, ws, bs = make_case(512, 512)
+    packed = O.pack_input(color, albedo, normal, 0, 0, 512, 512, True, 1.0, "f16")
+    got = gpu_forward_packed(ws, bs, packed, 9, "f16")
+    ref = O.unet_forward_packed(ws, bs, packed, 9, "f16")
+    err = rel_err(got, ref)
+    say(f"config3 512^2 f16: max_rel_err={err:.3e}")
+    assert err <= TOL["f16"]
+
+
+@pytest.mark.parametrize("precision", ["f16", "f32"])
+def test_end_to_end_tiled_matches_oracle(precision):
+    """200x150 image, 128-pixel tiles, overlap 32 -> a 4x3 grid with ragged
+    output spans; GPU and oracle run the same plan."""
+    color, albedo, normal, ws, bs = make_case(200, 150, seed=4)
+    assert len(U.oidn_plan_tiles(200, 150, 128, 32)) == 12
+    got = gpu_denoise(ws, bs, color, albedo, normal, precision, 128, 32, scale=1.5)
+    ref = O.unet_forward(ws, bs, color, albedo, normal, True, 1.5, 128, 32, precision)
+    assert not np.any(np.isnan(got))
+    assert np.array_equal(got[..., 3], color[..., 3])
+    err = rel_err(got, ref)
+    say(f"end-to-end tiled {precision}: max_rel_err={err:.3e}")
+    assert err <= TOL[precision]
+
+
+def test_tiled_equals_untiled_at_default_overlap():
+    """At overlap 96 (>= the receptive reach) tiling does not change the result;
+    the kernels' reduction order does not depend on position, so it is bit-exact."""
+    color, albedo, normal, ws, bs = make_case(400, 272, seed=5)
+    untiled = gpu_denoise(ws, bs, color, albedo, normal, "f16", 0, 96)
+    tiled = gpu_denoise(ws, bs, color, albedo, normal, "f16", 224, 96)
+    assert len(U.oidn_plan_tiles(400, 272, 224, 96)) > 1
+    assert np.array_equal(tiled, untiled)
+
+
+def _oracle_rect(ws, bs, color, albedo, normal, out_rect, precision):
+    """Oracle output of one output rectangle, computed on a 16-aligned input
+    window with >= 96 px of context (or the image's aligned edge) per side."""
+    img_h, img_w = color.shape[:2]
+    ox, oy, ow, oh = out_rect
+    ea_w, ea_h = O.align_up(img_w), O.align_up(img_h)
+    x0 = max(0, (ox - 96) // 16 * 16)
+    y0 = max(0, (oy - 96) // 16 * 16)
+    x1 = min(ea_w, O.align_up(ox + ow + 96))
+    y1 = min(ea_h, O.align_up(oy + oh + 96))
+    in_channels = 3 * (1 + (albedo is not None) + (normal is not None))
+    packed = O.pack_input(color, albedo, normal, x0, y0, x1 - x0, y1 - y0, True, 1.0, precision)
+    net = O.unet_forward_packed(ws, bs, packed, in_channels, precision)
+    out = np.full((img_h, img_w, 4), np.nan, np.float32)
+    O.unpack_output(net, ox - x0, oy - y0, color, ox, oy, ow, oh, True, 1.0, out)
+    return out[oy:oy + oh, ox:ox + ow]
+
+
+def test_config4_1080p_end_to_end_sampled():
+    """1920x1080 fp16, one 1920x1088 tile, HDR log with input scale 1:
+    the whole frame on the GPU; the oracle on sampled output rectangles."""
+    color, albedo, normal, ws, bs = make_case(1920, 1080)
+    got = gpu_denoise(ws, bs, color, albedo, normal, "f16", 0, 32)
+    assert not np.any(np.isnan(got))
+    assert np.array_equal(got[..., 3], color[..., 3])
+    for rect in [(0, 0, 48, 48), (1872, 1032, 48, 48), (944, 520, 32, 40), (1900, 300, 20, 16)]:
+        ref = _oracle_rect(ws, bs, color, albedo, normal, rect, "f16")
+        ox, oy, ow, oh = rect
+        err = rel_err(got[oy:oy + oh, ox:ox + ow], ref)
+        say(f"config4 rect {rect}: max_rel_err={err:.3e}")
+        assert err <= TOL["f16"]
+
+
+def test_config5_4k_tiled_sampled():
+    """3840x2160 fp16, max tile 1024, overlap 32 (12 tiles of 1024x784): the
+    oracle runs one whole tile of the same plan; another tile's interior is
+    checked against its own oracle window; the overlap-32 seam error against
+    a full-context reference is reported."""
+    color, albedo, normal, ws, bs = make_case(3840, 2160)
+    got = gpu_denoise(ws, bs, color, albedo, normal, "f16", 1024, 32)
+    assert not np.any(np.isnan(got))
+    tiles = U.oidn_plan_tiles(3840, 2160, 1024, 32)
+    assert len(tiles) == 12 and all(t[2:4] == (1024, 784) for t in tiles)
+    ix, iy, iw, ih, ox, oy, ow, oh = tiles[5]        # an interior tile
+    packed = O.pack_input(color, albedo, normal, ix, iy, iw, ih, True, 1.0, "f16")
+    net = O.unet_forward_packed(ws, bs, packed, 9, "f16")
+    ref = np.full((2160, 3840, 4), np.nan, np.float32)
+    O.unpack_output(net, ox - ix, oy - iy, color, ox, oy, ow, oh, True, 1.0, ref)
+    err = rel_err(got[oy:oy + oh, ox:ox + ow], ref[oy:oy + oh, ox:ox + ow])
+    say(f"config5 tile 5 (oracle, same plan): max_rel_err={err:.3e}")
+    assert err <= TOL["f16"]
+    # seam: the untiled answer near the tile border differs (overlap 32 < reach 94)
+    seam = _oracle_rect(ws, bs, color, albedo, normal, (ox, oy, 32, 32), "f16")
+    seam_err = rel_err(got[oy:oy + 32, ox:ox + 32], seam)
+    say(f"config5 overlap-32 seam error vs full context (reported, not a pass/fail): {seam_err:.3e}")
+
+
+def test_output_untouched_on_error():
+    color, albedo, normal, ws, bs = make_case(32, 32)
+    wd = packed_unet(ws, bs, 9, "f16")
+    out = empty((32, 32, 4), np.float32, fill=3.0)
+    work = empty((1024,), np.uint8)
+    with pytest.raises(U.OidnError) as e:
+        U.oidn_unet_forward(wd, 9, dev(color), dev(albedo), dev(normal), 32, 32, True,
+                            U.OIDN_TRANSFER_LOG, 1.0, 0, 32, work, 1024, out, U.OIDN_F16)
+    assert e.value.code == U.OIDN_E_WORKSPACE
+    assert np.all(host(out) == 3.0)

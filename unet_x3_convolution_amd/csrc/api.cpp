@@ -1,0 +1,814 @@
+// Host side of the C ABI: argument validation and error reporting, the tile
+// planner, weight packing, the liveness-planned UNet workspace and the
+// per-tile launch sequence.  Every device step is one of the HIP kernels in
+// this directory; nothing here computes on the host except packing weights.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/oidn_mi355x.h"
+#include "internal.h"
+
+using namespace oidn;
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int ok() {
+  g_error.clear();
+  return OIDN_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(OIDN_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_dtype(int dtype) {
+  if (dtype == OIDN_F32 || dtype == OIDN_F16) return OIDN_OK;
+  if (dtype == OIDN_BF16) return fail(OIDN_E_UNSUPPORTED, "bf16 storage is not supported by this build");
+  return fail(OIDN_E_INVALID, "unknown dtype %d", dtype);
+}
+
+size_t esize(int dtype) { return dtype == OIDN_F32 ? 4 : 2; }
+
+// ------------------------------------------------------------ tile planner
+struct Span { int in0, in_size, out0, out_size; };
+
+int align_up(int v, int a) { return (v + a - 1) / a * a; }
+
+int plan_axis(int extent, int tile, int overlap, std::vector<Span>& out) {
+  out.clear();
+  const int ea = align_up(extent, OIDN_TILE_ALIGN);
+  if (ea <= tile) {
+    out.push_back({0, ea, 0, extent});
+    return OIDN_OK;
+  }
+  const int step = tile - 2 * overlap;
+  if (step <= 0) return fail(OIDN_E_INVALID, "tile size %d must exceed twice the overlap %d", tile, overlap);
+  const int n = cdiv(extent, step);
+  const int span = align_up(cdiv(extent, n), OIDN_TILE_ALIGN);
+  const int size = span + 2 * overlap < ea ? span + 2 * overlap : ea;
+  for (int i = 0; i < n; ++i) {
+    const int o0 = i * span;
+    if (o0 >= extent) break;
+    const int o1 = o0 + span < extent ? o0 + span : extent;
+    int lo = o0 - overlap > 0 ? o0 - overlap : 0;
+    if (lo > ea - size) lo = ea - size;
+    out.push_back({lo, size, o0, o1 - o0});
+  }
+  return OIDN_OK;
+}
+
+int plan(int w, int h, int max_tile, int overlap, std::vector<oidn_tile>& tiles) {
+  if (w <= 0 || h <= 0) return fail(OIDN_E_INVALID, "image dimensions must be positive (got %dx%d)", w, h);
+  if (w > 65536 || h > 65536) return fail(OIDN_E_INVALID, "image dimensions above 65536 are not supported");
+  if (overlap < 0) overlap = OIDN_DEFAULT_OVERLAP;
+  if (overlap % OIDN_TILE_ALIGN) return fail(OIDN_E_INVALID, "overlap %d is not a multiple of 16", overlap);
+  if (max_tile < 0 || max_tile % OIDN_TILE_ALIGN)
+    return fail(OIDN_E_INVALID, "max tile size %d must be 0 or a positive multiple of 16", max_tile);
+  const int tile = max_tile > 0 ? max_tile : align_up(w > h ? w : h, OIDN_TILE_ALIGN);
+  std::vector<Span> xs, ys;
+  int rc = plan_axis(w, tile, overlap, xs);
+  if (rc) return rc;
+  rc = plan_axis(h, tile, overlap, ys);
+  if (rc) return rc;
+  tiles.clear();
+  for (const Span& y : ys)
+    for (const Span& x : xs)
+      tiles.push_back({x.in0, y.in0, x.in_size, y.in_size, x.out0, y.out0, x.out_size, y.out_size});
+  return OIDN_OK;
+}
+
+// ----------------------------------------------------------- conv helpers
+int conv_weights_bytes(int cin0, int cin1, int cout, int dtype, size_t* bytes) {
+  int rc = check_dtype(dtype);
+  if (rc) return rc;
+  if (cin0 <= 0 || cin1 < 0 || cout <= 0)
+    return fail(OIDN_E_INVALID, "channel counts must be positive (cin0=%d cin1=%d cout=%d)", cin0, cin1, cout);
+  if (cin0 > OIDN_MAX_SOURCE_CHANNELS || cin1 > OIDN_MAX_SOURCE_CHANNELS || cout > OIDN_MAX_OUT_CHANNELS)
+    return fail(OIDN_E_UNSUPPORTED, "channel counts above the limits (%d per source, %d out)",
+                OIDN_MAX_SOURCE_CHANNELS, OIDN_MAX_OUT_CHANNELS);
+  if (cin1 > 0 && cin0 % 4)
+    return fail(OIDN_E_INVALID, "the upsampled source needs a multiple of 4 channels (got %d)", cin0);
+  if (dtype == OIDN_F16) {
+    ConvLayout L;
+    if (!conv_f16_layout(stored_channels(cin0), cin1 ? stored_channels(cin1) : 0, cout, &L))
+      return fail(OIDN_E_UNSUPPORTED, "conv shape exceeds the fp16 kernel limits");
+    *bytes = L.bytes;
+  } else {
+    *bytes = conv_f32_bytes(stored_channels(cin0) + (cin1 ? stored_channels(cin1) : 0), cout);
+  }
+  return OIDN_OK;
+}
+
+// Host-side packing into `out` (sized by conv_weights_bytes).
+void pack_conv_host(const float* w, const float* b, int cin0, int cin1, int cout, int dtype,
+                    std::vector<unsigned char>& out) {
+  const int cin = cin0 + cin1;
+  const int cs0 = stored_channels(cin0), cs1 = cin1 ? stored_channels(cin1) : 0;
+  auto wat = [&](int o, int tap, int i) -> float {  // OHWI, logical channels
+    return w[((size_t)o * 9 + tap) * cin + i];
+  };
+  // logical input channel of stored channel `c` of source `s`, or -1
+  auto logical = [&](int s, int c) -> int {
+    if (s == 0) return c < cin0 ? c : -1;
+    return c < cin1 ? cin0 + c : -1;
+  };
+  std::fill(out.begin(), out.end(), 0);
+  if (dtype == OIDN_F16) {
+    ConvLayout L;
+    conv_f16_layout(cs0, cs1, cout, &L);
+    float* bias = reinterpret_cast<float*>(out.data());
+    for (int o = 0; o < cout; ++o) bias[o] = b[o];
+    _Float16* frag = reinterpret_cast<_Float16*>(out.data() + L.bias_bytes);
+    for (int ci = 0; ci < L.nchunks; ++ci) {
+      const ConvChunk& ch = L.chunk[ci];
+      for (int s = 0; s < ch.steps; ++s)
+        for (int q = 0; q < L.nf; ++q) {
+          _Float16* f = frag + ((size_t)(ch.wfrag + s * L.nf + q)) * (kFragBytes / 2);
+          for (int lane = 0; lane < 64; ++lane) {
+            const int r = lane & 15, grp4 = lane >> 4;
+            const int o = frag_row_to_cout(L.nf, q, r);
+            const int kg = 4 * s + grp4;
+            if (o >= cout || kg >= 9 * ch.cg) continue;
+            const int tap = kg / ch.cg, grp = kg % ch.cg;
+            for (int j = 0; j < 8; ++j) {
+              const int li = logical(ch.src, ch.coff + 8 * grp + j);
+              if (li >= 0) f[lane * 8 + j] = (_Float16)wat(o, tap, li);
+            }
+          }
+        }
+    }
+  } else {
+    const int cs = stored_channels(cout), cst = cs0 + cs1;
+    float* bias = reinterpret_cast<float*>(out.data());
+    for (int o = 0; o < cout; ++o) bias[o] = b[o];
+    float* wt = reinterpret_cast<float*>(out.data() + align256(sizeof(float) * cs));
+    for (int o = 0; o < cout; ++o)
+      for (int tap = 0; tap < 9; ++tap)
+        for (int c = 0; c < cst; ++c) {
+          const int li = c < cs0 ? logical(0, c) : logical(1, c - cs0);
+          if (li < 0) continue;
+          wt[(((size_t)(o / 4) * 9 + tap) * cst + c) * 4 + (o % 4)] = wat(o, tap, li);
+        }
+  }
+}
+
+// Validates and launches one conv.  Pointers already checked by the caller.
+int run_conv(const void* src0, int cin0, const void* src1, int cin1, bool upcat, int h, int w,
+             const void* wpk, void* y, int cout, int in_dtype, int out_dtype, unsigned flags,
+             hipStream_t stream) {
+  const bool pool = flags & OIDN_POOL2X2, relu = flags & OIDN_RELU;
+  hipError_t e;
+  if (in_dtype == OIDN_F16) {
+    ConvLayout L;
+    conv_f16_layout(stored_channels(cin0), cin1 ? stored_channels(cin1) : 0, cout, &L);
+    ConvF16Args a{};
+    a.src0 = src0;
+    a.src1 = src1;
+    a.cs0 = stored_channels(cin0);
+    a.cs1 = cin1 ? stored_channels(cin1) : 0;
+    a.h = h;
+    a.w = w;
+    a.bias = static_cast<const float*>(wpk);
+    a.wfrag = static_cast<const unsigned char*>(wpk) + L.bias_bytes;
+    a.y = y;
+    a.cout_stored = stored_channels(cout);
+    a.tiles_x = cdiv(w, 16);
+    a.tiles_y = cdiv(h, 16);
+    a.nchunks = L.nchunks;
+    for (int i = 0; i < L.nchunks; ++i) a.chunk[i] = L.chunk[i];
+    e = launch_conv_f16(a, L.nf, upcat, pool, relu, out_dtype == OIDN_F32, stream);
+  } else {
+    ConvF32Args a{};
+    a.src0 = static_cast<const float*>(src0);
+    a.src1 = static_cast<const float*>(src1);
+    a.cs0 = stored_channels(cin0);
+    a.cs1 = cin1 ? stored_channels(cin1) : 0;
+    a.h = h;
+    a.w = w;
+    a.bias = static_cast<const float*>(wpk);
+    a.wt = reinterpret_cast<const float*>(static_cast<const unsigned char*>(wpk) +
+                                          align256(sizeof(float) * stored_channels(cout)));
+    a.y = static_cast<float*>(y);
+    a.cout_stored = stored_channels(cout);
+    e = launch_conv_f32(a, upcat, pool, relu, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "conv3x3 launch");
+  return OIDN_OK;
+}
+
+int check_conv(int h, int w, int cin0, int cin1, int cout, int in_dtype, int out_dtype,
+               unsigned flags, bool upcat) {
+  int rc = check_dtype(in_dtype);
+  if (rc) return rc;
+  rc = check_dtype(out_dtype);
+  if (rc) return rc;
+  if (in_dtype == OIDN_F32 && out_dtype != OIDN_F32)
+    return fail(OIDN_E_UNSUPPORTED, "fp32 input needs fp32 output");
+  if (h <= 0 || w <= 0 || h > 65536 || w > 65536)
+    return fail(OIDN_E_INVALID, "conv size %dx%d out of range", w, h);
+  if (flags & ~(OIDN_RELU | OIDN_POOL2X2)) return fail(OIDN_E_INVALID, "unknown conv flags 0x%x", flags);
+  if ((flags & OIDN_POOL2X2) && (h % 2 || w % 2))
+    return fail(OIDN_E_INVALID, "fused 2x2 pool needs even sizes (got %dx%d)", w, h);
+  if (upcat && (h % 2 || w % 2))
+    return fail(OIDN_E_INVALID, "upsample-concat needs even sizes (got %dx%d)", w, h);
+  size_t bytes;
+  rc = conv_weights_bytes(cin0, cin1, cout, in_dtype, &bytes);
+  if (rc) return rc;
+  if ((double)h * w * (stored_channels(cin0) + stored_channels(cin1 > 0 ? cin1 : 0) + stored_channels(cout)) > 2.0e9)
+    return fail(OIDN_E_UNSUPPORTED, "tensor too large for 32-bit pixel indexing");
+  return OIDN_OK;
+}
+
+// ------------------------------------------------------------ UNet table
+struct Layer {
+  const char* name;
+  int src;     // value id: 0 = network input, k = output of layer k-1
+  int skip;    // value id or -1
+  int cout;
+  bool pool;
+  bool relu;
+};
+
+constexpr int kLayers = 16;
+const Layer kUNet[kLayers] = {
+    {"enc_conv0", 0, -1, 32, false, true},   {"enc_conv1", 1, -1, 32, true, true},
+    {"enc_conv2", 2, -1, 48, true, true},    {"enc_conv3", 3, -1, 64, true, true},
+    {"enc_conv4", 4, -1, 80, true, true},    {"enc_conv5a", 5, -1, 96, false, true},
+    {"enc_conv5b", 6, -1, 96, false, true},  {"dec_conv4a", 7, 4, 112, false, true},
+    {"dec_conv4b", 8, -1, 112, false, true}, {"dec_conv3a", 9, 3, 96, false, true},
+    {"dec_conv3b", 10, -1, 96, false, true}, {"dec_conv2a", 11, 2, 64, false, true},
+    {"dec_conv2b", 12, -1, 64, false, true}, {"dec_conv1a", 13, 0, 64, false, true},
+    {"dec_conv1b", 14, -1, 32, false, true}, {"dec_conv0", 15, -1, 3, false, false},
+};
+
+struct LayerShape {
+  int cin0, cin1, cout, level;  // level of the conv's output before pooling
+};
+
+bool unet_shapes(int in_channels, LayerShape* out) {
+  if (in_channels != 3 && in_channels != 6 && in_channels != 9) return false;
+  int ch[kLayers + 1], lvl[kLayers + 1];
+  ch[0] = in_channels;
+  lvl[0] = 0;
+  for (int i = 0; i < kLayers; ++i) {
+    const Layer& L = kUNet[i];
+    const int level = L.skip >= 0 ? lvl[L.skip] : lvl[L.src];
+    out[i] = {ch[L.src], L.skip >= 0 ? ch[L.skip] : 0, L.cout, level};
+    ch[i + 1] = L.cout;
+    lvl[i + 1] = level + (L.pool ? 1 : 0);
+  }
+  return true;
+}
+
+size_t unet_layer_offset(const LayerShape* s, int dtype, int layer) {
+  size_t off = 0;
+  for (int i = 0; i < layer; ++i) {
+    size_t b = 0;
+    conv_weights_bytes(s[i].cin0, s[i].cin1, s[i].cout, dtype, &b);
+    off += align256(b);
+  }
+  return off;
+}
+
+// Liveness-planned workspace ([web-0.4] NativeUNetExecutor._createExecution
+// reuses activation slots after a value's last use).  Values: 0 = input,
+// k = output of layer k-1 (pooled if the layer pools); the network output
+// (value 16) and, for the end-to-end call, the packed input are planned too
+// when `own_io` is set.  Greedy first fit in decreasing size.
+struct Plan {
+  size_t offset[kLayers + 1];
+  size_t bytes;
+};
+
+void plan_workspace(int in_channels, int tw, int th, int dtype, bool own_io, Plan* p) {
+  LayerShape s[kLayers];
+  unet_shapes(in_channels, s);
+  size_t size[kLayers + 1];
+  int def[kLayers + 1], last[kLayers + 1];
+  const size_t px0 = (size_t)tw * th;
+  size[0] = px0 * stored_channels(in_channels) * esize(dtype);
+  def[0] = -1;
+  last[0] = -1;
+  for (int i = 0; i < kLayers; ++i) {
+    const int lvl = s[i].level + (kUNet[i].pool ? 1 : 0);
+    const size_t px = px0 >> (2 * lvl);
+    const bool final_layer = i == kLayers - 1;
+    size[i + 1] = px * stored_channels(s[i].cout) * (final_layer ? 4 : esize(dtype));
+    def[i + 1] = i;
+    last[i + 1] = i;
+  }
+  for (int i = 0; i < kLayers; ++i) {
+    last[kUNet[i].src] = i > last[kUNet[i].src] ? i : last[kUNet[i].src];
+    if (kUNet[i].skip >= 0) last[kUNet[i].skip] = i > last[kUNet[i].skip] ? i : last[kUNet[i].skip];
+  }
+  last[kLayers] = kLayers;  // consumed by the output pass
+  bool placed[kLayers + 1] = {};
+  size_t end = 0;
+  for (int n = 0; n <= kLayers; ++n) {
+    int best = -1;
+    for (int v = 0; v <= kLayers; ++v) {
+      const bool external = !own_io && (v == 0 || v == kLayers);
+      if (placed[v] || external) continue;
+      if (best < 0 || size[v] > size[best]) best = v;
+    }
+    if (best < 0) break;
+    // candidate offsets: 0 and the end of every placed value alive at the same time
+    size_t chosen = (size_t)-1;
+    std::vector<size_t> cands{0};
+    for (int v = 0; v <= kLayers; ++v)
+      if (placed[v]) cands.push_back(p->offset[v] + align256(size[v]));
+    for (size_t c : cands) {
+      bool clash = false;
+      for (int v = 0; v <= kLayers && !clash; ++v) {
+        if (!placed[v]) continue;
+        const bool live = !(last[v] < def[best] || last[best] < def[v]);
+        const bool overlap = c < p->offset[v] + align256(size[v]) && p->offset[v] < c + align256(size[best]);
+        clash = live && overlap;
+      }
+      if (!clash && c < chosen) chosen = c;
+    }
+    p->offset[best] = chosen;
+    placed[best] = true;
+    if (chosen + align256(size[best]) > end) end = chosen + align256(size[best]);
+  }
+  p->bytes = end;
+}
+
+// Runs the sixteen convs of one tile.  events: optional, events[k] recorded
+// before layer k and events[16] after the last layer.
+int run_network(const unsigned char* weights, int in_channels, const void* packed_in, int tw,
+                int th, unsigned char* ws, const Plan& P, bool own_io, float* net_out, int dtype,
+                hipStream_t stream, void* const* events) {
+  LayerShape s[kLayers];
+  unet_shapes(in_channels, s);
+  const void* val[kLayers + 1];
+  val[0] = own_io ? ws + P.offset[0] : packed_in;
+  for (int i = 1; i <= kLayers; ++i) val[i] = ws + P.offset[i];
+  if (!own_io) val[kLayers] = net_out;
+  size_t woff = 0;
+  for (int i = 0; i < kLayers; ++i) {
+    const Layer& L = kUNet[i];
+    const int lvl = s[i].level;
+    const int h = th >> lvl, w = tw >> lvl;
+    if (events && events[i]) {
+      hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[i]), stream);
+      if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+    const unsigned flags = (L.relu ? OIDN_RELU : 0u) | (L.pool ? OIDN_POOL2X2 : 0u);
+    const int out_dtype = i == kLayers - 1 ? OIDN_F32 : dtype;
+    int rc = run_conv(val[L.src], s[i].cin0, L.skip >= 0 ? val[L.skip] : nullptr, s[i].cin1,
+                      L.skip >= 0, h, w, weights + woff, const_cast<void*>(val[i + 1]), s[i].cout,
+                      dtype, out_dtype, flags, stream);
+    if (rc) return rc;
+    size_t b = 0;
+    conv_weights_bytes(s[i].cin0, s[i].cin1, s[i].cout, dtype, &b);
+    woff += align256(b);
+  }
+  if (events && events[kLayers]) {
+    hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[kLayers]), stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  return OIDN_OK;
+}
+
+int check_network_tile(int in_channels, int tw, int th, int dtype) {
+  int rc = check_dtype(dtype);
+  if (rc) return rc;
+  if (in_channels != 3 && in_channels != 6 && in_channels != 9)
+    return fail(OIDN_E_INVALID, "input channels must be 3, 6 or 9 (got %d)", in_channels);
+  if (tw <= 0 || th <= 0 || tw % OIDN_TILE_ALIGN || th % OIDN_TILE_ALIGN)
+    return fail(OIDN_E_INVALID, "network tile %dx%d must be positive multiples of 16", tw, th);
+  if ((double)tw * th * 128 > 2.0e9) return fail(OIDN_E_UNSUPPORTED, "network tile %dx%d too large", tw, th);
+  return OIDN_OK;
+}
+
+int denoise(const void* d_weights, int in_channels, const float* color, const float* albedo,
+            const float* normal, int w, int h, int hdr, int transfer, float input_scale,
+            int max_tile, int overlap, void* workspace, size_t ws_bytes, float* out_rgba,
+            int dtype, hipStream_t stream, void* const* events, int n_events) {
+  if (!d_weights || !color || !workspace || !out_rgba)
+    return fail(OIDN_E_INVALID, "null weights, color, workspace or output pointer");
+  const int sources = 1 + (albedo != nullptr) + (normal != nullptr);
+  if (normal && !albedo) return fail(OIDN_E_INVALID, "a normal image needs an albedo image");
+  if (in_channels != 3 * sources)
+    return fail(OIDN_E_INVALID, "model expects %d input channels but %d images were given",
+                in_channels, sources);
+  if (transfer == OIDN_TRANSFER_PU && hdr)
+    return fail(OIDN_E_UNSUPPORTED, "the 'pu' transfer is not supported (formula unavailable)");
+  if (transfer != OIDN_TRANSFER_PU && transfer != OIDN_TRANSFER_LOG)
+    return fail(OIDN_E_INVALID, "unknown transfer %d", transfer);
+  if (hdr && !(input_scale > 0.f && input_scale < 3.402823466e+38f))
+    return fail(OIDN_E_INVALID, "input scale must be positive and finite");
+  if (events && n_events < kLayers + 3) return fail(OIDN_E_INVALID, "need at least 19 events");
+  if (!aligned16(color) || (albedo && !aligned16(albedo)) || (normal && !aligned16(normal)) ||
+      !aligned16(out_rgba) || !aligned16(workspace) || !aligned16(d_weights))
+    return fail(OIDN_E_INVALID, "device pointers must be 16-byte aligned");
+  std::vector<oidn_tile> tiles;
+  int rc = plan(w, h, max_tile, overlap, tiles);
+  if (rc) return rc;
+  int tw = 0, th = 0;
+  for (const oidn_tile& t : tiles) {
+    tw = t.in_w > tw ? t.in_w : tw;
+    th = t.in_h > th ? t.in_h : th;
+  }
+  rc = check_network_tile(in_channels, tw, th, dtype);
+  if (rc) return rc;
+  Plan P;
+  plan_workspace(in_channels, tw, th, dtype, true, &P);
+  if (ws_bytes < P.bytes)
+    return fail(OIDN_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, P.bytes);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  for (size_t k = 0; k < tiles.size(); ++k) {
+    const oidn_tile& t = tiles[k];
+    void* const* ev = (events && k == 0) ? events : nullptr;
+    hipError_t e;
+    if (ev && ev[0] && (e = hipEventRecord(static_cast<hipEvent_t>(ev[0]), stream)) != hipSuccess)
+      return hip_fail(e, "hipEventRecord");
+    PackArgs pa{};
+    pa.color = reinterpret_cast<const float4*>(color);
+    pa.albedo = reinterpret_cast<const float4*>(albedo);
+    pa.normal = reinterpret_cast<const float4*>(normal);
+    pa.img_w = w;
+    pa.img_h = h;
+    pa.tile_x = t.in_x;
+    pa.tile_y = t.in_y;
+    pa.tile_w = t.in_w;
+    pa.tile_h = t.in_h;
+    pa.hdr = hdr;
+    pa.input_scale = input_scale;
+    pa.sources = sources;
+    pa.packed = ws + P.offset[0];
+    if ((e = launch_pack(pa, dtype == OIDN_F16, stream)) != hipSuccess) return hip_fail(e, "pack launch");
+    rc = run_network(static_cast<const unsigned char*>(d_weights), in_channels, nullptr, t.in_w,
+                     t.in_h, ws, P, true, nullptr, dtype, stream, ev ? ev + 1 : nullptr);
+    if (rc) return rc;
+    UnpackArgs ua{};
+    ua.net = reinterpret_cast<const float4*>(ws + P.offset[kLayers]);
+    ua.tile_w = t.in_w;
+    ua.in_off_x = t.out_x - t.in_x;
+    ua.in_off_y = t.out_y - t.in_y;
+    ua.color = reinterpret_cast<const float4*>(color);
+    ua.img_w = w;
+    ua.out_x = t.out_x;
+    ua.out_y = t.out_y;
+    ua.out_w = t.out_w;
+    ua.out_h = t.out_h;
+    ua.hdr = hdr;
+    ua.input_scale = input_scale;
+    ua.out = reinterpret_cast<float4*>(out_rgba);
+    if ((e = launch_unpack(ua, stream)) != hipSuccess) return hip_fail(e, "unpack launch");
+    if (ev && ev[kLayers + 2] && (e = hipEventRecord(static_cast<hipEvent_t>(ev[kLayers + 2]), stream)) != hipSuccess)
+      return hip_fail(e, "hipEventRecord");
+  }
+  return ok();
+}
+
+int upload(const std::vector<unsigned char>& host, void* dst, hipStream_t stream) {
+  hipError_t e = hipMemcpyAsync(dst, host.data(), host.size(), hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "weight upload");
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "weight upload sync");
+  return OIDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* oidn_last_error(void) { return g_error.c_str(); }
+
+int oidn_version(void) { return 100; }
+
+int oidn_plan_tiles(int w, int h, int max_tile, int overlap, oidn_tile* tiles, int cap, int* count) {
+  if (!count) return fail(OIDN_E_INVALID, "null count pointer");
+  std::vector<oidn_tile> t;
+  int rc = plan(w, h, max_tile, overlap, t);
+  if (rc) return rc;
+  *count = (int)t.size();
+  if ((int)t.size() > cap) {
+    if (cap == 0 && tiles == nullptr) return ok();
+    return fail(OIDN_E_WORKSPACE, "%zu tiles do not fit in a capacity of %d", t.size(), cap);
+  }
+  if (!tiles) return fail(OIDN_E_INVALID, "null tiles pointer");
+  for (size_t i = 0; i < t.size(); ++i) tiles[i] = t[i];
+  return ok();
+}
+
+int oidn_conv3x3_weights_bytes(int cin0, int cin1, int cout, int dtype, size_t* bytes) {
+  if (!bytes) return fail(OIDN_E_INVALID, "null bytes pointer");
+  int rc = conv_weights_bytes(cin0, cin1, cout, dtype, bytes);
+  return rc ? rc : ok();
+}
+
+int oidn_conv3x3_pack_weights(const float* w_ohwi_host, const float* bias_host, int cin0, int cin1,
+                              int cout, int dtype, void* d_packed, hipStream_t stream) {
+  if (!w_ohwi_host || !bias_host || !d_packed) return fail(OIDN_E_INVALID, "null pointer");
+  size_t bytes;
+  int rc = conv_weights_bytes(cin0, cin1, cout, dtype, &bytes);
+  if (rc) return rc;
+  if (!aligned16(d_packed)) return fail(OIDN_E_INVALID, "packed weights must be 16-byte aligned");
+  std::vector<unsigned char> host(bytes);
+  pack_conv_host(w_ohwi_host, bias_host, cin0, cin1, cout, dtype, host);
+  rc = upload(host, d_packed, stream);
+  return rc ? rc : ok();
+}
+
+int oidn_conv3x3_pack_weights_host(const float* w_ohwi_host, const float* bias_host, int cin0,
+                                   int cin1, int cout, int dtype, void* host_packed) {
+  if (!w_ohwi_host || !bias_host || !host_packed) return fail(OIDN_E_INVALID, "null pointer");
+  size_t bytes;
+  int rc = conv_weights_bytes(cin0, cin1, cout, dtype, &bytes);
+  if (rc) return rc;
+  std::vector<unsigned char> host(bytes);
+  pack_conv_host(w_ohwi_host, bias_host, cin0, cin1, cout, dtype, host);
+  std::memcpy(host_packed, host.data(), bytes);
+  return ok();
+}
+
+int oidn_conv3x3(const void* x, int h, int w, int cin, const void* w_packed, void* y, int cout,
+                 int in_dtype, int out_dtype, unsigned flags, hipStream_t stream) {
+  if (!x || !w_packed || !y) return fail(OIDN_E_INVALID, "null pointer");
+  if (!aligned16(x) || !aligned16(w_packed) || !aligned16(y))
+    return fail(OIDN_E_INVALID, "device pointers must be 16-byte aligned");
+  int rc = check_conv(h, w, cin, 0, cout, in_dtype, out_dtype, flags, false);
+  if (rc) return rc;
+  rc = run_conv(x, cin, nullptr, 0, false, h, w, w_packed, y, cout, in_dtype, out_dtype, flags, stream);
+  return rc ? rc : ok();
+}
+
+int oidn_conv3x3_upcat(const void* low, int c_low, const void* skip, int c_skip, int h, int w,
+                       const void* w_packed, void* y, int cout, int in_dtype, int out_dtype,
+                       unsigned flags, hipStream_t stream) {
+  if (!low || !skip || !w_packed || !y) return fail(OIDN_E_INVALID, "null pointer");
+  if (!aligned16(low) || !aligned16(skip) || !aligned16(w_packed) || !aligned16(y))
+    return fail(OIDN_E_INVALID, "device pointers must be 16-byte aligned");
+  if (c_skip <= 0) return fail(OIDN_E_INVALID, "skip channels must be positive");
+  int rc = check_conv(h, w, c_low, c_skip, cout, in_dtype, out_dtype, flags, true);
+  if (rc) return rc;
+  rc = run_conv(low, c_low, skip, c_skip, true, h, w, w_packed, y, cout, in_dtype, out_dtype, flags,
+                stream);
+  return rc ? rc : ok();
+}
+
+int oidn_pool2x2(const void* x, int h, int w, int c, void* y, int dtype, hipStream_t stream) {
+  if (!x || !y) return fail(OIDN_E_INVALID, "null pointer");
+  int rc = check_dtype(dtype);
+  if (rc) return rc;
+  if (h <= 0 || w <= 0 || c <= 0 || h % 2 || w % 2)
+    return fail(OIDN_E_INVALID, "pool2x2 needs positive even sizes and channels (got %dx%dx%d)", w, h, c);
+  if (!aligned16(x) || !aligned16(y)) return fail(OIDN_E_INVALID, "device pointers must be 16-byte aligned");
+  if ((double)h * w * stored_channels(c) > 4.0e9) return fail(OIDN_E_UNSUPPORTED, "tensor too large");
+  hipError_t e = launch_pool(x, h, w, stored_channels(c), y, dtype == OIDN_F16, stream);
+  if (e != hipSuccess) return hip_fail(e, "pool launch");
+  return ok();
+}
+
+int oidn_upsample_concat(const void* low, int c_low, const void* skip, int c_skip, int h, int w,
+                         void* z, int dtype, hipStream_t stream) {
+  if (!low || !skip || !z) return fail(OIDN_E_INVALID, "null pointer");
+  int rc = check_dtype(dtype);
+  if (rc) return rc;
+  if (h <= 0 || w <= 0 || h % 2 || w % 2) return fail(OIDN_E_INVALID, "upsample-concat needs positive even sizes");
+  if (c_low <= 0 || c_skip <= 0 || c_low % 4)
+    return fail(OIDN_E_INVALID, "channels must be positive and the upsampled source a multiple of 4");
+  if (!aligned16(low) || !aligned16(skip) || !aligned16(z))
+    return fail(OIDN_E_INVALID, "device pointers must be 16-byte aligned");
+  if ((double)h * w * (c_low + stored_channels(c_skip)) > 4.0e9) return fail(OIDN_E_UNSUPPORTED, "tensor too large");
+  hipError_t e = launch_upcat(low, c_low, skip, stored_channels(c_skip), h, w, z, dtype == OIDN_F16, stream);
+  if (e != hipSuccess) return hip_fail(e, "upsample-concat launch");
+  return ok();
+}
+
+int oidn_pack_input(const float* color, const float* albedo, const float* normal, int img_w,
+                    int img_h, int tile_x, int tile_y, int tile_w, int tile_h, int hdr,
+                    int transfer, float input_scale, void* packed, int dtype, hipStream_t stream) {
+  if (!color || !packed) return fail(OIDN_E_INVALID, "null color or packed pointer");
+  if (normal && !albedo) return fail(OIDN_E_INVALID, "a normal image needs an albedo image");
+  int rc = check_dtype(dtype);
+  if (rc) return rc;
+  if (img_w <= 0 || img_h <= 0 || tile_w <= 0 || tile_h <= 0)
+    return fail(OIDN_E_INVALID, "image and tile dimensions must be positive");
+  if (img_w > 65536 || img_h > 65536 || tile_w > 65536 || tile_h > 65536)
+    return fail(OIDN_E_INVALID, "dimensions above 65536 are not supported");
+  if (transfer == OIDN_TRANSFER_PU && hdr)
+    return fail(OIDN_E_UNSUPPORTED, "the 'pu' transfer is not supported (formula unavailable)");
+  if (transfer != OIDN_TRANSFER_PU && transfer != OIDN_TRANSFER_LOG)
+    return fail(OIDN_E_INVALID, "unknown transfer %d", transfer);
+  if (hdr && !(input_scale > 0.f && input_scale < 3.402823466e+38f))
+    return fail(OIDN_E_INVALID, "input scale must be positive and finite");
+  if (!aligned16(color) || (albedo && !aligned16(albedo)) || (normal && !aligned16(normal)) || !aligned16(packed))
+    return fail(OIDN_E_INVALID, "device pointers must be 16-byte aligned");
+  PackArgs a{};
+  a.color = reinterpret_cast<const float4*>(color);
+  a.albedo = reinterpret_cast<const float4*>(albedo);
+  a.normal = reinterpret_cast<const float4*>(normal);
+  a.img_w = img_w;
+  a.img_h = img_h;
+  a.tile_x = tile_x;
+  a.tile_y = tile_y;
+  a.tile_w = tile_w;
+  a.tile_h = tile_h;
+  a.hdr = hdr;
+  a.input_scale = input_scale;
+  a.sources = 1 + (albedo != nullptr) + (normal != nullptr);
+  a.packed = packed;
+  hipError_t e = launch_pack(a, dtype == OIDN_F16, stream);
+  if (e != hipSuccess) return hip_fail(e, "pack launch");
+  return ok();
+}
+
+int oidn_unpack_output(const float* net_rgba, int tile_w, int tile_h, int in_off_x, int in_off_y,
+                       const float* color, int img_w, int img_h, int out_x, int out_y, int out_w,
+                       int out_h, int hdr, int transfer, float input_scale, float* out_rgba,
+                       hipStream_t stream) {
+  if (!net_rgba || !color || !out_rgba) return fail(OIDN_E_INVALID, "null pointer");
+  if (tile_w <= 0 || tile_h <= 0 || img_w <= 0 || img_h <= 0 || out_w <= 0 || out_h <= 0)
+    return fail(OIDN_E_INVALID, "dimensions must be positive");
+  if (in_off_x < 0 || in_off_y < 0 || in_off_x + out_w > tile_w || in_off_y + out_h > tile_h)
+    return fail(OIDN_E_INVALID, "output rectangle reads outside the tile");
+  if (out_x < 0 || out_y < 0 || out_x + out_w > img_w || out_y + out_h > img_h)
+    return fail(OIDN_E_INVALID, "output rectangle lies outside the image");
+  if (transfer == OIDN_TRANSFER_PU && hdr)
+    return fail(OIDN_E_UNSUPPORTED, "the 'pu' transfer is not supported (formula unavailable)");
+  if (transfer != OIDN_TRANSFER_PU && transfer != OIDN_TRANSFER_LOG)
+    return fail(OIDN_E_INVALID, "unknown transfer %d", transfer);
+  if (hdr && !(input_scale > 0.f && input_scale < 3.402823466e+38f))
+    return fail(OIDN_E_INVALID, "input scale must be positive and finite");
+  if (!aligned16(net_rgba) || !aligned16(color) || !aligned16(out_rgba))
+    return fail(OIDN_E_INVALID, "device pointers must be 16-byte aligned");
+  UnpackArgs a{};
+  a.net = reinterpret_cast<const float4*>(net_rgba);
+  a.tile_w = tile_w;
+  a.in_off_x = in_off_x;
+  a.in_off_y = in_off_y;
+  a.color = reinterpret_cast<const float4*>(color);
+  a.img_w = img_w;
+  a.out_x = out_x;
+  a.out_y = out_y;
+  a.out_w = out_w;
+  a.out_h = out_h;
+  a.hdr = hdr;
+  a.input_scale = input_scale;
+  a.out = reinterpret_cast<float4*>(out_rgba);
+  hipError_t e = launch_unpack(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "unpack launch");
+  return ok();
+}
+
+int oidn_unet_layer_count(void) { return kLayers; }
+
+int oidn_unet_layer_info(int in_channels, int layer, int* cin0, int* cin1, int* cout, int* level,
+                         unsigned* flags, const char** name) {
+  LayerShape s[kLayers];
+  if (!unet_shapes(in_channels, s)) return fail(OIDN_E_INVALID, "input channels must be 3, 6 or 9");
+  if (layer < 0 || layer >= kLayers) return fail(OIDN_E_INVALID, "layer %d out of range", layer);
+  if (cin0) *cin0 = s[layer].cin0;
+  if (cin1) *cin1 = s[layer].cin1;
+  if (cout) *cout = s[layer].cout;
+  if (level) *level = s[layer].level;
+  if (flags) *flags = (kUNet[layer].relu ? OIDN_RELU : 0u) | (kUNet[layer].pool ? OIDN_POOL2X2 : 0u);
+  if (name) *name = kUNet[layer].name;
+  return ok();
+}
+
+int oidn_unet_weights_bytes(int in_channels, int dtype, size_t* bytes) {
+  if (!bytes) return fail(OIDN_E_INVALID, "null bytes pointer");
+  int rc = check_dtype(dtype);
+  if (rc) return rc;
+  LayerShape s[kLayers];
+  if (!unet_shapes(in_channels, s)) return fail(OIDN_E_INVALID, "input channels must be 3, 6 or 9");
+  *bytes = unet_layer_offset(s, dtype, kLayers);
+  return ok();
+}
+
+int oidn_unet_pack_weights(const float* const* w_ohwi_host, const float* const* bias_host,
+                           int in_channels, int dtype, void* d_weights, hipStream_t stream) {
+  if (!w_ohwi_host || !bias_host || !d_weights) return fail(OIDN_E_INVALID, "null pointer");
+  int rc = check_dtype(dtype);
+  if (rc) return rc;
+  LayerShape s[kLayers];
+  if (!unet_shapes(in_channels, s)) return fail(OIDN_E_INVALID, "input channels must be 3, 6 or 9");
+  if (!aligned16(d_weights)) return fail(OIDN_E_INVALID, "weights must be 16-byte aligned");
+  for (int i = 0; i < kLayers; ++i)
+    if (!w_ohwi_host[i] || !bias_host[i]) return fail(OIDN_E_INVALID, "null weights of layer %d", i);
+  std::vector<unsigned char> all(unet_layer_offset(s, dtype, kLayers), 0);
+  size_t off = 0;
+  for (int i = 0; i < kLayers; ++i) {
+    size_t b = 0;
+    conv_weights_bytes(s[i].cin0, s[i].cin1, s[i].cout, dtype, &b);
+    std::vector<unsigned char> one(b);
+    pack_conv_host(w_ohwi_host[i], bias_host[i], s[i].cin0, s[i].cin1, s[i].cout, dtype, one);
+    std::memcpy(all.data() + off, one.data(), b);
+    off += align256(b);
+  }
+  rc = upload(all, d_weights, stream);
+  return rc ? rc : ok();
+}
+
+int oidn_unet_packed_workspace_bytes(int in_channels, int tw, int th, int dtype, size_t* bytes) {
+  if (!bytes) return fail(OIDN_E_INVALID, "null bytes pointer");
+  int rc = check_network_tile(in_channels, tw, th, dtype);
+  if (rc) return rc;
+  Plan P;
+  plan_workspace(in_channels, tw, th, dtype, false, &P);
+  *bytes = P.bytes;
+  return ok();
+}
+
+int oidn_unet_forward_packed(const void* d_weights, int in_channels, const void* packed_in, int tw,
+                             int th, void* workspace, size_t ws_bytes, float* net_out_rgba,
+                             int dtype, hipStream_t stream) {
+  if (!d_weights || !packed_in || !workspace || !net_out_rgba) return fail(OIDN_E_INVALID, "null pointer");
+  int rc = check_network_tile(in_channels, tw, th, dtype);
+  if (rc) return rc;
+  if (!aligned16(d_weights) || !aligned16(packed_in) || !aligned16(workspace) || !aligned16(net_out_rgba))
+    return fail(OIDN_E_INVALID, "device pointers must be 16-byte aligned");
+  Plan P;
+  plan_workspace(in_channels, tw, th, dtype, false, &P);
+  if (ws_bytes < P.bytes)
+    return fail(OIDN_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, P.bytes);
+  rc = run_network(static_cast<const unsigned char*>(d_weights), in_channels, packed_in, tw, th,
+                   static_cast<unsigned char*>(workspace), P, false, net_out_rgba, dtype, stream, nullptr);
+  return rc ? rc : ok();
+}
+
+int oidn_unet_workspace_bytes(int in_channels, int w, int h, int max_tile, int overlap, int dtype,
+                              size_t* bytes) {
+  if (!bytes) return fail(OIDN_E_INVALID, "null bytes pointer");
+  std::vector<oidn_tile> tiles;
+  int rc = plan(w, h, max_tile, overlap, tiles);
+  if (rc) return rc;
+  int tw = 0, th = 0;
+  for (const oidn_tile& t : tiles) {
+    tw = t.in_w > tw ? t.in_w : tw;
+    th = t.in_h > th ? t.in_h : th;
+  }
+  rc = check_network_tile(in_channels, tw, th, dtype);
+  if (rc) return rc;
+  Plan P;
+  plan_workspace(in_channels, tw, th, dtype, true, &P);
+  *bytes = P.bytes;
+  return ok();
+}
+
+int oidn_unet_forward(const void* d_weights, int in_channels, const float* color, const float* albedo,
+                      const float* normal, int w, int h, int hdr, int transfer, float input_scale,
+                      int max_tile, int overlap, void* workspace, size_t ws_bytes, float* out_rgba,
+                      int dtype, hipStream_t stream) {
+  return denoise(d_weights, in_channels, color, albedo, normal, w, h, hdr, transfer, input_scale,
+                 max_tile, overlap, workspace, ws_bytes, out_rgba, dtype, stream, nullptr, 0);
+}
+
+int oidn_unet_forward_timed(const void* d_weights, int in_channels, const float* color,
+                            const float* albedo, const float* normal, int w, int h, int hdr,
+                            int transfer, float input_scale, int max_tile, int overlap,
+                            void* workspace, size_t ws_bytes, float* out_rgba, int dtype,
+                            hipStream_t stream, void* const* events, int n_events) {
+  if (!events) return fail(OIDN_E_INVALID, "null events");
+  return denoise(d_weights, in_channels, color, albedo, normal, w, h, hdr, transfer, input_scale,
+                 max_tile, overlap, workspace, ws_bytes, out_rgba, dtype, stream, events, n_events);
+}
+
+int oidn_event_create(void** event) {
+  if (!event) return fail(OIDN_E_INVALID, "null event pointer");
+  hipEvent_t e;
+  hipError_t r = hipEventCreate(&e);
+  if (r != hipSuccess) return hip_fail(r, "hipEventCreate");
+  *event = e;
+  return ok();
+}
+
+int oidn_event_destroy(void* event) {
+  if (!event) return fail(OIDN_E_INVALID, "null event");
+  hipError_t r = hipEventDestroy(static_cast<hipEvent_t>(event));
+  if (r != hipSuccess) return hip_fail(r, "hipEventDestroy");
+  return ok();
+}
+
+int oidn_event_elapsed_ms(void* start, void* end, float* ms) {
+  if (!start || !end || !ms) return fail(OIDN_E_INVALID, "null pointer");
+  hipError_t r = hipEventSynchronize(static_cast<hipEvent_t>(end));
+  if (r != hipSuccess) return hip_fail(r, "hipEventSynchronize");
+  r = hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(end));
+  if (r != hipSuccess) return hip_fail(r, "hipEventElapsedTime");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,207 @@
+// Bandwidth-bound passes: input pack, output unpack, 2x2 max-pool and the
+// materialised nearest-2x upsample + concat.  One thread per output pixel (or
+// per 4-channel block), consecutive threads on consecutive addresses, 16-byte
+// loads where the layout allows.
+#include "internal.h"
+
+namespace oidn {
+namespace {
+
+constexpr int THREADS = 256;
+constexpr float kFltMax = 3.402823466e+38f;
+
+// NaN -> 0, otherwise clamp to [lo, hi] (reading of the pages' sanitize()).
+__device__ __forceinline__ float sanitize(float v, float lo, float hi) {
+  if (v != v) return 0.f;
+  return fminf(fmaxf(v, lo), hi);
+}
+
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+// [webgpu-0.6] inputShader ("oidn-webgpu 0.0.0-stage -> 0.6.0",
+// native/denoise.ts): clamp-to-edge read, sanitize, HDR log transfer of the
+// scaled colour, normals to [0, 1], channels packed densely into 4-lane
+// blocks with zero lanes ([web-0.4] createInputPackShader lane rule).
+template <bool F16>
+__global__ __launch_bounds__(THREADS) void pack_input_kernel(PackArgs a) {
+  const int t = blockIdx.x * THREADS + threadIdx.x;
+  if (t >= a.tile_w * a.tile_h) return;
+  const int ty = t / a.tile_w, tx = t - ty * a.tile_w;
+  const int sy = min(max(ty + a.tile_y, 0), a.img_h - 1);
+  const int sx = min(max(tx + a.tile_x, 0), a.img_w - 1);
+  const size_t src = (size_t)sy * a.img_w + sx;
+  float ch[12];
+#pragma unroll
+  for (int i = 0; i < 12; ++i) ch[i] = 0.f;
+  const float4 col = a.color[src];
+  if (a.hdr) {
+    const float s = a.input_scale;
+    ch[0] = log1pf(sanitize(col.x * s, 0.f, kFltMax));
+    ch[1] = log1pf(sanitize(col.y * s, 0.f, kFltMax));
+    ch[2] = log1pf(sanitize(col.z * s, 0.f, kFltMax));
+  } else {
+    ch[0] = sanitize(col.x, 0.f, 1.f);
+    ch[1] = sanitize(col.y, 0.f, 1.f);
+    ch[2] = sanitize(col.z, 0.f, 1.f);
+  }
+  if (a.sources > 1) {
+    const float4 al = a.albedo[src];
+    ch[3] = sanitize(al.x, 0.f, 1.f);
+    ch[4] = sanitize(al.y, 0.f, 1.f);
+    ch[5] = sanitize(al.z, 0.f, 1.f);
+  }
+  if (a.sources > 2) {
+    const float4 nr = a.normal[src];
+    ch[6] = sanitize(nr.x, -1.f, 1.f) * 0.5f + 0.5f;
+    ch[7] = sanitize(nr.y, -1.f, 1.f) * 0.5f + 0.5f;
+    ch[8] = sanitize(nr.z, -1.f, 1.f) * 0.5f + 0.5f;
+  }
+  const int nblk = a.sources == 1 ? 1 : (a.sources == 2 ? 2 : 3);
+  if constexpr (F16) {
+    uint2* out = static_cast<uint2*>(a.packed) + (size_t)t * nblk;
+#pragma unroll
+    for (int b = 0; b < 3; ++b)
+      if (b < nblk) out[b] = make_uint2(pack_h2(ch[4 * b], ch[4 * b + 1]), pack_h2(ch[4 * b + 2], ch[4 * b + 3]));
+  } else {
+    float4* out = static_cast<float4*>(a.packed) + (size_t)t * nblk;
+#pragma unroll
+    for (int b = 0; b < 3; ++b)
+      if (b < nblk) out[b] = make_float4(ch[4 * b], ch[4 * b + 1], ch[4 * b + 2], ch[4 * b + 3]);
+  }
+}
+
+// [webgpu-0.6] outputShader: sanitize the network RGB, invert the transfer and
+// the input scale, alpha from the input colour; only the output rectangle.
+__global__ __launch_bounds__(THREADS) void unpack_output_kernel(UnpackArgs a) {
+  const int t = blockIdx.x * THREADS + threadIdx.x;
+  if (t >= a.out_w * a.out_h) return;
+  const int y = t / a.out_w, x = t - y * a.out_w;
+  const float4 net = a.net[(size_t)(y + a.in_off_y) * a.tile_w + x + a.in_off_x];
+  const size_t o = (size_t)(y + a.out_y) * a.img_w + x + a.out_x;
+  const float alpha = a.color[o].w;
+  float4 r;
+  if (a.hdr) {
+    const float s = a.input_scale;
+    r.x = expm1f(sanitize(net.x, 0.f, kFltMax)) / s;
+    r.y = expm1f(sanitize(net.y, 0.f, kFltMax)) / s;
+    r.z = expm1f(sanitize(net.z, 0.f, kFltMax)) / s;
+  } else {
+    r.x = sanitize(net.x, 0.f, 1.f);
+    r.y = sanitize(net.y, 0.f, 1.f);
+    r.z = sanitize(net.z, 0.f, 1.f);
+  }
+  r.w = alpha;
+  a.out[o] = r;
+}
+
+// [web-0.4] createMaxPoolShader / [web-0.5] coalesced "channels" pool: one
+// thread per (output pixel, 4-channel block), threads of a wave walk the
+// blocks of consecutive pixels.
+template <bool F16>
+__global__ __launch_bounds__(THREADS) void pool2x2_kernel(const void* x, int h, int w, int cs,
+                                                          void* y) {
+  const int nb = cs / 4;
+  const int ow = w >> 1, oh = h >> 1;
+  const size_t t = (size_t)blockIdx.x * THREADS + threadIdx.x;
+  if (t >= (size_t)ow * oh * nb) return;
+  const int b = (int)(t % nb);
+  const size_t pix = t / nb;
+  const int ox = (int)(pix % ow), oy = (int)(pix / ow);
+  const size_t i00 = ((size_t)(2 * oy) * w + 2 * ox) * nb + b;
+  const size_t i01 = i00 + nb;
+  const size_t i10 = i00 + (size_t)w * nb;
+  const size_t i11 = i10 + nb;
+  if constexpr (F16) {
+    typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+    const half4* in = static_cast<const half4*>(x);
+    const half4 a0 = in[i00], a1 = in[i01], a2 = in[i10], a3 = in[i11];
+    half4 m;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = fmaxf(fmaxf((float)a0[i], (float)a1[i]), fmaxf((float)a2[i], (float)a3[i]));
+      m[i] = (_Float16)v;  // exact: v is one of the fp16 inputs
+    }
+    static_cast<half4*>(y)[t] = m;
+  } else {
+    const float4* in = static_cast<const float4*>(x);
+    const float4 a0 = in[i00], a1 = in[i01], a2 = in[i10], a3 = in[i11];
+    float4 m;
+    m.x = fmaxf(fmaxf(a0.x, a1.x), fmaxf(a2.x, a3.x));
+    m.y = fmaxf(fmaxf(a0.y, a1.y), fmaxf(a2.y, a3.y));
+    m.z = fmaxf(fmaxf(a0.z, a1.z), fmaxf(a2.z, a3.z));
+    m.w = fmaxf(fmaxf(a0.w, a1.w), fmaxf(a2.w, a3.w));
+    static_cast<float4*>(y)[t] = m;
+  }
+}
+
+// Materialised [up(low) | skip]: one thread per (pixel, 4-channel block of
+// the concat); a block is 8 bytes (fp16) or 16 bytes (fp32).
+template <typename Block>
+__global__ __launch_bounds__(THREADS) void upcat_kernel(const Block* low, int nb_low,
+                                                        const Block* skip, int nb_skip, int h,
+                                                        int w, Block* z) {
+  const int nb = nb_low + nb_skip;
+  const size_t t = (size_t)blockIdx.x * THREADS + threadIdx.x;
+  if (t >= (size_t)h * w * nb) return;
+  const int b = (int)(t % nb);
+  const size_t pix = t / nb;
+  const int x = (int)(pix % w), y = (int)(pix / w);
+  Block v;
+  if (b < nb_low)
+    v = low[((size_t)(y >> 1) * (w >> 1) + (x >> 1)) * nb_low + b];
+  else
+    v = skip[pix * nb_skip + (b - nb_low)];
+  z[t] = v;
+}
+
+inline dim3 grid_for(size_t n) { return dim3((unsigned)((n + THREADS - 1) / THREADS)); }
+
+}  // namespace
+
+hipError_t launch_pack(const PackArgs& a, bool f16, hipStream_t stream) {
+  const size_t n = (size_t)a.tile_w * a.tile_h;
+  if (n == 0) return hipSuccess;
+  if (f16)
+    hipLaunchKernelGGL(pack_input_kernel<true>, grid_for(n), dim3(THREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL(pack_input_kernel<false>, grid_for(n), dim3(THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack(const UnpackArgs& a, hipStream_t stream) {
+  const size_t n = (size_t)a.out_w * a.out_h;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(unpack_output_kernel, grid_for(n), dim3(THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool(const void* x, int h, int w, int cs, void* y, bool f16, hipStream_t stream) {
+  const size_t n = (size_t)(w / 2) * (h / 2) * (cs / 4);
+  if (n == 0) return hipSuccess;
+  if (f16)
+    hipLaunchKernelGGL(pool2x2_kernel<true>, grid_for(n), dim3(THREADS), 0, stream, x, h, w, cs, y);
+  else
+    hipLaunchKernelGGL(pool2x2_kernel<false>, grid_for(n), dim3(THREADS), 0, stream, x, h, w, cs, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_upcat(const void* low, int cs_low, const void* skip, int cs_skip, int h, int w,
+                        void* z, bool f16, hipStream_t stream) {
+  const int nb = (cs_low + cs_skip) / 4;
+  const size_t n = (size_t)h * w * nb;
+  if (n == 0) return hipSuccess;
+  if (f16)
+    hipLaunchKernelGGL(upcat_kernel<uint2>, grid_for(n), dim3(THREADS), 0, stream,
+                       static_cast<const uint2*>(low), cs_low / 4, static_cast<const uint2*>(skip),
+                       cs_skip / 4, h, w, static_cast<uint2*>(z));
+  else
+    hipLaunchKernelGGL(upcat_kernel<float4>, grid_for(n), dim3(THREADS), 0, stream,
+                       static_cast<const float4*>(low), cs_low / 4, static_cast<const float4*>(skip),
+                       cs_skip / 4, h, w, static_cast<float4*>(z));
+  return hipGetLastError();
+}
+
+}  // namespace oidn

@@ -1,0 +1,122 @@
+// Internal declarations shared by the host C-ABI code and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace oidn {
+
+constexpr int kMaxChunks = 20;        // 32-channel K chunks per conv (two sources)
+constexpr int kChunkChannels = 32;    // channels of one LDS-staged K chunk
+constexpr int kFragBytes = 1024;      // one 16x32 fp16 MFMA operand fragment (64 lanes x 16 B)
+
+inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+inline int stored_channels(int c) { return 4 * cdiv(c, 4); }
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// ---------------------------------------------------------------------------
+// fp16 MFMA implicit-GEMM conv.
+//
+// K runs over (input channel chunk, tap, 8-channel group).  A chunk covers up
+// to 32 stored channels of one source (cg = 1..4 groups of 8 channels); its
+// 9 * cg (tap, group) pairs are consumed four per MFMA step, one per 16-lane
+// group, so a step count is ceil(9 * cg / 4).
+// ---------------------------------------------------------------------------
+struct ConvChunk {
+  int src;    // 0: first source (upsampled source for the decoder), 1: skip
+  int coff;   // first stored channel of the chunk within its source
+  int cg;     // 8-channel groups in the chunk (1..4)
+  int steps;  // MFMA K steps of the chunk
+  int wfrag;  // index of the chunk's first weight fragment
+};
+
+struct ConvLayout {           // shared by the weight packer and the launcher
+  int nf;                     // 16-row output-channel fragments (N = 16 * nf)
+  int nchunks;
+  int total_steps;
+  ConvChunk chunk[kMaxChunks];
+  size_t bias_bytes;          // fp32 bias, 16 * nf floats, 256-aligned
+  size_t bytes;               // bias + fragments
+};
+
+// Computes the fp16 layout; returns false if the shape exceeds the limits.
+bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out);
+
+// Row r (0..15) of fragment q holds output channel
+//   4 * nf * (r / 4) + 4 * q + (r % 4)
+// so that the 16-lane group g of the accumulator owns the 4 * nf contiguous
+// channels [4 * nf * g, 4 * nf * (g + 1)).
+inline int frag_row_to_cout(int nf, int q, int r) { return 4 * nf * (r / 4) + 4 * q + (r % 4); }
+
+struct ConvF16Args {
+  const void* src0;   // fp16, h x w (or h/2 x w/2 when upsampled) x cs0
+  const void* src1;   // fp16, h x w x cs1 (skip), may be null
+  int cs0, cs1;       // stored channels per source
+  int h, w;           // conv input == output size before pooling
+  const float* bias;  // 16 * nf floats
+  const void* wfrag;  // fragments
+  void* y;
+  int cout_stored;
+  int tiles_x, tiles_y;
+  int nchunks;
+  ConvChunk chunk[kMaxChunks];
+};
+
+hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, bool relu,
+                           bool out_f32, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// fp32 direct conv (VALU FMA).  Packed weights: bias (cout_stored floats,
+// 256-aligned) then [out block][tap][stored input channel over both
+// sources][4 output lanes].
+// ---------------------------------------------------------------------------
+struct ConvF32Args {
+  const float* src0;
+  const float* src1;
+  int cs0, cs1;
+  int h, w;
+  const float* bias;
+  const float* wt;
+  float* y;
+  int cout_stored;
+};
+
+size_t conv_f32_bytes(int cin_stored_total, int cout);
+hipError_t launch_conv_f32(const ConvF32Args& a, bool upcat, bool pool, bool relu,
+                           hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Elementwise / gather passes.
+// ---------------------------------------------------------------------------
+struct PackArgs {
+  const float4* color;
+  const float4* albedo;
+  const float4* normal;
+  int img_w, img_h;
+  int tile_x, tile_y, tile_w, tile_h;
+  int hdr;
+  float input_scale;
+  int sources;       // 1, 2 or 3
+  void* packed;
+};
+hipError_t launch_pack(const PackArgs& a, bool f16, hipStream_t stream);
+
+struct UnpackArgs {
+  const float4* net;
+  int tile_w;
+  int in_off_x, in_off_y;
+  const float4* color;
+  int img_w;
+  int out_x, out_y, out_w, out_h;
+  int hdr;
+  float input_scale;
+  float4* out;
+};
+hipError_t launch_unpack(const UnpackArgs& a, hipStream_t stream);
+
+hipError_t launch_pool(const void* x, int h, int w, int cs, void* y, bool f16, hipStream_t stream);
+hipError_t launch_upcat(const void* low, int cs_low, const void* skip, int cs_skip, int h, int w,
+                        void* z, bool f16, hipStream_t stream);
+
+}  // namespace oidn
