@@ -100,13 +100,30 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise OidnError(OIDN_E_HIP, f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        # torch ships its own HIP runtime with the same soname; loading torch
+        # first makes the library bind to that one instead of mapping a second
+        # runtime (which would see no device and could not use torch's memory).
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
+        _check_single_hip_runtime()
         for name, (args, res) in _SIGS.items():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = res
         _lib = L
     return _lib
+
+
+def _check_single_hip_runtime():
+    try:
+        maps = open("/proc/self/maps").read()
+    except OSError:
+        return
+    runtimes = {line.split()[-1] for line in maps.splitlines()
+                if "libamdhip64" in line and line.split()[-1].startswith("/")}
+    if len(runtimes) > 1:
+        raise OidnError(OIDN_E_HIP, "two HIP runtimes are loaded in this process: "
+                        + ", ".join(sorted(runtimes)))
 
 
 def last_error() -> str:
