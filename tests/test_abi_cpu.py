@@ -79,43 +79,49 @@ def test_layer_table_matches_oracle(in_channels):
 def _decode_f16(packed, cin0, cin1, cout):
     """Decode the fp16 fragment layout from its documented description:
     bias (16 * nf floats, 256-aligned), then per chunk (<= 32 stored channels
-    of one source; sources in order), per K step, per output fragment q, a
-    1 KB fragment of 64 lanes x 8 halves; lane l holds row r = l % 16 (output
-    channel 4 * nf * (r // 4) + 4 * q + r % 4) and K group kg = 4 * step + l // 16
-    of the chunk, kg = tap * cg + group, channels coff + 8 * group + j."""
+    of one source, processed as cg = 4 groups of 8 channels if it holds more
+    than 16, else cg = 2; all cg = 4 chunks first, then the cg = 2 ones, each
+    in source order), per column group j, per ky, per output
+    fragment q, a 1 KB fragment of 64 lanes x 8 halves; lane l holds row
+    r = l % 16 (output channel 4 * nf * (r // 4) + 4 * q + r % 4) and slot
+    4 * j + l // 16 of the chunk, slot = kx * cg + group, channels
+    coff + 8 * group + 0..7."""
     cs = [O.stored(cin0), O.stored(cin1) if cin1 else 0]
     nf = -(-O.stored(cout) // 16)
     bias_bytes = -(-(4 * 16 * nf) // 256) * 256
     bias = packed[:4 * cout].view(np.float32)
     frags = packed[bias_bytes:].view(np.float16).reshape(-1, 64, 8)
-    w = np.full((cout, 9, cin0 + cin1), np.nan, np.float32)
+    w = np.full((cout, 3, 3, cin0 + cin1), np.nan, np.float32)
+    chunks = [(s_idx, off, 4 if min(32, cs[s_idx] - off) > 16 else 2)
+              for s_idx in range(2) for off in range(0, cs[s_idx], 32)]
+    chunks = [c for c in chunks if c[2] == 4] + [c for c in chunks if c[2] == 2]
     f = 0
-    for s_idx in range(2):
-        for off in range(0, cs[s_idx], 32):
-            cg = -(-min(32, cs[s_idx] - off) // 8)
-            steps = -(-9 * cg // 4)
-            for st in range(steps):
-                for q in range(nf):
-                    frag = frags[f]
-                    f += 1
-                    for lane in range(64):
-                        r, kg = lane % 16, 4 * st + lane // 16
-                        o = 4 * nf * (r // 4) + 4 * q + r % 4
-                        vals = frag[lane].astype(np.float32)
-                        if o >= cout or kg >= 9 * cg:
-                            assert np.all(vals == 0)
-                            continue
-                        tap, grp = divmod(kg, cg)
-                        for j in range(8):
-                            c = off + 8 * grp + j
-                            logical = c if s_idx == 0 else cin0 + c
-                            limit = cin0 if s_idx == 0 else cin1
-                            if c < limit:
-                                w[o, tap, logical] = vals[j]
-                            else:
-                                assert vals[j] == 0
+    for s_idx, off, cg in chunks:
+        if True:
+            ncg = -(-3 * cg // 4)
+            for j in range(ncg):
+                for ky in range(3):
+                    for q in range(nf):
+                        frag = frags[f]
+                        f += 1
+                        for lane in range(64):
+                            r, slot = lane % 16, 4 * j + lane // 16
+                            o = 4 * nf * (r // 4) + 4 * q + r % 4
+                            vals = frag[lane].astype(np.float32)
+                            if o >= cout or slot >= 3 * cg:
+                                assert np.all(vals == 0)
+                                continue
+                            kx, grp = divmod(slot, cg)
+                            for jj in range(8):
+                                c = off + 8 * grp + jj
+                                logical = c if s_idx == 0 else cin0 + c
+                                limit = cin0 if s_idx == 0 else cin1
+                                if c < limit:
+                                    w[o, ky, kx, logical] = vals[jj]
+                                else:
+                                    assert vals[jj] == 0
     assert f == frags.shape[0]
-    return w.reshape(cout, 3, 3, cin0 + cin1), bias
+    return w, bias
 
 
 @pytest.mark.parametrize("cin0,cin1,cout", [(9, 0, 32), (32, 0, 48), (64, 9, 64), (96, 64, 112),

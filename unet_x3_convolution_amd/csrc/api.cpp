@@ -138,21 +138,22 @@ void pack_conv_host(const float* w, const float* b, int cin0, int cin1, int cout
     _Float16* frag = reinterpret_cast<_Float16*>(out.data() + L.bias_bytes);
     for (int ci = 0; ci < L.nchunks; ++ci) {
       const ConvChunk& ch = L.chunk[ci];
-      for (int s = 0; s < ch.steps; ++s)
-        for (int q = 0; q < L.nf; ++q) {
-          _Float16* f = frag + ((size_t)(ch.wfrag + s * L.nf + q)) * (kFragBytes / 2);
-          for (int lane = 0; lane < 64; ++lane) {
-            const int r = lane & 15, grp4 = lane >> 4;
-            const int o = frag_row_to_cout(L.nf, q, r);
-            const int kg = 4 * s + grp4;
-            if (o >= cout || kg >= 9 * ch.cg) continue;
-            const int tap = kg / ch.cg, grp = kg % ch.cg;
-            for (int j = 0; j < 8; ++j) {
-              const int li = logical(ch.src, ch.coff + 8 * grp + j);
-              if (li >= 0) f[lane * 8 + j] = (_Float16)wat(o, tap, li);
+      for (int j = 0; j < ch.ncg; ++j)
+        for (int ky = 0; ky < 3; ++ky)
+          for (int q = 0; q < L.nf; ++q) {
+            _Float16* f = frag + ((size_t)(ch.wfrag + (j * 3 + ky) * L.nf + q)) * (kFragBytes / 2);
+            for (int lane = 0; lane < 64; ++lane) {
+              const int r = lane & 15, slot = 4 * j + (lane >> 4);
+              const int o = frag_row_to_cout(L.nf, q, r);
+              if (o >= cout || slot >= 3 * ch.cg) continue;
+              const int kx = slot / ch.cg, grp = slot % ch.cg;
+              const int tap = 3 * ky + kx;
+              for (int jj = 0; jj < 8; ++jj) {
+                const int li = logical(ch.src, ch.coff + 8 * grp + jj);
+                if (li >= 0) f[lane * 8 + jj] = (_Float16)wat(o, tap, li);
+              }
             }
           }
-        }
     }
   } else {
     const int cs = stored_channels(cout), cst = cs0 + cs1;
@@ -189,9 +190,8 @@ int run_conv(const void* src0, int cin0, const void* src1, int cin1, bool upcat,
     a.wfrag = static_cast<const unsigned char*>(wpk) + L.bias_bytes;
     a.y = y;
     a.cout_stored = stored_channels(cout);
-    a.tiles_x = cdiv(w, 16);
-    a.tiles_y = cdiv(h, 16);
     a.nchunks = L.nchunks;
+    a.nchunks4 = L.nchunks4;
     for (int i = 0; i < L.nchunks; ++i) a.chunk[i] = L.chunk[i];
     e = launch_conv_f16(a, L.nf, upcat, pool, relu, out_dtype == OIDN_F32, stream);
   } else {

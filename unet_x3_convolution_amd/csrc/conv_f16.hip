@@ -8,23 +8,32 @@
 // skip] and optionally followed by a 2x2 max-pool.  The tiling is our own:
 //
 //  * GEMM roles: D[cout][pixel] = A[cout][k] * B[k][pixel].  A holds packed
-//    weights, B is read straight from an LDS halo patch (no im2col), so each
-//    lane of the 16x16 accumulator owns 4 consecutive output channels of one
-//    pixel (a whole 4-lane channel block, stored with one 8-byte write).
-//  * K is (input chunk of <= 32 channels) x (tap) x (8-channel group).  One
-//    MFMA step eats four (tap, group) pairs, one per 16-lane group, so thin
-//    inputs (12 channels) fold several taps into one instruction instead of
-//    zero-padding channels to 32.
-//  * A workgroup of 4 waves computes a 16 x 16 pixel tile for all output
-//    channels; wave w owns rows 4w..4w+3 (one 16-pixel B fragment per row).
-//    Per chunk, the (16 + 2) x (16 + 2) halo patch is staged in LDS once
-//    (80-byte pixel stride: conflict-free 16-byte fragment reads); the
-//    decoder's upsampled source is gathered at (y >> 1, x >> 1) while staging.
-//  * Epilogue: bias, ReLU, then either the store or the fused 2x2 pool: the
-//    vertical pair sits in two rows held by the same lane, the horizontal pair
-//    in neighbouring lanes (one DPP swap).  Max is taken in fp32 before the
-//    single fp16 rounding; RNE is monotone, so this equals pooling the rounded
-//    conv output.
+//    weights (read from global memory, L2/L1 resident), B is read straight
+//    from an LDS halo patch (no im2col), so each lane of a 16x16 accumulator
+//    owns 4 consecutive output channels of one pixel -- a whole 4-lane channel
+//    block, stored with one 8-byte write.
+//  * A workgroup of 4 waves computes a (4 R) x 16 pixel tile for all output
+//    channels; wave w owns R consecutive rows, one 16-pixel B fragment each.
+//  * K order: chunk (<= 32 channels of one source, staged in LDS once) ->
+//    column group (four (kx, 8-channel group) slots, one per 16-lane group)
+//    -> ky.  All lanes of a column group read the same patch row, so the B
+//    fragment of patch row p serves output rows p, p - 1 and p - 2 with the
+//    weights of ky = 0, 1, 2: R + 2 fragment loads per column group instead
+//    of 3 R.  Thin inputs (12 channels) put two kx columns in one MFMA
+//    instead of padding channels to 32.
+//  * The decoder's upsampled source is gathered at (y >> 1, x >> 1) while
+//    staging; the skip follows as further chunks (concat order [up, skip]).
+//  * Epilogue: bias, ReLU, then the store or the fused 2x2 pool: the vertical
+//    pair sits in two rows held by the same lane, the horizontal pair in
+//    neighbouring lanes (one DPP swap).  Max is taken in fp32 before the
+//    single fp16 rounding; RNE is monotone, so this equals pooling the
+//    rounded conv output.
+//  * Tiles are dealt to blocks so that each of the 8 XCDs walks a contiguous
+//    band of tiles (halo rows shared through its own L2).
+//
+// The per-pixel reduction order depends only on the channel layout, never on
+// the pixel position or the image size, so tiled and untiled runs agree bit
+// for bit wherever their inputs agree.
 #include "internal.h"
 
 namespace oidn {
@@ -33,81 +42,96 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int TH = 16, TW = 16;               // output tile
-constexpr int PH = TH + 2, PW = TW + 2;       // halo patch
-constexpr int PSTR = 40;                      // halves per patch pixel (32 + 8 pad)
-constexpr int PATCH_HALVES = PH * PW * PSTR;
-constexpr int ZERO_OFF = PATCH_HALVES;        // 8 zero halves: B operand of padding K slots
+constexpr int TW = 16;                        // tile width (one B fragment)
+constexpr int PW = TW + 2;                    // patch width
+constexpr int PSTR = 40;                      // halves per patch pixel: 32 + 8 pad (80 B)
 constexpr int THREADS = 256;
+constexpr int kXcds = 8;
 
-__device__ __forceinline__ half8 as_half8(uint4 v) {
-  return __builtin_bit_cast(half8, v);
-}
+template <int R>
+struct Tile {
+  static constexpr int TH = 4 * R;
+  static constexpr int PH = TH + 2;
+  static constexpr int PATCH = PH * PW * PSTR;   // halves
+  static constexpr int ZERO = PATCH;             // 8 zero halves after the patch
+};
 
-// Stage the chunk's halo patch: CG groups of 8 channels per pixel, moved in
-// 4-channel (8-byte) units; channels past the source's stored count and
-// pixels outside the image are zero.
-template <int CG>
+__device__ __forceinline__ half8 as_half8(uint4 v) { return __builtin_bit_cast(half8, v); }
+
+// Stage one chunk's halo patch.  VEC16: channels move in 8-channel (16 B)
+// units, else in 4-channel (8 B) units.  Channels past the source's stored
+// count and pixels outside the image are zero.
+template <int R, int CG, bool VEC16>
 __device__ __forceinline__ void stage_patch(_Float16* lds, const _Float16* src, int cs, int coff,
                                             bool up, int h, int w, int y0, int x0, int tid) {
-  constexpr int UNITS = 2 * CG;
+  constexpr int PH = Tile<R>::PH;
+  constexpr int UNITS = VEC16 ? CG : 2 * CG;
+  constexpr int UCH = VEC16 ? 8 : 4;
   constexpr int TOTAL = PH * PW * UNITS;
   const int sw = up ? (w >> 1) : w;
+#pragma unroll 4
   for (int u = tid; u < TOTAL; u += THREADS) {
     const int pp = u / UNITS;
-    const int q4 = u - pp * UNITS;
+    const int q = u - pp * UNITS;
     const int py = pp / PW;
     const int px = pp - py * PW;
     const int iy = y0 - 1 + py;
     const int ix = x0 - 1 + px;
-    const int c4 = coff + 4 * q4;
-    uint2 v = make_uint2(0u, 0u);
-    if (iy >= 0 && iy < h && ix >= 0 && ix < w && c4 < cs) {
-      const int sy = up ? (iy >> 1) : iy;
-      const int sx = up ? (ix >> 1) : ix;
-      v = *reinterpret_cast<const uint2*>(src + ((size_t)sy * sw + sx) * cs + c4);
+    const int c = coff + UCH * q;
+    const bool inside = iy >= 0 && iy < h && ix >= 0 && ix < w && c < cs;
+    const int sy = up ? (iy >> 1) : iy;
+    const int sx = up ? (ix >> 1) : ix;
+    const _Float16* p = src + ((size_t)sy * sw + sx) * cs + c;
+    if constexpr (VEC16) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (inside) v = *reinterpret_cast<const uint4*>(p);
+      *reinterpret_cast<uint4*>(lds + pp * PSTR + UCH * q) = v;
+    } else {
+      uint2 v = make_uint2(0u, 0u);
+      if (inside) v = *reinterpret_cast<const uint2*>(p);
+      *reinterpret_cast<uint2*>(lds + pp * PSTR + UCH * q) = v;
     }
-    *reinterpret_cast<uint2*>(lds + pp * PSTR + 4 * q4) = v;
   }
 }
 
-template <int NF, int CG>
-__device__ __forceinline__ void mma_chunk(floatx4 (&acc)[4][NF], const _Float16* lds,
+// MFMAs of one chunk for one wave: rows [R * wave, R * wave + R) of the tile.
+template <int NF, int R, int CG>
+__device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NF], const _Float16* lds,
                                           const uint4* wchunk, int wave, int g, int c) {
-  constexpr int STEPS = (9 * CG + 3) / 4;
-  uint4 afr[NF];
-#pragma unroll
-  for (int q = 0; q < NF; ++q) afr[q] = wchunk[q * 64];
-#pragma unroll
-  for (int s = 0; s < STEPS; ++s) {
-    uint4 anext[NF];
-    if (s + 1 < STEPS) {
-#pragma unroll
-      for (int q = 0; q < NF; ++q) anext[q] = wchunk[((s + 1) * NF + q) * 64];
-    }
-    const int kg = 4 * s + g;
-    int boff = ZERO_OFF, rstride = 0;
-    if (kg < 9 * CG) {
-      const int tap = kg / CG;
-      const int grp = kg - tap * CG;
-      const int ky = tap / 3;
-      const int kx = tap - 3 * ky;
-      boff = ((4 * wave + ky) * PW + c + kx) * PSTR + 8 * grp;
+  constexpr int NCG = (3 * CG + 3) / 4;
+#pragma unroll 1
+  for (int j = 0; j < NCG; ++j) {
+    const int slot = 4 * j + g;
+    int base = Tile<R>::ZERO, rstride = 0;
+    if (slot < 3 * CG) {
+      const int kx = slot / CG;
+      const int grp = slot - kx * CG;
+      base = ((R * wave) * PW + c + kx) * PSTR + 8 * grp;
       rstride = PW * PSTR;
     }
+    uint4 a[3][NF];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const half8 b = *reinterpret_cast<const half8*>(lds + boff + r * rstride);
+    for (int ky = 0; ky < 3; ++ky)
 #pragma unroll
-      for (int q = 0; q < NF; ++q)
-        acc[r][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(afr[q]), b, acc[r][q], 0, 0, 0);
-    }
-    if (s + 1 < STEPS) {
+      for (int q = 0; q < NF; ++q) a[ky][q] = wchunk[((j * 3 + ky) * NF + q) * 64];
 #pragma unroll
-      for (int q = 0; q < NF; ++q) afr[q] = anext[q];
+    for (int p = 0; p < R + 2; ++p) {
+      const half8 b = *reinterpret_cast<const half8*>(lds + base + p * rstride);
+#pragma unroll
+      for (int ky = 0; ky < 3; ++ky) {
+        const int r = p - ky;
+        if (r >= 0 && r < R) {
+#pragma unroll
+          for (int q = 0; q < NF; ++q)
+            acc[r][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(a[ky][q]), b, acc[r][q],
+                                                               0, 0, 0);
+        }
+      }
     }
   }
 }
+
+__device__ __forceinline__ float act(float v, int relu) { return relu ? fmaxf(v, 0.f) : v; }
 
 __device__ __forceinline__ float swap_pair(float v) {
   // DPP quad_perm [1, 0, 3, 2]: exchange with the neighbouring lane.
@@ -127,47 +151,56 @@ __device__ __forceinline__ void store4(void* y, size_t idx, float v0, float v1, 
   }
 }
 
-template <int NF, bool OUTF32>
-__global__ __launch_bounds__(THREADS) void conv3x3_f16_mfma(ConvF16Args a, int upcat, int pool,
-                                                             int relu) {
-  __shared__ __attribute__((aligned(16))) _Float16 lds[PATCH_HALVES + 8];
+template <int NF, int R, bool OUTF32>
+__global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(ConvF16Args a, int upcat, int pool,
+                                                                int relu) {
+  using T = Tile<R>;
+  __shared__ __attribute__((aligned(16))) _Float16 lds[T::PATCH + 8];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;
-  const int tile = blockIdx.x;
+
+  // XCD-aware tile order: block b runs on XCD b % 8; give each XCD a band.
+  const int ntiles = a.tiles_x * a.tiles_y;
+  const int per = (ntiles + kXcds - 1) / kXcds;
+  const int tile = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  if (tile >= ntiles) return;
   const int ty = tile / a.tiles_x;
   const int tx = tile - ty * a.tiles_x;
-  const int y0 = ty * TH, x0 = tx * TW;
+  const int y0 = ty * T::TH, x0 = tx * TW;
 
-  if (tid < 2) reinterpret_cast<uint2*>(lds + ZERO_OFF)[tid] = make_uint2(0u, 0u);
+  if (tid < 2) reinterpret_cast<uint2*>(lds + T::ZERO)[tid] = make_uint2(0u, 0u);
 
-  floatx4 acc[4][NF];
+  floatx4 acc[R][NF];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int q = 0; q < NF; ++q) acc[r][q] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const uint4* wf = static_cast<const uint4*>(a.wfrag);
-  for (int ci = 0; ci < a.nchunks; ++ci) {
+#pragma unroll 1
+  for (int ci = 0; ci < a.nchunks4; ++ci) {
     const ConvChunk ch = a.chunk[ci];
     const _Float16* src = static_cast<const _Float16*>(ch.src ? a.src1 : a.src0);
     const int cs = ch.src ? a.cs1 : a.cs0;
     const bool up = upcat && ch.src == 0;
     __syncthreads();
-    switch (ch.cg) {
-      case 1: stage_patch<1>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid); break;
-      case 2: stage_patch<2>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid); break;
-      case 3: stage_patch<3>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid); break;
-      default: stage_patch<4>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid); break;
-    }
+    if ((cs & 7) == 0) stage_patch<R, 4, true>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid);
+    else stage_patch<R, 4, false>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid);
     __syncthreads();
-    const uint4* wchunk = wf + (size_t)ch.wfrag * 64 + lane;
-    switch (ch.cg) {
-      case 1: mma_chunk<NF, 1>(acc, lds, wchunk, wave, g, c); break;
-      case 2: mma_chunk<NF, 2>(acc, lds, wchunk, wave, g, c); break;
-      case 3: mma_chunk<NF, 3>(acc, lds, wchunk, wave, g, c); break;
-      default: mma_chunk<NF, 4>(acc, lds, wchunk, wave, g, c); break;
-    }
+    mma_chunk<NF, R, 4>(acc, lds, wf + (size_t)ch.wfrag * 64 + lane, wave, g, c);
+  }
+#pragma unroll 1
+  for (int ci = a.nchunks4; ci < a.nchunks; ++ci) {
+    const ConvChunk ch = a.chunk[ci];
+    const _Float16* src = static_cast<const _Float16*>(ch.src ? a.src1 : a.src0);
+    const int cs = ch.src ? a.cs1 : a.cs0;
+    const bool up = upcat && ch.src == 0;
+    __syncthreads();
+    if ((cs & 7) == 0) stage_patch<R, 2, true>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid);
+    else stage_patch<R, 2, false>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid);
+    __syncthreads();
+    mma_chunk<NF, R, 2>(acc, lds, wf + (size_t)ch.wfrag * 64 + lane, wave, g, c);
   }
 
   // Epilogue.  Lane (g, c) holds rows 4g..4g+3 of every fragment: output
@@ -178,43 +211,34 @@ __global__ __launch_bounds__(THREADS) void conv3x3_f16_mfma(ConvF16Args a, int u
   for (int q = 0; q < NF; ++q)
 #pragma unroll
     for (int i = 0; i < 4; ++i) bv[q][i] = a.bias[cbase + 4 * q + i];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int q = 0; q < NF; ++q)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = acc[r][q][i] + bv[q][i];
-        acc[r][q][i] = relu ? fmaxf(v, 0.f) : v;
-      }
-
   const int x = x0 + c;
+  const int yb = y0 + R * wave;
   if (!pool) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int yy = y0 + 4 * wave + r;
+    for (int r = 0; r < R; ++r) {
+      const int yy = yb + r;
       if (yy < a.h && x < a.w) {
         const size_t base = ((size_t)yy * a.w + x) * a.cout_stored + cbase;
 #pragma unroll
         for (int q = 0; q < NF; ++q)
           if (cbase + 4 * q < a.cout_stored)
-            store4<OUTF32>(a.y, base + 4 * q, acc[r][q][0], acc[r][q][1], acc[r][q][2],
-                           acc[r][q][3]);
+            store4<OUTF32>(a.y, base + 4 * q, act(acc[r][q][0] + bv[q][0], relu), act(acc[r][q][1] + bv[q][1], relu), act(acc[r][q][2] + bv[q][2], relu),
+                           act(acc[r][q][3] + bv[q][3], relu));
       }
     }
   } else {
     const int ow = a.w >> 1;
 #pragma unroll
-    for (int rp = 0; rp < 2; ++rp) {
+    for (int rp = 0; rp < R / 2; ++rp) {
       float m[NF][4];
 #pragma unroll
       for (int q = 0; q < NF; ++q)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float v = fmaxf(acc[2 * rp][q][i], acc[2 * rp + 1][q][i]);
+          const float v = act(fmaxf(acc[2 * rp][q][i], acc[2 * rp + 1][q][i]) + bv[q][i], relu);
           m[q][i] = fmaxf(v, swap_pair(v));
         }
-      const int yy = y0 + 4 * wave + 2 * rp;
+      const int yy = yb + 2 * rp;
       if ((c & 1) == 0 && yy < a.h && x < a.w) {
         const size_t base = ((size_t)(yy >> 1) * ow + (x >> 1)) * a.cout_stored + cbase;
 #pragma unroll
@@ -226,17 +250,32 @@ __global__ __launch_bounds__(THREADS) void conv3x3_f16_mfma(ConvF16Args a, int u
   }
 }
 
+template <int NF, int R>
+hipError_t launch_shape(ConvF16Args a, bool upcat, bool pool, bool relu, bool out_f32,
+                        hipStream_t stream) {
+  a.tiles_x = cdiv(a.w, TW);
+  a.tiles_y = cdiv(a.h, Tile<R>::TH);
+  const int ntiles = a.tiles_x * a.tiles_y;
+  const dim3 grid(cdiv(ntiles, kXcds) * kXcds), block(THREADS);
+  if (out_f32)
+    hipLaunchKernelGGL((conv3x3_f16_mfma<NF, R, true>), grid, block, 0, stream, a, (int)upcat,
+                       (int)pool, (int)relu);
+  else
+    hipLaunchKernelGGL((conv3x3_f16_mfma<NF, R, false>), grid, block, 0, stream, a, (int)upcat,
+                       (int)pool, (int)relu);
+  return hipGetLastError();
+}
+
+// Rows per wave: 8 where the accumulators fit (nf <= 4) and the image gives
+// at least two 32 x 16 tiles per CU, else 4.
 template <int NF>
 hipError_t launch_nf(const ConvF16Args& a, bool upcat, bool pool, bool relu, bool out_f32,
                      hipStream_t stream) {
-  const dim3 grid(a.tiles_x * a.tiles_y), block(THREADS);
-  if (out_f32)
-    hipLaunchKernelGGL((conv3x3_f16_mfma<NF, true>), grid, block, 0, stream, a, (int)upcat,
-                       (int)pool, (int)relu);
-  else
-    hipLaunchKernelGGL((conv3x3_f16_mfma<NF, false>), grid, block, 0, stream, a, (int)upcat,
-                       (int)pool, (int)relu);
-  return hipGetLastError();
+  if constexpr (NF <= 4) {
+    const long tiles8 = (long)cdiv(a.w, TW) * cdiv(a.h, 32);
+    if (tiles8 >= 512) return launch_shape<NF, 8>(a, upcat, pool, relu, out_f32, stream);
+  }
+  return launch_shape<NF, 4>(a, upcat, pool, relu, out_f32, stream);
 }
 
 }  // namespace
@@ -245,24 +284,35 @@ bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out
   ConvLayout L{};
   L.nf = cdiv(stored_channels(cout), 16);
   if (L.nf < 1 || L.nf > 8) return false;
-  int frag = 0, steps_total = 0, n = 0;
+  // Chunks of up to 32 channels per source; a chunk is processed as 4 groups
+  // of 8 channels if it holds more than 16, else as 2 (missing channels are
+  // zero).  Four-group chunks come first, then two-group chunks, each in
+  // source order: the kernel runs them in two loops of one shape each.
+  ConvChunk full[kMaxChunks], half[kMaxChunks];
+  int nfull = 0, nhalf = 0;
   const int cs[2] = {cin0_stored, cin1_stored};
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < 2; ++s)
     for (int off = 0; off < cs[s]; off += kChunkChannels) {
-      if (n >= kMaxChunks) return false;
-      ConvChunk& ch = L.chunk[n++];
+      const int rem = cs[s] - off < kChunkChannels ? cs[s] - off : kChunkChannels;
+      ConvChunk ch{};
       ch.src = s;
       ch.coff = off;
-      const int rem = cs[s] - off < kChunkChannels ? cs[s] - off : kChunkChannels;
-      ch.cg = cdiv(rem, 8);
-      ch.steps = cdiv(9 * ch.cg, 4);
-      ch.wfrag = frag;
-      frag += ch.steps * L.nf;
-      steps_total += ch.steps;
+      ch.cg = rem > 16 ? 4 : 2;
+      ch.ncg = cdiv(3 * ch.cg, 4);
+      if (nfull + nhalf >= kMaxChunks) return false;
+      if (ch.cg == 4) full[nfull++] = ch;
+      else half[nhalf++] = ch;
     }
+  int frag = 0, n = 0;
+  for (int i = 0; i < nfull + nhalf; ++i) {
+    ConvChunk ch = i < nfull ? full[i] : half[i - nfull];
+    ch.wfrag = frag;
+    frag += ch.ncg * 3 * L.nf;
+    L.chunk[n++] = ch;
   }
   L.nchunks = n;
-  L.total_steps = steps_total;
+  L.nchunks4 = nfull;
+  L.total_frags = frag;
   L.bias_bytes = align256(sizeof(float) * 16 * L.nf);
   L.bytes = L.bias_bytes + (size_t)frag * kFragBytes;
   *out = L;

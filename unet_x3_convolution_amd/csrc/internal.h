@@ -18,23 +18,32 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // ---------------------------------------------------------------------------
 // fp16 MFMA implicit-GEMM conv.
 //
-// K runs over (input channel chunk, tap, 8-channel group).  A chunk covers up
-// to 32 stored channels of one source (cg = 1..4 groups of 8 channels); its
-// 9 * cg (tap, group) pairs are consumed four per MFMA step, one per 16-lane
-// group, so a step count is ceil(9 * cg / 4).
+// K runs over (input chunk of <= 32 stored channels of one source) x (column
+// group) x (ky).  Inside a chunk of cg 8-channel groups the 3 * cg
+// (kx, group) "slots" are dealt four at a time (slot = kx * cg + group) to
+// the four 16-lane groups of an MFMA operand; such a set of four slots is a
+// column group (ncg = ceil(3 * cg / 4) per chunk), and each column group is
+// repeated for ky = 0, 1, 2.  Because every lane of one column group reads
+// the same patch row, one B fragment loaded from LDS serves three output
+// rows (one per ky).
 // ---------------------------------------------------------------------------
 struct ConvChunk {
   int src;    // 0: first source (upsampled source for the decoder), 1: skip
   int coff;   // first stored channel of the chunk within its source
-  int cg;     // 8-channel groups in the chunk (1..4)
-  int steps;  // MFMA K steps of the chunk
+  int cg;     // 8-channel groups the chunk is processed as (2 or 4)
+  int ncg;    // column groups of the chunk: ceil(3 * cg / 4)
   int wfrag;  // index of the chunk's first weight fragment
 };
 
+// Weight fragment of (chunk, column group j, ky, output fragment q):
+//   chunk.wfrag + (j * 3 + ky) * nf + q
+// 64 lanes x 8 halves; lane l holds output row r = l % 16 and slot
+// 4 * j + l / 16 of the chunk, channels coff + 8 * group + 0..7.
 struct ConvLayout {           // shared by the weight packer and the launcher
   int nf;                     // 16-row output-channel fragments (N = 16 * nf)
   int nchunks;
-  int total_steps;
+  int nchunks4;                // chunks processed as 4 groups (they come first)
+  int total_frags;
   ConvChunk chunk[kMaxChunks];
   size_t bias_bytes;          // fp32 bias, 16 * nf floats, 256-aligned
   size_t bytes;               // bias + fragments
@@ -60,6 +69,7 @@ struct ConvF16Args {
   int cout_stored;
   int tiles_x, tiles_y;
   int nchunks;
+  int nchunks4;
   ConvChunk chunk[kMaxChunks];
 };
 
