@@ -61,6 +61,8 @@ F16_CASES = [
     (1, 1, 4, 4, 0, "f16"),
     (2, 2, 8, 16, U.OIDN_RELU | U.OIDN_POOL2X2, "f32"),
     (70, 3, 96, 96, U.OIDN_RELU, "f16"),
+    (512, 1024, 32, 32, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),   # 32-row tiles, all fragments
+    (520, 1030, 12, 64, U.OIDN_RELU, "f16"),                    # 32-row tiles, ragged edges
 ]
 
 
@@ -132,6 +134,7 @@ UPCAT_CASES = [
     (20, 12, 8, 5, 16, "f16"),
     (18, 26, 112, 48, 96, "f16"),
     (12, 10, 16, 9, 8, "f32"),
+    (512, 1024, 64, 9, 64, "f16"),                              # 32-row tiles
 ]
 
 

@@ -94,13 +94,26 @@ __device__ __forceinline__ void stage_patch(_Float16* lds, const _Float16* src, 
   }
 }
 
-// MFMAs of one chunk for one wave: rows [R * wave, R * wave + R) of the tile.
-template <int NF, int R, int CG>
-__device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NF], const _Float16* lds,
-                                          const uint4* wchunk, int wave, int g, int c) {
+// MFMAs of one chunk for one wave: rows [R * wave, R * wave + R) of the
+// tile, output fragments [q0, q0 + NFW) of nf.  `acur` holds the chunk's
+// column-group-0 weights on entry; each column group loads the next one's
+// weights (or those of the next chunk, `wnext`) before its MFMAs, so weight
+// loads overlap the matrix work.  On return `acur` holds the next chunk's.
+template <int NFW, int R, int CG>
+__device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], uint4 (&acur)[3][NFW],
+                                          const _Float16* lds, const uint4* wchunk,
+                                          const uint4* wnext, int nf, int wave, int g, int c) {
   constexpr int NCG = (3 * CG + 3) / 4;
 #pragma unroll 1
   for (int j = 0; j < NCG; ++j) {
+    const uint4* wn = j + 1 < NCG ? wchunk + (size_t)(j + 1) * 3 * nf * 64 : wnext;
+    uint4 anext[3][NFW];
+    if (wn) {
+#pragma unroll
+      for (int ky = 0; ky < 3; ++ky)
+#pragma unroll
+        for (int q = 0; q < NFW; ++q) anext[ky][q] = wn[(ky * nf + q) * 64];
+    }
     const int slot = 4 * j + g;
     int base = Tile<R>::ZERO, rstride = 0;
     if (slot < 3 * CG) {
@@ -109,11 +122,6 @@ __device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NF], const _Float16*
       base = ((R * wave) * PW + c + kx) * PSTR + 8 * grp;
       rstride = PW * PSTR;
     }
-    uint4 a[3][NF];
-#pragma unroll
-    for (int ky = 0; ky < 3; ++ky)
-#pragma unroll
-      for (int q = 0; q < NF; ++q) a[ky][q] = wchunk[((j * 3 + ky) * NF + q) * 64];
 #pragma unroll
     for (int p = 0; p < R + 2; ++p) {
       const half8 b = *reinterpret_cast<const half8*>(lds + base + p * rstride);
@@ -122,11 +130,17 @@ __device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NF], const _Float16*
         const int r = p - ky;
         if (r >= 0 && r < R) {
 #pragma unroll
-          for (int q = 0; q < NF; ++q)
-            acc[r][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(a[ky][q]), b, acc[r][q],
-                                                               0, 0, 0);
+          for (int q = 0; q < NFW; ++q)
+            acc[r][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(acur[ky][q]), b,
+                                                               acc[r][q], 0, 0, 0);
         }
       }
+    }
+    if (wn) {
+#pragma unroll
+      for (int ky = 0; ky < 3; ++ky)
+#pragma unroll
+        for (int q = 0; q < NFW; ++q) acur[ky][q] = anext[ky][q];
     }
   }
 }
@@ -151,14 +165,16 @@ __device__ __forceinline__ void store4(void* y, size_t idx, float v0, float v1, 
   }
 }
 
-template <int NF, int R, bool OUTF32>
-__global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(ConvF16Args a, int upcat, int pool,
-                                                                int relu) {
+template <int NFW, int R, bool OUTF32>
+__global__ __launch_bounds__(THREADS, (NFW * R <= 16) ? 2 : 1) void conv3x3_f16_mfma(
+    ConvF16Args a, int upcat, int pool, int relu) {
   using T = Tile<R>;
   __shared__ __attribute__((aligned(16))) _Float16 lds[T::PATCH + 8];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;
+  const int nf = a.nf;
+  const int q0 = blockIdx.y * NFW;          // this block's output fragments
 
   // XCD-aware tile order: block b runs on XCD b % 8; give each XCD a band.
   const int ntiles = a.tiles_x * a.tiles_y;
@@ -171,24 +187,33 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(ConvF16Args a, in
 
   if (tid < 2) reinterpret_cast<uint2*>(lds + T::ZERO)[tid] = make_uint2(0u, 0u);
 
-  floatx4 acc[R][NF];
+  floatx4 acc[R][NFW];
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int q = 0; q < NF; ++q) acc[r][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < NFW; ++q) acc[r][q] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const uint4* wf = static_cast<const uint4*>(a.wfrag);
+  const uint4* wf = static_cast<const uint4*>(a.wfrag) + lane + q0 * 64;
+  uint4 acur[3][NFW];
+  {
+    const uint4* w0 = wf + (size_t)a.chunk[0].wfrag * 64;
+#pragma unroll
+    for (int ky = 0; ky < 3; ++ky)
+#pragma unroll
+      for (int q = 0; q < NFW; ++q) acur[ky][q] = w0[(ky * nf + q) * 64];
+  }
 #pragma unroll 1
   for (int ci = 0; ci < a.nchunks4; ++ci) {
     const ConvChunk ch = a.chunk[ci];
     const _Float16* src = static_cast<const _Float16*>(ch.src ? a.src1 : a.src0);
     const int cs = ch.src ? a.cs1 : a.cs0;
     const bool up = upcat && ch.src == 0;
+    const uint4* wnext = ci + 1 < a.nchunks ? wf + (size_t)a.chunk[ci + 1].wfrag * 64 : nullptr;
     __syncthreads();
     if ((cs & 7) == 0) stage_patch<R, 4, true>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid);
     else stage_patch<R, 4, false>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid);
     __syncthreads();
-    mma_chunk<NF, R, 4>(acc, lds, wf + (size_t)ch.wfrag * 64 + lane, wave, g, c);
+    mma_chunk<NFW, R, 4>(acc, acur, lds, wf + (size_t)ch.wfrag * 64, wnext, nf, wave, g, c);
   }
 #pragma unroll 1
   for (int ci = a.nchunks4; ci < a.nchunks; ++ci) {
@@ -196,19 +221,21 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(ConvF16Args a, in
     const _Float16* src = static_cast<const _Float16*>(ch.src ? a.src1 : a.src0);
     const int cs = ch.src ? a.cs1 : a.cs0;
     const bool up = upcat && ch.src == 0;
+    const uint4* wnext = ci + 1 < a.nchunks ? wf + (size_t)a.chunk[ci + 1].wfrag * 64 : nullptr;
     __syncthreads();
     if ((cs & 7) == 0) stage_patch<R, 2, true>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid);
     else stage_patch<R, 2, false>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid);
     __syncthreads();
-    mma_chunk<NF, R, 2>(acc, lds, wf + (size_t)ch.wfrag * 64 + lane, wave, g, c);
+    mma_chunk<NFW, R, 2>(acc, acur, lds, wf + (size_t)ch.wfrag * 64, wnext, nf, wave, g, c);
   }
 
-  // Epilogue.  Lane (g, c) holds rows 4g..4g+3 of every fragment: output
-  // channels cbase + 4q + i with cbase = 4 * NF * g, for pixel column c.
-  const int cbase = 4 * NF * g;
-  float bv[NF][4];
+  // Epilogue.  Lane (g, c) holds rows 4g..4g+3 of every fragment: fragment
+  // q0 + q carries output channels cbase + 4 (q0 + q) + i with
+  // cbase = 4 * nf * g, for pixel column c.
+  const int cbase = 4 * nf * g + 4 * q0;
+  float bv[NFW][4];
 #pragma unroll
-  for (int q = 0; q < NF; ++q)
+  for (int q = 0; q < NFW; ++q)
 #pragma unroll
     for (int i = 0; i < 4; ++i) bv[q][i] = a.bias[cbase + 4 * q + i];
   const int x = x0 + c;
@@ -220,9 +247,10 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(ConvF16Args a, in
       if (yy < a.h && x < a.w) {
         const size_t base = ((size_t)yy * a.w + x) * a.cout_stored + cbase;
 #pragma unroll
-        for (int q = 0; q < NF; ++q)
+        for (int q = 0; q < NFW; ++q)
           if (cbase + 4 * q < a.cout_stored)
-            store4<OUTF32>(a.y, base + 4 * q, act(acc[r][q][0] + bv[q][0], relu), act(acc[r][q][1] + bv[q][1], relu), act(acc[r][q][2] + bv[q][2], relu),
+            store4<OUTF32>(a.y, base + 4 * q, act(acc[r][q][0] + bv[q][0], relu),
+                           act(acc[r][q][1] + bv[q][1], relu), act(acc[r][q][2] + bv[q][2], relu),
                            act(acc[r][q][3] + bv[q][3], relu));
       }
     }
@@ -230,9 +258,9 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(ConvF16Args a, in
     const int ow = a.w >> 1;
 #pragma unroll
     for (int rp = 0; rp < R / 2; ++rp) {
-      float m[NF][4];
+      float m[NFW][4];
 #pragma unroll
-      for (int q = 0; q < NF; ++q)
+      for (int q = 0; q < NFW; ++q)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float v = act(fmaxf(acc[2 * rp][q][i], acc[2 * rp + 1][q][i]) + bv[q][i], relu);
@@ -242,7 +270,7 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(ConvF16Args a, in
       if ((c & 1) == 0 && yy < a.h && x < a.w) {
         const size_t base = ((size_t)(yy >> 1) * ow + (x >> 1)) * a.cout_stored + cbase;
 #pragma unroll
-        for (int q = 0; q < NF; ++q)
+        for (int q = 0; q < NFW; ++q)
           if (cbase + 4 * q < a.cout_stored)
             store4<OUTF32>(a.y, base + 4 * q, m[q][0], m[q][1], m[q][2], m[q][3]);
       }
@@ -250,35 +278,62 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(ConvF16Args a, in
   }
 }
 
-template <int NF, int R>
-hipError_t launch_shape(ConvF16Args a, bool upcat, bool pool, bool relu, bool out_f32,
-                        hipStream_t stream) {
+template <int NFW, int R>
+hipError_t launch_shape(ConvF16Args a, int nsplit, bool upcat, bool pool, bool relu,
+                        bool out_f32, hipStream_t stream) {
   a.tiles_x = cdiv(a.w, TW);
   a.tiles_y = cdiv(a.h, Tile<R>::TH);
   const int ntiles = a.tiles_x * a.tiles_y;
-  const dim3 grid(cdiv(ntiles, kXcds) * kXcds), block(THREADS);
+  const dim3 grid(cdiv(ntiles, kXcds) * kXcds, nsplit), block(THREADS);
   if (out_f32)
-    hipLaunchKernelGGL((conv3x3_f16_mfma<NF, R, true>), grid, block, 0, stream, a, (int)upcat,
+    hipLaunchKernelGGL((conv3x3_f16_mfma<NFW, R, true>), grid, block, 0, stream, a, (int)upcat,
                        (int)pool, (int)relu);
   else
-    hipLaunchKernelGGL((conv3x3_f16_mfma<NF, R, false>), grid, block, 0, stream, a, (int)upcat,
+    hipLaunchKernelGGL((conv3x3_f16_mfma<NFW, R, false>), grid, block, 0, stream, a, (int)upcat,
                        (int)pool, (int)relu);
   return hipGetLastError();
 }
 
-// Rows per wave: 8 where the accumulators fit (nf <= 4) and the image gives
-// at least two 32 x 16 tiles per CU, else 4.
-template <int NF>
-hipError_t launch_nf(const ConvF16Args& a, bool upcat, bool pool, bool relu, bool out_f32,
-                     hipStream_t stream) {
-  if constexpr (NF <= 4) {
-    const long tiles8 = (long)cdiv(a.w, TW) * cdiv(a.h, 32);
-    if (tiles8 >= 512) return launch_shape<NF, 8>(a, upcat, pool, relu, out_f32, stream);
+template <int NFW>
+hipError_t launch_rows(const ConvF16Args& a, int rows, int nsplit, bool upcat, bool pool,
+                       bool relu, bool out_f32, hipStream_t stream) {
+  if constexpr (NFW <= 4) {
+    if (rows == 8) return launch_shape<NFW, 8>(a, nsplit, upcat, pool, relu, out_f32, stream);
+    if (rows == 2) return launch_shape<NFW, 2>(a, nsplit, upcat, pool, relu, out_f32, stream);
   }
-  return launch_shape<NF, 4>(a, upcat, pool, relu, out_f32, stream);
+  return launch_shape<NFW, 4>(a, nsplit, upcat, pool, relu, out_f32, stream);
 }
 
 }  // namespace
+
+// Work decomposition.  Each block covers a (4 R) x 16 pixel tile and NFW of
+// the nf output fragments.  Big images use R = 8 with all fragments; smaller
+// ones split the output channels across blocks and shrink the tile until the
+// grid has about four blocks per CU.
+void conv_f16_plan(int h, int w, int nf, int* rows, int* nfw) {
+  constexpr long kTarget = 1024;
+  const long t8 = (long)cdiv(w, TW) * cdiv(h, 32);
+  if (nf <= 4 && t8 >= kTarget) {
+    *rows = 8;
+    *nfw = nf;
+    return;
+  }
+  for (int r : {4, 2}) {
+    const long t = (long)cdiv(w, TW) * cdiv(h, 4 * r);
+    for (int split = 1; split <= nf; ++split) {
+      if (nf % split) continue;
+      const int width = nf / split;
+      if (r == 2 && width > 4) continue;
+      if (t * split >= kTarget) {
+        *rows = r;
+        *nfw = width;
+        return;
+      }
+    }
+  }
+  *rows = 2;
+  *nfw = 1;
+}
 
 bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out) {
   ConvLayout L{};
@@ -321,15 +376,20 @@ bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out
 
 hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, bool relu,
                            bool out_f32, hipStream_t stream) {
-  switch (nf) {
-    case 1: return launch_nf<1>(a, upcat, pool, relu, out_f32, stream);
-    case 2: return launch_nf<2>(a, upcat, pool, relu, out_f32, stream);
-    case 3: return launch_nf<3>(a, upcat, pool, relu, out_f32, stream);
-    case 4: return launch_nf<4>(a, upcat, pool, relu, out_f32, stream);
-    case 5: return launch_nf<5>(a, upcat, pool, relu, out_f32, stream);
-    case 6: return launch_nf<6>(a, upcat, pool, relu, out_f32, stream);
-    case 7: return launch_nf<7>(a, upcat, pool, relu, out_f32, stream);
-    case 8: return launch_nf<8>(a, upcat, pool, relu, out_f32, stream);
+  int rows = 4, nfw = nf;
+  conv_f16_plan(a.h, a.w, nf, &rows, &nfw);
+  ConvF16Args b = a;
+  b.nf = nf;
+  const int nsplit = nf / nfw;
+  switch (nfw) {
+    case 1: return launch_rows<1>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
+    case 2: return launch_rows<2>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
+    case 3: return launch_rows<3>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
+    case 4: return launch_rows<4>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
+    case 5: return launch_rows<5>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
+    case 6: return launch_rows<6>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
+    case 7: return launch_rows<7>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
+    case 8: return launch_rows<8>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -67,6 +67,7 @@ struct ConvF16Args {
   const void* wfrag;  // fragments
   void* y;
   int cout_stored;
+  int nf;             // output fragments of the whole conv
   int tiles_x, tiles_y;
   int nchunks;
   int nchunks4;
@@ -75,6 +76,9 @@ struct ConvF16Args {
 
 hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, bool relu,
                            bool out_f32, hipStream_t stream);
+
+// Tile height (4 * rows) and output fragments per block chosen for a conv.
+void conv_f16_plan(int h, int w, int nf, int* rows, int* nfw);
 
 // ---------------------------------------------------------------------------
 // fp32 direct conv (VALU FMA).  Packed weights: bias (cout_stored floats,
