@@ -21,11 +21,6 @@ PEAK_F16_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0
 
 
-def conv_symbol(cout, final):
-    nf = -(-(4 * -(-cout // 4)) // 16)
-    return f"conv3x3_f16_mfma<{nf}, {'true' if final else 'false'}>"
-
-
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,7 +105,7 @@ def main():
         px = (tw >> level) * (th >> level)
         flops = 2.0 * px * co * 9 * (c0 + c1)
         ms = float(avg_ms[i + 1])
-        sym = conv_symbol(co, i == 15)
+        sym, nblocks = U.oidn_unet_layer_kernel(9, i, tw, th, U.OIDN_F16)
         g = groups.setdefault(sym, {"flops": 0.0, "ms": 0.0, "launches": 0})
         g["flops"] += flops
         g["ms"] += ms
@@ -118,8 +113,9 @@ def main():
         conv_flops += flops
         conv_ms += ms
         layers.append({"layer": name, "us": round(ms * 1e3, 2),
-                       "tflops": round(flops / ms / 1e9, 1)})
-        print(f"  {name:11s} {ms * 1e3:8.1f} us  {flops / ms / 1e9:7.1f} TFLOP/s", file=sys.stderr)
+                       "tflops": round(flops / ms / 1e9, 1), "kernel": sym, "blocks": nblocks})
+        print(f"  {name:11s} {ms * 1e3:8.1f} us  {flops / ms / 1e9:7.1f} TFLOP/s  {sym} x{nblocks}",
+              file=sys.stderr)
     px0 = tw * th
     pack_bytes = W * H * 48 + px0 * 12 * 2 if len(tiles) == 1 else None
     unpack_bytes = W * H * (32 + 16)

@@ -209,6 +209,13 @@ int oidn_unet_layer_count(void);
 int oidn_unet_layer_info(int in_channels, int layer, int* cin0, int* cin1, int* cout,
                          int* level, unsigned* flags, const char** name);
 
+/* Name of the kernel instance that runs `layer` on a tw x th tile (for
+ * matching per-kernel timings and profiles), written NUL-terminated into
+ * buf (cap bytes), e.g. "conv3x3_f16_mfma<4, 8, false>"; *blocks receives the
+ * launch's workgroup count.  Host only. */
+int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int dtype, char* buf,
+                           int cap, int* blocks);
+
 /* Bytes of the packed weights of all sixteen layers. */
 int oidn_unet_weights_bytes(int in_channels, int dtype, size_t* bytes);
 

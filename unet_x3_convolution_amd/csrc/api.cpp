@@ -688,6 +688,32 @@ int oidn_unet_layer_info(int in_channels, int layer, int* cin0, int* cin1, int* 
   return ok();
 }
 
+int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int dtype, char* buf,
+                           int cap, int* blocks) {
+  if (!buf || cap <= 0) return fail(OIDN_E_INVALID, "null or empty name buffer");
+  int rc = check_network_tile(in_channels, tw, th, dtype);
+  if (rc) return rc;
+  if (layer < 0 || layer >= kLayers) return fail(OIDN_E_INVALID, "layer %d out of range", layer);
+  LayerShape s[kLayers];
+  unet_shapes(in_channels, s);
+  const int h = th >> s[layer].level, w = tw >> s[layer].level;
+  const bool final_layer = layer == kLayers - 1;
+  int nb = 0;
+  if (dtype == OIDN_F16) {
+    const int nf = cdiv(stored_channels(s[layer].cout), 16);
+    int rows = 4, nfw = nf;
+    conv_f16_plan(h, w, nf, &rows, &nfw);
+    snprintf(buf, cap, "conv3x3_f16_mfma<%d, %d, %s>", nfw, rows, final_layer ? "true" : "false");
+    nb = cdiv(cdiv(w, 16) * cdiv(h, 4 * rows), 8) * 8 * (nf / nfw);
+  } else {
+    snprintf(buf, cap, "conv3x3_f32_direct");
+    const int oh = kUNet[layer].pool ? h / 2 : h, ow = kUNet[layer].pool ? w / 2 : w;
+    nb = (int)cdiv(ow * oh * (stored_channels(s[layer].cout) / 4), 256);
+  }
+  if (blocks) *blocks = nb;
+  return ok();
+}
+
 int oidn_unet_weights_bytes(int in_channels, int dtype, size_t* bytes) {
   if (!bytes) return fail(OIDN_E_INVALID, "null bytes pointer");
   int rc = check_dtype(dtype);

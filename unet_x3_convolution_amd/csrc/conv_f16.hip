@@ -99,14 +99,21 @@ __device__ __forceinline__ void stage_patch(_Float16* lds, const _Float16* src, 
 // column-group-0 weights on entry; each column group loads the next one's
 // weights (or those of the next chunk, `wnext`) before its MFMAs, so weight
 // loads overlap the matrix work.  On return `acur` holds the next chunk's.
-template <int NFW, int R, int CG>
+template <int NFW, int R, int CG, bool PF>
 __device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], uint4 (&acur)[3][NFW],
                                           const _Float16* lds, const uint4* wchunk,
                                           const uint4* wnext, int nf, int wave, int g, int c) {
   constexpr int NCG = (3 * CG + 3) / 4;
 #pragma unroll 1
   for (int j = 0; j < NCG; ++j) {
-    const uint4* wn = j + 1 < NCG ? wchunk + (size_t)(j + 1) * 3 * nf * 64 : wnext;
+    if constexpr (!PF) {
+      // no register double buffer (keeps occupancy): load this group's weights now
+#pragma unroll
+      for (int ky = 0; ky < 3; ++ky)
+#pragma unroll
+        for (int q = 0; q < NFW; ++q) acur[ky][q] = wchunk[((size_t)(j * 3 + ky) * nf + q) * 64];
+    }
+    const uint4* wn = !PF ? nullptr : j + 1 < NCG ? wchunk + (size_t)(j + 1) * 3 * nf * 64 : wnext;
     uint4 anext[3][NFW];
     if (wn) {
 #pragma unroll
@@ -166,7 +173,7 @@ __device__ __forceinline__ void store4(void* y, size_t idx, float v0, float v1, 
 }
 
 template <int NFW, int R, bool OUTF32>
-__global__ __launch_bounds__(THREADS, (NFW * R <= 16) ? 2 : 1) void conv3x3_f16_mfma(
+__global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
     ConvF16Args a, int upcat, int pool, int relu) {
   using T = Tile<R>;
   __shared__ __attribute__((aligned(16))) _Float16 lds[T::PATCH + 8];
@@ -175,6 +182,9 @@ __global__ __launch_bounds__(THREADS, (NFW * R <= 16) ? 2 : 1) void conv3x3_f16_
   const int g = lane >> 4, c = lane & 15;
   const int nf = a.nf;
   const int q0 = blockIdx.y * NFW;          // this block's output fragments
+  // Weight prefetch costs 12 * NFW registers; use it only where two waves
+  // per SIMD still fit.
+  constexpr bool PF = NFW * R <= 16;
 
   // XCD-aware tile order: block b runs on XCD b % 8; give each XCD a band.
   const int ntiles = a.tiles_x * a.tiles_y;
@@ -195,7 +205,7 @@ __global__ __launch_bounds__(THREADS, (NFW * R <= 16) ? 2 : 1) void conv3x3_f16_
 
   const uint4* wf = static_cast<const uint4*>(a.wfrag) + lane + q0 * 64;
   uint4 acur[3][NFW];
-  {
+  if (PF) {
     const uint4* w0 = wf + (size_t)a.chunk[0].wfrag * 64;
 #pragma unroll
     for (int ky = 0; ky < 3; ++ky)
@@ -213,7 +223,7 @@ __global__ __launch_bounds__(THREADS, (NFW * R <= 16) ? 2 : 1) void conv3x3_f16_
     if ((cs & 7) == 0) stage_patch<R, 4, true>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid);
     else stage_patch<R, 4, false>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid);
     __syncthreads();
-    mma_chunk<NFW, R, 4>(acc, acur, lds, wf + (size_t)ch.wfrag * 64, wnext, nf, wave, g, c);
+    mma_chunk<NFW, R, 4, PF>(acc, acur, lds, wf + (size_t)ch.wfrag * 64, wnext, nf, wave, g, c);
   }
 #pragma unroll 1
   for (int ci = a.nchunks4; ci < a.nchunks; ++ci) {
@@ -226,7 +236,7 @@ __global__ __launch_bounds__(THREADS, (NFW * R <= 16) ? 2 : 1) void conv3x3_f16_
     if ((cs & 7) == 0) stage_patch<R, 2, true>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid);
     else stage_patch<R, 2, false>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid);
     __syncthreads();
-    mma_chunk<NFW, R, 2>(acc, acur, lds, wf + (size_t)ch.wfrag * 64, wnext, nf, wave, g, c);
+    mma_chunk<NFW, R, 2, PF>(acc, acur, lds, wf + (size_t)ch.wfrag * 64, wnext, nf, wave, g, c);
   }
 
   // Epilogue.  Lane (g, c) holds rows 4g..4g+3 of every fragment: fragment
@@ -313,7 +323,7 @@ hipError_t launch_rows(const ConvF16Args& a, int rows, int nsplit, bool upcat, b
 void conv_f16_plan(int h, int w, int nf, int* rows, int* nfw) {
   constexpr long kTarget = 1024;
   const long t8 = (long)cdiv(w, TW) * cdiv(h, 32);
-  if (nf <= 4 && t8 >= kTarget) {
+  if (nf <= 4 && t8 >= kTarget / 2) {
     *rows = 8;
     *nfw = nf;
     return;
