@@ -704,7 +704,7 @@ int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int dtype
     int rows = 4, nfw = nf;
     conv_f16_plan(h, w, nf, &rows, &nfw);
     snprintf(buf, cap, "conv3x3_f16_mfma<%d, %d, %s>", nfw, rows, final_layer ? "true" : "false");
-    nb = cdiv(cdiv(w, 16) * cdiv(h, 4 * rows), 8) * 8 * (nf / nfw);
+    nb = conv_f16_blocks(h, w, nf);
   } else {
     snprintf(buf, cap, "conv3x3_f32_direct");
     const int oh = kUNet[layer].pool ? h / 2 : h, ow = kUNet[layer].pool ? w / 2 : w;

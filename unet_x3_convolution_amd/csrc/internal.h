@@ -30,7 +30,7 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 struct ConvChunk {
   int src;    // 0: first source (upsampled source for the decoder), 1: skip
   int coff;   // first stored channel of the chunk within its source
-  int cg;     // 8-channel groups the chunk is processed as (2 or 4)
+  int cg;     // 8-channel groups the chunk is processed as (always 4)
   int ncg;    // column groups of the chunk: ceil(3 * cg / 4)
   int wfrag;  // index of the chunk's first weight fragment
 };
@@ -77,8 +77,10 @@ struct ConvF16Args {
 hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, bool relu,
                            bool out_f32, hipStream_t stream);
 
-// Tile height (4 * rows) and output fragments per block chosen for a conv.
+// Tile height (4 * rows) and output fragments per block chosen for a conv,
+// and the launch's workgroup count.
 void conv_f16_plan(int h, int w, int nf, int* rows, int* nfw);
+int conv_f16_blocks(int h, int w, int nf);
 
 // ---------------------------------------------------------------------------
 // fp32 direct conv (VALU FMA).  Packed weights: bias (cout_stored floats,
