@@ -64,7 +64,7 @@ constexpr int kXcds = 8;
 constexpr int kCUs = 256;
 
 // Zero block that padding lanes of the patch loads read from.
-__device__ __attribute__((aligned(16))) uint4 g_zero16[1];
+__device__ __attribute__((aligned(16))) unsigned int g_zero16[4] = {0u, 0u, 0u, 0u};
 
 template <int R>
 struct Tile {
