@@ -171,9 +171,10 @@ void pack_conv_host(const float* w, const float* b, int cin0, int cin1, int cout
 }
 
 // Validates and launches one conv.  Pointers already checked by the caller.
+// cs0/cs1: stored channels per pixel of the sources (0 = 4 * ceil(cin / 4)).
 int run_conv(const void* src0, int cin0, const void* src1, int cin1, bool upcat, int h, int w,
              const void* wpk, void* y, int cout, int in_dtype, int out_dtype, unsigned flags,
-             hipStream_t stream) {
+             hipStream_t stream, int cs0 = 0, int cs1 = 0) {
   const bool pool = flags & OIDN_POOL2X2, relu = flags & OIDN_RELU;
   hipError_t e;
   if (in_dtype == OIDN_F16) {
@@ -182,8 +183,8 @@ int run_conv(const void* src0, int cin0, const void* src1, int cin1, bool upcat,
     ConvF16Args a{};
     a.src0 = src0;
     a.src1 = src1;
-    a.cs0 = stored_channels(cin0);
-    a.cs1 = cin1 ? stored_channels(cin1) : 0;
+    a.cs0 = cs0 ? cs0 : stored_channels(cin0);
+    a.cs1 = cin1 ? (cs1 ? cs1 : stored_channels(cin1)) : 0;
     a.h = h;
     a.w = w;
     a.bias = static_cast<const float*>(wpk);
@@ -297,13 +298,21 @@ struct Plan {
   size_t bytes;
 };
 
+// Stored channels of the network input inside the end-to-end fp16 path: a
+// multiple of 8, so the conv's patch loads move whole 16-byte channel groups.
+int internal_input_lanes(int in_channels, int dtype) {
+  const int cs = stored_channels(in_channels);
+  return dtype == OIDN_F16 ? (cs + 7) / 8 * 8 : cs;
+}
+
 void plan_workspace(int in_channels, int tw, int th, int dtype, bool own_io, Plan* p) {
   LayerShape s[kLayers];
   unet_shapes(in_channels, s);
   size_t size[kLayers + 1];
   int def[kLayers + 1], last[kLayers + 1];
   const size_t px0 = (size_t)tw * th;
-  size[0] = px0 * stored_channels(in_channels) * esize(dtype);
+  size[0] = px0 * (own_io ? internal_input_lanes(in_channels, dtype)
+                          : stored_channels(in_channels)) * esize(dtype);
   def[0] = -1;
   last[0] = -1;
   for (int i = 0; i < kLayers; ++i) {
@@ -373,9 +382,11 @@ int run_network(const unsigned char* weights, int in_channels, const void* packe
     }
     const unsigned flags = (L.relu ? OIDN_RELU : 0u) | (L.pool ? OIDN_POOL2X2 : 0u);
     const int out_dtype = i == kLayers - 1 ? OIDN_F32 : dtype;
+    const int in_cs = own_io ? internal_input_lanes(in_channels, dtype) : 0;
     int rc = run_conv(val[L.src], s[i].cin0, L.skip >= 0 ? val[L.skip] : nullptr, s[i].cin1,
                       L.skip >= 0, h, w, weights + woff, const_cast<void*>(val[i + 1]), s[i].cout,
-                      dtype, out_dtype, flags, stream);
+                      dtype, out_dtype, flags, stream, L.src == 0 ? in_cs : 0,
+                      L.skip == 0 ? in_cs : 0);
     if (rc) return rc;
     size_t b = 0;
     conv_weights_bytes(s[i].cin0, s[i].cin1, s[i].cout, dtype, &b);
@@ -454,6 +465,7 @@ int denoise(const void* d_weights, int in_channels, const float* color, const fl
     pa.hdr = hdr;
     pa.input_scale = input_scale;
     pa.sources = sources;
+    pa.lanes = internal_input_lanes(in_channels, dtype);
     pa.packed = ws + P.offset[0];
     if ((e = launch_pack(pa, dtype == OIDN_F16, stream)) != hipSuccess) return hip_fail(e, "pack launch");
     rc = run_network(static_cast<const unsigned char*>(d_weights), in_channels, nullptr, t.in_w,
@@ -628,6 +640,7 @@ int oidn_pack_input(const float* color, const float* albedo, const float* normal
   a.hdr = hdr;
   a.input_scale = input_scale;
   a.sources = 1 + (albedo != nullptr) + (normal != nullptr);
+  a.lanes = stored_channels(3 * a.sources);
   a.packed = packed;
   hipError_t e = launch_pack(a, dtype == OIDN_F16, stream);
   if (e != hipSuccess) return hip_fail(e, "pack launch");

@@ -22,14 +22,13 @@
 //    ky = 0, 1, 2: R + 2 fragment loads per column group instead of 3 R.
 //  * Pipeline.  Workgroups are persistent: each walks a list of (tile,
 //    chunk) items.  While item k computes from one LDS patch buffer, the halo
-//    patch of item k + 1 is already in flight into the other buffer by direct
-//    global -> LDS loads (global_load_lds, no registers), and its weights are
-//    in flight into a second register set.  The loads of item k + 1 are
-//    issued weights first, patch second, so nothing inside the MFMA phase
-//    waits on the patch; the one barrier per item drains both.  The two LDS
-//    buffers are distinct arrays selected at compile time (the item loop is
-//    unrolled by two) so the compiler can see that reads of one never alias
-//    the loads into the other.
+//    patch and the weight fragments of item k + 1 are already in flight into
+//    the other pair of buffers by direct global -> LDS loads
+//    (global_load_lds: no registers, one copy of the weights per workgroup).
+//    Nothing inside the MFMA phase waits on them; the one barrier per item
+//    drains them.  The buffer pairs are distinct arrays selected at compile
+//    time (the item loop is unrolled by two) so the compiler can see that
+//    reads of one never alias the loads into the other.
 //  * The decoder's upsampled source is gathered at (y >> 1, x >> 1) by the
 //    patch loads; the skip follows as further chunks (concat order [up, skip]).
 //    Channels past a source's stored count, and pixels outside the image,
@@ -132,24 +131,29 @@ __device__ __forceinline__ void load_patch(uint4* buf, const _Float16* src, int 
   }
 }
 
-// Weights of one chunk for output fragments [q0, q0 + NFW) (wchunk already
-// offset by q0): fragment (column group j, ky, q) is chunk.wfrag + (3 j + ky) * nf + q.
+// Global -> LDS loads of one chunk's weights for output fragments
+// [q0, q0 + NFW) (wchunk already offset by q0): LDS fragment (3 j + ky) * NFW + q
+// is global fragment chunk.wfrag + (3 j + ky) * nf + q, one 1 KB wave load each.
 template <int NFW>
-__device__ __forceinline__ void load_weights(uint4 (&a)[3][3][NFW], const uint4* wchunk, int nf) {
-#pragma unroll
-  for (int j = 0; j < 3; ++j)
-#pragma unroll
-    for (int ky = 0; ky < 3; ++ky)
-#pragma unroll
-      for (int q = 0; q < NFW; ++q) a[j][ky][q] = wchunk[((3 * j + ky) * nf + q) * 64];
+__device__ __forceinline__ void load_weights(uint4* abuf, const uint4* wchunk, int nf, int wave) {
+  for (int i = wave; i < 9 * NFW; i += 4) {
+    const int jk = i / NFW;
+    __builtin_amdgcn_global_load_lds(wchunk + (jk * nf + (i - jk * NFW)) * 64, abuf + i * 64, 16,
+                                     0, 0);
+  }
 }
 
 template <int NFW, int R>
-__device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], const uint4 (&a)[3][3][NFW],
-                                          const uint4* buf, int wave, int g, int c) {
+__device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], const uint4* abuf,
+                                          const uint4* buf, int wave, int g, int c, int lane) {
   const _Float16* patch = reinterpret_cast<const _Float16*>(buf);
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
+    uint4 a[3][NFW];
+#pragma unroll
+    for (int ky = 0; ky < 3; ++ky)
+#pragma unroll
+      for (int q = 0; q < NFW; ++q) a[ky][q] = abuf[((3 * j + ky) * NFW + q) * 64 + lane];
     const int base = ((R * wave) * PW + c + j) * PIX_HALVES + SLOT_HALVES * g;
 #pragma unroll
     for (int p = 0; p < R + 2; ++p) {
@@ -160,7 +164,7 @@ __device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], const uint4 (&
         if (r >= 0 && r < R) {
 #pragma unroll
           for (int q = 0; q < NFW; ++q)
-            acc[r][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(a[j][ky][q]), b,
+            acc[r][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(a[ky][q]), b,
                                                                acc[r][q], 0, 0, 0);
         }
       }
@@ -249,6 +253,8 @@ __global__ __launch_bounds__(THREADS, 1) void conv3x3_f16_mfma(ConvF16Args a, in
   using T = Tile<R>;
   __shared__ __attribute__((aligned(16))) uint4 buf0[T::BUF_SLOTS];
   __shared__ __attribute__((aligned(16))) uint4 buf1[T::BUF_SLOTS];
+  __shared__ __attribute__((aligned(16))) uint4 wbuf0[9 * NFW * 64];
+  __shared__ __attribute__((aligned(16))) uint4 wbuf1[9 * NFW * 64];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;
@@ -272,13 +278,13 @@ __global__ __launch_bounds__(THREADS, 1) void conv3x3_f16_mfma(ConvF16Args a, in
 
   if (!item_valid(0)) return;
 
-  const uint4* wf = static_cast<const uint4*>(a.wfrag) + lane + q0 * 64;
-  auto issue = [&](int k, uint4 (&aw)[3][3][NFW], uint4* dst) {
+  auto issue = [&](int k, uint4* wdst, uint4* dst) {
     const ConvChunk ch = a.chunk[k % nch];
     const int t = item_tile(k);
     const int ty = t / a.tiles_x;
     const int tx = t - ty * a.tiles_x;
-    load_weights<NFW>(aw, wf + (size_t)ch.wfrag * 64, nf);
+    load_weights<NFW>(wdst, static_cast<const uint4*>(a.wfrag) + ((size_t)ch.wfrag + q0) * 64, nf,
+                      wave);
     load_patch<R>(dst, static_cast<const _Float16*>(ch.src ? a.src1 : a.src0),
                   ch.src ? a.cs1 : a.cs0, ch.coff, upcat && ch.src == 0, a.h, a.w, ty * T::TH,
                   tx * TW, wave, lane);
@@ -290,16 +296,14 @@ __global__ __launch_bounds__(THREADS, 1) void conv3x3_f16_mfma(ConvF16Args a, in
 #pragma unroll
     for (int q = 0; q < NFW; ++q) acc[r][q] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 wa[3][3][NFW], wb[3][3][NFW];
-  issue(0, wa, buf0);
+  issue(0, wbuf0, buf0);
 
   // One pipeline step: wait for item k's loads, start item k + 1's, compute k.
-  auto step = [&](int k, uint4 (&wcur)[3][3][NFW], uint4 (&wnxt)[3][3][NFW], const uint4* cur,
-                  uint4* nxt) -> bool {
+  auto step = [&](int k, const uint4* wcur, uint4* wnxt, const uint4* cur, uint4* nxt) -> bool {
     __syncthreads();
     const bool more = item_valid(k + 1);
     if (more) issue(k + 1, wnxt, nxt);
-    mma_chunk<NFW, R>(acc, wcur, cur, wave, g, c);
+    mma_chunk<NFW, R>(acc, wcur, cur, wave, g, c, lane);
     if (k % nch == nch - 1) {
       const int t = item_tile(k);
       const int ty = t / a.tiles_x;
@@ -310,8 +314,8 @@ __global__ __launch_bounds__(THREADS, 1) void conv3x3_f16_mfma(ConvF16Args a, in
   };
 #pragma unroll 1
   for (int k = 0;; k += 2) {
-    if (!step(k, wa, wb, buf0, buf1)) break;
-    if (!step(k + 1, wb, wa, buf1, buf0)) break;
+    if (!step(k, wbuf0, wbuf1, buf0, buf1)) break;
+    if (!step(k + 1, wbuf1, wbuf0, buf1, buf0)) break;
   }
 }
 
@@ -338,7 +342,9 @@ hipError_t launch_shape(ConvF16Args a, int nsplit, bool upcat, bool pool, bool r
 template <int NFW>
 hipError_t launch_rows(const ConvF16Args& a, int rows, int nsplit, bool upcat, bool pool,
                        bool relu, bool out_f32, hipStream_t stream) {
-  if (rows == 8) return launch_shape<NFW, 8>(a, nsplit, upcat, pool, relu, out_f32, stream);
+  if constexpr (NFW <= 3) {
+    if (rows == 8) return launch_shape<NFW, 8>(a, nsplit, upcat, pool, relu, out_f32, stream);
+  }
   if (rows == 2) return launch_shape<NFW, 2>(a, nsplit, upcat, pool, relu, out_f32, stream);
   return launch_shape<NFW, 4>(a, nsplit, upcat, pool, relu, out_f32, stream);
 }
@@ -348,14 +354,14 @@ hipError_t launch_rows(const ConvF16Args& a, int rows, int nsplit, bool upcat, b
 // Work decomposition: tile height 4 * rows and NFW (<= 4) of the nf output
 // fragments per workgroup, nf / NFW workgroups sharing each tile.  Tiles as
 // tall as possible while every CU still gets four or more items (32-row
-// tiles only up to NFW = 3, whose registers still fit without spilling).
+// tiles only up to NFW = 3, whose two patch and weight buffers fit in LDS).
 void conv_f16_plan(int h, int w, int nf, int* rows, int* nfw) {
   int width = nf;
   if (nf > 4) width = nf % 4 == 0 ? 4 : (nf % 3 == 0 ? 3 : (nf % 2 == 0 ? 2 : 1));
   const int split = nf / width;
   *nfw = width;
   for (int r : {8, 4}) {
-    if (r == 8 && width > 3) continue;   // 32-row tiles with 4 fragments exceed the register file
+    if (r == 8 && width > 3) continue;   // LDS: 2 x (49 KB patch + 9 NFW KB weights)
     const long items = (long)cdiv(w, TW) * cdiv(h, 4 * r) * split;
     if (items >= 4L * kCUs) {
       *rows = r;

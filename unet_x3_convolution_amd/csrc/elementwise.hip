@@ -59,17 +59,21 @@ __global__ __launch_bounds__(THREADS) void pack_input_kernel(PackArgs a) {
     ch[7] = sanitize(nr.y, -1.f, 1.f) * 0.5f + 0.5f;
     ch[8] = sanitize(nr.z, -1.f, 1.f) * 0.5f + 0.5f;
   }
-  const int nblk = a.sources == 1 ? 1 : (a.sources == 2 ? 2 : 3);
+  const int nblk = a.lanes / 4;   // blocks past the data (lanes 12..15) are zero
   if constexpr (F16) {
     uint2* out = static_cast<uint2*>(a.packed) + (size_t)t * nblk;
 #pragma unroll
-    for (int b = 0; b < 3; ++b)
-      if (b < nblk) out[b] = make_uint2(pack_h2(ch[4 * b], ch[4 * b + 1]), pack_h2(ch[4 * b + 2], ch[4 * b + 3]));
+    for (int b = 0; b < 4; ++b)
+      if (b < nblk)
+        out[b] = b < 3 ? make_uint2(pack_h2(ch[4 * b], ch[4 * b + 1]), pack_h2(ch[4 * b + 2], ch[4 * b + 3]))
+                       : make_uint2(0u, 0u);
   } else {
     float4* out = static_cast<float4*>(a.packed) + (size_t)t * nblk;
 #pragma unroll
-    for (int b = 0; b < 3; ++b)
-      if (b < nblk) out[b] = make_float4(ch[4 * b], ch[4 * b + 1], ch[4 * b + 2], ch[4 * b + 3]);
+    for (int b = 0; b < 4; ++b)
+      if (b < nblk)
+        out[b] = b < 3 ? make_float4(ch[4 * b], ch[4 * b + 1], ch[4 * b + 2], ch[4 * b + 3])
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 }
 

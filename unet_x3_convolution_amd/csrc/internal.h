@@ -114,6 +114,7 @@ struct PackArgs {
   int hdr;
   float input_scale;
   int sources;       // 1, 2 or 3
+  int lanes;         // stored channels per output pixel (>= 4 * ceil(3 * sources / 4))
   void* packed;
 };
 hipError_t launch_pack(const PackArgs& a, bool f16, hipStream_t stream);
