@@ -1,5 +1,5 @@
 // 3x3 convolution as an fp16 MFMA implicit GEMM with fp32 accumulation
-// (gfx950, v_mfma_f32_16x16x32_f16), persistent and software-pipelined.
+// (gfx950, v_mfma_f32_16x16x32_f16).
 //
 // What it computes is [web-0.4] createConvShader / createTiledConvShader /
 // createTiledDecoderShader / createFusedConvPoolShader ("oidn-web 0.3.4 ->
@@ -8,38 +8,28 @@
 // skip] and optionally followed by a 2x2 max-pool.  The tiling is our own:
 //
 //  * GEMM roles: D[cout][pixel] = A[cout][k] * B[k][pixel].  A holds packed
-//    weights (global memory, L2/L1 resident), B is read straight from an LDS
-//    halo patch (no im2col), so each lane of a 16x16 accumulator owns 4
-//    consecutive output channels of one pixel -- a whole 4-lane channel
+//    weights (read from global memory, L2/L1 resident), B is read straight
+//    from an LDS halo patch (no im2col), so each lane of a 16x16 accumulator
+//    owns 4 consecutive output channels of one pixel -- a whole 4-lane channel
 //    block, stored with one 8-byte write.
-//  * A workgroup of 4 waves computes (4 R) x 16 pixel tiles for NFW of the
-//    nf output fragments; wave w owns R consecutive rows of a tile, one
-//    16-pixel B fragment per row.
-//  * K order: chunk (32 channels of one source) -> column group kx (the four
-//    8-channel groups of the chunk, one per 16-lane group) -> ky.  All lanes
-//    of a column group read the same patch row, so the B fragment of patch
-//    row p serves output rows p, p - 1 and p - 2 with the weights of
-//    ky = 0, 1, 2: R + 2 fragment loads per column group instead of 3 R.
-//  * Pipeline.  Workgroups are persistent: each walks a list of (tile,
-//    chunk) items.  While item k computes from one LDS patch buffer, the halo
-//    patch and the weight fragments of item k + 1 are already in flight into
-//    the other pair of buffers by direct global -> LDS loads
-//    (global_load_lds: no registers, one copy of the weights per workgroup).
-//    Nothing inside the MFMA phase waits on them; the one barrier per item
-//    drains them.  The buffer pairs are distinct arrays selected at compile
-//    time (the item loop is unrolled by two) so the compiler can see that
-//    reads of one never alias the loads into the other.
-//  * The decoder's upsampled source is gathered at (y >> 1, x >> 1) by the
-//    patch loads; the skip follows as further chunks (concat order [up, skip]).
-//    Channels past a source's stored count, and pixels outside the image,
-//    load from a 16-byte zero block, which gives the zero padding.
+//  * A workgroup of 4 waves computes a (4 R) x 16 pixel tile for all output
+//    channels; wave w owns R consecutive rows, one 16-pixel B fragment each.
+//  * K order: chunk (<= 32 channels of one source, staged in LDS once) ->
+//    column group (four (kx, 8-channel group) slots, one per 16-lane group)
+//    -> ky.  All lanes of a column group read the same patch row, so the B
+//    fragment of patch row p serves output rows p, p - 1 and p - 2 with the
+//    weights of ky = 0, 1, 2: R + 2 fragment loads per column group instead
+//    of 3 R.  Thin inputs (12 channels) put two kx columns in one MFMA
+//    instead of padding channels to 32.
+//  * The decoder's upsampled source is gathered at (y >> 1, x >> 1) while
+//    staging; the skip follows as further chunks (concat order [up, skip]).
 //  * Epilogue: bias, ReLU, then the store or the fused 2x2 pool: the vertical
 //    pair sits in two rows held by the same lane, the horizontal pair in
 //    neighbouring lanes (one DPP swap).  Max is taken in fp32 before the
 //    single fp16 rounding; RNE is monotone, so this equals pooling the
 //    rounded conv output.
-//  * Tiles are dealt so that each of the 8 XCDs walks a contiguous band of
-//    tiles (halo rows shared through its own L2).
+//  * Tiles are dealt to blocks so that each of the 8 XCDs walks a contiguous
+//    band of tiles (halo rows shared through its own L2).
 //
 // The per-pixel reduction order depends only on the channel layout, never on
 // the pixel position or the image size, so tiled and untiled runs agree bit
@@ -52,122 +42,112 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int TW = 16;                 // tile width (one B fragment)
-constexpr int PW = TW + 2;             // patch width
-constexpr int SLOT_HALVES = 8;         // one 16-byte LDS slot
-constexpr int PIX_SLOTS = 5;           // per patch pixel: 4 channel groups + 1 pad (80 B stride,
-                                       // conflict-free 16-byte fragment reads)
-constexpr int PIX_HALVES = PIX_SLOTS * SLOT_HALVES;
+constexpr int TW = 16;                        // tile width (one B fragment)
+constexpr int PW = TW + 2;                    // patch width
+constexpr int PSTR = 40;                      // halves per patch pixel: 32 + 8 pad (80 B)
 constexpr int THREADS = 256;
 constexpr int kXcds = 8;
-constexpr int kCUs = 256;
-
-// Zero block that padding lanes of the patch loads read from.
-__device__ __attribute__((aligned(16))) unsigned int g_zero16[4] = {0u, 0u, 0u, 0u};
 
 template <int R>
 struct Tile {
   static constexpr int TH = 4 * R;
   static constexpr int PH = TH + 2;
-  static constexpr int PIX = PH * PW;
-  static constexpr int SLOTS = PIX * PIX_SLOTS;
-  static constexpr int LOADS16 = (SLOTS + 63) / 64;       // 16-byte-per-lane wave loads
-  static constexpr int LOADS4 = (SLOTS * 4 + 63) / 64;    // 4-byte-per-lane wave loads
-  static constexpr int BUF_SLOTS = LOADS16 * 64;          // >= LOADS4 * 16
+  static constexpr int PATCH = PH * PW * PSTR;   // halves
+  static constexpr int ZERO = PATCH;             // 8 zero halves after the patch
 };
 
 __device__ __forceinline__ half8 as_half8(uint4 v) { return __builtin_bit_cast(half8, v); }
 
-// Global -> LDS loads of one chunk's halo patch into `buf` (BUF_SLOTS slots).
-// Wave load k fills slots [64 k, 64 k + 64); slot s is pixel s / 5, channel
-// group s % 5 (group 4 is the pad slot).  Sources whose stored channel count
-// is a multiple of 8 move 16 bytes per lane; others (the 12-channel network
-// input) move 4 bytes per lane.
-template <int R>
-__device__ __forceinline__ void load_patch(uint4* buf, const _Float16* src, int cs, int coff,
-                                           bool up, int h, int w, int y0, int x0, int wave,
-                                           int lane) {
-  using T = Tile<R>;
+// Stage one chunk's halo patch.  VEC16: channels move in 8-channel (16 B)
+// units, else in 4-channel (8 B) units.  Channels past the source's stored
+// count and pixels outside the image are zero.
+template <int R, int CG, bool VEC16>
+__device__ __forceinline__ void stage_patch(_Float16* lds, const _Float16* src, int cs, int coff,
+                                            bool up, int h, int w, int y0, int x0, int tid) {
+  constexpr int PH = Tile<R>::PH;
+  constexpr int UNITS = VEC16 ? CG : 2 * CG;
+  constexpr int UCH = VEC16 ? 8 : 4;
+  constexpr int TOTAL = PH * PW * UNITS;
   const int sw = up ? (w >> 1) : w;
-  if ((cs & 7) == 0) {
-    for (int k = wave; k < T::LOADS16; k += 4) {
-      const int s = k * 64 + lane;
-      const int p = s / PIX_SLOTS;
-      const int u = s - p * PIX_SLOTS;
-      const void* gp = g_zero16;
-      if (u < 4 && p < T::PIX) {
-        const int py = p / PW;
-        const int iy = y0 - 1 + py;
-        const int ix = x0 - 1 + (p - py * PW);
-        const int c = coff + 8 * u;
-        if (iy >= 0 && iy < h && ix >= 0 && ix < w && c < cs) {
-          const int sy = up ? (iy >> 1) : iy;
-          const int sx = up ? (ix >> 1) : ix;
-          gp = src + ((size_t)sy * sw + sx) * cs + c;
-        }
-      }
-      __builtin_amdgcn_global_load_lds(gp, buf + k * 64, 16, 0, 0);
-    }
-  } else {
-    for (int k = wave; k < T::LOADS4; k += 4) {
-      const int d = k * 64 + lane;          // dword index
-      const int s = d >> 2;
-      const int p = s / PIX_SLOTS;
-      const int u = s - p * PIX_SLOTS;
-      const void* gp = g_zero16;
-      if (u < 4 && p < T::PIX) {
-        const int py = p / PW;
-        const int iy = y0 - 1 + py;
-        const int ix = x0 - 1 + (p - py * PW);
-        const int c = coff + 8 * u + 2 * (d & 3);
-        if (iy >= 0 && iy < h && ix >= 0 && ix < w && c < cs) {
-          const int sy = up ? (iy >> 1) : iy;
-          const int sx = up ? (ix >> 1) : ix;
-          gp = src + ((size_t)sy * sw + sx) * cs + c;
-        }
-      }
-      __builtin_amdgcn_global_load_lds(gp, reinterpret_cast<uint32_t*>(buf) + k * 64, 4, 0, 0);
+#pragma unroll 4
+  for (int u = tid; u < TOTAL; u += THREADS) {
+    const int pp = u / UNITS;
+    const int q = u - pp * UNITS;
+    const int py = pp / PW;
+    const int px = pp - py * PW;
+    const int iy = y0 - 1 + py;
+    const int ix = x0 - 1 + px;
+    const int c = coff + UCH * q;
+    const bool inside = iy >= 0 && iy < h && ix >= 0 && ix < w && c < cs;
+    const int sy = up ? (iy >> 1) : iy;
+    const int sx = up ? (ix >> 1) : ix;
+    const _Float16* p = src + ((size_t)sy * sw + sx) * cs + c;
+    if constexpr (VEC16) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (inside) v = *reinterpret_cast<const uint4*>(p);
+      *reinterpret_cast<uint4*>(lds + pp * PSTR + UCH * q) = v;
+    } else {
+      uint2 v = make_uint2(0u, 0u);
+      if (inside) v = *reinterpret_cast<const uint2*>(p);
+      *reinterpret_cast<uint2*>(lds + pp * PSTR + UCH * q) = v;
     }
   }
 }
 
-// Global -> LDS loads of one chunk's weights for output fragments
-// [q0, q0 + NFW) (wchunk already offset by q0): LDS fragment (3 j + ky) * NFW + q
-// is global fragment chunk.wfrag + (3 j + ky) * nf + q, one 1 KB wave load each.
-template <int NFW>
-__device__ __forceinline__ void load_weights(uint4* abuf, const uint4* wchunk, int nf, int wave) {
-  for (int i = wave; i < 9 * NFW; i += 4) {
-    const int jk = i / NFW;
-    __builtin_amdgcn_global_load_lds(wchunk + (jk * nf + (i - jk * NFW)) * 64, abuf + i * 64, 16,
-                                     0, 0);
-  }
-}
-
-template <int NFW, int R>
-__device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], const uint4* abuf,
-                                          const uint4* buf, int wave, int g, int c, int lane) {
-  const _Float16* patch = reinterpret_cast<const _Float16*>(buf);
+// MFMAs of one chunk for one wave: rows [R * wave, R * wave + R) of the
+// tile, output fragments [q0, q0 + NFW) of nf.  `acur` holds the chunk's
+// column-group-0 weights on entry; each column group loads the next one's
+// weights (or those of the next chunk, `wnext`) before its MFMAs, so weight
+// loads overlap the matrix work.  On return `acur` holds the next chunk's.
+template <int NFW, int R, int CG, bool PF>
+__device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], uint4 (&acur)[3][NFW],
+                                          const _Float16* lds, const uint4* wchunk,
+                                          const uint4* wnext, int nf, int wave, int g, int c) {
+  constexpr int NCG = (3 * CG + 3) / 4;
+#pragma unroll 1
+  for (int j = 0; j < NCG; ++j) {
+    if constexpr (!PF) {
+      // no register double buffer (keeps occupancy): load this group's weights now
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    uint4 a[3][NFW];
+      for (int ky = 0; ky < 3; ++ky)
 #pragma unroll
-    for (int ky = 0; ky < 3; ++ky)
+        for (int q = 0; q < NFW; ++q) acur[ky][q] = wchunk[((size_t)(j * 3 + ky) * nf + q) * 64];
+    }
+    const uint4* wn = !PF ? nullptr : j + 1 < NCG ? wchunk + (size_t)(j + 1) * 3 * nf * 64 : wnext;
+    uint4 anext[3][NFW];
+    if (wn) {
 #pragma unroll
-      for (int q = 0; q < NFW; ++q) a[ky][q] = abuf[((3 * j + ky) * NFW + q) * 64 + lane];
-    const int base = ((R * wave) * PW + c + j) * PIX_HALVES + SLOT_HALVES * g;
+      for (int ky = 0; ky < 3; ++ky)
+#pragma unroll
+        for (int q = 0; q < NFW; ++q) anext[ky][q] = wn[(ky * nf + q) * 64];
+    }
+    const int slot = 4 * j + g;
+    int base = Tile<R>::ZERO, rstride = 0;
+    if (slot < 3 * CG) {
+      const int kx = slot / CG;
+      const int grp = slot - kx * CG;
+      base = ((R * wave) * PW + c + kx) * PSTR + 8 * grp;
+      rstride = PW * PSTR;
+    }
 #pragma unroll
     for (int p = 0; p < R + 2; ++p) {
-      const half8 b = *reinterpret_cast<const half8*>(patch + base + p * PW * PIX_HALVES);
+      const half8 b = *reinterpret_cast<const half8*>(lds + base + p * rstride);
 #pragma unroll
       for (int ky = 0; ky < 3; ++ky) {
         const int r = p - ky;
         if (r >= 0 && r < R) {
 #pragma unroll
           for (int q = 0; q < NFW; ++q)
-            acc[r][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(a[ky][q]), b,
+            acc[r][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(acur[ky][q]), b,
                                                                acc[r][q], 0, 0, 0);
         }
       }
+    }
+    if (wn) {
+#pragma unroll
+      for (int ky = 0; ky < 3; ++ky)
+#pragma unroll
+        for (int q = 0; q < NFW; ++q) acur[ky][q] = anext[ky][q];
     }
   }
 }
@@ -192,12 +172,77 @@ __device__ __forceinline__ void store4(void* y, size_t idx, float v0, float v1, 
   }
 }
 
-// Bias, ReLU, optional 2x2 pool, store; then clear the accumulators.
 template <int NFW, int R, bool OUTF32>
-__device__ __forceinline__ void epilogue(floatx4 (&acc)[R][NFW], const ConvF16Args& a, int q0,
-                                         int y0, int x0, int wave, int g, int c, int pool,
-                                         int relu) {
-  const int cbase = 4 * a.nf * g + 4 * q0;
+__global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
+    ConvF16Args a, int upcat, int pool, int relu) {
+  using T = Tile<R>;
+  __shared__ __attribute__((aligned(16))) _Float16 lds[T::PATCH + 8];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, c = lane & 15;
+  const int nf = a.nf;
+  const int q0 = blockIdx.y * NFW;          // this block's output fragments
+  // Weight prefetch costs 12 * NFW registers; use it only where two waves
+  // per SIMD still fit.
+  constexpr bool PF = NFW * R <= 16;
+
+  // XCD-aware tile order: block b runs on XCD b % 8; give each XCD a band.
+  const int ntiles = a.tiles_x * a.tiles_y;
+  const int per = (ntiles + kXcds - 1) / kXcds;
+  const int tile = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  if (tile >= ntiles) return;
+  const int ty = tile / a.tiles_x;
+  const int tx = tile - ty * a.tiles_x;
+  const int y0 = ty * T::TH, x0 = tx * TW;
+
+  if (tid < 2) reinterpret_cast<uint2*>(lds + T::ZERO)[tid] = make_uint2(0u, 0u);
+
+  floatx4 acc[R][NFW];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int q = 0; q < NFW; ++q) acc[r][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const uint4* wf = static_cast<const uint4*>(a.wfrag) + lane + q0 * 64;
+  uint4 acur[3][NFW];
+  if (PF) {
+    const uint4* w0 = wf + (size_t)a.chunk[0].wfrag * 64;
+#pragma unroll
+    for (int ky = 0; ky < 3; ++ky)
+#pragma unroll
+      for (int q = 0; q < NFW; ++q) acur[ky][q] = w0[(ky * nf + q) * 64];
+  }
+#pragma unroll 1
+  for (int ci = 0; ci < a.nchunks4; ++ci) {
+    const ConvChunk ch = a.chunk[ci];
+    const _Float16* src = static_cast<const _Float16*>(ch.src ? a.src1 : a.src0);
+    const int cs = ch.src ? a.cs1 : a.cs0;
+    const bool up = upcat && ch.src == 0;
+    const uint4* wnext = ci + 1 < a.nchunks ? wf + (size_t)a.chunk[ci + 1].wfrag * 64 : nullptr;
+    __syncthreads();
+    if ((cs & 7) == 0) stage_patch<R, 4, true>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid);
+    else stage_patch<R, 4, false>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid);
+    __syncthreads();
+    mma_chunk<NFW, R, 4, PF>(acc, acur, lds, wf + (size_t)ch.wfrag * 64, wnext, nf, wave, g, c);
+  }
+#pragma unroll 1
+  for (int ci = a.nchunks4; ci < a.nchunks; ++ci) {
+    const ConvChunk ch = a.chunk[ci];
+    const _Float16* src = static_cast<const _Float16*>(ch.src ? a.src1 : a.src0);
+    const int cs = ch.src ? a.cs1 : a.cs0;
+    const bool up = upcat && ch.src == 0;
+    const uint4* wnext = ci + 1 < a.nchunks ? wf + (size_t)a.chunk[ci + 1].wfrag * 64 : nullptr;
+    __syncthreads();
+    if ((cs & 7) == 0) stage_patch<R, 2, true>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid);
+    else stage_patch<R, 2, false>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid);
+    __syncthreads();
+    mma_chunk<NFW, R, 2, PF>(acc, acur, lds, wf + (size_t)ch.wfrag * 64, wnext, nf, wave, g, c);
+  }
+
+  // Epilogue.  Lane (g, c) holds rows 4g..4g+3 of every fragment: fragment
+  // q0 + q carries output channels cbase + 4 (q0 + q) + i with
+  // cbase = 4 * nf * g, for pixel column c.
+  const int cbase = 4 * nf * g + 4 * q0;
   float bv[NFW][4];
 #pragma unroll
   for (int q = 0; q < NFW; ++q)
@@ -241,82 +286,6 @@ __device__ __forceinline__ void epilogue(floatx4 (&acc)[R][NFW], const ConvF16Ar
       }
     }
   }
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int q = 0; q < NFW; ++q) acc[r][q] = floatx4{0.f, 0.f, 0.f, 0.f};
-}
-
-template <int NFW, int R, bool OUTF32>
-__global__ __launch_bounds__(THREADS, 1) void conv3x3_f16_mfma(ConvF16Args a, int upcat, int pool,
-                                                                int relu) {
-  using T = Tile<R>;
-  __shared__ __attribute__((aligned(16))) uint4 buf0[T::BUF_SLOTS];
-  __shared__ __attribute__((aligned(16))) uint4 buf1[T::BUF_SLOTS];
-  __shared__ __attribute__((aligned(16))) uint4 wbuf0[9 * NFW * 64];
-  __shared__ __attribute__((aligned(16))) uint4 wbuf1[9 * NFW * 64];
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, c = lane & 15;
-  const int nf = a.nf;
-  const int q0 = blockIdx.y * NFW;
-
-  // Items: workgroup bx runs on XCD bx % 8; XCD x owns tiles
-  // [x * per, (x + 1) * per), taken round robin by its gridDim.x / 8
-  // workgroups.  Item k is chunk k % nch of this workgroup's (k / nch)-th tile.
-  const int ntiles = a.tiles_x * a.tiles_y;
-  const int per = (ntiles + kXcds - 1) / kXcds;
-  const int xcd = blockIdx.x % kXcds;
-  const int first = blockIdx.x / kXcds;
-  const int stride = gridDim.x / kXcds;
-  const int nch = a.nchunks;
-  auto item_valid = [&](int k) {
-    const int local = first + (k / nch) * stride;
-    return local < per && xcd * per + local < ntiles;
-  };
-  auto item_tile = [&](int k) { return xcd * per + first + (k / nch) * stride; };
-
-  if (!item_valid(0)) return;
-
-  auto issue = [&](int k, uint4* wdst, uint4* dst) {
-    const ConvChunk ch = a.chunk[k % nch];
-    const int t = item_tile(k);
-    const int ty = t / a.tiles_x;
-    const int tx = t - ty * a.tiles_x;
-    load_weights<NFW>(wdst, static_cast<const uint4*>(a.wfrag) + ((size_t)ch.wfrag + q0) * 64, nf,
-                      wave);
-    load_patch<R>(dst, static_cast<const _Float16*>(ch.src ? a.src1 : a.src0),
-                  ch.src ? a.cs1 : a.cs0, ch.coff, upcat && ch.src == 0, a.h, a.w, ty * T::TH,
-                  tx * TW, wave, lane);
-  };
-
-  floatx4 acc[R][NFW];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int q = 0; q < NFW; ++q) acc[r][q] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  issue(0, wbuf0, buf0);
-
-  // One pipeline step: wait for item k's loads, start item k + 1's, compute k.
-  auto step = [&](int k, const uint4* wcur, uint4* wnxt, const uint4* cur, uint4* nxt) -> bool {
-    __syncthreads();
-    const bool more = item_valid(k + 1);
-    if (more) issue(k + 1, wnxt, nxt);
-    mma_chunk<NFW, R>(acc, wcur, cur, wave, g, c, lane);
-    if (k % nch == nch - 1) {
-      const int t = item_tile(k);
-      const int ty = t / a.tiles_x;
-      epilogue<NFW, R, OUTF32>(acc, a, q0, ty * T::TH, (t - ty * a.tiles_x) * TW, wave, g, c,
-                               pool, relu);
-    }
-    return more;
-  };
-#pragma unroll 1
-  for (int k = 0;; k += 2) {
-    if (!step(k, wbuf0, wbuf1, buf0, buf1)) break;
-    if (!step(k + 1, wbuf1, wbuf0, buf1, buf0)) break;
-  }
 }
 
 template <int NFW, int R>
@@ -325,11 +294,7 @@ hipError_t launch_shape(ConvF16Args a, int nsplit, bool upcat, bool pool, bool r
   a.tiles_x = cdiv(a.w, TW);
   a.tiles_y = cdiv(a.h, Tile<R>::TH);
   const int ntiles = a.tiles_x * a.tiles_y;
-  // one resident workgroup per CU over all splits, at most one per tile
-  int gx = cdiv(cdiv(kCUs, nsplit), kXcds) * kXcds;
-  const int gmax = cdiv(ntiles, kXcds) * kXcds;
-  if (gx > gmax) gx = gmax;
-  const dim3 grid(gx, nsplit), block(THREADS);
+  const dim3 grid(cdiv(ntiles, kXcds) * kXcds, nsplit), block(THREADS);
   if (out_f32)
     hipLaunchKernelGGL((conv3x3_f16_mfma<NFW, R, true>), grid, block, 0, stream, a, (int)upcat,
                        (int)pool, (int)relu);
@@ -342,68 +307,83 @@ hipError_t launch_shape(ConvF16Args a, int nsplit, bool upcat, bool pool, bool r
 template <int NFW>
 hipError_t launch_rows(const ConvF16Args& a, int rows, int nsplit, bool upcat, bool pool,
                        bool relu, bool out_f32, hipStream_t stream) {
-  if constexpr (NFW <= 3) {
+  if constexpr (NFW <= 4) {
     if (rows == 8) return launch_shape<NFW, 8>(a, nsplit, upcat, pool, relu, out_f32, stream);
+    if (rows == 2) return launch_shape<NFW, 2>(a, nsplit, upcat, pool, relu, out_f32, stream);
   }
-  if (rows == 2) return launch_shape<NFW, 2>(a, nsplit, upcat, pool, relu, out_f32, stream);
   return launch_shape<NFW, 4>(a, nsplit, upcat, pool, relu, out_f32, stream);
 }
 
 }  // namespace
 
-// Work decomposition: tile height 4 * rows and NFW (<= 4) of the nf output
-// fragments per workgroup, nf / NFW workgroups sharing each tile.  Tiles as
-// tall as possible while every CU still gets four or more items (32-row
-// tiles only up to NFW = 3, whose two patch and weight buffers fit in LDS).
+// Work decomposition.  Each block covers a (4 R) x 16 pixel tile and NFW of
+// the nf output fragments.  Big images use R = 8 with all fragments; smaller
+// ones split the output channels across blocks and shrink the tile until the
+// grid has about four blocks per CU.
 void conv_f16_plan(int h, int w, int nf, int* rows, int* nfw) {
-  int width = nf;
-  if (nf > 4) width = nf % 4 == 0 ? 4 : (nf % 3 == 0 ? 3 : (nf % 2 == 0 ? 2 : 1));
-  const int split = nf / width;
-  *nfw = width;
-  for (int r : {8, 4}) {
-    if (r == 8 && width > 3) continue;   // LDS: 2 x (49 KB patch + 9 NFW KB weights)
-    const long items = (long)cdiv(w, TW) * cdiv(h, 4 * r) * split;
-    if (items >= 4L * kCUs) {
-      *rows = r;
-      return;
+  constexpr long kTarget = 1024;
+  const long t8 = (long)cdiv(w, TW) * cdiv(h, 32);
+  if (nf <= 4 && t8 >= kTarget / 2) {
+    *rows = 8;
+    *nfw = nf;
+    return;
+  }
+  for (int r : {4, 2}) {
+    const long t = (long)cdiv(w, TW) * cdiv(h, 4 * r);
+    for (int split = 1; split <= nf; ++split) {
+      if (nf % split) continue;
+      const int width = nf / split;
+      if (r == 2 && width > 4) continue;
+      if (t * split >= kTarget) {
+        *rows = r;
+        *nfw = width;
+        return;
+      }
     }
   }
   *rows = 2;
+  *nfw = 1;
 }
 
-// Grid of the conv launch (for reporting).
+// Workgroups of the launch (for reporting).
 int conv_f16_blocks(int h, int w, int nf) {
   int rows, nfw;
   conv_f16_plan(h, w, nf, &rows, &nfw);
-  const int nsplit = nf / nfw;
-  const int ntiles = cdiv(w, TW) * cdiv(h, 4 * rows);
-  int gx = cdiv(cdiv(kCUs, nsplit), kXcds) * kXcds;
-  const int gmax = cdiv(ntiles, kXcds) * kXcds;
-  return (gx > gmax ? gmax : gx) * nsplit;
+  return cdiv(cdiv(w, TW) * cdiv(h, 4 * rows), kXcds) * kXcds * (nf / nfw);
 }
 
 bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out) {
   ConvLayout L{};
   L.nf = cdiv(stored_channels(cout), 16);
   if (L.nf < 1 || L.nf > 8) return false;
-  // Chunks of 32 channels per source, the last one zero-filled past the
-  // source's stored channels; a chunk is 3 column groups x 3 ky x nf
-  // fragments.
-  int frag = 0, n = 0;
+  // Chunks of up to 32 channels per source; a chunk is processed as 4 groups
+  // of 8 channels if it holds more than 16, else as 2 (missing channels are
+  // zero).  Four-group chunks come first, then two-group chunks, each in
+  // source order: the kernel runs them in two loops of one shape each.
+  ConvChunk full[kMaxChunks], half[kMaxChunks];
+  int nfull = 0, nhalf = 0;
   const int cs[2] = {cin0_stored, cin1_stored};
   for (int s = 0; s < 2; ++s)
     for (int off = 0; off < cs[s]; off += kChunkChannels) {
-      if (n >= kMaxChunks) return false;
-      ConvChunk& ch = L.chunk[n++];
+      const int rem = cs[s] - off < kChunkChannels ? cs[s] - off : kChunkChannels;
+      ConvChunk ch{};
       ch.src = s;
       ch.coff = off;
-      ch.cg = 4;
-      ch.ncg = 3;
-      ch.wfrag = frag;
-      frag += ch.ncg * 3 * L.nf;
+      ch.cg = rem > 16 ? 4 : 2;
+      ch.ncg = cdiv(3 * ch.cg, 4);
+      if (nfull + nhalf >= kMaxChunks) return false;
+      if (ch.cg == 4) full[nfull++] = ch;
+      else half[nhalf++] = ch;
     }
+  int frag = 0, n = 0;
+  for (int i = 0; i < nfull + nhalf; ++i) {
+    ConvChunk ch = i < nfull ? full[i] : half[i - nfull];
+    ch.wfrag = frag;
+    frag += ch.ncg * 3 * L.nf;
+    L.chunk[n++] = ch;
+  }
   L.nchunks = n;
-  L.nchunks4 = n;
+  L.nchunks4 = nfull;
   L.total_frags = frag;
   L.bias_bytes = align256(sizeof(float) * 16 * L.nf);
   L.bytes = L.bias_bytes + (size_t)frag * kFragBytes;
@@ -423,6 +403,10 @@ hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, 
     case 2: return launch_rows<2>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
     case 3: return launch_rows<3>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
     case 4: return launch_rows<4>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
+    case 5: return launch_rows<5>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
+    case 6: return launch_rows<6>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
+    case 7: return launch_rows<7>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
+    case 8: return launch_rows<8>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -30,7 +30,7 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 struct ConvChunk {
   int src;    // 0: first source (upsampled source for the decoder), 1: skip
   int coff;   // first stored channel of the chunk within its source
-  int cg;     // 8-channel groups the chunk is processed as (always 4)
+  int cg;     // 8-channel groups the chunk is processed as (2 or 4)
   int ncg;    // column groups of the chunk: ceil(3 * cg / 4)
   int wfrag;  // index of the chunk's first weight fragment
 };
