@@ -714,10 +714,16 @@ int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int dtype
   int nb = 0;
   if (dtype == OIDN_F16) {
     const int nf = cdiv(stored_channels(s[layer].cout), 16);
-    int rows = 4, nfw = nf;
-    conv_f16_plan(h, w, nf, &rows, &nfw);
-    snprintf(buf, cap, "conv3x3_f16_mfma<%d, %d, %s>", nfw, rows, final_layer ? "true" : "false");
-    nb = conv_f16_blocks(h, w, nf);
+    const int cs0 = layer == 0 ? internal_input_lanes(in_channels, dtype)
+                               : stored_channels(s[layer].cin0);
+    const int cs1 = kUNet[layer].skip == 0 ? internal_input_lanes(in_channels, dtype)
+                                           : (s[layer].cin1 ? stored_channels(s[layer].cin1) : 0);
+    ConvLayout L;
+    conv_f16_layout(stored_channels(s[layer].cin0), s[layer].cin1 ? stored_channels(s[layer].cin1) : 0,
+                    s[layer].cout, &L);
+    (void)cs0;
+    (void)cs1;
+    conv_f16_describe(h, w, nf, L.nchunks4, L.nchunks - L.nchunks4, final_layer, buf, cap, &nb);
   } else {
     snprintf(buf, cap, "conv3x3_f32_direct");
     const int oh = kUNet[layer].pool ? h / 2 : h, ow = kUNet[layer].pool ? w / 2 : w;

@@ -34,6 +34,8 @@
 // The per-pixel reduction order depends only on the channel layout, never on
 // the pixel position or the image size, so tiled and untiled runs agree bit
 // for bit wherever their inputs agree.
+#include <cstdio>
+
 #include "internal.h"
 
 namespace oidn {
@@ -391,12 +393,29 @@ bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out
   return true;
 }
 
+void conv_f16_describe(int h, int w, int nf, int n4, int n2, bool out_f32, char* buf, int cap,
+                       int* blocks) {
+  int rows, nfw;
+  if (conv_f16_ws_plan(h, w, nf, n4, n2, out_f32, &rows, &nfw)) {
+    snprintf(buf, cap, "conv3x3_f16_ws<%d, %d, %d, %d, %s>", nfw, rows, n4, n2,
+             out_f32 ? "true" : "false");
+    *blocks = conv_f16_ws_blocks(h, w, nf, rows, nfw);
+    return;
+  }
+  conv_f16_plan(h, w, nf, &rows, &nfw);
+  snprintf(buf, cap, "conv3x3_f16_mfma<%d, %d, %s>", nfw, rows, out_f32 ? "true" : "false");
+  *blocks = conv_f16_blocks(h, w, nf);
+}
+
 hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, bool relu,
                            bool out_f32, hipStream_t stream) {
   int rows = 4, nfw = nf;
-  conv_f16_plan(a.h, a.w, nf, &rows, &nfw);
   ConvF16Args b = a;
   b.nf = nf;
+  if (conv_f16_ws_plan(a.h, a.w, nf, a.nchunks4, a.nchunks - a.nchunks4, out_f32, &rows, &nfw))
+    return launch_conv_f16_ws(b, rows, nfw, a.nchunks4, a.nchunks - a.nchunks4, upcat, pool, relu,
+                              out_f32, stream);
+  conv_f16_plan(a.h, a.w, nf, &rows, &nfw);
   const int nsplit = nf / nfw;
   switch (nfw) {
     case 1: return launch_rows<1>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);

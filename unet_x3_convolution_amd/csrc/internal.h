@@ -78,9 +78,20 @@ hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, 
                            bool out_f32, hipStream_t stream);
 
 // Tile height (4 * rows) and output fragments per block chosen for a conv,
-// and the launch's workgroup count.
+// and the launch's workgroup count (multi-workgroup kernel).
 void conv_f16_plan(int h, int w, int nf, int* rows, int* nfw);
 int conv_f16_blocks(int h, int w, int nf);
+
+// Weight-stationary persistent kernel for large layers: plan (false if the
+// shape is not covered), workgroup count, launch.
+bool conv_f16_ws_plan(int h, int w, int nf, int n4, int n2, bool out_f32, int* rows, int* nfw);
+int conv_f16_ws_blocks(int h, int w, int nf, int rows, int nfw);
+hipError_t launch_conv_f16_ws(const ConvF16Args& a, int rows, int nfw, int n4, int n2, bool upcat,
+                              bool pool, bool relu, bool out_f32, hipStream_t stream);
+
+// Name of the kernel instance launch_conv_f16 runs for a shape, and its grid.
+void conv_f16_describe(int h, int w, int nf, int n4, int n2, bool out_f32, char* buf, int cap,
+                       int* blocks);
 
 // ---------------------------------------------------------------------------
 // fp32 direct conv (VALU FMA).  Packed weights: bias (cout_stored floats,
