@@ -79,9 +79,9 @@ def test_layer_table_matches_oracle(in_channels):
 def _decode_f16(packed, cin0, cin1, cout):
     """Decode the fp16 fragment layout from its documented description:
     bias (16 * nf floats, 256-aligned), then per chunk (<= 32 stored channels
-    of one source, processed as cg = 4 groups of 8 channels if it holds more
-    than 16, else cg = 2; all cg = 4 chunks first, then the cg = 2 ones, each
-    in source order), per column group j, per ky, per output
+    of one source, sources and channels in order, processed as cg = 4 groups
+    of 8 channels if it holds more than 16, else cg = 2), per column group j,
+    per ky, per output
     fragment q, a 1 KB fragment of 64 lanes x 8 halves; lane l holds row
     r = l % 16 (output channel 4 * nf * (r // 4) + 4 * q + r % 4) and slot
     4 * j + l // 16 of the chunk, slot = kx * cg + group, channels
@@ -94,7 +94,6 @@ def _decode_f16(packed, cin0, cin1, cout):
     w = np.full((cout, 3, 3, cin0 + cin1), np.nan, np.float32)
     chunks = [(s_idx, off, 4 if min(32, cs[s_idx] - off) > 16 else 2)
               for s_idx in range(2) for off in range(0, cs[s_idx], 32)]
-    chunks = [c for c in chunks if c[2] == 4] + [c for c in chunks if c[2] == 2]
     f = 0
     for s_idx, off, cg in chunks:
         if True:

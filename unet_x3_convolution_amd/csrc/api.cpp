@@ -192,7 +192,9 @@ int run_conv(const void* src0, int cin0, const void* src1, int cin1, bool upcat,
     a.y = y;
     a.cout_stored = stored_channels(cout);
     a.nchunks = L.nchunks;
-    a.nchunks4 = L.nchunks4;
+    a.nup4 = L.nup4;
+    a.nup = L.nup;
+    a.npl4 = L.npl4;
     for (int i = 0; i < L.nchunks; ++i) a.chunk[i] = L.chunk[i];
     e = launch_conv_f16(a, L.nf, upcat, pool, relu, out_dtype == OIDN_F32, stream);
   } else {
@@ -714,16 +716,7 @@ int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int dtype
   int nb = 0;
   if (dtype == OIDN_F16) {
     const int nf = cdiv(stored_channels(s[layer].cout), 16);
-    const int cs0 = layer == 0 ? internal_input_lanes(in_channels, dtype)
-                               : stored_channels(s[layer].cin0);
-    const int cs1 = kUNet[layer].skip == 0 ? internal_input_lanes(in_channels, dtype)
-                                           : (s[layer].cin1 ? stored_channels(s[layer].cin1) : 0);
-    ConvLayout L;
-    conv_f16_layout(stored_channels(s[layer].cin0), s[layer].cin1 ? stored_channels(s[layer].cin1) : 0,
-                    s[layer].cout, &L);
-    (void)cs0;
-    (void)cs1;
-    conv_f16_describe(h, w, nf, L.nchunks4, L.nchunks - L.nchunks4, final_layer, buf, cap, &nb);
+    conv_f16_describe(h, w, nf, final_layer, buf, cap, &nb);
   } else {
     snprintf(buf, cap, "conv3x3_f32_direct");
     const int oh = kUNet[layer].pool ? h / 2 : h, ow = kUNet[layer].pool ? w / 2 : w;

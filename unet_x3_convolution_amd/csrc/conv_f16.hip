@@ -50,40 +50,48 @@ constexpr int PSTR = 40;                      // halves per patch pixel: 32 + 8 
 constexpr int THREADS = 256;
 constexpr int kXcds = 8;
 
+constexpr int LPW = TW / 2 + 2;               // half-resolution patch width
+
 template <int R>
 struct Tile {
   static constexpr int TH = 4 * R;
   static constexpr int PH = TH + 2;
+  static constexpr int LPH = 2 * R + 2;         // half-resolution patch height
   static constexpr int PATCH = PH * PW * PSTR;   // halves
   static constexpr int ZERO = PATCH;             // 8 zero halves after the patch
 };
 
 __device__ __forceinline__ half8 as_half8(uint4 v) { return __builtin_bit_cast(half8, v); }
 
-// Stage one chunk's halo patch.  VEC16: channels move in 8-channel (16 B)
-// units, else in 4-channel (8 B) units.  Channels past the source's stored
-// count and pixels outside the image are zero.
-template <int R, int CG, bool VEC16>
+// Stage one chunk's halo patch.  Full resolution: (4R + 2) x 18 pixels at
+// (y0 - 1, x0 - 1).  UP (the decoder's upsampled source): the same window
+// at half resolution, (2R + 2) x 10 low-resolution pixels at
+// (y0 / 2 - 1, x0 / 2 - 1) -- nearest upsampling repeats each of them 2 x 2
+// times, so staging them once cuts the staged bytes about four-fold.
+// VEC16: channels move in 8-channel (16 B) units, else in 4-channel (8 B)
+// units.  Channels past the source's stored count and pixels outside the
+// image are zero.
+template <int R, int CG, bool VEC16, bool UP>
 __device__ __forceinline__ void stage_patch(_Float16* lds, const _Float16* src, int cs, int coff,
-                                            bool up, int h, int w, int y0, int x0, int tid) {
-  constexpr int PH = Tile<R>::PH;
+                                            int h, int w, int y0, int x0, int tid) {
+  constexpr int PH = UP ? Tile<R>::LPH : Tile<R>::PH;
+  constexpr int PWD = UP ? LPW : PW;
   constexpr int UNITS = VEC16 ? CG : 2 * CG;
   constexpr int UCH = VEC16 ? 8 : 4;
-  constexpr int TOTAL = PH * PW * UNITS;
-  const int sw = up ? (w >> 1) : w;
+  constexpr int TOTAL = PH * PWD * UNITS;
+  const int sh = UP ? (h >> 1) : h, sw = UP ? (w >> 1) : w;
+  const int oy = UP ? (y0 >> 1) - 1 : y0 - 1, ox = UP ? (x0 >> 1) - 1 : x0 - 1;
 #pragma unroll 4
   for (int u = tid; u < TOTAL; u += THREADS) {
     const int pp = u / UNITS;
     const int q = u - pp * UNITS;
-    const int py = pp / PW;
-    const int px = pp - py * PW;
-    const int iy = y0 - 1 + py;
-    const int ix = x0 - 1 + px;
+    const int py = pp / PWD;
+    const int px = pp - py * PWD;
+    const int iy = oy + py;
+    const int ix = ox + px;
     const int c = coff + UCH * q;
-    const bool inside = iy >= 0 && iy < h && ix >= 0 && ix < w && c < cs;
-    const int sy = up ? (iy >> 1) : iy;
-    const int sx = up ? (ix >> 1) : ix;
-    const _Float16* p = src + ((size_t)sy * sw + sx) * cs + c;
+    const bool inside = iy >= 0 && iy < sh && ix >= 0 && ix < sw && c < cs;
+    const _Float16* p = src + ((size_t)iy * sw + ix) * cs + c;
     if constexpr (VEC16) {
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
       if (inside) v = *reinterpret_cast<const uint4*>(p);
@@ -101,7 +109,7 @@ __device__ __forceinline__ void stage_patch(_Float16* lds, const _Float16* src, 
 // column-group-0 weights on entry; each column group loads the next one's
 // weights (or those of the next chunk, `wnext`) before its MFMAs, so weight
 // loads overlap the matrix work.  On return `acur` holds the next chunk's.
-template <int NFW, int R, int CG, bool PF>
+template <int NFW, int R, int CG, bool PF, bool UP>
 __device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], uint4 (&acur)[3][NFW],
                                           const _Float16* lds, const uint4* wchunk,
                                           const uint4* wnext, int nf, int wave, int g, int c) {
@@ -128,12 +136,20 @@ __device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], uint4 (&acur)[
     if (slot < 3 * CG) {
       const int kx = slot / CG;
       const int grp = slot - kx * CG;
-      base = ((R * wave) * PW + c + kx) * PSTR + 8 * grp;
-      rstride = PW * PSTR;
+      if constexpr (UP) {
+        // patch row p of this wave's window is half-resolution row
+        // (R / 2) wave + (p + 1) / 2; column c + kx - 1 is (c + kx + 1) / 2
+        base = ((R / 2) * wave * LPW + ((c + kx + 1) >> 1)) * PSTR + 8 * grp;
+        rstride = LPW * PSTR;
+      } else {
+        base = ((R * wave) * PW + c + kx) * PSTR + 8 * grp;
+        rstride = PW * PSTR;
+      }
     }
 #pragma unroll
     for (int p = 0; p < R + 2; ++p) {
-      const half8 b = *reinterpret_cast<const half8*>(lds + base + p * rstride);
+      const int prow = UP ? (p + 1) >> 1 : p;
+      const half8 b = *reinterpret_cast<const half8*>(lds + base + prow * rstride);
 #pragma unroll
       for (int ky = 0; ky < 3; ++ky) {
         const int r = p - ky;
@@ -184,6 +200,7 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
   const int g = lane >> 4, c = lane & 15;
   const int nf = a.nf;
   const int q0 = blockIdx.y * NFW;          // this block's output fragments
+  (void)upcat;
   // Weight prefetch costs 12 * NFW registers; use it only where two waves
   // per SIMD still fit.
   constexpr bool PF = NFW * R <= 16;
@@ -214,32 +231,30 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
 #pragma unroll
       for (int q = 0; q < NFW; ++q) acur[ky][q] = w0[(ky * nf + q) * 64];
   }
-#pragma unroll 1
-  for (int ci = 0; ci < a.nchunks4; ++ci) {
-    const ConvChunk ch = a.chunk[ci];
-    const _Float16* src = static_cast<const _Float16*>(ch.src ? a.src1 : a.src0);
-    const int cs = ch.src ? a.cs1 : a.cs0;
-    const bool up = upcat && ch.src == 0;
-    const uint4* wnext = ci + 1 < a.nchunks ? wf + (size_t)a.chunk[ci + 1].wfrag * 64 : nullptr;
-    __syncthreads();
-    if ((cs & 7) == 0) stage_patch<R, 4, true>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid);
-    else stage_patch<R, 4, false>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid);
-    __syncthreads();
-    mma_chunk<NFW, R, 4, PF>(acc, acur, lds, wf + (size_t)ch.wfrag * 64, wnext, nf, wave, g, c);
+  // Chunks run in four loops of one shape each: upsampled source (32- then
+  // 16-channel chunks), then the plain source (32- then 16-channel chunks).
+  const int bounds[5] = {0, a.nup4, a.nup, a.nup + a.npl4, a.nchunks};
+#define OIDN_CHUNK_LOOP(K, CG, UP)                                                              \
+  _Pragma("unroll 1") for (int ci = bounds[K]; ci < bounds[K + 1]; ++ci) {                      \
+    const ConvChunk ch = a.chunk[ci];                                                           \
+    const _Float16* src = static_cast<const _Float16*>(ch.src ? a.src1 : a.src0);               \
+    const int cs = ch.src ? a.cs1 : a.cs0;                                                      \
+    const uint4* wnext = ci + 1 < a.nchunks ? wf + (size_t)a.chunk[ci + 1].wfrag * 64 : nullptr; \
+    __syncthreads();                                                                            \
+    if ((cs & 7) == 0)                                                                          \
+      stage_patch<R, CG, true, UP>(lds, src, cs, ch.coff, a.h, a.w, y0, x0, tid);               \
+    else                                                                                        \
+      stage_patch<R, CG, false, UP>(lds, src, cs, ch.coff, a.h, a.w, y0, x0, tid);              \
+    __syncthreads();                                                                            \
+    mma_chunk<NFW, R, CG, PF, UP>(acc, acur, lds, wf + (size_t)ch.wfrag * 64, wnext, nf, wave,  \
+                                  g, c);                                                        \
   }
-#pragma unroll 1
-  for (int ci = a.nchunks4; ci < a.nchunks; ++ci) {
-    const ConvChunk ch = a.chunk[ci];
-    const _Float16* src = static_cast<const _Float16*>(ch.src ? a.src1 : a.src0);
-    const int cs = ch.src ? a.cs1 : a.cs0;
-    const bool up = upcat && ch.src == 0;
-    const uint4* wnext = ci + 1 < a.nchunks ? wf + (size_t)a.chunk[ci + 1].wfrag * 64 : nullptr;
-    __syncthreads();
-    if ((cs & 7) == 0) stage_patch<R, 2, true>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid);
-    else stage_patch<R, 2, false>(lds, src, cs, ch.coff, up, a.h, a.w, y0, x0, tid);
-    __syncthreads();
-    mma_chunk<NFW, R, 2, PF>(acc, acur, lds, wf + (size_t)ch.wfrag * 64, wnext, nf, wave, g, c);
-  }
+  OIDN_CHUNK_LOOP(0, 4, true)
+  OIDN_CHUNK_LOOP(1, 2, true)
+  OIDN_CHUNK_LOOP(2, 4, false)
+  OIDN_CHUNK_LOOP(3, 2, false)
+#undef OIDN_CHUNK_LOOP
+  (void)upcat;
 
   // Epilogue.  Lane (g, c) holds rows 4g..4g+3 of every fragment: fragment
   // q0 + q carries output channels cbase + 4 (q0 + q) + i with
@@ -358,34 +373,32 @@ bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out
   ConvLayout L{};
   L.nf = cdiv(stored_channels(cout), 16);
   if (L.nf < 1 || L.nf > 8) return false;
-  // Chunks of up to 32 channels per source; a chunk is processed as 4 groups
-  // of 8 channels if it holds more than 16, else as 2 (missing channels are
-  // zero).  Four-group chunks come first, then two-group chunks, each in
-  // source order: the kernel runs them in two loops of one shape each.
-  ConvChunk full[kMaxChunks], half[kMaxChunks];
-  int nfull = 0, nhalf = 0;
+  // Chunks of up to 32 channels, sources in order, channels in order; a chunk
+  // is processed as 4 groups of 8 channels if it holds more than 16, else as
+  // 2 (missing channels are zero).  With two sources the first is the
+  // upsampled one.  Only a source's last chunk can be a 2-group chunk, so the
+  // order is: upsampled 4-group, upsampled 2-group, plain 4-group, plain
+  // 2-group -- the kernel's four loops.
+  const bool two = cin1_stored > 0;
   const int cs[2] = {cin0_stored, cin1_stored};
+  int frag = 0, n = 0;
   for (int s = 0; s < 2; ++s)
     for (int off = 0; off < cs[s]; off += kChunkChannels) {
+      if (n >= kMaxChunks) return false;
       const int rem = cs[s] - off < kChunkChannels ? cs[s] - off : kChunkChannels;
-      ConvChunk ch{};
+      ConvChunk& ch = L.chunk[n++];
       ch.src = s;
       ch.coff = off;
       ch.cg = rem > 16 ? 4 : 2;
       ch.ncg = cdiv(3 * ch.cg, 4);
-      if (nfull + nhalf >= kMaxChunks) return false;
-      if (ch.cg == 4) full[nfull++] = ch;
-      else half[nhalf++] = ch;
+      ch.wfrag = frag;
+      frag += ch.ncg * 3 * L.nf;
+      const bool up = two && s == 0;
+      if (up && ch.cg == 4) ++L.nup4;
+      if (up) ++L.nup;
+      if (!up && ch.cg == 4) ++L.npl4;
     }
-  int frag = 0, n = 0;
-  for (int i = 0; i < nfull + nhalf; ++i) {
-    ConvChunk ch = i < nfull ? full[i] : half[i - nfull];
-    ch.wfrag = frag;
-    frag += ch.ncg * 3 * L.nf;
-    L.chunk[n++] = ch;
-  }
   L.nchunks = n;
-  L.nchunks4 = nfull;
   L.total_frags = frag;
   L.bias_bytes = align256(sizeof(float) * 16 * L.nf);
   L.bytes = L.bias_bytes + (size_t)frag * kFragBytes;
@@ -393,15 +406,8 @@ bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out
   return true;
 }
 
-void conv_f16_describe(int h, int w, int nf, int n4, int n2, bool out_f32, char* buf, int cap,
-                       int* blocks) {
+void conv_f16_describe(int h, int w, int nf, bool out_f32, char* buf, int cap, int* blocks) {
   int rows, nfw;
-  if (conv_f16_ws_plan(h, w, nf, n4, n2, out_f32, &rows, &nfw)) {
-    snprintf(buf, cap, "conv3x3_f16_ws<%d, %d, %d, %d, %s>", nfw, rows, n4, n2,
-             out_f32 ? "true" : "false");
-    *blocks = conv_f16_ws_blocks(h, w, nf, rows, nfw);
-    return;
-  }
   conv_f16_plan(h, w, nf, &rows, &nfw);
   snprintf(buf, cap, "conv3x3_f16_mfma<%d, %d, %s>", nfw, rows, out_f32 ? "true" : "false");
   *blocks = conv_f16_blocks(h, w, nf);
@@ -412,9 +418,6 @@ hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, 
   int rows = 4, nfw = nf;
   ConvF16Args b = a;
   b.nf = nf;
-  if (conv_f16_ws_plan(a.h, a.w, nf, a.nchunks4, a.nchunks - a.nchunks4, out_f32, &rows, &nfw))
-    return launch_conv_f16_ws(b, rows, nfw, a.nchunks4, a.nchunks - a.nchunks4, upcat, pool, relu,
-                              out_f32, stream);
   conv_f16_plan(a.h, a.w, nf, &rows, &nfw);
   const int nsplit = nf / nfw;
   switch (nfw) {

@@ -42,7 +42,8 @@ struct ConvChunk {
 struct ConvLayout {           // shared by the weight packer and the launcher
   int nf;                     // 16-row output-channel fragments (N = 16 * nf)
   int nchunks;
-  int nchunks4;                // chunks processed as 4 groups (they come first)
+  int nup4, nup;               // upsampled-source chunks (4-group ones, all)
+  int npl4;                    // plain-source 4-group chunks
   int total_frags;
   ConvChunk chunk[kMaxChunks];
   size_t bias_bytes;          // fp32 bias, 16 * nf floats, 256-aligned
@@ -70,7 +71,7 @@ struct ConvF16Args {
   int nf;             // output fragments of the whole conv
   int tiles_x, tiles_y;
   int nchunks;
-  int nchunks4;
+  int nup4, nup, npl4;   // chunk ranges of the four loops (see ConvLayout)
   ConvChunk chunk[kMaxChunks];
 };
 
@@ -82,16 +83,8 @@ hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, 
 void conv_f16_plan(int h, int w, int nf, int* rows, int* nfw);
 int conv_f16_blocks(int h, int w, int nf);
 
-// Weight-stationary persistent kernel for large layers: plan (false if the
-// shape is not covered), workgroup count, launch.
-bool conv_f16_ws_plan(int h, int w, int nf, int n4, int n2, bool out_f32, int* rows, int* nfw);
-int conv_f16_ws_blocks(int h, int w, int nf, int rows, int nfw);
-hipError_t launch_conv_f16_ws(const ConvF16Args& a, int rows, int nfw, int n4, int n2, bool upcat,
-                              bool pool, bool relu, bool out_f32, hipStream_t stream);
-
 // Name of the kernel instance launch_conv_f16 runs for a shape, and its grid.
-void conv_f16_describe(int h, int w, int nf, int n4, int n2, bool out_f32, char* buf, int cap,
-                       int* blocks);
+void conv_f16_describe(int h, int w, int nf, bool out_f32, char* buf, int cap, int* blocks);
 
 // ---------------------------------------------------------------------------
 // fp32 direct conv (VALU FMA).  Packed weights: bias (cout_stored floats,
