@@ -57,9 +57,15 @@ struct Tile {
   static constexpr int TH = 4 * R;
   static constexpr int PH = TH + 2;
   static constexpr int LPH = 2 * R + 2;         // half-resolution patch height
-  static constexpr int PATCH = PH * PW * PSTR;   // halves
-  static constexpr int ZERO = PATCH;             // 8 zero halves after the patch
+  // The patch occupies whole 64-slot (1 KB) blocks so that direct
+  // global -> LDS loads, which fill 64 consecutive 16-byte slots each, stay
+  // inside it; 8 zero halves follow.
+  static constexpr int PATCH = (PH * PW * PSTR + 511) / 512 * 512;   // halves
+  static constexpr int ZERO = PATCH;
 };
+
+// Zero block that padding lanes of the direct patch loads read from.
+__device__ __attribute__((aligned(16))) unsigned int g_zero16[4] = {0u, 0u, 0u, 0u};
 
 __device__ __forceinline__ half8 as_half8(uint4 v) { return __builtin_bit_cast(half8, v); }
 
@@ -71,6 +77,45 @@ __device__ __forceinline__ half8 as_half8(uint4 v) { return __builtin_bit_cast(h
 // VEC16: channels move in 8-channel (16 B) units, else in 4-channel (8 B)
 // units.  Channels past the source's stored count and pixels outside the
 // image are zero.
+// Direct global -> LDS staging of the same patch for sources whose stored
+// channel count is a multiple of 8: wave load k fills LDS slots
+// [64 k, 64 k + 64); slot s is patch pixel s / 5, channel group s % 5 (the
+// fifth slot of a pixel is the row pad).  Every load of the chunk is issued
+// back to back (nothing waits on registers); the barrier that follows drains
+// them.  Slots with no data (pad, channel groups past the chunk or the
+// source, pixels outside the image) load the zero block.
+template <int R, int CG, bool UP>
+__device__ __forceinline__ void stage_patch_direct(_Float16* lds, const _Float16* src, int cs,
+                                                   int coff, int h, int w, int y0, int x0,
+                                                   int wave, int lane) {
+  constexpr int PH = UP ? Tile<R>::LPH : Tile<R>::PH;
+  constexpr int PWD = UP ? LPW : PW;
+  constexpr int NPIX = PH * PWD;
+  constexpr int NLOAD = (NPIX * 5 + 63) / 64;
+  static_assert(NLOAD * 64 * 8 <= Tile<R>::PATCH, "patch buffer");
+  const int sh = UP ? (h >> 1) : h, sw = UP ? (w >> 1) : w;
+  const int oy = UP ? (y0 >> 1) - 1 : y0 - 1, ox = UP ? (x0 >> 1) - 1 : x0 - 1;
+  uint4* slots = reinterpret_cast<uint4*>(lds);
+#pragma unroll
+  for (int i = 0; i < (NLOAD + 3) / 4; ++i) {
+    const int k = wave + 4 * i;
+    if (k >= NLOAD) break;
+    const int sl = k * 64 + lane;
+    const int pp = sl / 5;
+    const int u = sl - pp * 5;
+    const void* gp = g_zero16;
+    if (u < CG && pp < NPIX) {
+      const int py = pp / PWD;
+      const int iy = oy + py;
+      const int ix = ox + (pp - py * PWD);
+      const int c = coff + 8 * u;
+      if (iy >= 0 && iy < sh && ix >= 0 && ix < sw && c < cs)
+        gp = src + ((size_t)iy * sw + ix) * cs + c;
+    }
+    __builtin_amdgcn_global_load_lds(gp, slots + k * 64, 16, 0, 0);
+  }
+}
+
 template <int R, int CG, bool VEC16, bool UP>
 __device__ __forceinline__ void stage_patch(_Float16* lds, const _Float16* src, int cs, int coff,
                                             int h, int w, int y0, int x0, int tid) {
@@ -242,7 +287,7 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
     const uint4* wnext = ci + 1 < a.nchunks ? wf + (size_t)a.chunk[ci + 1].wfrag * 64 : nullptr; \
     __syncthreads();                                                                            \
     if ((cs & 7) == 0)                                                                          \
-      stage_patch<R, CG, true, UP>(lds, src, cs, ch.coff, a.h, a.w, y0, x0, tid);               \
+      stage_patch_direct<R, CG, UP>(lds, src, cs, ch.coff, a.h, a.w, y0, x0, wave, lane);       \
     else                                                                                        \
       stage_patch<R, CG, false, UP>(lds, src, cs, ch.coff, a.h, a.w, y0, x0, tid);              \
     __syncthreads();                                                                            \
