@@ -47,6 +47,11 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int TW = 16;                        // tile width (one B fragment)
 constexpr int PW = TW + 2;                    // patch width
 constexpr int PSTR = 40;                      // halves per patch pixel: 32 + 8 pad (80 B)
+// Pixel stride of a chunk of CG channel groups: 4 groups -> 5 slots (80 B),
+// 2 groups -> 3 slots (48 B); both keep 16 consecutive pixels of a fragment
+// read on distinct LDS banks.
+template <int CG>
+constexpr int pstride() { return CG == 4 ? PSTR : 24; }
 constexpr int THREADS = 256;
 constexpr int kXcds = 8;
 
@@ -79,8 +84,8 @@ __device__ __forceinline__ half8 as_half8(uint4 v) { return __builtin_bit_cast(h
 // image are zero.
 // Direct global -> LDS staging of the same patch for sources whose stored
 // channel count is a multiple of 8: wave load k fills LDS slots
-// [64 k, 64 k + 64); slot s is patch pixel s / 5, channel group s % 5 (the
-// fifth slot of a pixel is the row pad).  Every load of the chunk is issued
+// [64 k, 64 k + 64); slot s is patch pixel s / SPP, channel group s % SPP
+// (the last slot of a pixel is the pad).  Every load of the chunk is issued
 // back to back (nothing waits on registers); the barrier that follows drains
 // them.  Slots with no data (pad, channel groups past the chunk or the
 // source, pixels outside the image) load the zero block.
@@ -91,7 +96,8 @@ __device__ __forceinline__ void stage_patch_direct(_Float16* lds, const _Float16
   constexpr int PH = UP ? Tile<R>::LPH : Tile<R>::PH;
   constexpr int PWD = UP ? LPW : PW;
   constexpr int NPIX = PH * PWD;
-  constexpr int NLOAD = (NPIX * 5 + 63) / 64;
+  constexpr int SPP = pstride<CG>() / 8;        // 16-byte slots per pixel
+  constexpr int NLOAD = (NPIX * SPP + 63) / 64;
   static_assert(NLOAD * 64 * 8 <= Tile<R>::PATCH, "patch buffer");
   const int sh = UP ? (h >> 1) : h, sw = UP ? (w >> 1) : w;
   const int oy = UP ? (y0 >> 1) - 1 : y0 - 1, ox = UP ? (x0 >> 1) - 1 : x0 - 1;
@@ -101,8 +107,8 @@ __device__ __forceinline__ void stage_patch_direct(_Float16* lds, const _Float16
     const int k = wave + 4 * i;
     if (k >= NLOAD) break;
     const int sl = k * 64 + lane;
-    const int pp = sl / 5;
-    const int u = sl - pp * 5;
+    const int pp = sl / SPP;
+    const int u = sl - pp * SPP;
     const void* gp = g_zero16;
     if (u < CG && pp < NPIX) {
       const int py = pp / PWD;
@@ -140,11 +146,11 @@ __device__ __forceinline__ void stage_patch(_Float16* lds, const _Float16* src, 
     if constexpr (VEC16) {
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
       if (inside) v = *reinterpret_cast<const uint4*>(p);
-      *reinterpret_cast<uint4*>(lds + pp * PSTR + UCH * q) = v;
+      *reinterpret_cast<uint4*>(lds + pp * pstride<CG>() + UCH * q) = v;
     } else {
       uint2 v = make_uint2(0u, 0u);
       if (inside) v = *reinterpret_cast<const uint2*>(p);
-      *reinterpret_cast<uint2*>(lds + pp * PSTR + UCH * q) = v;
+      *reinterpret_cast<uint2*>(lds + pp * pstride<CG>() + UCH * q) = v;
     }
   }
 }
@@ -181,14 +187,15 @@ __device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], uint4 (&acur)[
     if (slot < 3 * CG) {
       const int kx = slot / CG;
       const int grp = slot - kx * CG;
+      constexpr int PS = pstride<CG>();
       if constexpr (UP) {
         // patch row p of this wave's window is half-resolution row
         // (R / 2) wave + (p + 1) / 2; column c + kx - 1 is (c + kx + 1) / 2
-        base = ((R / 2) * wave * LPW + ((c + kx + 1) >> 1)) * PSTR + 8 * grp;
-        rstride = LPW * PSTR;
+        base = ((R / 2) * wave * LPW + ((c + kx + 1) >> 1)) * PS + 8 * grp;
+        rstride = LPW * PS;
       } else {
-        base = ((R * wave) * PW + c + kx) * PSTR + 8 * grp;
-        rstride = PW * PSTR;
+        base = ((R * wave) * PW + c + kx) * PS + 8 * grp;
+        rstride = PW * PS;
       }
     }
 #pragma unroll
@@ -248,7 +255,7 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
   (void)upcat;
   // Weight prefetch costs 12 * NFW registers; use it only where two waves
   // per SIMD still fit.
-  constexpr bool PF = NFW * R <= 16;
+  constexpr bool PF = NFW * R <= 16 || NFW <= 3;
 
   // XCD-aware tile order: block b runs on XCD b % 8; give each XCD a band.
   const int ntiles = a.tiles_x * a.tiles_y;
