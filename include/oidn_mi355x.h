@@ -130,6 +130,14 @@ int oidn_conv3x3_upcat(const void* low, int c_low, const void* skip, int c_skip,
                        int h, int w, const void* w_packed, void* y, int cout,
                        int in_dtype, int out_dtype, unsigned flags, hipStream_t stream);
 
+/* Name of the kernel instance that oidn_conv3x3 (cin1 == 0) or
+ * oidn_conv3x3_upcat (cin0 = c_low, cin1 = c_skip) runs for this shape,
+ * written NUL-terminated into buf (cap bytes), e.g.
+ * "conv3x3_f16_mfma<4, 8, false>"; *blocks (may be null) receives the
+ * launch's workgroup count.  Same validation as those calls; host only. */
+int oidn_conv3x3_kernel(int h, int w, int cin0, int cin1, int cout, int in_dtype,
+                        int out_dtype, unsigned flags, char* buf, int cap, int* blocks);
+
 /* ========================================================================
  * Elementwise and gather passes
  * ======================================================================== */

@@ -83,7 +83,8 @@ def _decode_f16(packed, cin0, cin1, cout):
     of 8 channels if it holds more than 16, else cg = 2), per column group j,
     per ky, per output
     fragment q, a 1 KB fragment of 64 lanes x 8 halves; lane l holds row
-    r = l % 16 (output channel 4 * nf * (r // 4) + 4 * q + r % 4) and slot
+    r = l % 16 (output channel 32 (q // 2) + 8 (r // 4) + 4 (q % 2) + r % 4
+    when fragments q and q ^ 1 both exist, else 32 (q // 2) + r) and slot
     4 * j + l // 16 of the chunk, slot = kx * cg + group, channels
     coff + 8 * group + 0..7."""
     cs = [O.stored(cin0), O.stored(cin1) if cin1 else 0]
@@ -105,7 +106,8 @@ def _decode_f16(packed, cin0, cin1, cout):
                         f += 1
                         for lane in range(64):
                             r, slot = lane % 16, 4 * j + lane // 16
-                            o = 4 * nf * (r // 4) + 4 * q + r % 4
+                            o = (32 * (q // 2) + 8 * (r // 4) + 4 * (q % 2) + r % 4
+                                 if (q | 1) < nf else 32 * (q // 2) + r)
                             vals = frag[lane].astype(np.float32)
                             if o >= cout or slot >= 3 * cg:
                                 assert np.all(vals == 0)
@@ -240,3 +242,16 @@ def test_unet_argument_errors():
                  U.OIDN_F16, 0) == W
     assert _code(U.oidn_unet_layer_info, 9, 16) == E
     assert "layer 16" in U.last_error()
+
+
+def test_conv_kernel_selection():
+    """The name reported for a single conv is the kernel instance of its
+    launch plan: 32-row tiles with all fragments for large layers, output
+    channels split across workgroups and shorter tiles for small ones."""
+    F, F32, R, P = U.OIDN_F16, U.OIDN_F32, U.OIDN_RELU, U.OIDN_POOL2X2
+    assert U.oidn_conv3x3_kernel(544, 960, 64, 16, 64, F, F, R) == ("conv3x3_f16_mfma<4, 8, false>", 1024)
+    assert U.oidn_conv3x3_kernel(1088, 1920, 32, 0, 3, F, F32, 0) == ("conv3x3_f16_mfma<1, 8, true>", 4080)
+    assert U.oidn_conv3x3_kernel(136, 240, 160, 0, 112, F, F, R)[0] == "conv3x3_f16_mfma<1, 2, false>"
+    assert U.oidn_conv3x3_kernel(8, 8, 9, 0, 32, F32, F32, R)[0] == "conv3x3_f32_direct"
+    with pytest.raises(U.OidnError):
+        U.oidn_conv3x3_kernel(8, 8, 300, 0, 32, F, F, R)

@@ -63,6 +63,12 @@ F16_CASES = [
     (70, 3, 96, 96, U.OIDN_RELU, "f16"),
     (512, 1024, 32, 32, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),   # 32-row tiles, all fragments
     (520, 1030, 12, 64, U.OIDN_RELU, "f16"),                    # 32-row tiles, ragged edges
+    # 16-byte patch loads (sources a multiple of 8 channels), many 32 x 16 tiles
+    (544, 960, 16, 32, U.OIDN_RELU, "f16"),                     # 16-channel chunk, 2 fragments
+    (520, 1030, 32, 3, 0, "f32"),                               # 1 fragment, fp32 out, ragged
+    (512, 1000, 32, 48, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),   # 3 fragments, pooled, ragged
+    (530, 1024, 64, 32, U.OIDN_RELU, "f16"),                    # two chunks per tile
+    (544, 512, 32, 64, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),    # 4 fragments
 ]
 
 
@@ -135,6 +141,8 @@ UPCAT_CASES = [
     (18, 26, 112, 48, 96, "f16"),
     (12, 10, 16, 9, 8, "f32"),
     (512, 1024, 64, 9, 64, "f16"),                              # 32-row tiles
+    (544, 960, 64, 16, 64, "f16"),                              # 16-channel skip, 3 chunks
+    (514, 1026, 32, 16, 32, "f16"),                             # ragged
 ]
 
 
@@ -170,3 +178,24 @@ def test_conv_ladder_config2():
         check(got, oracle_conv(x, cin, wt, b, cout, "f16", flags), cout, "f16",
               f"ladder stage {i} {x.shape[0]}^2 {cin}->{cout}")
         x = got
+
+
+def test_conv_result_independent_of_launch_plan_bit_exact():
+    """Large images run 32-row tiles with all output fragments per
+    workgroup, small ones shorter tiles with the outputs split across
+    workgroups; every output is accumulated in the same order either way, so
+    a conv over a crop reproduces the interior of the conv over the image."""
+    r = np.random.default_rng(7)
+    h, w, cin, cout = 544, 960, 32, 64
+    x = O.round_to(S.relu_normal_activation(r, h, w, cin, cin), "f16")
+    wt = S.he_normal(r, cout, cin)
+    b = S.bias(r, cout)
+    assert U.oidn_conv3x3_kernel(h, w, cin, 0, cout, U.OIDN_F16, U.OIDN_F16, U.OIDN_RELU)[0] == \
+        "conv3x3_f16_mfma<4, 8, false>"
+    assert U.oidn_conv3x3_kernel(40, 52, cin, 0, cout, U.OIDN_F16, U.OIDN_F16, U.OIDN_RELU)[0] == \
+        "conv3x3_f16_mfma<1, 2, false>"
+    full = run_conv(x, cin, wt, b, cout, "f16", U.OIDN_RELU)
+    y0, x0, ch, cw = 101, 333, 40, 52
+    crop = run_conv(np.ascontiguousarray(x[y0:y0 + ch, x0:x0 + cw]), cin, wt, b, cout, "f16",
+                    U.OIDN_RELU)
+    assert np.array_equal(crop[1:-1, 1:-1], full[y0 + 1:y0 + ch - 1, x0 + 1:x0 + cw - 1])

@@ -38,7 +38,7 @@ EXPORTS = (
     "oidn_last_error", "oidn_version", "oidn_conv3x3_weights_bytes",
     "oidn_conv3x3_pack_weights", "oidn_conv3x3_pack_weights_host", "oidn_conv3x3", "oidn_conv3x3_upcat", "oidn_pool2x2",
     "oidn_upsample_concat", "oidn_pack_input", "oidn_unpack_output", "oidn_plan_tiles",
-    "oidn_unet_layer_count", "oidn_unet_layer_info", "oidn_unet_layer_kernel",
+    "oidn_conv3x3_kernel", "oidn_unet_layer_count", "oidn_unet_layer_info", "oidn_unet_layer_kernel",
     "oidn_unet_weights_bytes",
     "oidn_unet_pack_weights", "oidn_unet_packed_workspace_bytes", "oidn_unet_forward_packed",
     "oidn_unet_workspace_bytes", "oidn_unet_forward", "oidn_unet_forward_timed",
@@ -81,6 +81,8 @@ _SIGS = {
                               ctypes.POINTER(_i), ctypes.POINTER(_u),
                               ctypes.POINTER(ctypes.c_char_p)], _i),
     "oidn_unet_layer_kernel": ([_i, _i, _i, _i, _i, ctypes.c_char_p, _i, ctypes.POINTER(_i)], _i),
+    "oidn_conv3x3_kernel": ([_i, _i, _i, _i, _i, _i, _i, _u, ctypes.c_char_p, _i,
+                             ctypes.POINTER(_i)], _i),
     "oidn_unet_weights_bytes": ([_i, _i, ctypes.POINTER(_sz)], _i),
     "oidn_unet_pack_weights": ([ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i, _i, _vp, _vp], _i),
     "oidn_unet_packed_workspace_bytes": ([_i, _i, _i, _i, ctypes.POINTER(_sz)], _i),
@@ -248,6 +250,16 @@ def oidn_unet_layer_info(in_channels: int, layer: int):
                                       ctypes.byref(co), ctypes.byref(lv), ctypes.byref(fl),
                                       ctypes.byref(nm)))
     return nm.value.decode(), c0.value, c1.value, co.value, lv.value, fl.value
+
+
+def oidn_conv3x3_kernel(h: int, w: int, cin0: int, cin1: int, cout: int, in_dtype: int,
+                        out_dtype: int, flags: int):
+    """(kernel instance name, workgroups) of one conv (cin1 > 0: decoder conv)."""
+    buf = ctypes.create_string_buffer(128)
+    nb = _i()
+    _check(lib().oidn_conv3x3_kernel(h, w, cin0, cin1, cout, in_dtype, out_dtype, flags, buf, 128,
+                                     ctypes.byref(nb)))
+    return buf.value.decode(), nb.value
 
 
 def oidn_unet_layer_kernel(in_channels: int, layer: int, tw: int, th: int, dtype: int):

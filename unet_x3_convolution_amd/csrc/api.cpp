@@ -170,6 +170,23 @@ void pack_conv_host(const float* w, const float* b, int cin0, int cin1, int cout
   }
 }
 
+// Shape fields of an fp16 conv launch (no pointers); cs0/cs1 as in run_conv.
+ConvF16Args f16_args(int cin0, int cin1, int cout, int h, int w, int cs0, int cs1, ConvLayout* L) {
+  conv_f16_layout(stored_channels(cin0), cin1 ? stored_channels(cin1) : 0, cout, L);
+  ConvF16Args a{};
+  a.cs0 = cs0 ? cs0 : stored_channels(cin0);
+  a.cs1 = cin1 ? (cs1 ? cs1 : stored_channels(cin1)) : 0;
+  a.h = h;
+  a.w = w;
+  a.cout_stored = stored_channels(cout);
+  a.nchunks = L->nchunks;
+  a.nup4 = L->nup4;
+  a.nup = L->nup;
+  a.npl4 = L->npl4;
+  for (int i = 0; i < L->nchunks; ++i) a.chunk[i] = L->chunk[i];
+  return a;
+}
+
 // Validates and launches one conv.  Pointers already checked by the caller.
 // cs0/cs1: stored channels per pixel of the sources (0 = 4 * ceil(cin / 4)).
 int run_conv(const void* src0, int cin0, const void* src1, int cin1, bool upcat, int h, int w,
@@ -179,23 +196,12 @@ int run_conv(const void* src0, int cin0, const void* src1, int cin1, bool upcat,
   hipError_t e;
   if (in_dtype == OIDN_F16) {
     ConvLayout L;
-    conv_f16_layout(stored_channels(cin0), cin1 ? stored_channels(cin1) : 0, cout, &L);
-    ConvF16Args a{};
+    ConvF16Args a = f16_args(cin0, cin1, cout, h, w, cs0, cs1, &L);
     a.src0 = src0;
     a.src1 = src1;
-    a.cs0 = cs0 ? cs0 : stored_channels(cin0);
-    a.cs1 = cin1 ? (cs1 ? cs1 : stored_channels(cin1)) : 0;
-    a.h = h;
-    a.w = w;
     a.bias = static_cast<const float*>(wpk);
     a.wfrag = static_cast<const unsigned char*>(wpk) + L.bias_bytes;
     a.y = y;
-    a.cout_stored = stored_channels(cout);
-    a.nchunks = L.nchunks;
-    a.nup4 = L.nup4;
-    a.nup = L.nup;
-    a.npl4 = L.npl4;
-    for (int i = 0; i < L.nchunks; ++i) a.chunk[i] = L.chunk[i];
     e = launch_conv_f16(a, L.nf, upcat, pool, relu, out_dtype == OIDN_F32, stream);
   } else {
     ConvF32Args a{};
@@ -581,6 +587,26 @@ int oidn_conv3x3_upcat(const void* low, int c_low, const void* skip, int c_skip,
   return rc ? rc : ok();
 }
 
+int oidn_conv3x3_kernel(int h, int w, int cin0, int cin1, int cout, int in_dtype, int out_dtype,
+                        unsigned flags, char* buf, int cap, int* blocks) {
+  if (!buf || cap <= 0) return fail(OIDN_E_INVALID, "null or empty name buffer");
+  if (cin1 < 0) return fail(OIDN_E_INVALID, "skip channels must not be negative");
+  int rc = check_conv(h, w, cin0, cin1, cout, in_dtype, out_dtype, flags, cin1 > 0);
+  if (rc) return rc;
+  int nb = 0;
+  if (in_dtype == OIDN_F16) {
+    ConvLayout L;
+    const ConvF16Args a = f16_args(cin0, cin1, cout, h, w, 0, 0, &L);
+    conv_f16_describe(a, L.nf, out_dtype == OIDN_F32, buf, cap, &nb);
+  } else {
+    snprintf(buf, cap, "conv3x3_f32_direct");
+    const bool pool = flags & OIDN_POOL2X2;
+    nb = (int)cdiv((pool ? w / 2 : w) * (pool ? h / 2 : h) * (stored_channels(cout) / 4), 256);
+  }
+  if (blocks) *blocks = nb;
+  return ok();
+}
+
 int oidn_pool2x2(const void* x, int h, int w, int c, void* y, int dtype, hipStream_t stream) {
   if (!x || !y) return fail(OIDN_E_INVALID, "null pointer");
   int rc = check_dtype(dtype);
@@ -715,8 +741,13 @@ int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int dtype
   const bool final_layer = layer == kLayers - 1;
   int nb = 0;
   if (dtype == OIDN_F16) {
-    const int nf = cdiv(stored_channels(s[layer].cout), 16);
-    conv_f16_describe(h, w, nf, final_layer, buf, cap, &nb);
+    // as oidn_unet_forward runs it: the input packed with a multiple of 8 lanes
+    const int in_cs = internal_input_lanes(in_channels, dtype);
+    const Layer& L = kUNet[layer];
+    ConvLayout lay;
+    const ConvF16Args a = f16_args(s[layer].cin0, s[layer].cin1, s[layer].cout, h, w,
+                                   L.src == 0 ? in_cs : 0, L.skip == 0 ? in_cs : 0, &lay);
+    conv_f16_describe(a, lay.nf, final_layer, buf, cap, &nb);
   } else {
     snprintf(buf, cap, "conv3x3_f32_direct");
     const int oh = kUNet[layer].pool ? h / 2 : h, ow = kUNet[layer].pool ? w / 2 : w;

@@ -85,40 +85,40 @@ __device__ __forceinline__ half8 as_half8(uint4 v) { return __builtin_bit_cast(h
 // Direct global -> LDS staging of the same patch for sources whose stored
 // channel count is a multiple of 8: wave load k fills LDS slots
 // [64 k, 64 k + 64); slot s is patch pixel s / SPP, channel group s % SPP
-// (the last slot of a pixel is the pad).  Every load of the chunk is issued
-// back to back (nothing waits on registers); the barrier that follows drains
-// them.  Slots with no data (pad, channel groups past the chunk or the
+// (the last slot of a pixel is the pad, which no lane loads).  Every load of
+// the chunk is issued back to back (nothing waits on registers); the barrier
+// that follows drains them.  Slots with no data (channel groups past the
 // source, pixels outside the image) load the zero block.
-template <int R, int CG, bool UP>
-__device__ __forceinline__ void stage_patch_direct(_Float16* lds, const _Float16* src, int cs,
+// TH: tile height; NW: waves sharing the work; CAP: buffer capacity in slots.
+template <int TH, int NW, int CAP, int CG, bool UP>
+__device__ __forceinline__ void stage_patch_direct(uint4* slots, const _Float16* src, int cs,
                                                    int coff, int h, int w, int y0, int x0,
                                                    int wave, int lane) {
-  constexpr int PH = UP ? Tile<R>::LPH : Tile<R>::PH;
+  constexpr int PH = UP ? TH / 2 + 2 : TH + 2;
   constexpr int PWD = UP ? LPW : PW;
   constexpr int NPIX = PH * PWD;
   constexpr int SPP = pstride<CG>() / 8;        // 16-byte slots per pixel
   constexpr int NLOAD = (NPIX * SPP + 63) / 64;
-  static_assert(NLOAD * 64 * 8 <= Tile<R>::PATCH, "patch buffer");
+  static_assert(NLOAD * 64 <= CAP, "patch buffer");
   const int sh = UP ? (h >> 1) : h, sw = UP ? (w >> 1) : w;
   const int oy = UP ? (y0 >> 1) - 1 : y0 - 1, ox = UP ? (x0 >> 1) - 1 : x0 - 1;
-  uint4* slots = reinterpret_cast<uint4*>(lds);
 #pragma unroll
-  for (int i = 0; i < (NLOAD + 3) / 4; ++i) {
-    const int k = wave + 4 * i;
+  for (int i = 0; i < (NLOAD + NW - 1) / NW; ++i) {
+    const int k = wave + NW * i;
     if (k >= NLOAD) break;
     const int sl = k * 64 + lane;
     const int pp = sl / SPP;
     const int u = sl - pp * SPP;
-    const void* gp = g_zero16;
-    if (u < CG && pp < NPIX) {
+    if (u < CG && pp < NPIX) {   // pad slots are never read: those lanes stay idle
       const int py = pp / PWD;
       const int iy = oy + py;
       const int ix = ox + (pp - py * PWD);
       const int c = coff + 8 * u;
+      const void* gp = g_zero16;
       if (iy >= 0 && iy < sh && ix >= 0 && ix < sw && c < cs)
         gp = src + ((size_t)iy * sw + ix) * cs + c;
+      __builtin_amdgcn_global_load_lds(gp, slots + k * 64, 16, 0, 0);
     }
-    __builtin_amdgcn_global_load_lds(gp, slots + k * 64, 16, 0, 0);
   }
 }
 
@@ -155,15 +155,19 @@ __device__ __forceinline__ void stage_patch(_Float16* lds, const _Float16* src, 
   }
 }
 
-// MFMAs of one chunk for one wave: rows [R * wave, R * wave + R) of the
-// tile, output fragments [q0, q0 + NFW) of nf.  `acur` holds the chunk's
-// column-group-0 weights on entry; each column group loads the next one's
-// weights (or those of the next chunk, `wnext`) before its MFMAs, so weight
-// loads overlap the matrix work.  On return `acur` holds the next chunk's.
-template <int NFW, int R, int CG, bool PF, bool UP>
+// MFMAs of one chunk for one wave: rows [R * rg, R * rg + R) of the tile
+// (row group rg), NFW output fragments.  The chunk's patch starts `cur`
+// halves into `lds`; `zero` is the offset of 8 zero halves.  With PF,
+// `acur` holds the chunk's column-group-0 weights on entry; each column
+// group loads the next one's weights (or those of the next chunk, `wnext`)
+// before its MFMAs, so weight loads overlap the matrix work, and on return
+// `acur` holds the next chunk's.  `hook` runs once, right after the first
+// of those prefetches is issued.
+template <int NFW, int R, int CG, bool PF, bool UP, typename Hook>
 __device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], uint4 (&acur)[3][NFW],
-                                          const _Float16* lds, const uint4* wchunk,
-                                          const uint4* wnext, int nf, int wave, int g, int c) {
+                                          const _Float16* lds, int cur, int zero,
+                                          const uint4* wchunk, const uint4* wnext, int nf,
+                                          int rg, int g, int c, Hook&& hook) {
   constexpr int NCG = (3 * CG + 3) / 4;
 #pragma unroll 1
   for (int j = 0; j < NCG; ++j) {
@@ -182,8 +186,9 @@ __device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], uint4 (&acur)[
 #pragma unroll
         for (int q = 0; q < NFW; ++q) anext[ky][q] = wn[(ky * nf + q) * 64];
     }
+    if (j == 0) hook();
     const int slot = 4 * j + g;
-    int base = Tile<R>::ZERO, rstride = 0;
+    int base = zero, rstride = 0;
     if (slot < 3 * CG) {
       const int kx = slot / CG;
       const int grp = slot - kx * CG;
@@ -191,10 +196,10 @@ __device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], uint4 (&acur)[
       if constexpr (UP) {
         // patch row p of this wave's window is half-resolution row
         // (R / 2) wave + (p + 1) / 2; column c + kx - 1 is (c + kx + 1) / 2
-        base = ((R / 2) * wave * LPW + ((c + kx + 1) >> 1)) * PS + 8 * grp;
+        base = cur + ((R / 2) * rg * LPW + ((c + kx + 1) >> 1)) * PS + 8 * grp;
         rstride = LPW * PS;
       } else {
-        base = ((R * wave) * PW + c + kx) * PS + 8 * grp;
+        base = cur + ((R * rg) * PW + c + kx) * PS + 8 * grp;
         rstride = PW * PS;
       }
     }
@@ -239,6 +244,99 @@ __device__ __forceinline__ void store4(void* y, size_t idx, float v0, float v1, 
     p.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
     p.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
     *reinterpret_cast<uint2*>(static_cast<_Float16*>(y) + idx) = p;
+  }
+}
+
+template <bool OUTF32>
+__device__ __forceinline__ void store8(void* y, size_t idx, const float (&v)[8]) {
+  if constexpr (OUTF32) {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(y) + idx);
+    p[0] = make_float4(v[0], v[1], v[2], v[3]);
+    p[1] = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    uint4 p;
+    uint32_t* w = reinterpret_cast<uint32_t*>(&p);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2 * k]) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2 * k + 1]) << 16);
+    *reinterpret_cast<uint4*>(static_cast<_Float16*>(y) + idx) = p;
+  }
+}
+
+// Stores one pixel's values of this lane's NFW fragments (fragments q0 ..):
+// v[q][i] is output channel chan[q] + i.  The two fragments of a pair held
+// by the same lane are 8 consecutive channels and go out as one 16-byte
+// store; others as 8-byte stores.
+template <int NFW, bool OUTF32>
+__device__ __forceinline__ void store_pixel(void* y, size_t pix, const int (&chan)[NFW],
+                                            const bool (&lead)[NFW], const bool (&tail)[NFW],
+                                            int cout_stored, const float (&v)[NFW][4]) {
+#pragma unroll
+  for (int q = 0; q < NFW; ++q) {
+    if (chan[q] >= cout_stored || tail[q]) continue;
+    if (q + 1 < NFW && lead[q]) {
+      const float w8[8] = {v[q][0], v[q][1], v[q][2], v[q][3],
+                           v[q + 1][0], v[q + 1][1], v[q + 1][2], v[q + 1][3]};
+      store8<OUTF32>(y, pix + chan[q], w8);
+    } else {
+      store4<OUTF32>(y, pix + chan[q], v[q][0], v[q][1], v[q][2], v[q][3]);
+    }
+  }
+}
+
+// Epilogue of one wave: bias, ReLU, then the store or the fused 2x2 pool.
+// acc[r][q] holds, for this lane (16-lane group g), rows 4 g .. 4 g + 3 of
+// fragment q0 + q for pixel (yb + r, x); c is the pixel column in the tile.
+template <int NFW, int R, bool OUTF32>
+__device__ __forceinline__ void store_tile(const floatx4 (&acc)[R][NFW], const ConvF16Args& a,
+                                           int q0, int g, int yb, int x, int c, int pool,
+                                           int relu) {
+  const int nf = a.nf;
+  int chan[NFW];
+  bool lead[NFW], tail[NFW];   // first / second fragment of a pair this lane holds both of
+  float bv[NFW][4];
+#pragma unroll
+  for (int q = 0; q < NFW; ++q) {
+    const int f = q0 + q;
+    const bool paired = (f | 1) < nf;
+    chan[q] = 32 * (f >> 1) + (paired ? 8 * g + 4 * (f & 1) : 4 * g);
+    lead[q] = paired && (f & 1) == 0 && q + 1 < NFW;
+    tail[q] = paired && (f & 1) == 1 && q >= 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bv[q][i] = a.bias[chan[q] + i];
+  }
+  if (!pool) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int yy = yb + r;
+      if (yy < a.h && x < a.w) {
+        float v[NFW][4];
+#pragma unroll
+        for (int q = 0; q < NFW; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[q][i] = act(acc[r][q][i] + bv[q][i], relu);
+        store_pixel<NFW, OUTF32>(a.y, ((size_t)yy * a.w + x) * a.cout_stored, chan, lead, tail,
+                                 a.cout_stored, v);
+      }
+    }
+  } else {
+    const int ow = a.w >> 1;
+#pragma unroll
+    for (int rp = 0; rp < R / 2; ++rp) {
+      float m[NFW][4];
+#pragma unroll
+      for (int q = 0; q < NFW; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = act(fmaxf(acc[2 * rp][q][i], acc[2 * rp + 1][q][i]) + bv[q][i], relu);
+          m[q][i] = fmaxf(v, swap_pair(v));
+        }
+      const int yy = yb + 2 * rp;
+      if ((c & 1) == 0 && yy < a.h && x < a.w)
+        store_pixel<NFW, OUTF32>(a.y, ((size_t)(yy >> 1) * ow + (x >> 1)) * a.cout_stored, chan,
+                                 lead, tail, a.cout_stored, m);
+    }
   }
 }
 
@@ -294,12 +392,13 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
     const uint4* wnext = ci + 1 < a.nchunks ? wf + (size_t)a.chunk[ci + 1].wfrag * 64 : nullptr; \
     __syncthreads();                                                                            \
     if ((cs & 7) == 0)                                                                          \
-      stage_patch_direct<R, CG, UP>(lds, src, cs, ch.coff, a.h, a.w, y0, x0, wave, lane);       \
+      stage_patch_direct<T::TH, 4, T::PATCH / 8, CG, UP>(reinterpret_cast<uint4*>(lds), src, cs, \
+                                                         ch.coff, a.h, a.w, y0, x0, wave, lane); \
     else                                                                                        \
       stage_patch<R, CG, false, UP>(lds, src, cs, ch.coff, a.h, a.w, y0, x0, tid);              \
     __syncthreads();                                                                            \
-    mma_chunk<NFW, R, CG, PF, UP>(acc, acur, lds, wf + (size_t)ch.wfrag * 64, wnext, nf, wave,  \
-                                  g, c);                                                        \
+    mma_chunk<NFW, R, CG, PF, UP>(acc, acur, lds, 0, T::ZERO, wf + (size_t)ch.wfrag * 64, wnext, \
+                                  nf, wave, g, c, [] {});                                       \
   }
   OIDN_CHUNK_LOOP(0, 4, true)
   OIDN_CHUNK_LOOP(1, 2, true)
@@ -308,53 +407,7 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
 #undef OIDN_CHUNK_LOOP
   (void)upcat;
 
-  // Epilogue.  Lane (g, c) holds rows 4g..4g+3 of every fragment: fragment
-  // q0 + q carries output channels cbase + 4 (q0 + q) + i with
-  // cbase = 4 * nf * g, for pixel column c.
-  const int cbase = 4 * nf * g + 4 * q0;
-  float bv[NFW][4];
-#pragma unroll
-  for (int q = 0; q < NFW; ++q)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) bv[q][i] = a.bias[cbase + 4 * q + i];
-  const int x = x0 + c;
-  const int yb = y0 + R * wave;
-  if (!pool) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int yy = yb + r;
-      if (yy < a.h && x < a.w) {
-        const size_t base = ((size_t)yy * a.w + x) * a.cout_stored + cbase;
-#pragma unroll
-        for (int q = 0; q < NFW; ++q)
-          if (cbase + 4 * q < a.cout_stored)
-            store4<OUTF32>(a.y, base + 4 * q, act(acc[r][q][0] + bv[q][0], relu),
-                           act(acc[r][q][1] + bv[q][1], relu), act(acc[r][q][2] + bv[q][2], relu),
-                           act(acc[r][q][3] + bv[q][3], relu));
-      }
-    }
-  } else {
-    const int ow = a.w >> 1;
-#pragma unroll
-    for (int rp = 0; rp < R / 2; ++rp) {
-      float m[NFW][4];
-#pragma unroll
-      for (int q = 0; q < NFW; ++q)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = act(fmaxf(acc[2 * rp][q][i], acc[2 * rp + 1][q][i]) + bv[q][i], relu);
-          m[q][i] = fmaxf(v, swap_pair(v));
-        }
-      const int yy = yb + 2 * rp;
-      if ((c & 1) == 0 && yy < a.h && x < a.w) {
-        const size_t base = ((size_t)(yy >> 1) * ow + (x >> 1)) * a.cout_stored + cbase;
-#pragma unroll
-        for (int q = 0; q < NFW; ++q)
-          if (cbase + 4 * q < a.cout_stored)
-            store4<OUTF32>(a.y, base + 4 * q, m[q][0], m[q][1], m[q][2], m[q][3]);
-      }
-    }
-  }
+  store_tile<NFW, R, OUTF32>(acc, a, q0, g, y0 + R * wave, x0 + c, c, pool, relu);
 }
 
 template <int NFW, int R>
@@ -458,7 +511,9 @@ bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out
   return true;
 }
 
-void conv_f16_describe(int h, int w, int nf, bool out_f32, char* buf, int cap, int* blocks) {
+void conv_f16_describe(const ConvF16Args& a, int nf, bool out_f32, char* buf, int cap,
+                       int* blocks) {
+  const int h = a.h, w = a.w;
   int rows, nfw;
   conv_f16_plan(h, w, nf, &rows, &nfw);
   snprintf(buf, cap, "conv3x3_f16_mfma<%d, %d, %s>", nfw, rows, out_f32 ? "true" : "false");
@@ -467,9 +522,9 @@ void conv_f16_describe(int h, int w, int nf, bool out_f32, char* buf, int cap, i
 
 hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, bool relu,
                            bool out_f32, hipStream_t stream) {
-  int rows = 4, nfw = nf;
   ConvF16Args b = a;
   b.nf = nf;
+  int rows = 4, nfw = nf;
   conv_f16_plan(a.h, a.w, nf, &rows, &nfw);
   const int nsplit = nf / nfw;
   switch (nfw) {

@@ -53,11 +53,17 @@ struct ConvLayout {           // shared by the weight packer and the launcher
 // Computes the fp16 layout; returns false if the shape exceeds the limits.
 bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out);
 
-// Row r (0..15) of fragment q holds output channel
-//   4 * nf * (r / 4) + 4 * q + (r % 4)
-// so that the 16-lane group g of the accumulator owns the 4 * nf contiguous
-// channels [4 * nf * g, 4 * nf * (g + 1)).
-inline int frag_row_to_cout(int nf, int q, int r) { return 4 * nf * (r / 4) + 4 * q + (r % 4); }
+// Output fragments go in pairs (2p, 2p + 1) that cover the 32 channels
+// [32 p, 32 p + 32).  Row r (0..15) of fragment q holds output channel
+//   32 (q / 2) + 8 (r / 4) + 4 (q % 2) + r % 4   if q is in a full pair,
+//   32 (q / 2) + r                                for the last fragment of an odd nf,
+// so that the 16-lane group g of a pair's two accumulators owns 8
+// consecutive channels: one 16-byte store per lane, 64 contiguous bytes
+// per pixel per store instruction.
+inline bool frag_paired(int nf, int q) { return (q | 1) < nf; }
+inline int frag_row_to_cout(int nf, int q, int r) {
+  return 32 * (q / 2) + (frag_paired(nf, q) ? 8 * (r / 4) + 4 * (q % 2) + r % 4 : r);
+}
 
 struct ConvF16Args {
   const void* src0;   // fp16, h x w (or h/2 x w/2 when upsampled) x cs0
@@ -83,8 +89,10 @@ hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, 
 void conv_f16_plan(int h, int w, int nf, int* rows, int* nfw);
 int conv_f16_blocks(int h, int w, int nf);
 
-// Name of the kernel instance launch_conv_f16 runs for a shape, and its grid.
-void conv_f16_describe(int h, int w, int nf, bool out_f32, char* buf, int cap, int* blocks);
+// Name of the kernel instance launch_conv_f16 would run for `a` (h, w,
+// cs0, cs1 and the chunk fields set) and its grid.
+void conv_f16_describe(const ConvF16Args& a, int nf, bool out_f32, char* buf, int cap,
+                       int* blocks);
 
 // ---------------------------------------------------------------------------
 // fp32 direct conv (VALU FMA).  Packed weights: bias (cout_stored floats,
