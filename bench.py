@@ -19,6 +19,99 @@ sys.path.insert(0, ROOT)
 METRIC = "megapixels/s for full UNet denoise at 1080p fp16; conv TFLOP/s and % MFMA peak"
 PEAK_F16_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0
+COPY_BYTES = 1 << 30       # device copy timed for counter calibration
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv_kernels_1080p_hbm_traffic.md")
+# Sources whose change invalidates the recorded traffic of the conv kernels.
+TRAFFIC_SOURCES = ("unet_x3_convolution_amd/csrc/conv_f16.hip",
+                   "unet_x3_convolution_amd/csrc/internal.h")
+
+
+def conv_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def kernel_symbol(name):
+    """'void oidn::(anonymous namespace)::conv3x3_f16_mfma<4, 8, false>(...)' -> 'conv3x3_f16_mfma<4, 8, false>'."""
+    name = name.replace("(anonymous namespace)::", "").replace("oidn::", "").replace("void ", "")
+    depth = 0
+    for i, ch in enumerate(name):
+        depth += ch == "<"
+        depth -= ch == ">"
+        if ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def recorded_traffic(symbol):
+    """HBM bytes per launch of `symbol` from the committed counter summary,
+    or None if there is none or the conv sources changed since."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    block = text.split("```json", 1)[-1].split("```", 1)[0] if "```json" in text else ""
+    try:
+        rec = json.loads(block)
+    except ValueError:
+        return None
+    if rec.get("source_sha256") != conv_source_hash():
+        return None
+    return rec.get("bytes_per_launch", {}).get(symbol)
+
+
+def traffic_summary(fetch_dir, write_dir):
+    """Writes TRAFFIC_FILE from two rocprofv3 --pmc runs of this script with
+    --copy-calibration (FETCH_SIZE, then WRITE_SIZE): KiB per dispatch per
+    kernel, each counter scaled by its reading for the 1 GiB device copy."""
+    import csv
+    import glob
+    per = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = []
+        for f in glob.glob(os.path.join(d, "*counter_collection.csv")):
+            rows += [r for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
+        copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        if len(copy) != 1:
+            raise SystemExit(f"{d}: expected one device copy dispatch, found {len(copy)}")
+        scale = COPY_BYTES / 1024.0 / copy[0]
+        for r in rows:
+            if "oidn::" not in r["Kernel_Name"]:
+                continue
+            e = per.setdefault(kernel_symbol(r["Kernel_Name"]), {})
+            e.setdefault(counter, []).append(float(r["Counter_Value"]))
+            e[counter + "_scale"] = scale
+            e["copy_" + counter] = copy[0]
+    lines = ["# HBM traffic per launch: kernels of the UNet denoise at 1920x1080, fp16", "",
+             "Commands (repository root, one MI355X):", "", "```"]
+    for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        lines.append(f"rocprofv3 --pmc {c} --output-format csv -d {d} -o run -- python -u bench.py "
+                     "--steps 3 --warmup 1 --no-cpu-baseline --copy-calibration")
+    lines += [f"python bench.py --traffic-summary {fetch_dir} {write_dir}", "```", ""]
+    any_e = next(iter(per.values()))
+    fs, ws = any_e["FETCH_SIZE_scale"], any_e["WRITE_SIZE_scale"]
+    lines += [f"Calibration: the 1 GiB device copy reads FETCH_SIZE = {any_e['copy_FETCH_SIZE']:.0f} KiB "
+              f"and WRITE_SIZE = {any_e['copy_WRITE_SIZE']:.0f} KiB, so the counters are scaled by "
+              f"{fs:.4f} (fetch) and {ws:.4f} (write).", "",
+              "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled MB per launch |",
+              "|---|---|---|---|---|"]
+    out = {}
+    for sym, e in per.items():
+        f = sum(e["FETCH_SIZE"]) / len(e["FETCH_SIZE"])
+        w = sum(e["WRITE_SIZE"]) / len(e["WRITE_SIZE"])
+        b = 1024.0 * (f * fs + w * ws)
+        out[sym] = round(b)
+        lines.append(f"| `{sym}` | {len(e['FETCH_SIZE'])} | {f:.0f} | {w:.0f} | {b / 1e6:.1f} |")
+    lines += ["", "Averages are over every dispatch of the kernel symbol in the profiled run "
+              "(all layers it serves), i.e. per launch.", "",
+              "```json", json.dumps({"source_sha256": conv_source_hash(), "fetch_scale": fs,
+                                     "write_scale": ws, "bytes_per_launch": out}, indent=1), "```"]
+    open(TRAFFIC_FILE, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def main():
@@ -33,7 +126,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for HBM counter calibration)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the HBM traffic summary from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(tiles would shard across GPUs; see the design notes)", file=sys.stderr)
@@ -144,8 +242,10 @@ def main():
         "conv_tflops": round(conv_flops / conv_ms / 1e9, 1),
         "conv_mfma_frac": round(conv_flops / conv_ms / 1e9 / PEAK_F16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "kernel": sym, "launches_per_step": g["launches"],
+                     "avg_launch_us": round(g["ms"] / g["launches"] * 1e3, 2),
                      "achieved": round(achieved, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+                     "traffic": recorded_traffic(sym)},
         "elementwise": {
             "input_pass_us": round(float(avg_ms[0]) * 1e3, 2),
             "input_pass_gbs": round(pack_bytes / avg_ms[0] / 1e6, 1) if pack_bytes else None,
@@ -156,7 +256,7 @@ def main():
     }
 
     if args.copy_calibration:
-        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
         a.fill_(1.0)
         torch.cuda.synchronize()
