@@ -246,12 +246,13 @@ def test_unet_argument_errors():
 
 def test_conv_kernel_selection():
     """The name reported for a single conv is the kernel instance of its
-    launch plan: 32-row tiles with all fragments for large layers, output
-    channels split across workgroups and shorter tiles for small ones."""
+    launch plan (fragments per wave, rows per wave, row groups): 32-row tiles
+    with all fragments in one workgroup for large layers, output channels
+    split across workgroups and shorter tiles for small ones."""
     F, F32, R, P = U.OIDN_F16, U.OIDN_F32, U.OIDN_RELU, U.OIDN_POOL2X2
-    assert U.oidn_conv3x3_kernel(544, 960, 64, 16, 64, F, F, R) == ("conv3x3_f16_mfma<4, 8, false>", 1024)
-    assert U.oidn_conv3x3_kernel(1088, 1920, 32, 0, 3, F, F32, 0) == ("conv3x3_f16_mfma<1, 8, true>", 4080)
-    assert U.oidn_conv3x3_kernel(136, 240, 160, 0, 112, F, F, R)[0] == "conv3x3_f16_mfma<1, 2, false>"
+    assert U.oidn_conv3x3_kernel(544, 960, 64, 16, 64, F, F, R) == ("conv3x3_f16_mfma<2, 16, 2, false>", 1024)
+    assert U.oidn_conv3x3_kernel(1088, 1920, 32, 0, 3, F, F32, 0) == ("conv3x3_f16_mfma<1, 8, 4, true>", 4080)
+    assert U.oidn_conv3x3_kernel(136, 240, 160, 0, 112, F, F, R)[0] == "conv3x3_f16_mfma<1, 2, 4, false>"
     assert U.oidn_conv3x3_kernel(8, 8, 9, 0, 32, F32, F32, R)[0] == "conv3x3_f32_direct"
     with pytest.raises(U.OidnError):
         U.oidn_conv3x3_kernel(8, 8, 300, 0, 32, F, F, R)

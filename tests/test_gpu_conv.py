@@ -191,9 +191,9 @@ def test_conv_result_independent_of_launch_plan_bit_exact():
     wt = S.he_normal(r, cout, cin)
     b = S.bias(r, cout)
     assert U.oidn_conv3x3_kernel(h, w, cin, 0, cout, U.OIDN_F16, U.OIDN_F16, U.OIDN_RELU)[0] == \
-        "conv3x3_f16_mfma<4, 8, false>"
+        "conv3x3_f16_mfma<2, 16, 2, false>"
     assert U.oidn_conv3x3_kernel(40, 52, cin, 0, cout, U.OIDN_F16, U.OIDN_F16, U.OIDN_RELU)[0] == \
-        "conv3x3_f16_mfma<1, 2, false>"
+        "conv3x3_f16_mfma<1, 2, 4, false>"
     full = run_conv(x, cin, wt, b, cout, "f16", U.OIDN_RELU)
     y0, x0, ch, cw = 101, 333, 40, 52
     crop = run_conv(np.ascontiguousarray(x[y0:y0 + ch, x0:x0 + cw]), cin, wt, b, cout, "f16",

@@ -57,11 +57,11 @@ constexpr int kXcds = 8;
 
 constexpr int LPW = TW / 2 + 2;               // half-resolution patch width
 
-template <int R>
+template <int TH_>
 struct Tile {
-  static constexpr int TH = 4 * R;
+  static constexpr int TH = TH_;                // tile height (rows)
   static constexpr int PH = TH + 2;
-  static constexpr int LPH = 2 * R + 2;         // half-resolution patch height
+  static constexpr int LPH = TH / 2 + 2;        // half-resolution patch height
   // The patch occupies whole 64-slot (1 KB) blocks so that direct
   // global -> LDS loads, which fill 64 consecutive 16-byte slots each, stay
   // inside it; 8 zero halves follow.
@@ -74,9 +74,9 @@ __device__ __attribute__((aligned(16))) unsigned int g_zero16[4] = {0u, 0u, 0u, 
 
 __device__ __forceinline__ half8 as_half8(uint4 v) { return __builtin_bit_cast(half8, v); }
 
-// Stage one chunk's halo patch.  Full resolution: (4R + 2) x 18 pixels at
+// Stage one chunk's halo patch.  Full resolution: (TH + 2) x 18 pixels at
 // (y0 - 1, x0 - 1).  UP (the decoder's upsampled source): the same window
-// at half resolution, (2R + 2) x 10 low-resolution pixels at
+// at half resolution, (TH / 2 + 2) x 10 low-resolution pixels at
 // (y0 / 2 - 1, x0 / 2 - 1) -- nearest upsampling repeats each of them 2 x 2
 // times, so staging them once cuts the staged bytes about four-fold.
 // VEC16: channels move in 8-channel (16 B) units, else in 4-channel (8 B)
@@ -122,10 +122,10 @@ __device__ __forceinline__ void stage_patch_direct(uint4* slots, const _Float16*
   }
 }
 
-template <int R, int CG, bool VEC16, bool UP>
+template <int TH, int CG, bool VEC16, bool UP>
 __device__ __forceinline__ void stage_patch(_Float16* lds, const _Float16* src, int cs, int coff,
                                             int h, int w, int y0, int x0, int tid) {
-  constexpr int PH = UP ? Tile<R>::LPH : Tile<R>::PH;
+  constexpr int PH = UP ? Tile<TH>::LPH : Tile<TH>::PH;
   constexpr int PWD = UP ? LPW : PW;
   constexpr int UNITS = VEC16 ? CG : 2 * CG;
   constexpr int UCH = VEC16 ? 8 : 4;
@@ -340,20 +340,28 @@ __device__ __forceinline__ void store_tile(const floatx4 (&acc)[R][NFW], const C
   }
 }
 
-template <int NFW, int R, bool OUTF32>
+// Weight prefetch doubles the A registers (12 NFW more); use it only where
+// accumulators and both A sets leave room for two waves per SIMD.
+template <int NFW, int R>
+constexpr bool kPrefetch = 4 * R * NFW + 24 * NFW <= 176;
+
+// A workgroup of 4 waves covers a (WR R) x 16 tile for NFW (4 / WR) output
+// fragments: wave w computes rows [R (w % WR), + R) for the NFW fragments
+// starting at (4 / WR) NFW blockIdx.y + NFW (w / WR).
+template <int NFW, int R, int WR, bool OUTF32>
 __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
     ConvF16Args a, int upcat, int pool, int relu) {
-  using T = Tile<R>;
+  static_assert(WR == 1 || WR == 2 || WR == 4, "row groups");
+  using T = Tile<WR * R>;
   __shared__ __attribute__((aligned(16))) _Float16 lds[T::PATCH + 8];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;
   const int nf = a.nf;
-  const int q0 = blockIdx.y * NFW;          // this block's output fragments
+  const int rg = wave % WR;
+  const int q0 = (blockIdx.y * (4 / WR) + wave / WR) * NFW;   // this wave's output fragments
   (void)upcat;
-  // Weight prefetch costs 12 * NFW registers; use it only where two waves
-  // per SIMD still fit.
-  constexpr bool PF = NFW * R <= 16 || NFW <= 3;
+  constexpr bool PF = kPrefetch<NFW, R>;
 
   // XCD-aware tile order: block b runs on XCD b % 8; give each XCD a band.
   const int ntiles = a.tiles_x * a.tiles_y;
@@ -395,10 +403,10 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
       stage_patch_direct<T::TH, 4, T::PATCH / 8, CG, UP>(reinterpret_cast<uint4*>(lds), src, cs, \
                                                          ch.coff, a.h, a.w, y0, x0, wave, lane); \
     else                                                                                        \
-      stage_patch<R, CG, false, UP>(lds, src, cs, ch.coff, a.h, a.w, y0, x0, tid);              \
+      stage_patch<T::TH, CG, false, UP>(lds, src, cs, ch.coff, a.h, a.w, y0, x0, tid);          \
     __syncthreads();                                                                            \
     mma_chunk<NFW, R, CG, PF, UP>(acc, acur, lds, 0, T::ZERO, wf + (size_t)ch.wfrag * 64, wnext, \
-                                  nf, wave, g, c, [] {});                                       \
+                                  nf, rg, g, c, [] {});                                         \
   }
   OIDN_CHUNK_LOOP(0, 4, true)
   OIDN_CHUNK_LOOP(1, 2, true)
@@ -407,71 +415,74 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
 #undef OIDN_CHUNK_LOOP
   (void)upcat;
 
-  store_tile<NFW, R, OUTF32>(acc, a, q0, g, y0 + R * wave, x0 + c, c, pool, relu);
+  store_tile<NFW, R, OUTF32>(acc, a, q0, g, y0 + R * rg, x0 + c, c, pool, relu);
 }
 
-template <int NFW, int R>
+template <int NFW, int R, int WR>
 hipError_t launch_shape(ConvF16Args a, int nsplit, bool upcat, bool pool, bool relu,
                         bool out_f32, hipStream_t stream) {
   a.tiles_x = cdiv(a.w, TW);
-  a.tiles_y = cdiv(a.h, Tile<R>::TH);
+  a.tiles_y = cdiv(a.h, WR * R);
   const int ntiles = a.tiles_x * a.tiles_y;
   const dim3 grid(cdiv(ntiles, kXcds) * kXcds, nsplit), block(THREADS);
   if (out_f32)
-    hipLaunchKernelGGL((conv3x3_f16_mfma<NFW, R, true>), grid, block, 0, stream, a, (int)upcat,
-                       (int)pool, (int)relu);
+    hipLaunchKernelGGL((conv3x3_f16_mfma<NFW, R, WR, true>), grid, block, 0, stream, a,
+                       (int)upcat, (int)pool, (int)relu);
   else
-    hipLaunchKernelGGL((conv3x3_f16_mfma<NFW, R, false>), grid, block, 0, stream, a, (int)upcat,
-                       (int)pool, (int)relu);
+    hipLaunchKernelGGL((conv3x3_f16_mfma<NFW, R, WR, false>), grid, block, 0, stream, a,
+                       (int)upcat, (int)pool, (int)relu);
   return hipGetLastError();
 }
 
+// Instances: 32-row tiles as 4 x 8 rows (any NFW <= 4) or 2 x 16 rows
+// (NFW <= 2); 16-row tiles as 4 x 4 rows; 8-row tiles as 4 x 2 rows (NFW <= 4).
 template <int NFW>
-hipError_t launch_rows(const ConvF16Args& a, int rows, int nsplit, bool upcat, bool pool,
+hipError_t launch_plan(const ConvF16Args& a, const ConvPlan& P, int nsplit, bool upcat, bool pool,
                        bool relu, bool out_f32, hipStream_t stream) {
+  if constexpr (NFW <= 2)
+    if (P.wr == 2 && P.rows == 16)
+      return launch_shape<NFW, 16, 2>(a, nsplit, upcat, pool, relu, out_f32, stream);
   if constexpr (NFW <= 4) {
-    if (rows == 8) return launch_shape<NFW, 8>(a, nsplit, upcat, pool, relu, out_f32, stream);
-    if (rows == 2) return launch_shape<NFW, 2>(a, nsplit, upcat, pool, relu, out_f32, stream);
+    if (P.rows == 8) return launch_shape<NFW, 8, 4>(a, nsplit, upcat, pool, relu, out_f32, stream);
+    if (P.rows == 2) return launch_shape<NFW, 2, 4>(a, nsplit, upcat, pool, relu, out_f32, stream);
   }
-  return launch_shape<NFW, 4>(a, nsplit, upcat, pool, relu, out_f32, stream);
+  return launch_shape<NFW, 4, 4>(a, nsplit, upcat, pool, relu, out_f32, stream);
 }
 
 }  // namespace
 
-// Work decomposition.  Each block covers a (4 R) x 16 pixel tile and NFW of
-// the nf output fragments.  Big images use R = 8 with all fragments; smaller
-// ones split the output channels across blocks and shrink the tile until the
-// grid has about four blocks per CU.
-void conv_f16_plan(int h, int w, int nf, int* rows, int* nfw) {
+// Work decomposition.  Big images use 32-row tiles with all output
+// fragments in one workgroup.  Smaller ones
+// split the output channels across workgroups and shrink the tile until the
+// grid has about four workgroups per CU.
+ConvPlan conv_f16_plan(int h, int w, int nf) {
   constexpr long kTarget = 1024;
   const long t8 = (long)cdiv(w, TW) * cdiv(h, 32);
   if (nf <= 4 && t8 >= kTarget / 2) {
-    *rows = 8;
-    *nfw = nf;
-    return;
+    // nf = 4: waves as 2 row groups x 2 fragment pairs (16 rows each), so a
+    // wave loads the weights of 2 fragments, not 4.
+    if (nf == 4) return {16, 2, 2};
+    return {8, nf, 4};
   }
   for (int r : {4, 2}) {
     const long t = (long)cdiv(w, TW) * cdiv(h, 4 * r);
     for (int split = 1; split <= nf; ++split) {
       if (nf % split) continue;
       const int width = nf / split;
-      if (r == 2 && width > 4) continue;
-      if (t * split >= kTarget) {
-        *rows = r;
-        *nfw = width;
-        return;
-      }
+      if ((r == 2 && width > 4) || width > 7) continue;
+      if (t * split >= kTarget) return {r, width, 4};
     }
   }
-  *rows = 2;
-  *nfw = 1;
+  return {2, 1, 4};
 }
+
+// Fragments one workgroup computes.
+int plan_block_frags(const ConvPlan& P) { return P.nfw * (4 / P.wr); }
 
 // Workgroups of the launch (for reporting).
 int conv_f16_blocks(int h, int w, int nf) {
-  int rows, nfw;
-  conv_f16_plan(h, w, nf, &rows, &nfw);
-  return cdiv(cdiv(w, TW) * cdiv(h, 4 * rows), kXcds) * kXcds * (nf / nfw);
+  const ConvPlan P = conv_f16_plan(h, w, nf);
+  return cdiv(cdiv(w, TW) * cdiv(h, P.wr * P.rows), kXcds) * kXcds * (nf / plan_block_frags(P));
 }
 
 bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out) {
@@ -514,9 +525,9 @@ bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out
 void conv_f16_describe(const ConvF16Args& a, int nf, bool out_f32, char* buf, int cap,
                        int* blocks) {
   const int h = a.h, w = a.w;
-  int rows, nfw;
-  conv_f16_plan(h, w, nf, &rows, &nfw);
-  snprintf(buf, cap, "conv3x3_f16_mfma<%d, %d, %s>", nfw, rows, out_f32 ? "true" : "false");
+  const ConvPlan P = conv_f16_plan(h, w, nf);
+  snprintf(buf, cap, "conv3x3_f16_mfma<%d, %d, %d, %s>", P.nfw, P.rows, P.wr,
+           out_f32 ? "true" : "false");
   *blocks = conv_f16_blocks(h, w, nf);
 }
 
@@ -524,18 +535,16 @@ hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, 
                            bool out_f32, hipStream_t stream) {
   ConvF16Args b = a;
   b.nf = nf;
-  int rows = 4, nfw = nf;
-  conv_f16_plan(a.h, a.w, nf, &rows, &nfw);
-  const int nsplit = nf / nfw;
-  switch (nfw) {
-    case 1: return launch_rows<1>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
-    case 2: return launch_rows<2>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
-    case 3: return launch_rows<3>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
-    case 4: return launch_rows<4>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
-    case 5: return launch_rows<5>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
-    case 6: return launch_rows<6>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
-    case 7: return launch_rows<7>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
-    case 8: return launch_rows<8>(b, rows, nsplit, upcat, pool, relu, out_f32, stream);
+  const ConvPlan P = conv_f16_plan(a.h, a.w, nf);
+  const int nsplit = nf / plan_block_frags(P);
+  switch (P.nfw) {
+    case 1: return launch_plan<1>(b, P, nsplit, upcat, pool, relu, out_f32, stream);
+    case 2: return launch_plan<2>(b, P, nsplit, upcat, pool, relu, out_f32, stream);
+    case 3: return launch_plan<3>(b, P, nsplit, upcat, pool, relu, out_f32, stream);
+    case 4: return launch_plan<4>(b, P, nsplit, upcat, pool, relu, out_f32, stream);
+    case 5: return launch_plan<5>(b, P, nsplit, upcat, pool, relu, out_f32, stream);
+    case 6: return launch_plan<6>(b, P, nsplit, upcat, pool, relu, out_f32, stream);
+    case 7: return launch_plan<7>(b, P, nsplit, upcat, pool, relu, out_f32, stream);
     default: return hipErrorInvalidValue;
   }
 }

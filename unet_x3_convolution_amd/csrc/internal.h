@@ -84,9 +84,14 @@ struct ConvF16Args {
 hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, bool relu,
                            bool out_f32, hipStream_t stream);
 
-// Tile height (4 * rows) and output fragments per block chosen for a conv,
-// and the launch's workgroup count (multi-workgroup kernel).
-void conv_f16_plan(int h, int w, int nf, int* rows, int* nfw);
+// Launch plan of a conv: a workgroup of 4 waves covers a (wr * rows) x 16
+// tile; each wave computes `rows` rows of `nfw` output fragments, the waves
+// forming wr row groups x (4 / wr) fragment groups; the nf fragments are
+// split across nf / (nfw * 4 / wr) workgroups.
+struct ConvPlan {
+  int rows, nfw, wr;
+};
+ConvPlan conv_f16_plan(int h, int w, int nf);
 int conv_f16_blocks(int h, int w, int nf);
 
 // Name of the kernel instance launch_conv_f16 would run for `a` (h, w,
