@@ -251,8 +251,32 @@ def test_conv_kernel_selection():
     split across workgroups and shorter tiles for small ones."""
     F, F32, R, P = U.OIDN_F16, U.OIDN_F32, U.OIDN_RELU, U.OIDN_POOL2X2
     assert U.oidn_conv3x3_kernel(544, 960, 64, 16, 64, F, F, R) == ("conv3x3_f16_mfma<2, 16, 2, false>", 1024)
-    assert U.oidn_conv3x3_kernel(1088, 1920, 32, 0, 3, F, F32, 0) == ("conv3x3_f16_mfma<1, 8, 4, true>", 4080)
-    assert U.oidn_conv3x3_kernel(136, 240, 160, 0, 112, F, F, R)[0] == "conv3x3_f16_mfma<1, 2, 4, false>"
+    assert U.oidn_conv3x3_kernel(1088, 1920, 32, 0, 3, F, F32, 0) == ("conv3x3_f16_mfma<1, 4, 4, true>", 8160)
+    assert U.oidn_conv3x3_kernel(136, 240, 160, 0, 112, F, F, R) == ("conv3x3_f16_mfma<1, 4, 4, false>", 952)
+    assert U.oidn_conv3x3_kernel(40, 52, 32, 0, 64, F, F, R) == ("conv3x3_f16_mfma<1, 2, 4, false>", 96)
     assert U.oidn_conv3x3_kernel(8, 8, 9, 0, 32, F32, F32, R)[0] == "conv3x3_f32_direct"
     with pytest.raises(U.OidnError):
         U.oidn_conv3x3_kernel(8, 8, 300, 0, 32, F, F, R)
+
+
+# Launch plans of the 1920x1088 network tile (fragments per wave, rows per
+# wave, row groups): the first candidate of each fragment count that gives
+# at least 480 workgroups, else the one with the most.
+UNET_1080P_PLANS = {
+    "enc_conv0": ("<1, 8, 2, false>", 8160), "enc_conv1": ("<1, 8, 2, false>", 8160),
+    "enc_conv2": ("<3, 8, 4, false>", 1024), "enc_conv3": ("<2, 8, 2, false>", 512),
+    "enc_conv4": ("<1, 2, 4, false>", 1280), "enc_conv5a": ("<1, 2, 4, false>", 432),
+    "enc_conv5b": ("<1, 2, 4, false>", 432), "dec_conv4a": ("<1, 4, 4, false>", 952),
+    "dec_conv4b": ("<1, 4, 4, false>", 952), "dec_conv3a": ("<3, 8, 2, false>", 512),
+    "dec_conv3b": ("<3, 8, 2, false>", 512), "dec_conv2a": ("<2, 16, 2, false>", 1024),
+    "dec_conv2b": ("<2, 16, 2, false>", 1024), "dec_conv1a": ("<2, 16, 2, false>", 4080),
+    "dec_conv1b": ("<1, 8, 2, false>", 8160), "dec_conv0": ("<1, 4, 4, true>", 8160),
+}
+
+
+def test_unet_1080p_launch_plans():
+    for i in range(U.oidn_unet_layer_count()):
+        name = U.oidn_unet_layer_info(9, i)[0]
+        sym, blocks = U.oidn_unet_layer_kernel(9, i, 1920, 1088, U.OIDN_F16)
+        inst, nb = UNET_1080P_PLANS[name]
+        assert (sym, blocks) == ("conv3x3_f16_mfma" + inst, nb), name

@@ -69,6 +69,18 @@ F16_CASES = [
     (512, 1000, 32, 48, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),   # 3 fragments, pooled, ragged
     (530, 1024, 64, 32, U.OIDN_RELU, "f16"),                    # two chunks per tile
     (544, 512, 32, 64, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),    # 4 fragments
+    # one case per launch plan instance <fragments/wave, rows/wave, row groups>
+    (272, 480, 48, 64, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),    # <2, 8, 2>
+    (272, 480, 96, 96, U.OIDN_RELU, "f16"),                     # <3, 8, 2>
+    (256, 256, 64, 64, U.OIDN_RELU, "f16"),                     # <1, 8, 1>
+    (256, 256, 32, 32, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),    # <1, 4, 2>
+    (128, 256, 64, 128, U.OIDN_RELU, "f16"),                    # <2, 4, 2>, outputs split in two
+    (256, 512, 32, 48, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),    # <3, 4, 4>
+    (128, 512, 96, 96, U.OIDN_RELU, "f16"),                     # <3, 4, 2>
+    (256, 512, 32, 128, U.OIDN_RELU, "f16"),                    # <4, 8, 2>
+    (128, 512, 32, 128, U.OIDN_RELU, "f16"),                    # <4, 4, 2>
+    (256, 512, 64, 80, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),    # <5, 4, 4>
+    (256, 512, 32, 112, U.OIDN_RELU, "f16"),                    # <7, 4, 4>
 ]
 
 
@@ -143,6 +155,7 @@ UPCAT_CASES = [
     (512, 1024, 64, 9, 64, "f16"),                              # 32-row tiles
     (544, 960, 64, 16, 64, "f16"),                              # 16-channel skip, 3 chunks
     (514, 1026, 32, 16, 32, "f16"),                             # ragged
+    (272, 480, 112, 48, 96, "f16"),                             # <3, 8, 2>: 2 row groups
 ]
 
 
@@ -182,7 +195,7 @@ def test_conv_ladder_config2():
 
 def test_conv_result_independent_of_launch_plan_bit_exact():
     """Large images run 32-row tiles with all output fragments per
-    workgroup, small ones shorter tiles with the outputs split across
+    workgroup, small ones 8-row tiles with the outputs split across four
     workgroups; every output is accumulated in the same order either way, so
     a conv over a crop reproduces the interior of the conv over the image."""
     r = np.random.default_rng(7)

@@ -434,56 +434,70 @@ hipError_t launch_shape(ConvF16Args a, int nsplit, bool upcat, bool pool, bool r
   return hipGetLastError();
 }
 
-// Instances: 32-row tiles as 4 x 8 rows (any NFW <= 4) or 2 x 16 rows
-// (NFW <= 2); 16-row tiles as 4 x 4 rows; 8-row tiles as 4 x 2 rows (NFW <= 4).
-template <int NFW>
+// The instances the planner can choose (see kPlanCandidates).
+#define OIDN_PLAN_INSTANCES(X) \
+  X(1, 4, 4) X(1, 2, 4) X(1, 8, 2) X(1, 4, 2) X(1, 8, 1) X(2, 16, 2) X(2, 8, 2) X(2, 4, 2) \
+  X(3, 8, 4) X(3, 4, 4) X(3, 2, 4) X(3, 8, 2) X(3, 4, 2) X(4, 8, 2) X(4, 4, 2) X(5, 4, 4)  \
+  X(7, 4, 4)
+
 hipError_t launch_plan(const ConvF16Args& a, const ConvPlan& P, int nsplit, bool upcat, bool pool,
                        bool relu, bool out_f32, hipStream_t stream) {
-  if constexpr (NFW <= 2)
-    if (P.wr == 2 && P.rows == 16)
-      return launch_shape<NFW, 16, 2>(a, nsplit, upcat, pool, relu, out_f32, stream);
-  if constexpr (NFW <= 4) {
-    if (P.rows == 8) return launch_shape<NFW, 8, 4>(a, nsplit, upcat, pool, relu, out_f32, stream);
-    if (P.rows == 2) return launch_shape<NFW, 2, 4>(a, nsplit, upcat, pool, relu, out_f32, stream);
-  }
-  return launch_shape<NFW, 4, 4>(a, nsplit, upcat, pool, relu, out_f32, stream);
+#define OIDN_TRY(NFW, R, WR)                                                                \
+  if (P.nfw == NFW && P.rows == R && P.wr == WR)                                            \
+    return launch_shape<NFW, R, WR>(a, nsplit, upcat, pool, relu, out_f32, stream);
+  OIDN_PLAN_INSTANCES(OIDN_TRY)
+#undef OIDN_TRY
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-// Work decomposition.  Big images use 32-row tiles with all output
-// fragments in one workgroup.  Smaller ones
-// split the output channels across workgroups and shrink the tile until the
-// grid has about four workgroups per CU.
+// Work decomposition.  For each fragment count nf, candidate plans from the
+// fewest workgroups per tile and the largest per-wave tiles (weights loaded
+// by fewer waves, patch rows reused longer) to the most workgroups; the
+// planner takes the first that gives at least kMinBlocks workgroups (about
+// two per CU), else the one with the most.  The lists come from timing every
+// plan at the UNet's layer shapes: large layers keep all fragments in one
+// workgroup, small deep layers split the output channels.
+constexpr long kMinBlocks = 480;
+constexpr int kMaxCandidates = 4;
+const ConvPlan kPlanCandidates[9][kMaxCandidates] = {
+    {},
+    {{4, 1, 4}, {2, 1, 4}},                                  // nf = 1
+    {{8, 1, 2}, {4, 1, 2}, {2, 1, 4}},                       // nf = 2
+    {{8, 3, 4}, {4, 3, 4}, {2, 3, 4}, {2, 1, 4}},            // nf = 3
+    {{16, 2, 2}, {8, 2, 2}, {8, 1, 1}, {2, 1, 4}},           // nf = 4
+    {{4, 5, 4}, {2, 1, 4}},                                  // nf = 5
+    {{8, 3, 2}, {4, 3, 2}, {4, 1, 2}, {2, 1, 4}},            // nf = 6
+    {{4, 7, 4}, {4, 1, 4}, {2, 1, 4}},                       // nf = 7
+    {{8, 4, 2}, {4, 4, 2}, {4, 2, 2}, {2, 1, 4}},            // nf = 8
+};
+
+long plan_blocks(int h, int w, int nf, const ConvPlan& P) {
+  const int frags = P.nfw * (4 / P.wr);
+  return (long)cdiv(cdiv(w, TW) * cdiv(h, P.wr * P.rows), kXcds) * kXcds * (nf / frags);
+}
+
 ConvPlan conv_f16_plan(int h, int w, int nf) {
-  constexpr long kTarget = 1024;
-  const long t8 = (long)cdiv(w, TW) * cdiv(h, 32);
-  if (nf <= 4 && t8 >= kTarget / 2) {
-    // nf = 4: waves as 2 row groups x 2 fragment pairs (16 rows each), so a
-    // wave loads the weights of 2 fragments, not 4.
-    if (nf == 4) return {16, 2, 2};
-    return {8, nf, 4};
-  }
-  for (int r : {4, 2}) {
-    const long t = (long)cdiv(w, TW) * cdiv(h, 4 * r);
-    for (int split = 1; split <= nf; ++split) {
-      if (nf % split) continue;
-      const int width = nf / split;
-      if ((r == 2 && width > 4) || width > 7) continue;
-      if (t * split >= kTarget) return {r, width, 4};
+  ConvPlan best{};
+  long most = -1;
+  for (const ConvPlan& P : kPlanCandidates[nf < 1 ? 1 : nf > 8 ? 8 : nf]) {
+    if (P.rows == 0) break;
+    const long b = plan_blocks(h, w, nf, P);
+    if (b >= kMinBlocks) return P;
+    if (b > most) {
+      most = b;
+      best = P;
     }
   }
-  return {2, 1, 4};
+  return best;
 }
 
 // Fragments one workgroup computes.
 int plan_block_frags(const ConvPlan& P) { return P.nfw * (4 / P.wr); }
 
 // Workgroups of the launch (for reporting).
-int conv_f16_blocks(int h, int w, int nf) {
-  const ConvPlan P = conv_f16_plan(h, w, nf);
-  return cdiv(cdiv(w, TW) * cdiv(h, P.wr * P.rows), kXcds) * kXcds * (nf / plan_block_frags(P));
-}
+int conv_f16_blocks(int h, int w, int nf) { return (int)plan_blocks(h, w, nf, conv_f16_plan(h, w, nf)); }
 
 bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out) {
   ConvLayout L{};
@@ -537,16 +551,7 @@ hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, 
   b.nf = nf;
   const ConvPlan P = conv_f16_plan(a.h, a.w, nf);
   const int nsplit = nf / plan_block_frags(P);
-  switch (P.nfw) {
-    case 1: return launch_plan<1>(b, P, nsplit, upcat, pool, relu, out_f32, stream);
-    case 2: return launch_plan<2>(b, P, nsplit, upcat, pool, relu, out_f32, stream);
-    case 3: return launch_plan<3>(b, P, nsplit, upcat, pool, relu, out_f32, stream);
-    case 4: return launch_plan<4>(b, P, nsplit, upcat, pool, relu, out_f32, stream);
-    case 5: return launch_plan<5>(b, P, nsplit, upcat, pool, relu, out_f32, stream);
-    case 6: return launch_plan<6>(b, P, nsplit, upcat, pool, relu, out_f32, stream);
-    case 7: return launch_plan<7>(b, P, nsplit, upcat, pool, relu, out_f32, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return launch_plan(b, P, nsplit, upcat, pool, relu, out_f32, stream);
 }
 
 }  // namespace oidn
