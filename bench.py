@@ -198,22 +198,36 @@ def main():
     layers = []
     groups = {}
     conv_flops = conv_ms = 0.0
+    prev_sym = None
     for i in range(U.oidn_unet_layer_count()):
         name, c0, c1, co, level, flags = U.oidn_unet_layer_info(9, i)
         px = (tw >> level) * (th >> level)
         flops = 2.0 * px * co * 9 * (c0 + c1)
         ms = float(avg_ms[i + 1])
         sym, nblocks = U.oidn_unet_layer_kernel(9, i, tw, th, U.OIDN_F16)
+        conv_flops += flops
+        conv_ms += ms
         g = groups.setdefault(sym, {"flops": 0.0, "ms": 0.0, "launches": 0})
         g["flops"] += flops
         g["ms"] += ms
+        if sym.startswith("conv3x3_pair") and sym == prev_sym:
+            # second layer of a fused pair: its work ran in the previous launch
+            prev = layers[-1]
+            prev["layer"] += "+" + name
+            prev["flops"] += flops
+            prev["us"] = round(prev["us"] + ms * 1e3, 2)
+            prev["tflops"] = round(prev["flops"] / (prev["us"] / 1e3) / 1e9, 1)
+            print(f"  {name:11s}  (fused into the previous launch)", file=sys.stderr)
+            prev_sym = None
+            continue
         g["launches"] += 1
-        conv_flops += flops
-        conv_ms += ms
-        layers.append({"layer": name, "us": round(ms * 1e3, 2),
+        prev_sym = sym
+        layers.append({"layer": name, "us": round(ms * 1e3, 2), "flops": flops,
                        "tflops": round(flops / ms / 1e9, 1), "kernel": sym, "blocks": nblocks})
         print(f"  {name:11s} {ms * 1e3:8.1f} us  {flops / ms / 1e9:7.1f} TFLOP/s  {sym} x{nblocks}",
               file=sys.stderr)
+    for L in layers:
+        del L["flops"]
     px0 = tw * th
     pack_bytes = W * H * 48 + px0 * 12 * 2 if len(tiles) == 1 else None
     unpack_bytes = W * H * (32 + 16)

@@ -130,6 +130,21 @@ int oidn_conv3x3_upcat(const void* low, int c_low, const void* skip, int c_skip,
                        int h, int w, const void* w_packed, void* y, int cout,
                        int in_dtype, int out_dtype, unsigned flags, hipStream_t stream);
 
+/* Two convs in one pass, y = convB(relu(convA(x))), the 32-channel
+ * intermediate never leaving the chip: convA is cin -> 32 (bias, ReLU,
+ * fp16 rounding as oidn_conv3x3 with OIDN_RELU), convB is 32 -> cout with
+ * `flags` and `out_dtype` as in oidn_conv3x3.  Both convs as defined by
+ * [web-0.4] createConvShader ("oidn-web 0.3.4 -> 0.4.0", nativeUNet.ts);
+ * the fusion is this library's.  fp16 storage only.  wa_packed / wb_packed:
+ * oidn_conv3x3_pack_weights output for (cin, 0, 32) and (32, 0, cout).
+ * x: h x w x 4 ceil(cin / 4) fp16; y as oidn_conv3x3's output.  The result
+ * equals oidn_conv3x3(convB) applied to oidn_conv3x3(convA) bit for bit.
+ * Needs 4 ceil(cin / 4) a multiple of 8 and either <= 32 or a multiple of
+ * 32, and cout <= 32 (else OIDN_E_UNSUPPORTED). */
+int oidn_conv3x3_pair(const void* x, int h, int w, int cin, const void* wa_packed,
+                      const void* wb_packed, void* y, int cout, int out_dtype, unsigned flags,
+                      hipStream_t stream);
+
 /* Name of the kernel instance that oidn_conv3x3 (cin1 == 0) or
  * oidn_conv3x3_upcat (cin0 = c_low, cin1 = c_skip) runs for this shape,
  * written NUL-terminated into buf (cap bytes), e.g.

@@ -261,16 +261,18 @@ def test_conv_kernel_selection():
 
 # Launch plans of the 1920x1088 network tile (fragments per wave, rows per
 # wave, row groups): the first candidate of each fragment count that gives
-# at least 480 workgroups, else the one with the most.
+# at least 480 workgroups, else the one with the most.  enc_conv0 ->
+# enc_conv1 and dec_conv1b -> dec_conv0 run as fused pairs (both layers
+# report the pair kernel: convA chunk groups, convB fragments, fp32 output).
 UNET_1080P_PLANS = {
-    "enc_conv0": ("<1, 8, 2, false>", 8160), "enc_conv1": ("<1, 8, 2, false>", 8160),
+    "enc_conv0": ("pair<2, 2, false>", 4352), "enc_conv1": ("pair<2, 2, false>", 4352),
     "enc_conv2": ("<3, 8, 4, false>", 1024), "enc_conv3": ("<2, 8, 2, false>", 512),
     "enc_conv4": ("<1, 2, 4, false>", 1280), "enc_conv5a": ("<1, 2, 4, false>", 432),
     "enc_conv5b": ("<1, 2, 4, false>", 432), "dec_conv4a": ("<1, 4, 4, false>", 952),
     "dec_conv4b": ("<1, 4, 4, false>", 952), "dec_conv3a": ("<3, 8, 2, false>", 512),
     "dec_conv3b": ("<3, 8, 2, false>", 512), "dec_conv2a": ("<2, 16, 2, false>", 1024),
     "dec_conv2b": ("<2, 16, 2, false>", 1024), "dec_conv1a": ("<2, 16, 2, false>", 4080),
-    "dec_conv1b": ("<1, 8, 2, false>", 8160), "dec_conv0": ("<1, 4, 4, true>", 8160),
+    "dec_conv1b": ("pair<4, 1, true>", 4352), "dec_conv0": ("pair<4, 1, true>", 4352),
 }
 
 
@@ -279,4 +281,5 @@ def test_unet_1080p_launch_plans():
         name = U.oidn_unet_layer_info(9, i)[0]
         sym, blocks = U.oidn_unet_layer_kernel(9, i, 1920, 1088, U.OIDN_F16)
         inst, nb = UNET_1080P_PLANS[name]
-        assert (sym, blocks) == ("conv3x3_f16_mfma" + inst, nb), name
+        want = ("conv3x3_pair_f16" + inst[4:]) if inst.startswith("pair") else "conv3x3_f16_mfma" + inst
+        assert (sym, blocks) == (want, nb), name

@@ -81,6 +81,10 @@ F16_CASES = [
     (128, 512, 32, 128, U.OIDN_RELU, "f16"),                    # <4, 4, 2>
     (256, 512, 64, 80, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),    # <5, 4, 4>
     (256, 512, 32, 112, U.OIDN_RELU, "f16"),                    # <7, 4, 4>
+    # cout inside a fragment pair: 16-byte stores must stop at cout_stored
+    (544, 512, 32, 52, U.OIDN_RELU, "f16"),                     # <2, 16, 2>, pair (2, 3) partial
+    (272, 480, 96, 84, U.OIDN_RELU, "f16"),                     # <3, 8, 2>, pair (4, 5) partial
+    (256, 256, 64, 60, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),    # <1, 8, 1>
 ]
 
 

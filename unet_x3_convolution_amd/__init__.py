@@ -38,7 +38,7 @@ EXPORTS = (
     "oidn_last_error", "oidn_version", "oidn_conv3x3_weights_bytes",
     "oidn_conv3x3_pack_weights", "oidn_conv3x3_pack_weights_host", "oidn_conv3x3", "oidn_conv3x3_upcat", "oidn_pool2x2",
     "oidn_upsample_concat", "oidn_pack_input", "oidn_unpack_output", "oidn_plan_tiles",
-    "oidn_conv3x3_kernel", "oidn_unet_layer_count", "oidn_unet_layer_info", "oidn_unet_layer_kernel",
+    "oidn_conv3x3_pair", "oidn_conv3x3_kernel", "oidn_unet_layer_count", "oidn_unet_layer_info", "oidn_unet_layer_kernel",
     "oidn_unet_weights_bytes",
     "oidn_unet_pack_weights", "oidn_unet_packed_workspace_bytes", "oidn_unet_forward_packed",
     "oidn_unet_workspace_bytes", "oidn_unet_forward", "oidn_unet_forward_timed",
@@ -81,6 +81,7 @@ _SIGS = {
                               ctypes.POINTER(_i), ctypes.POINTER(_u),
                               ctypes.POINTER(ctypes.c_char_p)], _i),
     "oidn_unet_layer_kernel": ([_i, _i, _i, _i, _i, ctypes.c_char_p, _i, ctypes.POINTER(_i)], _i),
+    "oidn_conv3x3_pair": ([_vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _u, _vp], _i),
     "oidn_conv3x3_kernel": ([_i, _i, _i, _i, _i, _i, _i, _u, ctypes.c_char_p, _i,
                              ctypes.POINTER(_i)], _i),
     "oidn_unet_weights_bytes": ([_i, _i, ctypes.POINTER(_sz)], _i),
@@ -199,6 +200,12 @@ def oidn_conv3x3_upcat(low, c_low: int, skip, c_skip: int, h: int, w: int, w_pac
                        cout: int, in_dtype: int, out_dtype: int, flags: int, stream=None):
     _check(lib().oidn_conv3x3_upcat(_p(low), c_low, _p(skip), c_skip, h, w, _p(w_packed), _p(y),
                                     cout, in_dtype, out_dtype, flags, _s(stream)))
+
+
+def oidn_conv3x3_pair(x, h: int, w: int, cin: int, wa_packed, wb_packed, y, cout: int,
+                      out_dtype: int, flags: int, stream=None):
+    _check(lib().oidn_conv3x3_pair(_p(x), h, w, cin, _p(wa_packed), _p(wb_packed), _p(y), cout,
+                                   out_dtype, flags, _s(stream)))
 
 
 # ------------------------------------------------------------ elementwise

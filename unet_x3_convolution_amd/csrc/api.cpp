@@ -245,6 +245,42 @@ int check_conv(int h, int w, int cin0, int cin1, int cout, int in_dtype, int out
   return OIDN_OK;
 }
 
+// ------------------------------------------------------------ fused conv pair
+// y = convB(relu(convA(x))), convA: cin -> 32, convB: 32 -> cout (fp16
+// storage).  cs: stored channels per pixel of x (0 = 4 * ceil(cin / 4)).
+// Supported when x moves in 16-byte units and convA's chunks are all of one
+// kind (one chunk, or whole 32-channel chunks).
+bool pair_supported(int cin, int cs, int cout) {
+  const int st = stored_channels(cin);
+  if (!cs) cs = st;
+  return cs % 8 == 0 && (st <= kChunkChannels || st % kChunkChannels == 0) &&
+         st <= 8 * kChunkChannels && cout >= 1 && cout <= 32;
+}
+
+int run_pair(const void* x, int cin, int cs, int h, int w, const void* wA, const void* wB, void* y,
+             int cout, int out_dtype, unsigned flags, hipStream_t stream) {
+  ConvLayout LA, LB;
+  conv_f16_layout(stored_channels(cin), 0, 32, &LA);
+  conv_f16_layout(32, 0, cout, &LB);
+  PairArgs p{};
+  p.x = x;
+  p.cs = cs ? cs : stored_channels(cin);
+  p.h = h;
+  p.w = w;
+  p.nchunks = LA.nchunks;
+  for (int i = 0; i < LA.nchunks; ++i) p.wfragA[i] = LA.chunk[i].wfrag;
+  p.biasA = static_cast<const float*>(wA);
+  p.wA = static_cast<const unsigned char*>(wA) + LA.bias_bytes;
+  p.biasB = static_cast<const float*>(wB);
+  p.wB = static_cast<const unsigned char*>(wB) + LB.bias_bytes;
+  p.y = y;
+  p.cout_stored = stored_channels(cout);
+  hipError_t e = launch_conv_pair_f16(p, LA.chunk[0].cg, LB.nf, flags & OIDN_POOL2X2,
+                                      flags & OIDN_RELU, out_dtype == OIDN_F32, stream);
+  if (e != hipSuccess) return hip_fail(e, "conv3x3 pair launch");
+  return OIDN_OK;
+}
+
 // ------------------------------------------------------------ UNet table
 struct Layer {
   const char* name;
@@ -313,6 +349,24 @@ int internal_input_lanes(int in_channels, int dtype) {
   return dtype == OIDN_F16 ? (cs + 7) / 8 * 8 : cs;
 }
 
+// Layer i runs fused with layer i + 1 (y = conv_{i+1}(conv_i(x)) through LDS)
+// when conv_i is a plain ReLU conv to 32 channels whose output only conv_{i+1}
+// reads, conv_{i+1} is a plain 32 -> <= 32 conv, and the pair kernel takes
+// conv_i's source.  In this network: enc_conv0 -> enc_conv1 and
+// dec_conv1b -> dec_conv0 on the fp16 path.
+bool fuse_with_next(int in_channels, int i, int dtype, bool own_io) {
+  if (dtype != OIDN_F16 || i + 1 >= kLayers) return false;
+  LayerShape s[kLayers];
+  unet_shapes(in_channels, s);
+  const Layer &A = kUNet[i], &B = kUNet[i + 1];
+  if (A.skip >= 0 || A.pool || !A.relu || s[i].cout != 32) return false;
+  if (B.src != i + 1 || B.skip >= 0 || s[i + 1].cin0 != 32 || s[i + 1].cout > 32) return false;
+  for (int j = 0; j < kLayers; ++j)
+    if (j != i + 1 && (kUNet[j].src == i + 1 || kUNet[j].skip == i + 1)) return false;
+  const int cs = A.src == 0 && own_io ? internal_input_lanes(in_channels, dtype) : 0;
+  return pair_supported(s[i].cin0, cs, s[i + 1].cout);
+}
+
 void plan_workspace(int in_channels, int tw, int th, int dtype, bool own_io, Plan* p) {
   LayerShape s[kLayers];
   unet_shapes(in_channels, s);
@@ -336,6 +390,15 @@ void plan_workspace(int in_channels, int tw, int th, int dtype, bool own_io, Pla
     if (kUNet[i].skip >= 0) last[kUNet[i].skip] = i > last[kUNet[i].skip] ? i : last[kUNet[i].skip];
   }
   last[kLayers] = kLayers;  // consumed by the output pass
+  // A fused pair (layers i, i + 1) reads layer i's source while it writes
+  // layer i + 1's output, so that source lives through layer i + 1; the
+  // intermediate between them is never stored.
+  for (int i = 0; i + 1 < kLayers; ++i)
+    if (fuse_with_next(in_channels, i, dtype, own_io)) {
+      int& l = last[kUNet[i].src];
+      l = l > i + 1 ? l : i + 1;
+      size[i + 1] = 0;
+    }
   bool placed[kLayers + 1] = {};
   size_t end = 0;
   for (int n = 0; n <= kLayers; ++n) {
@@ -391,6 +454,24 @@ int run_network(const unsigned char* weights, int in_channels, const void* packe
     const unsigned flags = (L.relu ? OIDN_RELU : 0u) | (L.pool ? OIDN_POOL2X2 : 0u);
     const int out_dtype = i == kLayers - 1 ? OIDN_F32 : dtype;
     const int in_cs = own_io ? internal_input_lanes(in_channels, dtype) : 0;
+    if (fuse_with_next(in_channels, i, dtype, own_io)) {
+      const Layer& B = kUNet[i + 1];
+      const unsigned flags_b = (B.relu ? OIDN_RELU : 0u) | (B.pool ? OIDN_POOL2X2 : 0u);
+      size_t ba = 0, bb = 0;
+      conv_weights_bytes(s[i].cin0, 0, 32, dtype, &ba);
+      conv_weights_bytes(32, 0, s[i + 1].cout, dtype, &bb);
+      int rc = run_pair(val[L.src], s[i].cin0, L.src == 0 ? in_cs : 0, h, w, weights + woff,
+                        weights + woff + align256(ba), const_cast<void*>(val[i + 2]),
+                        s[i + 1].cout, i + 1 == kLayers - 1 ? OIDN_F32 : dtype, flags_b, stream);
+      if (rc) return rc;
+      if (events && events[i + 1]) {   // the second layer's interval is empty
+        hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[i + 1]), stream);
+        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+      }
+      woff += align256(ba) + align256(bb);
+      ++i;
+      continue;
+    }
     int rc = run_conv(val[L.src], s[i].cin0, L.skip >= 0 ? val[L.skip] : nullptr, s[i].cin1,
                       L.skip >= 0, h, w, weights + woff, const_cast<void*>(val[i + 1]), s[i].cout,
                       dtype, out_dtype, flags, stream, L.src == 0 ? in_cs : 0,
@@ -587,6 +668,24 @@ int oidn_conv3x3_upcat(const void* low, int c_low, const void* skip, int c_skip,
   return rc ? rc : ok();
 }
 
+int oidn_conv3x3_pair(const void* x, int h, int w, int cin, const void* wa_packed,
+                      const void* wb_packed, void* y, int cout, int out_dtype, unsigned flags,
+                      hipStream_t stream) {
+  if (!x || !wa_packed || !wb_packed || !y) return fail(OIDN_E_INVALID, "null pointer");
+  if (!aligned16(x) || !aligned16(wa_packed) || !aligned16(wb_packed) || !aligned16(y))
+    return fail(OIDN_E_INVALID, "device pointers must be 16-byte aligned");
+  int rc = check_conv(h, w, cin, 0, 32, OIDN_F16, OIDN_F16, OIDN_RELU, false);
+  if (rc) return rc;
+  rc = check_conv(h, w, 32, 0, cout, OIDN_F16, out_dtype, flags, false);
+  if (rc) return rc;
+  if (!pair_supported(cin, 0, cout))
+    return fail(OIDN_E_UNSUPPORTED,
+                "conv pair needs cin <= 32 or a multiple of 32 (and a multiple of 8 stored), "
+                "cout <= 32 (got %d -> 32 -> %d)", cin, cout);
+  rc = run_pair(x, cin, 0, h, w, wa_packed, wb_packed, y, cout, out_dtype, flags, stream);
+  return rc ? rc : ok();
+}
+
 int oidn_conv3x3_kernel(int h, int w, int cin0, int cin1, int cout, int in_dtype, int out_dtype,
                         unsigned flags, char* buf, int cap, int* blocks) {
   if (!buf || cap <= 0) return fail(OIDN_E_INVALID, "null or empty name buffer");
@@ -740,7 +839,18 @@ int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int dtype
   const int h = th >> s[layer].level, w = tw >> s[layer].level;
   const bool final_layer = layer == kLayers - 1;
   int nb = 0;
-  if (dtype == OIDN_F16) {
+  if (dtype == OIDN_F16 && (fuse_with_next(in_channels, layer, dtype, true) ||
+                            (layer > 0 && fuse_with_next(in_channels, layer - 1, dtype, true)))) {
+    // both layers of a fused pair report the pair kernel (sized by the first)
+    const int first = fuse_with_next(in_channels, layer, dtype, true) ? layer : layer - 1;
+    const int fh = th >> s[first].level, fw = tw >> s[first].level;
+    const int st = stored_channels(s[first].cin0);
+    const int cs = kUNet[first].src == 0 ? internal_input_lanes(in_channels, dtype) : st;
+    snprintf(buf, cap, "conv3x3_pair_f16<%d, %d, %s>", st > 16 ? 4 : 2,
+             cdiv(stored_channels(s[first + 1].cout), 16), first + 1 == kLayers - 1 ? "true" : "false");
+    (void)cs;
+    nb = conv_pair_blocks(fh, fw);
+  } else if (dtype == OIDN_F16) {
     // as oidn_unet_forward runs it: the input packed with a multiple of 8 lanes
     const int in_cs = internal_input_lanes(in_channels, dtype);
     const Layer& L = kUNet[layer];

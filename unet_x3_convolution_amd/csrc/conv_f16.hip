@@ -163,11 +163,13 @@ __device__ __forceinline__ void stage_patch(_Float16* lds, const _Float16* src, 
 // before its MFMAs, so weight loads overlap the matrix work, and on return
 // `acur` holds the next chunk's.  `hook` runs once, right after the first
 // of those prefetches is issued.
-template <int NFW, int R, int CG, bool PF, bool UP, typename Hook>
+// The wave's window starts at patch row row0 (even for UP) and column col0;
+// PWID is the full-resolution patch width in pixels.
+template <int NFW, int R, int CG, bool PF, bool UP, int PWID = PW, typename Hook>
 __device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], uint4 (&acur)[3][NFW],
                                           const _Float16* lds, int cur, int zero,
                                           const uint4* wchunk, const uint4* wnext, int nf,
-                                          int rg, int g, int c, Hook&& hook) {
+                                          int row0, int col0, int g, int c, Hook&& hook) {
   constexpr int NCG = (3 * CG + 3) / 4;
 #pragma unroll 1
   for (int j = 0; j < NCG; ++j) {
@@ -195,12 +197,12 @@ __device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], uint4 (&acur)[
       constexpr int PS = pstride<CG>();
       if constexpr (UP) {
         // patch row p of this wave's window is half-resolution row
-        // (R / 2) wave + (p + 1) / 2; column c + kx - 1 is (c + kx + 1) / 2
-        base = cur + ((R / 2) * rg * LPW + ((c + kx + 1) >> 1)) * PS + 8 * grp;
+        // row0 / 2 + (p + 1) / 2; column c + kx - 1 is (c + kx + 1) / 2
+        base = cur + ((row0 >> 1) * LPW + ((col0 + c + kx + 1) >> 1)) * PS + 8 * grp;
         rstride = LPW * PS;
       } else {
-        base = cur + ((R * rg) * PW + c + kx) * PS + 8 * grp;
-        rstride = PW * PS;
+        base = cur + (row0 * PWID + col0 + c + kx) * PS + 8 * grp;
+        rstride = PWID * PS;
       }
     }
 #pragma unroll
@@ -267,15 +269,17 @@ __device__ __forceinline__ void store8(void* y, size_t idx, const float (&v)[8])
 // Stores one pixel's values of this lane's NFW fragments (fragments q0 ..):
 // v[q][i] is output channel chan[q] + i.  The two fragments of a pair held
 // by the same lane are 8 consecutive channels and go out as one 16-byte
-// store; others as 8-byte stores.
+// store when all 8 are stored channels; others as 8-byte stores.  Channels
+// at or past cout_stored (a multiple of 4) are never written.
 template <int NFW, bool OUTF32>
 __device__ __forceinline__ void store_pixel(void* y, size_t pix, const int (&chan)[NFW],
                                             const bool (&lead)[NFW], const bool (&tail)[NFW],
                                             int cout_stored, const float (&v)[NFW][4]) {
 #pragma unroll
   for (int q = 0; q < NFW; ++q) {
-    if (chan[q] >= cout_stored || tail[q]) continue;
-    if (q + 1 < NFW && lead[q]) {
+    if (chan[q] >= cout_stored) continue;
+    if (tail[q] && chan[q] + 4 <= cout_stored) continue;   // written with its pair's lead
+    if (q + 1 < NFW && lead[q] && chan[q] + 8 <= cout_stored) {
       const float w8[8] = {v[q][0], v[q][1], v[q][2], v[q][3],
                            v[q + 1][0], v[q + 1][1], v[q + 1][2], v[q + 1][3]};
       store8<OUTF32>(y, pix + chan[q], w8);
@@ -288,10 +292,11 @@ __device__ __forceinline__ void store_pixel(void* y, size_t pix, const int (&cha
 // Epilogue of one wave: bias, ReLU, then the store or the fused 2x2 pool.
 // acc[r][q] holds, for this lane (16-lane group g), rows 4 g .. 4 g + 3 of
 // fragment q0 + q for pixel (yb + r, x); c is the pixel column in the tile.
+// Pixels at or past column xend (<= the image width) are not stored.
 template <int NFW, int R, bool OUTF32>
 __device__ __forceinline__ void store_tile(const floatx4 (&acc)[R][NFW], const ConvF16Args& a,
                                            int q0, int g, int yb, int x, int c, int pool,
-                                           int relu) {
+                                           int relu, int xend) {
   const int nf = a.nf;
   int chan[NFW];
   bool lead[NFW], tail[NFW];   // first / second fragment of a pair this lane holds both of
@@ -310,7 +315,7 @@ __device__ __forceinline__ void store_tile(const floatx4 (&acc)[R][NFW], const C
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int yy = yb + r;
-      if (yy < a.h && x < a.w) {
+      if (yy < a.h && x < xend) {
         float v[NFW][4];
 #pragma unroll
         for (int q = 0; q < NFW; ++q)
@@ -333,7 +338,7 @@ __device__ __forceinline__ void store_tile(const floatx4 (&acc)[R][NFW], const C
           m[q][i] = fmaxf(v, swap_pair(v));
         }
       const int yy = yb + 2 * rp;
-      if ((c & 1) == 0 && yy < a.h && x < a.w)
+      if ((c & 1) == 0 && yy < a.h && x < xend)
         store_pixel<NFW, OUTF32>(a.y, ((size_t)(yy >> 1) * ow + (x >> 1)) * a.cout_stored, chan,
                                  lead, tail, a.cout_stored, m);
     }
@@ -406,7 +411,7 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
       stage_patch<T::TH, CG, false, UP>(lds, src, cs, ch.coff, a.h, a.w, y0, x0, tid);          \
     __syncthreads();                                                                            \
     mma_chunk<NFW, R, CG, PF, UP>(acc, acur, lds, 0, T::ZERO, wf + (size_t)ch.wfrag * 64, wnext, \
-                                  nf, rg, g, c, [] {});                                         \
+                                  nf, R * rg, 0, g, c, [] {});                                  \
   }
   OIDN_CHUNK_LOOP(0, 4, true)
   OIDN_CHUNK_LOOP(1, 2, true)
@@ -415,7 +420,7 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
 #undef OIDN_CHUNK_LOOP
   (void)upcat;
 
-  store_tile<NFW, R, OUTF32>(acc, a, q0, g, y0 + R * rg, x0 + c, c, pool, relu);
+  store_tile<NFW, R, OUTF32>(acc, a, q0, g, y0 + R * rg, x0 + c, c, pool, relu, a.w);
 }
 
 template <int NFW, int R, int WR>
@@ -431,6 +436,177 @@ hipError_t launch_shape(ConvF16Args a, int nsplit, bool upcat, bool pool, bool r
   else
     hipLaunchKernelGGL((conv3x3_f16_mfma<NFW, R, WR, false>), grid, block, 0, stream, a,
                        (int)upcat, (int)pool, (int)relu);
+  return hipGetLastError();
+}
+
+
+// ---------------------------------------------------------------------------
+// Fused pair: y = convB(relu(convA(x))) for a 32-channel intermediate that
+// never leaves LDS.  A workgroup of 4 waves covers a 16 x 30 output tile:
+// convA runs on the 18 x 32 intermediate window around it (two B fragments
+// per row, rows split 9 + 9 between wave pairs), its fp16 result -- zero
+// outside the image, the zero padding convB sees -- overwrites the input
+// patch in LDS, and convB runs on the 16 x 32 output window (the last two
+// columns are computed but not stored).  Every value is rounded and
+// accumulated as by two separate launches, so the results are identical.
+// ---------------------------------------------------------------------------
+constexpr int PAIR_TH = 16, PAIR_TW = 30;          // output tile
+constexpr int PAIR_MH = PAIR_TH + 2;               // intermediate rows
+constexpr int PAIR_IH = PAIR_TH + 4;               // input patch rows
+constexpr int PAIR_PW = 34;                        // patch width (input and intermediate)
+
+template <int CGA>
+struct PairLds {
+  static constexpr int IN = PAIR_IH * PAIR_PW * pstride<CGA>();     // halves
+  static constexpr int MID = PAIR_MH * PAIR_PW * PSTR;
+  static constexpr int REGION = ((IN > MID ? IN : MID) + 511) / 512 * 512;
+  static constexpr int ZERO = REGION;
+};
+
+// Stages one convA chunk: the (PAIR_IH x PAIR_PW)-pixel window at
+// (y0 - 2, x0 - 2), same slot rules as stage_patch_direct.
+template <int CG>
+__device__ __forceinline__ void stage_pair_input(uint4* slots, const _Float16* src, int cs,
+                                                 int coff, int h, int w, int y0, int x0,
+                                                 int wave, int lane) {
+  constexpr int NPIX = PAIR_IH * PAIR_PW;
+  constexpr int SPP = pstride<CG>() / 8;
+  constexpr int NLOAD = (NPIX * SPP + 63) / 64;
+  static_assert(NLOAD * 64 * 8 <= PairLds<CG>::REGION, "pair patch buffer");
+#pragma unroll
+  for (int i = 0; i < (NLOAD + 3) / 4; ++i) {
+    const int k = wave + 4 * i;
+    if (k >= NLOAD) break;
+    const int sl = k * 64 + lane;
+    const int pp = sl / SPP;
+    const int u = sl - pp * SPP;
+    if (u < CG && pp < NPIX) {
+      const int py = pp / PAIR_PW;
+      const int iy = y0 - 2 + py;
+      const int ix = x0 - 2 + (pp - py * PAIR_PW);
+      const int c = coff + 8 * u;
+      const void* gp = g_zero16;
+      if (iy >= 0 && iy < h && ix >= 0 && ix < w && c < cs)
+        gp = src + ((size_t)iy * w + ix) * cs + c;
+      __builtin_amdgcn_global_load_lds(gp, slots + k * 64, 16, 0, 0);
+    }
+  }
+}
+
+template <int CGA, int NFB, bool OUTF32>
+__global__ __launch_bounds__(THREADS, 2) void conv3x3_pair_f16(PairArgs p, int pool, int relu) {
+  using L = PairLds<CGA>;
+  __shared__ __attribute__((aligned(16))) _Float16 lds[L::REGION + 8];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, c = lane & 15;
+  const int cf = wave & 1, rh = wave >> 1;        // column fragment, row half
+
+  const int ntiles = p.tiles_x * p.tiles_y;
+  const int per = (ntiles + kXcds - 1) / kXcds;
+  const int tile = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  if (tile >= ntiles) return;
+  const int ty = tile / p.tiles_x;
+  const int y0 = ty * PAIR_TH, x0 = (tile - ty * p.tiles_x) * PAIR_TW;
+  if (tid < 2) reinterpret_cast<uint2*>(lds + L::ZERO)[tid] = make_uint2(0u, 0u);
+
+  // convA: intermediate rows [9 rh, 9 rh + 9), columns [16 cf, 16 cf + 16)
+  // of the window at (y0 - 1, x0 - 1); both fragments of the 32 channels.
+  constexpr int RA = PAIR_MH / 2;
+  floatx4 acc[RA][2];
+#pragma unroll
+  for (int r = 0; r < RA; ++r) acc[r][0] = acc[r][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+  {
+    const uint4* wf = static_cast<const uint4*>(p.wA) + lane;
+    uint4 acur[3][2];
+#pragma unroll
+    for (int ky = 0; ky < 3; ++ky)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) acur[ky][q] = wf[(ky * 2 + q) * 64];
+    const _Float16* src = static_cast<const _Float16*>(p.x);
+#pragma unroll 1
+    for (int ci = 0; ci < p.nchunks; ++ci) {
+      __syncthreads();
+      stage_pair_input<CGA>(reinterpret_cast<uint4*>(lds), src, p.cs, ci * kChunkChannels, p.h,
+                            p.w, y0, x0, wave, lane);
+      __syncthreads();
+      const uint4* wchunk = wf + (size_t)p.wfragA[ci] * 64;
+      const uint4* wnext = ci + 1 < p.nchunks ? wf + (size_t)p.wfragA[ci + 1] * 64 : nullptr;
+      mma_chunk<2, RA, CGA, true, false, PAIR_PW>(acc, acur, lds, 0, L::ZERO, wchunk, wnext, 2,
+                                                  RA * rh, 16 * cf, g, c, [] {});
+    }
+  }
+  __syncthreads();   // every wave is done with the input patch
+  {
+    // bias, ReLU, fp16; zero outside the image.  Lane group g of the pair
+    // of fragments owns channels 8 g .. 8 g + 7 (one 16-byte slot).
+    float bA[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bA[i] = p.biasA[8 * g + i];
+      bA[4 + i] = p.biasA[8 * g + 4 + i];
+    }
+    const int x = x0 - 1 + 16 * cf + c;
+#pragma unroll
+    for (int r = 0; r < RA; ++r) {
+      const int y = y0 - 1 + RA * rh + r;
+      const bool inside = y >= 0 && y < p.h && x >= 0 && x < p.w;
+      uint4 v;
+      uint32_t* wv = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i0 = 2 * k, i1 = 2 * k + 1;
+        const float f0 = (i0 < 4 ? acc[r][0][i0] : acc[r][1][i0 - 4]) + bA[i0];
+        const float f1 = (i1 < 4 ? acc[r][0][i1] : acc[r][1][i1 - 4]) + bA[i1];
+        const _Float16 h0 = inside ? (_Float16)fmaxf(f0, 0.f) : (_Float16)0.f;
+        const _Float16 h1 = inside ? (_Float16)fmaxf(f1, 0.f) : (_Float16)0.f;
+        wv[k] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+      }
+      const int px = (RA * rh + r) * PAIR_PW + 16 * cf + c;
+      *reinterpret_cast<uint4*>(lds + px * PSTR + 8 * g) = v;
+    }
+  }
+  __syncthreads();
+  // convB: output rows [8 rh, 8 rh + 8), columns [16 cf, 16 cf + 16).
+  constexpr int RB = PAIR_TH / 2;
+  floatx4 accb[RB][NFB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int q = 0; q < NFB; ++q) accb[r][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+  {
+    const uint4* wf = static_cast<const uint4*>(p.wB) + lane;
+    uint4 acur[3][NFB];
+#pragma unroll
+    for (int ky = 0; ky < 3; ++ky)
+#pragma unroll
+      for (int q = 0; q < NFB; ++q) acur[ky][q] = wf[(ky * NFB + q) * 64];
+    mma_chunk<NFB, RB, 4, true, false, PAIR_PW>(accb, acur, lds, 0, L::ZERO, wf, nullptr, NFB,
+                                                RB * rh, 16 * cf, g, c, [] {});
+  }
+  ConvF16Args a{};
+  a.h = p.h;
+  a.w = p.w;
+  a.bias = p.biasB;
+  a.y = p.y;
+  a.cout_stored = p.cout_stored;
+  a.nf = NFB;
+  const int xend = x0 + PAIR_TW < p.w ? x0 + PAIR_TW : p.w;
+  store_tile<NFB, RB, OUTF32>(accb, a, 0, g, y0 + RB * rh, x0 + 16 * cf + c, c, pool, relu, xend);
+}
+
+template <int CGA, int NFB>
+hipError_t launch_pair_shape(PairArgs p, bool pool, bool relu, bool out_f32, hipStream_t stream) {
+  p.tiles_x = cdiv(p.w, PAIR_TW);
+  p.tiles_y = cdiv(p.h, PAIR_TH);
+  const dim3 grid(cdiv(p.tiles_x * p.tiles_y, kXcds) * kXcds), block(THREADS);
+  if (out_f32)
+    hipLaunchKernelGGL((conv3x3_pair_f16<CGA, NFB, true>), grid, block, 0, stream, p, (int)pool,
+                       (int)relu);
+  else
+    hipLaunchKernelGGL((conv3x3_pair_f16<CGA, NFB, false>), grid, block, 0, stream, p, (int)pool,
+                       (int)relu);
   return hipGetLastError();
 }
 
@@ -552,6 +728,19 @@ hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, 
   const ConvPlan P = conv_f16_plan(a.h, a.w, nf);
   const int nsplit = nf / plan_block_frags(P);
   return launch_plan(b, P, nsplit, upcat, pool, relu, out_f32, stream);
+}
+
+hipError_t launch_conv_pair_f16(const PairArgs& p, int cga, int nfb, bool pool, bool relu,
+                                bool out_f32, hipStream_t stream) {
+  if (cga == 2 && nfb == 2) return launch_pair_shape<2, 2>(p, pool, relu, out_f32, stream);
+  if (cga == 2 && nfb == 1) return launch_pair_shape<2, 1>(p, pool, relu, out_f32, stream);
+  if (cga == 4 && nfb == 2) return launch_pair_shape<4, 2>(p, pool, relu, out_f32, stream);
+  if (cga == 4 && nfb == 1) return launch_pair_shape<4, 1>(p, pool, relu, out_f32, stream);
+  return hipErrorInvalidValue;
+}
+
+int conv_pair_blocks(int h, int w) {
+  return cdiv(cdiv(w, PAIR_TW) * cdiv(h, PAIR_TH), kXcds) * kXcds;
 }
 
 }  // namespace oidn

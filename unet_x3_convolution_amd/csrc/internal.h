@@ -99,6 +99,26 @@ int conv_f16_blocks(int h, int w, int nf);
 void conv_f16_describe(const ConvF16Args& a, int nf, bool out_f32, char* buf, int cap,
                        int* blocks);
 
+// Fused pair y = convB(relu(convA(x))) through a 32-channel intermediate kept
+// in LDS (both fp16 layouts as above; convA: one source whose stored channel
+// count is a multiple of 8, all chunks of one kind; convB: 32 -> cout <= 32).
+struct PairArgs {
+  const void* x;           // fp16, h x w x cs
+  int cs, h, w;
+  int nchunks;             // convA chunks (<= 32 channels each, in order)
+  int wfragA[8];           // first weight fragment of each convA chunk
+  const float* biasA;      // 32 floats
+  const void* wA;          // convA fragments (nf = 2)
+  const float* biasB;      // 16 * nfB floats
+  const void* wB;          // convB fragments (one 32-channel chunk)
+  void* y;
+  int cout_stored;
+  int tiles_x, tiles_y;
+};
+hipError_t launch_conv_pair_f16(const PairArgs& p, int cga, int nfb, bool pool, bool relu,
+                                bool out_f32, hipStream_t stream);
+int conv_pair_blocks(int h, int w);
+
 // ---------------------------------------------------------------------------
 // fp32 direct conv (VALU FMA).  Packed weights: bias (cout_stored floats,
 // 256-aligned) then [out block][tap][stored input channel over both
