@@ -28,8 +28,8 @@
 //    neighbouring lanes (one DPP swap).  Max is taken in fp32 before the
 //    single fp16 rounding; RNE is monotone, so this equals pooling the
 //    rounded conv output.
-//  * Tiles are dealt to blocks so that each of the 8 XCDs walks a contiguous
-//    band of tiles (halo rows shared through its own L2).
+//  * Tiles are dealt to blocks in 8 x 8-tile super-tiles, each of the 8 XCDs
+//    taking a contiguous range of them (halos shared through its own L2).
 //
 // The per-pixel reduction order depends only on the channel layout, never on
 // the pixel position or the image size, so tiled and untiled runs agree bit
@@ -73,6 +73,30 @@ struct Tile {
 __device__ __attribute__((aligned(16))) unsigned int g_zero16[4] = {0u, 0u, 0u, 0u};
 
 __device__ __forceinline__ half8 as_half8(uint4 v) { return __builtin_bit_cast(half8, v); }
+
+// Tile order.  Tiles are walked in super-tiles of kSuperW x kSuperH tiles
+// (row-major inside a super-tile, super-tiles row-major), and XCD x takes
+// the x-th contiguous eighth of that order; block b runs on XCD b % 8.  The
+// 64 or so workgroups an XCD runs at once then cover a near-square patch of
+// the image, so halo rows and columns shared by neighbouring tiles are
+// fetched into that XCD's L2 once.  Returns false for the padding blocks
+// past the last tile.
+constexpr int kSuperW = 8, kSuperH = 8;
+__device__ __forceinline__ bool tile_of_block(int b, int tiles_x, int tiles_y, int& tx, int& ty) {
+  const int ntiles = tiles_x * tiles_y;
+  const int per = (ntiles + kXcds - 1) / kXcds;
+  const int t = (b % kXcds) * per + b / kXcds;
+  if (t >= ntiles) return false;
+  const int row0 = t / (kSuperH * tiles_x) * kSuperH;    // first tile row of the super-row
+  const int sh = min(kSuperH, tiles_y - row0);            // its rows
+  const int u = t - row0 * tiles_x;                       // index inside the super-row
+  const int col0 = u / (sh * kSuperW) * kSuperW;          // first tile column of the super-tile
+  const int sw = min(kSuperW, tiles_x - col0);            // its columns
+  const int v = u - col0 * sh;                            // index inside the super-tile
+  ty = row0 + v / sw;
+  tx = col0 + v - (v / sw) * sw;
+  return true;
+}
 
 // Stage one chunk's halo patch.  Full resolution: (TH + 2) x 18 pixels at
 // (y0 - 1, x0 - 1).  UP (the decoder's upsampled source): the same window
@@ -368,13 +392,8 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
   (void)upcat;
   constexpr bool PF = kPrefetch<NFW, R>;
 
-  // XCD-aware tile order: block b runs on XCD b % 8; give each XCD a band.
-  const int ntiles = a.tiles_x * a.tiles_y;
-  const int per = (ntiles + kXcds - 1) / kXcds;
-  const int tile = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-  if (tile >= ntiles) return;
-  const int ty = tile / a.tiles_x;
-  const int tx = tile - ty * a.tiles_x;
+  int tx, ty;
+  if (!tile_of_block(blockIdx.x, a.tiles_x, a.tiles_y, tx, ty)) return;
   const int y0 = ty * T::TH, x0 = tx * TW;
 
   if (tid < 2) reinterpret_cast<uint2*>(lds + T::ZERO)[tid] = make_uint2(0u, 0u);
@@ -502,12 +521,9 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_pair_f16(PairArgs p, int p
   const int g = lane >> 4, c = lane & 15;
   const int cf = wave & 1, rh = wave >> 1;        // column fragment, row half
 
-  const int ntiles = p.tiles_x * p.tiles_y;
-  const int per = (ntiles + kXcds - 1) / kXcds;
-  const int tile = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-  if (tile >= ntiles) return;
-  const int ty = tile / p.tiles_x;
-  const int y0 = ty * PAIR_TH, x0 = (tile - ty * p.tiles_x) * PAIR_TW;
+  int tx, ty;
+  if (!tile_of_block(blockIdx.x, p.tiles_x, p.tiles_y, tx, ty)) return;
+  const int y0 = ty * PAIR_TH, x0 = tx * PAIR_TW;
   if (tid < 2) reinterpret_cast<uint2*>(lds + L::ZERO)[tid] = make_uint2(0u, 0u);
 
   // convA: intermediate rows [9 rh, 9 rh + 9), columns [16 cf, 16 cf + 16)
