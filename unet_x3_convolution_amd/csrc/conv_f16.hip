@@ -512,8 +512,14 @@ __device__ __forceinline__ void stage_pair_input(uint4* slots, const _Float16* s
   }
 }
 
+// A 16-channel convA source leaves LDS for three workgroups per CU; the
+// registers are held to that.  32-channel chunks need more LDS: two.
+template <int CGA>
+constexpr int kPairWaves = CGA == 2 ? 3 : 2;
+
 template <int CGA, int NFB, bool OUTF32>
-__global__ __launch_bounds__(THREADS, 2) void conv3x3_pair_f16(PairArgs p, int pool, int relu) {
+__global__ __launch_bounds__(THREADS, (kPairWaves<CGA>)) void conv3x3_pair_f16(PairArgs p, int pool,
+                                                                              int relu) {
   using L = PairLds<CGA>;
   __shared__ __attribute__((aligned(16))) _Float16 lds[L::REGION + 8];
   const int tid = threadIdx.x;
