@@ -235,7 +235,7 @@ def main():
     for L in layers:
         del L["flops"]
     px0 = tw * th
-    pack_bytes = W * H * 48 + px0 * 12 * 2 if len(tiles) == 1 else None
+    pack_bytes = W * H * 48 + px0 * 16 * 2 if len(tiles) == 1 else None   # 16 lanes fp16 out
     unpack_bytes = W * H * (32 + 16)
     for j, nm in ((0, "input pass"), (nk - 1, "output pass")):
         print(f"  {nm:11s} {avg_ms[j] * 1e3:8.1f} us", file=sys.stderr)
