@@ -47,26 +47,34 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int TW = 16;                        // tile width (one B fragment)
 constexpr int PW = TW + 2;                    // patch width
 constexpr int PSTR = 40;                      // halves per patch pixel: 32 + 8 pad (80 B)
-// Pixel stride of a chunk of CG channel groups: 4 groups -> 5 slots (80 B),
-// 2 groups -> 3 slots (48 B); both keep 16 consecutive pixels of a fragment
-// read on distinct LDS banks.
-template <int CG>
-constexpr int pstride() { return CG == 4 ? PSTR : 24; }
+// Two patch layouts.  Padded (SW false): a chunk of CG channel groups takes
+// 4 groups -> 5 slots (80 B), 2 groups -> 3 slots (48 B) per pixel; the odd
+// stride keeps 16 consecutive pixels of a fragment read on distinct LDS
+// banks.  Swizzled (SW true): no pad (64 B / 32 B per pixel); channel group
+// grp of the pixel in patch column col sits in slot gslot(col, grp), the
+// group index XOR column bits, which spreads the same 16-pixel reads over 16
+// distinct 16-byte bank groups in 4/5 (CG 4) or 2/3 (CG 2) of the space.
+template <int CG, bool SW = false>
+constexpr int pstride() { return SW ? 8 * CG : CG == 4 ? PSTR : 24; }
+template <int CG, bool SW>
+__device__ __forceinline__ int gslot(int col, int grp) {
+  if constexpr (!SW) return grp;
+  else return CG == 4 ? grp ^ ((col >> 2) & 3) : grp ^ ((col >> 3) & 1);
+}
 constexpr int THREADS = 256;
 constexpr int kXcds = 8;
 
 constexpr int LPW = TW / 2 + 2;               // half-resolution patch width
 
-template <int TH_>
+template <int TH_, bool SW = false>
 struct Tile {
   static constexpr int TH = TH_;                // tile height (rows)
   static constexpr int PH = TH + 2;
   static constexpr int LPH = TH / 2 + 2;        // half-resolution patch height
   // The patch occupies whole 64-slot (1 KB) blocks so that direct
   // global -> LDS loads, which fill 64 consecutive 16-byte slots each, stay
-  // inside it; 8 zero halves follow.
-  static constexpr int PATCH = (PH * PW * PSTR + 511) / 512 * 512;   // halves
-  static constexpr int ZERO = PATCH;
+  // inside it.
+  static constexpr int PATCH = (PH * PW * pstride<4, SW>() + 511) / 512 * 512;   // halves
 };
 
 // Zero block that padding lanes of the direct patch loads read from.
@@ -108,20 +116,21 @@ __device__ __forceinline__ bool tile_of_block(int b, int tiles_x, int tiles_y, i
 // image are zero.
 // Direct global -> LDS staging of the same patch for sources whose stored
 // channel count is a multiple of 8: wave load k fills LDS slots
-// [64 k, 64 k + 64); slot s is patch pixel s / SPP, channel group s % SPP
-// (the last slot of a pixel is the pad, which no lane loads).  Every load of
+// [64 k, 64 k + 64); slot s is patch pixel s / SPP, position s % SPP
+// (padded layout: channel group s % SPP, the last slot of a pixel is the
+// pad, which no lane loads; swizzled: the group gslot maps to it).  Every load of
 // the chunk is issued back to back (nothing waits on registers); the barrier
 // that follows drains them.  Slots with no data (channel groups past the
 // source, pixels outside the image) load the zero block.
 // TH: tile height; NW: waves sharing the work; CAP: buffer capacity in slots.
-template <int TH, int NW, int CAP, int CG, bool UP>
+template <int TH, int NW, int CAP, int CG, bool UP, bool SW = false>
 __device__ __forceinline__ void stage_patch_direct(uint4* slots, const _Float16* src, int cs,
                                                    int coff, int h, int w, int y0, int x0,
                                                    int wave, int lane) {
   constexpr int PH = UP ? TH / 2 + 2 : TH + 2;
   constexpr int PWD = UP ? LPW : PW;
   constexpr int NPIX = PH * PWD;
-  constexpr int SPP = pstride<CG>() / 8;        // 16-byte slots per pixel
+  constexpr int SPP = pstride<CG, SW>() / 8;    // 16-byte slots per pixel
   constexpr int NLOAD = (NPIX * SPP + 63) / 64;
   static_assert(NLOAD * 64 <= CAP, "patch buffer");
   const int sh = UP ? (h >> 1) : h, sw = UP ? (w >> 1) : w;
@@ -135,9 +144,10 @@ __device__ __forceinline__ void stage_patch_direct(uint4* slots, const _Float16*
     const int u = sl - pp * SPP;
     if (u < CG && pp < NPIX) {   // pad slots are never read: those lanes stay idle
       const int py = pp / PWD;
+      const int px = pp - py * PWD;
       const int iy = oy + py;
-      const int ix = ox + (pp - py * PWD);
-      const int c = coff + 8 * u;
+      const int ix = ox + px;
+      const int c = coff + 8 * gslot<CG, SW>(px, u);   // gslot is its own inverse
       const void* gp = g_zero16;
       if (iy >= 0 && iy < sh && ix >= 0 && ix < sw && c < cs)
         gp = src + ((size_t)iy * sw + ix) * cs + c;
@@ -146,7 +156,7 @@ __device__ __forceinline__ void stage_patch_direct(uint4* slots, const _Float16*
   }
 }
 
-template <int TH, int CG, bool VEC16, bool UP>
+template <int TH, int CG, bool VEC16, bool UP, bool SW = false>
 __device__ __forceinline__ void stage_patch(_Float16* lds, const _Float16* src, int cs, int coff,
                                             int h, int w, int y0, int x0, int tid) {
   constexpr int PH = UP ? Tile<TH>::LPH : Tile<TH>::PH;
@@ -170,11 +180,12 @@ __device__ __forceinline__ void stage_patch(_Float16* lds, const _Float16* src, 
     if constexpr (VEC16) {
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
       if (inside) v = *reinterpret_cast<const uint4*>(p);
-      *reinterpret_cast<uint4*>(lds + pp * pstride<CG>() + UCH * q) = v;
+      *reinterpret_cast<uint4*>(lds + pp * pstride<CG, SW>() + 8 * gslot<CG, SW>(px, q)) = v;
     } else {
       uint2 v = make_uint2(0u, 0u);
       if (inside) v = *reinterpret_cast<const uint2*>(p);
-      *reinterpret_cast<uint2*>(lds + pp * pstride<CG>() + UCH * q) = v;
+      *reinterpret_cast<uint2*>(lds + pp * pstride<CG, SW>() + 8 * gslot<CG, SW>(px, q >> 1) +
+                                4 * (q & 1)) = v;
     }
   }
 }
@@ -188,8 +199,10 @@ __device__ __forceinline__ void stage_patch(_Float16* lds, const _Float16* src, 
 // `acur` holds the next chunk's.  `hook` runs once, right after the first
 // of those prefetches is issued.
 // The wave's window starts at patch row row0 (even for UP) and column col0;
-// PWID is the full-resolution patch width in pixels.
-template <int NFW, int R, int CG, bool PF, bool UP, int PWID = PW, typename Hook>
+// PWID is the full-resolution patch width in pixels; SW selects the
+// swizzled patch layout.  `wchunk` may point into LDS (weights staged there);
+// `nf` is then the fragment count of a staged weight row.
+template <int NFW, int R, int CG, bool PF, bool UP, int PWID = PW, bool SW = false, typename Hook>
 __device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], uint4 (&acur)[3][NFW],
                                           const _Float16* lds, int cur, int zero,
                                           const uint4* wchunk, const uint4* wnext, int nf,
@@ -218,14 +231,16 @@ __device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], uint4 (&acur)[
     if (slot < 3 * CG) {
       const int kx = slot / CG;
       const int grp = slot - kx * CG;
-      constexpr int PS = pstride<CG>();
+      constexpr int PS = pstride<CG, SW>();
       if constexpr (UP) {
         // patch row p of this wave's window is half-resolution row
         // row0 / 2 + (p + 1) / 2; column c + kx - 1 is (c + kx + 1) / 2
-        base = cur + ((row0 >> 1) * LPW + ((col0 + c + kx + 1) >> 1)) * PS + 8 * grp;
+        const int col = (col0 + c + kx + 1) >> 1;
+        base = cur + ((row0 >> 1) * LPW + col) * PS + 8 * gslot<CG, SW>(col, grp);
         rstride = LPW * PS;
       } else {
-        base = cur + (row0 * PWID + col0 + c + kx) * PS + 8 * grp;
+        const int col = col0 + c + kx;
+        base = cur + (row0 * PWID + col) * PS + 8 * gslot<CG, SW>(col, grp);
         rstride = PWID * PS;
       }
     }
@@ -369,20 +384,59 @@ __device__ __forceinline__ void store_tile(const floatx4 (&acc)[R][NFW], const C
   }
 }
 
+// Direct global -> LDS copy of a chunk's weight rows for the workgroup's FB
+// fragments: NB = (column groups) x 3 x FB blocks of 1 KB; block k is
+// fragment k % FB of weight row k / FB (a row holds nf fragments, `w` points
+// at the workgroup's first one, lane offset included).  The four waves
+// issue them round-robin; the barrier that follows drains them.
+template <int NB>
+__device__ __forceinline__ void stage_weights(_Float16* dst, const uint4* w, int nf, int fb,
+                                              int wave) {
+  uint4* slots = reinterpret_cast<uint4*>(dst);
+#pragma unroll
+  for (int i = 0; i < (NB + 3) / 4; ++i) {
+    const int k = wave + 4 * i;
+    if (k >= NB) break;
+    const int row = k / fb;
+    __builtin_amdgcn_global_load_lds(w + (size_t)(row * nf + (k - row * fb)) * 64, slots + k * 64,
+                                     16, 0, 0);
+  }
+}
+
 // Weight prefetch doubles the A registers (12 NFW more); use it only where
 // accumulators and both A sets leave room for two waves per SIMD.
 template <int NFW, int R>
 constexpr bool kPrefetch = 4 * R * NFW + 24 * NFW <= 176;
 
-// A workgroup of 4 waves covers a (WR R) x 16 tile for NFW (4 / WR) output
-// fragments: wave w computes rows [R (w % WR), + R) for the NFW fragments
-// starting at (4 / WR) NFW blockIdx.y + NFW (w / WR).
+// Staged weights: the workgroup's FB fragments of one chunk take
+// 9 FB KB (3 column groups x 3 ky x FB, 1 KB each).  They go to LDS where
+// the swizzled patch and those weights leave room for two workgroups per CU.
+template <int NFW, int R, int WR>
+constexpr int kWeightSlots = 9 * NFW * (4 / WR) * 64;
+template <int NFW, int R, int WR>
+constexpr bool kWeightsInLds =
+    2 * (2 * Tile<WR * R, true>::PATCH + 16 * kWeightSlots<NFW, R, WR> + 16) <= 160 * 1024;
+
+// A workgroup of 4 waves covers a (WR R) x 16 tile for FB = NFW (4 / WR)
+// output fragments: wave w computes rows [R (w % WR), + R) for the NFW
+// fragments starting at FB blockIdx.y + NFW (w / WR).
+// With the weights in LDS (WL) each chunk's weight rows for the FB
+// fragments are copied there with the chunk's patch (one 1 KB direct load
+// per (column group, ky, fragment)), so the four waves share one copy and
+// the A operands come from LDS; the patch uses the swizzled layout.  Else
+// every wave reads its A operands from global memory (L1/L2), with the next
+// column group's prefetched into registers where they fit.
 template <int NFW, int R, int WR, bool OUTF32>
 __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
     ConvF16Args a, int upcat, int pool, int relu) {
   static_assert(WR == 1 || WR == 2 || WR == 4, "row groups");
-  using T = Tile<WR * R>;
-  __shared__ __attribute__((aligned(16))) _Float16 lds[T::PATCH + 8];
+  constexpr bool WL = kWeightsInLds<NFW, R, WR>;
+  constexpr bool SW = WL;
+  constexpr int FB = NFW * (4 / WR);             // fragments per workgroup
+  using T = Tile<WR * R, SW>;
+  constexpr int WOFF = T::PATCH;                 // staged weights (halves)
+  constexpr int ZERO = WOFF + (WL ? 8 * kWeightSlots<NFW, R, WR> : 0);
+  __shared__ __attribute__((aligned(16))) _Float16 lds[ZERO + 8];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;
@@ -390,13 +444,13 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
   const int rg = wave % WR;
   const int q0 = (blockIdx.y * (4 / WR) + wave / WR) * NFW;   // this wave's output fragments
   (void)upcat;
-  constexpr bool PF = kPrefetch<NFW, R>;
+  constexpr bool PF = !WL && kPrefetch<NFW, R>;
 
   int tx, ty;
   if (!tile_of_block(blockIdx.x, a.tiles_x, a.tiles_y, tx, ty)) return;
   const int y0 = ty * T::TH, x0 = tx * TW;
 
-  if (tid < 2) reinterpret_cast<uint2*>(lds + T::ZERO)[tid] = make_uint2(0u, 0u);
+  if (tid < 2) reinterpret_cast<uint2*>(lds + ZERO)[tid] = make_uint2(0u, 0u);
 
   floatx4 acc[R][NFW];
 #pragma unroll
@@ -405,6 +459,9 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
     for (int q = 0; q < NFW; ++q) acc[r][q] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const uint4* wf = static_cast<const uint4*>(a.wfrag) + lane + q0 * 64;
+  // the workgroup's weight rows (direct loads) and this wave's staged A operands
+  const uint4* wblk = static_cast<const uint4*>(a.wfrag) + lane + blockIdx.y * FB * 64;
+  const uint4* wl = reinterpret_cast<const uint4*>(lds + WOFF) + lane + (wave / WR) * NFW * 64;
   uint4 acur[3][NFW];
   if (PF) {
     const uint4* w0 = wf + (size_t)a.chunk[0].wfrag * 64;
@@ -424,13 +481,20 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
     const uint4* wnext = ci + 1 < a.nchunks ? wf + (size_t)a.chunk[ci + 1].wfrag * 64 : nullptr; \
     __syncthreads();                                                                            \
     if ((cs & 7) == 0)                                                                          \
-      stage_patch_direct<T::TH, 4, T::PATCH / 8, CG, UP>(reinterpret_cast<uint4*>(lds), src, cs, \
-                                                         ch.coff, a.h, a.w, y0, x0, wave, lane); \
+      stage_patch_direct<T::TH, 4, T::PATCH / 8, CG, UP, SW>(reinterpret_cast<uint4*>(lds), src, \
+                                                             cs, ch.coff, a.h, a.w, y0, x0, wave, \
+                                                             lane);                             \
     else                                                                                        \
-      stage_patch<T::TH, CG, false, UP>(lds, src, cs, ch.coff, a.h, a.w, y0, x0, tid);          \
+      stage_patch<T::TH, CG, false, UP, SW>(lds, src, cs, ch.coff, a.h, a.w, y0, x0, tid);      \
+    if constexpr (WL) stage_weights<(3 * CG + 3) / 4 * 3 * FB>(lds + WOFF, wblk + (size_t)ch.wfrag * 64, \
+                                                              nf, FB, wave);                    \
     __syncthreads();                                                                            \
-    mma_chunk<NFW, R, CG, PF, UP>(acc, acur, lds, 0, T::ZERO, wf + (size_t)ch.wfrag * 64, wnext, \
-                                  nf, R * rg, 0, g, c, [] {});                                  \
+    if constexpr (WL)                                                                           \
+      mma_chunk<NFW, R, CG, false, UP, PW, SW>(acc, acur, lds, 0, ZERO, wl, nullptr, FB, R * rg, \
+                                               0, g, c, [] {});                                 \
+    else                                                                                        \
+      mma_chunk<NFW, R, CG, PF, UP>(acc, acur, lds, 0, ZERO, wf + (size_t)ch.wfrag * 64, wnext, \
+                                    nf, R * rg, 0, g, c, [] {});                                \
   }
   OIDN_CHUNK_LOOP(0, 4, true)
   OIDN_CHUNK_LOOP(1, 2, true)
