@@ -69,6 +69,9 @@ F16_CASES = [
     (512, 1000, 32, 48, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),   # 3 fragments, pooled, ragged
     (530, 1024, 64, 32, U.OIDN_RELU, "f16"),                    # two chunks per tile
     (544, 512, 32, 64, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),    # 4 fragments
+    (546, 1002, 48, 64, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),   # ragged, 32 + 16 chunks, pooled
+    (530, 1010, 32, 64, 0, "f32"),                              # ragged, fp32 out, no ReLU
+    (544, 520, 96, 64, U.OIDN_RELU, "f16"),                     # three chunks per tile
     # one case per launch plan instance <fragments/wave, rows/wave, row groups>
     (272, 480, 48, 64, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),    # <2, 8, 2>
     (272, 480, 96, 96, U.OIDN_RELU, "f16"),                     # <3, 8, 2>
@@ -158,6 +161,7 @@ UPCAT_CASES = [
     (12, 10, 16, 9, 8, "f32"),
     (512, 1024, 64, 9, 64, "f16"),                              # 32-row tiles
     (544, 960, 64, 16, 64, "f16"),                              # 16-channel skip, 3 chunks
+    (546, 1002, 96, 32, 64, "f16"),                             # ragged, 4 chunks
     (514, 1026, 32, 16, 32, "f16"),                             # ragged
     (272, 480, 112, 48, 96, "f16"),                             # <3, 8, 2>: 2 row groups
 ]
