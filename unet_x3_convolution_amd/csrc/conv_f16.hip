@@ -77,6 +77,26 @@ struct Tile {
   static constexpr int PATCH = (PH * PW * pstride<4, SW>() + 511) / 512 * 512;   // halves
 };
 
+// One direct global -> LDS load: 16 bytes per lane, lane i filling the
+// 16-byte slot i from `lds` (wave-uniform).  ASM issues it through inline
+// assembly: the compiler then tracks no LDS write for it and adds no wait
+// for it before later memory operations, so the caller must wait (vmcnt)
+// before reading what it copies.  M0 is set right before the load (the
+// compiler sets M0 itself before each of its own uses).
+template <bool ASM>
+__device__ __forceinline__ void dma16(const void* gp, uint4* lds) {
+  if constexpr (ASM) {
+    const unsigned m0 = __builtin_amdgcn_readfirstlane(
+        (unsigned)(unsigned long)(__attribute__((address_space(3))) void*)lds);
+    // an SALU write of M0 needs one wait state before a load that uses it
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0),
+                 "v"(gp)
+                 : "memory");
+  } else {
+    __builtin_amdgcn_global_load_lds(gp, lds, 16, 0, 0);
+  }
+}
+
 // Zero block that padding lanes of the direct patch loads read from.
 __device__ __attribute__((aligned(16))) unsigned int g_zero16[4] = {0u, 0u, 0u, 0u};
 
@@ -388,8 +408,9 @@ __device__ __forceinline__ void store_tile(const floatx4 (&acc)[R][NFW], const C
 // fragments: NB = (column groups) x 3 x FB blocks of 1 KB; block k is
 // fragment k % FB of weight row k / FB (a row holds nf fragments, `w` points
 // at the workgroup's first one, lane offset included).  The four waves
-// issue them round-robin; the barrier that follows drains them.
-template <int NB>
+// issue them round-robin; the barrier that follows drains them (with ASM,
+// after an explicit vmcnt wait).
+template <int NB, bool ASM = false>
 __device__ __forceinline__ void stage_weights(_Float16* dst, const uint4* w, int nf, int fb,
                                               int wave) {
   uint4* slots = reinterpret_cast<uint4*>(dst);
@@ -398,8 +419,7 @@ __device__ __forceinline__ void stage_weights(_Float16* dst, const uint4* w, int
     const int k = wave + 4 * i;
     if (k >= NB) break;
     const int row = k / fb;
-    __builtin_amdgcn_global_load_lds(w + (size_t)(row * nf + (k - row * fb)) * 64, slots + k * 64,
-                                     16, 0, 0);
+    dma16<ASM>(w + (size_t)(row * nf + (k - row * fb)) * 64, slots + k * 64);
   }
 }
 
@@ -538,22 +558,33 @@ constexpr int PAIR_MH = PAIR_TH + 2;               // intermediate rows
 constexpr int PAIR_IH = PAIR_TH + 4;               // input patch rows
 constexpr int PAIR_PW = 34;                        // patch width (input and intermediate)
 
+// With 32-channel convA chunks (SW) the input patch and the intermediate
+// use the swizzled layout and the weights are staged in LDS: each convA
+// chunk's rows (2 fragments) with its patch, then convB's (NFB <= 2
+// fragments) while the intermediate is written -- the four waves share one
+// copy instead of each reading every A operand from global memory.  That
+// still leaves two workgroups per CU.  16-channel convA chunks (three
+// workgroups per CU, no LDS to spare) keep the padded layout and global
+// weights.
 template <int CGA>
 struct PairLds {
-  static constexpr int IN = PAIR_IH * PAIR_PW * pstride<CGA>();     // halves
-  static constexpr int MID = PAIR_MH * PAIR_PW * PSTR;
+  static constexpr bool SW = CGA == 4;
+  static constexpr int IN = PAIR_IH * PAIR_PW * pstride<CGA, SW>();     // halves
+  static constexpr int MID = PAIR_MH * PAIR_PW * pstride<4, SW>();
   static constexpr int REGION = ((IN > MID ? IN : MID) + 511) / 512 * 512;
-  static constexpr int ZERO = REGION;
+  static constexpr int WSLOTS = SW ? 9 * 2 * 64 : 0;                 // weight rows (16 B slots)
+  static constexpr int WOFF = REGION;
+  static constexpr int ZERO = REGION + 8 * WSLOTS;
 };
 
 // Stages one convA chunk: the (PAIR_IH x PAIR_PW)-pixel window at
 // (y0 - 2, x0 - 2), same slot rules as stage_patch_direct.
-template <int CG>
+template <int CG, bool SW>
 __device__ __forceinline__ void stage_pair_input(uint4* slots, const _Float16* src, int cs,
                                                  int coff, int h, int w, int y0, int x0,
                                                  int wave, int lane) {
   constexpr int NPIX = PAIR_IH * PAIR_PW;
-  constexpr int SPP = pstride<CG>() / 8;
+  constexpr int SPP = pstride<CG, SW>() / 8;
   constexpr int NLOAD = (NPIX * SPP + 63) / 64;
   static_assert(NLOAD * 64 * 8 <= PairLds<CG>::REGION, "pair patch buffer");
 #pragma unroll
@@ -565,9 +596,10 @@ __device__ __forceinline__ void stage_pair_input(uint4* slots, const _Float16* s
     const int u = sl - pp * SPP;
     if (u < CG && pp < NPIX) {
       const int py = pp / PAIR_PW;
+      const int px = pp - py * PAIR_PW;
       const int iy = y0 - 2 + py;
-      const int ix = x0 - 2 + (pp - py * PAIR_PW);
-      const int c = coff + 8 * u;
+      const int ix = x0 - 2 + px;
+      const int c = coff + 8 * gslot<CG, SW>(px, u);
       const void* gp = g_zero16;
       if (iy >= 0 && iy < h && ix >= 0 && ix < w && c < cs)
         gp = src + ((size_t)iy * w + ix) * cs + c;
@@ -585,7 +617,8 @@ template <int CGA, int NFB, bool OUTF32>
 __global__ __launch_bounds__(THREADS, (kPairWaves<CGA>)) void conv3x3_pair_f16(PairArgs p, int pool,
                                                                               int relu) {
   using L = PairLds<CGA>;
-  __shared__ __attribute__((aligned(16))) _Float16 lds[L::REGION + 8];
+  constexpr bool WL = L::SW;                      // weights in LDS, swizzled layouts
+  __shared__ __attribute__((aligned(16))) _Float16 lds[L::ZERO + 8];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;
@@ -596,6 +629,19 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA>)) void conv3x3_pair_f16(P
   const int y0 = ty * PAIR_TH, x0 = tx * PAIR_TW;
   if (tid < 2) reinterpret_cast<uint2*>(lds + L::ZERO)[tid] = make_uint2(0u, 0u);
 
+  // convA's biases for this lane: lane group g of the pair of fragments owns
+  // channels 8 g .. 8 g + 7 (one 16-byte slot of the intermediate).  Read
+  // up front with staged weights (see below); else after convA, where the
+  // registers are free (three workgroups per CU leave no room during it).
+  float bA[8];
+  auto load_bias = [&] {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bA[i] = p.biasA[8 * g + i];
+      bA[4 + i] = p.biasA[8 * g + 4 + i];
+    }
+  };
+  if constexpr (WL) load_bias();
   // convA: intermediate rows [9 rh, 9 rh + 9), columns [16 cf, 16 cf + 16)
   // of the window at (y0 - 1, x0 - 1); both fragments of the 32 channels.
   constexpr int RA = PAIR_MH / 2;
@@ -605,33 +651,48 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA>)) void conv3x3_pair_f16(P
   {
     const uint4* wf = static_cast<const uint4*>(p.wA) + lane;
     uint4 acur[3][2];
+    if constexpr (!WL) {
 #pragma unroll
-    for (int ky = 0; ky < 3; ++ky)
+      for (int ky = 0; ky < 3; ++ky)
 #pragma unroll
-      for (int q = 0; q < 2; ++q) acur[ky][q] = wf[(ky * 2 + q) * 64];
+        for (int q = 0; q < 2; ++q) acur[ky][q] = wf[(ky * 2 + q) * 64];
+    }
     const _Float16* src = static_cast<const _Float16*>(p.x);
+    const uint4* wl = reinterpret_cast<const uint4*>(lds + L::WOFF) + lane;
 #pragma unroll 1
     for (int ci = 0; ci < p.nchunks; ++ci) {
       __syncthreads();
-      stage_pair_input<CGA>(reinterpret_cast<uint4*>(lds), src, p.cs, ci * kChunkChannels, p.h,
-                            p.w, y0, x0, wave, lane);
-      __syncthreads();
+      stage_pair_input<CGA, WL>(reinterpret_cast<uint4*>(lds), src, p.cs, ci * kChunkChannels,
+                                p.h, p.w, y0, x0, wave, lane);
       const uint4* wchunk = wf + (size_t)p.wfragA[ci] * 64;
-      const uint4* wnext = ci + 1 < p.nchunks ? wf + (size_t)p.wfragA[ci + 1] * 64 : nullptr;
-      mma_chunk<2, RA, CGA, true, false, PAIR_PW>(acc, acur, lds, 0, L::ZERO, wchunk, wnext, 2,
-                                                  RA * rh, 16 * cf, g, c, [] {});
+      if constexpr (WL) stage_weights<(3 * CGA + 3) / 4 * 3 * 2>(lds + L::WOFF, wchunk, 2, 2, wave);
+      __syncthreads();
+      if constexpr (WL) {
+        mma_chunk<2, RA, CGA, false, false, PAIR_PW, true>(acc, acur, lds, 0, L::ZERO, wl, nullptr,
+                                                           2, RA * rh, 16 * cf, g, c, [] {});
+      } else {
+        const uint4* wnext = ci + 1 < p.nchunks ? wf + (size_t)p.wfragA[ci + 1] * 64 : nullptr;
+        mma_chunk<2, RA, CGA, true, false, PAIR_PW>(acc, acur, lds, 0, L::ZERO, wchunk, wnext, 2,
+                                                    RA * rh, 16 * cf, g, c, [] {});
+      }
     }
   }
-  __syncthreads();   // every wave is done with the input patch
+  // bias, ReLU, fp16; zero outside the image (see bA above).  convB's weight
+  // copy goes out through inline assembly, so no wait for it lands before
+  // the intermediate is written; the barrier before convB waits for it.
+  // The empty asm consumes the biases first: the compiler's wait for them
+  // (which, not knowing the copy, would be a full drain) lands here, long
+  // after they arrived.
+  if constexpr (WL)
+    asm volatile("" ::"v"(bA[0]), "v"(bA[1]), "v"(bA[2]), "v"(bA[3]), "v"(bA[4]), "v"(bA[5]),
+                 "v"(bA[6]), "v"(bA[7]));
+  else
+    load_bias();
+  __syncthreads();   // every wave is done with the input patch (and convA's weights)
+  if constexpr (WL)
+    stage_weights<9 * NFB, true>(lds + L::WOFF, static_cast<const uint4*>(p.wB) + lane, NFB, NFB,
+                                 wave);
   {
-    // bias, ReLU, fp16; zero outside the image.  Lane group g of the pair
-    // of fragments owns channels 8 g .. 8 g + 7 (one 16-byte slot).
-    float bA[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      bA[i] = p.biasA[8 * g + i];
-      bA[4 + i] = p.biasA[8 * g + 4 + i];
-    }
     const int x = x0 - 1 + 16 * cf + c;
 #pragma unroll
     for (int r = 0; r < RA; ++r) {
@@ -649,10 +710,12 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA>)) void conv3x3_pair_f16(P
         wv[k] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
                 ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
       }
-      const int px = (RA * rh + r) * PAIR_PW + 16 * cf + c;
-      *reinterpret_cast<uint4*>(lds + px * PSTR + 8 * g) = v;
+      const int col = 16 * cf + c;
+      const int px = (RA * rh + r) * PAIR_PW + col;
+      *reinterpret_cast<uint4*>(lds + px * pstride<4, WL>() + 8 * gslot<4, WL>(col, g)) = v;
     }
   }
+  if constexpr (WL) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // convB's weight copy
   __syncthreads();
   // convB: output rows [8 rh, 8 rh + 8), columns [16 cf, 16 cf + 16).
   constexpr int RB = PAIR_TH / 2;
@@ -664,12 +727,18 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA>)) void conv3x3_pair_f16(P
   {
     const uint4* wf = static_cast<const uint4*>(p.wB) + lane;
     uint4 acur[3][NFB];
+    if constexpr (WL) {
+      const uint4* wl = reinterpret_cast<const uint4*>(lds + L::WOFF) + lane;
+      mma_chunk<NFB, RB, 4, false, false, PAIR_PW, true>(accb, acur, lds, 0, L::ZERO, wl, nullptr,
+                                                         NFB, RB * rh, 16 * cf, g, c, [] {});
+    } else {
 #pragma unroll
-    for (int ky = 0; ky < 3; ++ky)
+      for (int ky = 0; ky < 3; ++ky)
 #pragma unroll
-      for (int q = 0; q < NFB; ++q) acur[ky][q] = wf[(ky * NFB + q) * 64];
-    mma_chunk<NFB, RB, 4, true, false, PAIR_PW>(accb, acur, lds, 0, L::ZERO, wf, nullptr, NFB,
-                                                RB * rh, 16 * cf, g, c, [] {});
+        for (int q = 0; q < NFB; ++q) acur[ky][q] = wf[(ky * NFB + q) * 64];
+      mma_chunk<NFB, RB, 4, true, false, PAIR_PW>(accb, acur, lds, 0, L::ZERO, wf, nullptr, NFB,
+                                                  RB * rh, 16 * cf, g, c, [] {});
+    }
   }
   ConvF16Args a{};
   a.h = p.h;
