@@ -261,7 +261,8 @@ def test_conv_kernel_selection():
 
 # Launch plans of the 1920x1088 network tile (fragments per wave, rows per
 # wave, row groups): the first candidate of each fragment count that gives
-# at least 480 workgroups, else the one with the most.  enc_conv0 ->
+# at least 480 workgroups, else the one with the most (4 fragments with four
+# or more K chunks per tile: a list led by 4-fragment waves).  enc_conv0 ->
 # enc_conv1 and dec_conv1b -> dec_conv0 run as fused pairs (both layers
 # report the pair kernel: convA chunk groups, convB fragments, fp32 output).
 UNET_1080P_PLANS = {
@@ -270,7 +271,7 @@ UNET_1080P_PLANS = {
     "enc_conv4": ("<1, 2, 4, false>", 1280), "enc_conv5a": ("<1, 2, 4, false>", 432),
     "enc_conv5b": ("<1, 2, 4, false>", 432), "dec_conv4a": ("<1, 4, 4, false>", 952),
     "dec_conv4b": ("<1, 4, 4, false>", 952), "dec_conv3a": ("<3, 8, 2, false>", 512),
-    "dec_conv3b": ("<3, 8, 2, false>", 512), "dec_conv2a": ("<2, 16, 2, false>", 1024),
+    "dec_conv3b": ("<3, 8, 2, false>", 512), "dec_conv2a": ("<4, 8, 4, false>", 1024),
     "dec_conv2b": ("<2, 16, 2, false>", 1024), "dec_conv1a": ("<2, 16, 2, false>", 4080),
     "dec_conv1b": ("pair<4, 1, true>", 4352), "dec_conv0": ("pair<4, 1, true>", 4352),
 }

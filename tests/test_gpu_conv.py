@@ -74,11 +74,15 @@ F16_CASES = [
     (544, 520, 96, 64, U.OIDN_RELU, "f16"),                     # three chunks per tile
     # one case per launch plan instance <fragments/wave, rows/wave, row groups>
     (272, 480, 48, 64, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),    # <2, 8, 2>
+    (256, 512, 80, 64, U.OIDN_RELU, "f16"),                     # <2, 8, 2>: 3 chunks
+    (128, 512, 80, 64, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),    # <1, 8, 1>
+    (512, 480, 128, 64, U.OIDN_RELU, "f16"),                    # <4, 8, 4>: 4 chunks
     (272, 480, 96, 96, U.OIDN_RELU, "f16"),                     # <3, 8, 2>
     (256, 256, 64, 64, U.OIDN_RELU, "f16"),                     # <1, 8, 1>
     (256, 256, 32, 32, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),    # <1, 4, 2>
     (128, 256, 64, 128, U.OIDN_RELU, "f16"),                    # <2, 4, 2>, outputs split in two
     (256, 512, 32, 48, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),    # <3, 4, 4>
+    (128, 512, 32, 48, U.OIDN_RELU, "f16"),                     # <3, 2, 4>
     (128, 512, 96, 96, U.OIDN_RELU, "f16"),                     # <3, 4, 2>
     (256, 512, 32, 128, U.OIDN_RELU, "f16"),                    # <4, 8, 2>
     (128, 512, 32, 128, U.OIDN_RELU, "f16"),                    # <4, 4, 2>
@@ -88,6 +92,7 @@ F16_CASES = [
     (544, 512, 32, 52, U.OIDN_RELU, "f16"),                     # <2, 16, 2>, pair (2, 3) partial
     (272, 480, 96, 84, U.OIDN_RELU, "f16"),                     # <3, 8, 2>, pair (4, 5) partial
     (256, 256, 64, 60, U.OIDN_RELU | U.OIDN_POOL2X2, "f16"),    # <1, 8, 1>
+    (512, 480, 128, 60, U.OIDN_RELU, "f16"),                    # <4, 8, 4>, pair (2, 3) partial
 ]
 
 
@@ -161,7 +166,7 @@ UPCAT_CASES = [
     (12, 10, 16, 9, 8, "f32"),
     (512, 1024, 64, 9, 64, "f16"),                              # 32-row tiles
     (544, 960, 64, 16, 64, "f16"),                              # 16-channel skip, 3 chunks
-    (546, 1002, 96, 32, 64, "f16"),                             # ragged, 4 chunks
+    (546, 1002, 96, 32, 64, "f16"),                             # <4, 8, 4>, ragged, 4 chunks
     (514, 1026, 32, 16, 32, "f16"),                             # ragged
     (272, 480, 112, 48, 96, "f16"),                             # <3, 8, 2>: 2 row groups
 ]
@@ -201,18 +206,23 @@ def test_conv_ladder_config2():
         x = got
 
 
-def test_conv_result_independent_of_launch_plan_bit_exact():
+@pytest.mark.parametrize("cin,full_kernel", [
+    (32, "conv3x3_f16_mfma<2, 16, 2, false>"),   # one chunk: 32-row tiles, 2-fragment waves
+    (128, "conv3x3_f16_mfma<4, 8, 4, false>"),   # four chunks: 4-fragment waves
+])
+def test_conv_result_independent_of_launch_plan_bit_exact(cin, full_kernel):
     """Large images run 32-row tiles with all output fragments per
     workgroup, small ones 8-row tiles with the outputs split across four
-    workgroups; every output is accumulated in the same order either way, so
-    a conv over a crop reproduces the interior of the conv over the image."""
+    workgroups;
+    every output is accumulated in the same order either way, so a conv over
+    a crop reproduces the interior of the conv over the image."""
     r = np.random.default_rng(7)
-    h, w, cin, cout = 544, 960, 32, 64
+    h, w, cout = 544, 960, 64
     x = O.round_to(S.relu_normal_activation(r, h, w, cin, cin), "f16")
     wt = S.he_normal(r, cout, cin)
     b = S.bias(r, cout)
     assert U.oidn_conv3x3_kernel(h, w, cin, 0, cout, U.OIDN_F16, U.OIDN_F16, U.OIDN_RELU)[0] == \
-        "conv3x3_f16_mfma<2, 16, 2, false>"
+        full_kernel
     assert U.oidn_conv3x3_kernel(40, 52, cin, 0, cout, U.OIDN_F16, U.OIDN_F16, U.OIDN_RELU)[0] == \
         "conv3x3_f16_mfma<1, 2, 4, false>"
     full = run_conv(x, cin, wt, b, cout, "f16", U.OIDN_RELU)

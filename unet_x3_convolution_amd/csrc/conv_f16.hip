@@ -768,8 +768,8 @@ hipError_t launch_pair_shape(PairArgs p, bool pool, bool relu, bool out_f32, hip
 // The instances the planner can choose (see kPlanCandidates).
 #define OIDN_PLAN_INSTANCES(X) \
   X(1, 4, 4) X(1, 2, 4) X(1, 8, 2) X(1, 4, 2) X(1, 8, 1) X(2, 16, 2) X(2, 8, 2) X(2, 4, 2) \
-  X(3, 8, 4) X(3, 4, 4) X(3, 2, 4) X(3, 8, 2) X(3, 4, 2) X(4, 8, 2) X(4, 4, 2) X(5, 4, 4)  \
-  X(7, 4, 4)
+  X(3, 8, 4) X(3, 4, 4) X(3, 2, 4) X(3, 8, 2) X(3, 4, 2) X(4, 8, 4) X(4, 8, 2) X(4, 4, 2)  \
+  X(5, 4, 4) X(7, 4, 4)
 
 hipError_t launch_plan(const ConvF16Args& a, const ConvPlan& P, int nsplit, bool upcat, bool pool,
                        bool relu, bool out_f32, hipStream_t stream) {
@@ -788,8 +788,10 @@ hipError_t launch_plan(const ConvF16Args& a, const ConvPlan& P, int nsplit, bool
 // by fewer waves, patch rows reused longer) to the most workgroups; the
 // planner takes the first that gives at least kMinBlocks workgroups (about
 // two per CU), else the one with the most.  The lists come from timing every
-// plan at the UNet's layer shapes: large layers keep all fragments in one
-// workgroup, small deep layers split the output channels.
+// plan at the UNet's layer shapes (each layer's kernel durations in a
+// kernel trace, in the network and alone): large layers keep all fragments
+// in one workgroup, small deep layers split the output channels.  For
+// nf = 4 with four or more K chunks per tile, waves of four fragments win.
 constexpr long kMinBlocks = 480;
 constexpr int kMaxCandidates = 4;
 const ConvPlan kPlanCandidates[9][kMaxCandidates] = {
@@ -797,22 +799,30 @@ const ConvPlan kPlanCandidates[9][kMaxCandidates] = {
     {{4, 1, 4}, {2, 1, 4}},                                  // nf = 1
     {{8, 1, 2}, {4, 1, 2}, {2, 1, 4}},                       // nf = 2
     {{8, 3, 4}, {4, 3, 4}, {2, 3, 4}, {2, 1, 4}},            // nf = 3
-    {{16, 2, 2}, {8, 2, 2}, {8, 1, 1}, {2, 1, 4}},           // nf = 4
+    {{16, 2, 2}, {8, 2, 2}, {8, 1, 1}, {2, 1, 4}},           // nf = 4, up to 3 chunks
     {{4, 5, 4}, {2, 1, 4}},                                  // nf = 5
     {{8, 3, 2}, {4, 3, 2}, {4, 1, 2}, {2, 1, 4}},            // nf = 6
     {{4, 7, 4}, {4, 1, 4}, {2, 1, 4}},                       // nf = 7
     {{8, 4, 2}, {4, 4, 2}, {4, 2, 2}, {2, 1, 4}},            // nf = 8
 };
+const ConvPlan kPlanManyChunks[kMaxCandidates] = {{8, 4, 4}, {8, 2, 2}, {8, 1, 1}, {2, 1, 4}};
+
+const ConvPlan* plan_candidates(int nf, int nchunks) {
+  if (nf == 4 && nchunks >= 4) return kPlanManyChunks;
+  return kPlanCandidates[nf < 1 ? 1 : nf > 8 ? 8 : nf];
+}
 
 long plan_blocks(int h, int w, int nf, const ConvPlan& P) {
   const int frags = P.nfw * (4 / P.wr);
   return (long)cdiv(cdiv(w, TW) * cdiv(h, P.wr * P.rows), kXcds) * kXcds * (nf / frags);
 }
 
-ConvPlan conv_f16_plan(int h, int w, int nf) {
+ConvPlan conv_f16_plan(int h, int w, int nf, int nchunks) {
   ConvPlan best{};
   long most = -1;
-  for (const ConvPlan& P : kPlanCandidates[nf < 1 ? 1 : nf > 8 ? 8 : nf]) {
+  const ConvPlan* cand = plan_candidates(nf, nchunks);
+  for (int i = 0; i < kMaxCandidates; ++i) {
+    const ConvPlan& P = cand[i];
     if (P.rows == 0) break;
     const long b = plan_blocks(h, w, nf, P);
     if (b >= kMinBlocks) return P;
@@ -828,7 +838,9 @@ ConvPlan conv_f16_plan(int h, int w, int nf) {
 int plan_block_frags(const ConvPlan& P) { return P.nfw * (4 / P.wr); }
 
 // Workgroups of the launch (for reporting).
-int conv_f16_blocks(int h, int w, int nf) { return (int)plan_blocks(h, w, nf, conv_f16_plan(h, w, nf)); }
+int conv_f16_blocks(int h, int w, int nf, int nchunks) {
+  return (int)plan_blocks(h, w, nf, conv_f16_plan(h, w, nf, nchunks));
+}
 
 bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out) {
   ConvLayout L{};
@@ -870,17 +882,17 @@ bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out
 void conv_f16_describe(const ConvF16Args& a, int nf, bool out_f32, char* buf, int cap,
                        int* blocks) {
   const int h = a.h, w = a.w;
-  const ConvPlan P = conv_f16_plan(h, w, nf);
+  const ConvPlan P = conv_f16_plan(h, w, nf, a.nchunks);
   snprintf(buf, cap, "conv3x3_f16_mfma<%d, %d, %d, %s>", P.nfw, P.rows, P.wr,
            out_f32 ? "true" : "false");
-  *blocks = conv_f16_blocks(h, w, nf);
+  *blocks = conv_f16_blocks(h, w, nf, a.nchunks);
 }
 
 hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, bool relu,
                            bool out_f32, hipStream_t stream) {
   ConvF16Args b = a;
   b.nf = nf;
-  const ConvPlan P = conv_f16_plan(a.h, a.w, nf);
+  const ConvPlan P = conv_f16_plan(a.h, a.w, nf, a.nchunks);
   const int nsplit = nf / plan_block_frags(P);
   return launch_plan(b, P, nsplit, upcat, pool, relu, out_f32, stream);
 }
