@@ -173,14 +173,30 @@ def test_workspace_plan_is_liveness_bounded():
     assert full >= 1920 * 1088 * (12 * 2 + 16)
 
 
+def _a256(n):
+    return -(-n // 256) * 256
+
+
 def test_weight_bytes_sum_per_layer():
-    for dtype in (U.OIDN_F16, U.OIDN_F32):
-        total = U.oidn_unet_weights_bytes(9, dtype)
-        per = sum(-(-U.oidn_conv3x3_weights_bytes(U.oidn_unet_layer_info(9, i)[1],
-                                                   U.oidn_unet_layer_info(9, i)[2],
-                                                   U.oidn_unet_layer_info(9, i)[3], dtype) // 256) * 256
-                  for i in range(16))
-        assert total == per
+    """The blob is the sixteen layers' packed weights back to back (256-byte
+    aligned); with 9 input channels on the fp16 path it ends with the tap
+    variants of the two layers that read the network input (enc_conv0's
+    source, dec_conv1a's skip): the same fragments except that the input's
+    chunk has one column group (3 K-steps per output) instead of two."""
+    for ic in (3, 6, 9):
+        for dtype in (U.OIDN_F16, U.OIDN_F32):
+            total = U.oidn_unet_weights_bytes(ic, dtype)
+            info = [U.oidn_unet_layer_info(ic, i) for i in range(16)]
+            per = sum(_a256(U.oidn_conv3x3_weights_bytes(n[1], n[2], n[3], dtype)) for n in info)
+            extra = 0
+            if ic == 9 and dtype == U.OIDN_F16:
+                for i in (0, 13):   # fragments: (column groups x 3 ky x nf) of 1 KB, bias 16 nf floats
+                    name, c0, c1, co = info[i][:4]
+                    nf = -(-co // 16)
+                    chunks = [3] * (c0 // 32) if c1 else []   # the upsampled source: 32-channel chunks
+                    ncg = sum(chunks) + 1                      # plus the tap chunk
+                    extra += _a256(_a256(16 * nf * 4) + ncg * 3 * nf * 1024)
+            assert total == per + extra, (ic, dtype)
 
 
 # ---- argument errors: rejected before any device work (no GPU involved) ----
@@ -264,16 +280,17 @@ def test_conv_kernel_selection():
 # at least 480 workgroups, else the one with the most (4 fragments with four
 # or more K chunks per tile: a list led by 4-fragment waves).  enc_conv0 ->
 # enc_conv1 and dec_conv1b -> dec_conv0 run as fused pairs (both layers
-# report the pair kernel: convA chunk groups, convB fragments, fp32 output).
+# report the pair kernel: convA chunk groups, convB fragments, fp32 output,
+# convA reads the tap-packed network input).
 UNET_1080P_PLANS = {
-    "enc_conv0": ("pair<2, 2, false>", 4352), "enc_conv1": ("pair<2, 2, false>", 4352),
+    "enc_conv0": ("pair<2, 2, false, true>", 4352), "enc_conv1": ("pair<2, 2, false, true>", 4352),
     "enc_conv2": ("<3, 8, 4, false>", 1024), "enc_conv3": ("<2, 8, 2, false>", 512),
     "enc_conv4": ("<1, 2, 4, false>", 1280), "enc_conv5a": ("<1, 2, 4, false>", 432),
     "enc_conv5b": ("<1, 2, 4, false>", 432), "dec_conv4a": ("<1, 4, 4, false>", 952),
     "dec_conv4b": ("<1, 4, 4, false>", 952), "dec_conv3a": ("<3, 8, 2, false>", 512),
     "dec_conv3b": ("<3, 8, 2, false>", 512), "dec_conv2a": ("<4, 8, 4, false>", 1024),
     "dec_conv2b": ("<2, 16, 2, false>", 1024), "dec_conv1a": ("<2, 16, 2, false>", 4080),
-    "dec_conv1b": ("pair<4, 1, true>", 4352), "dec_conv0": ("pair<4, 1, true>", 4352),
+    "dec_conv1b": ("pair<4, 1, true, false>", 4352), "dec_conv0": ("pair<4, 1, true, false>", 4352),
 }
 
 

@@ -95,7 +95,7 @@ int plan(int w, int h, int max_tile, int overlap, std::vector<oidn_tile>& tiles)
 }
 
 // ----------------------------------------------------------- conv helpers
-int conv_weights_bytes(int cin0, int cin1, int cout, int dtype, size_t* bytes) {
+int conv_weights_bytes(int cin0, int cin1, int cout, int dtype, size_t* bytes, int tap_src = -1) {
   int rc = check_dtype(dtype);
   if (rc) return rc;
   if (cin0 <= 0 || cin1 < 0 || cout <= 0)
@@ -107,7 +107,7 @@ int conv_weights_bytes(int cin0, int cin1, int cout, int dtype, size_t* bytes) {
     return fail(OIDN_E_INVALID, "the upsampled source needs a multiple of 4 channels (got %d)", cin0);
   if (dtype == OIDN_F16) {
     ConvLayout L;
-    if (!conv_f16_layout(stored_channels(cin0), cin1 ? stored_channels(cin1) : 0, cout, &L))
+    if (!conv_f16_layout(stored_channels(cin0), cin1 ? stored_channels(cin1) : 0, cout, &L, tap_src))
       return fail(OIDN_E_UNSUPPORTED, "conv shape exceeds the fp16 kernel limits");
     *bytes = L.bytes;
   } else {
@@ -116,9 +116,10 @@ int conv_weights_bytes(int cin0, int cin1, int cout, int dtype, size_t* bytes) {
   return OIDN_OK;
 }
 
-// Host-side packing into `out` (sized by conv_weights_bytes).
+// Host-side packing into `out` (sized by conv_weights_bytes).  tap_src: the
+// source packed as a tap chunk (fp16 only; see ConvChunk), -1 for none.
 void pack_conv_host(const float* w, const float* b, int cin0, int cin1, int cout, int dtype,
-                    std::vector<unsigned char>& out) {
+                    std::vector<unsigned char>& out, int tap_src = -1) {
   const int cin = cin0 + cin1;
   const int cs0 = stored_channels(cin0), cs1 = cin1 ? stored_channels(cin1) : 0;
   auto wat = [&](int o, int tap, int i) -> float {  // OHWI, logical channels
@@ -132,7 +133,7 @@ void pack_conv_host(const float* w, const float* b, int cin0, int cin1, int cout
   std::fill(out.begin(), out.end(), 0);
   if (dtype == OIDN_F16) {
     ConvLayout L;
-    conv_f16_layout(cs0, cs1, cout, &L);
+    conv_f16_layout(cs0, cs1, cout, &L, tap_src);
     float* bias = reinterpret_cast<float*>(out.data());
     for (int o = 0; o < cout; ++o) bias[o] = b[o];
     _Float16* frag = reinterpret_cast<_Float16*>(out.data() + L.bias_bytes);
@@ -145,6 +146,17 @@ void pack_conv_host(const float* w, const float* b, int cin0, int cin1, int cout
             for (int lane = 0; lane < 64; ++lane) {
               const int r = lane & 15, slot = 4 * j + (lane >> 4);
               const int o = frag_row_to_cout(L.nf, q, r);
+              if (ch.src == tap_src) {
+                // slots 0..2: channels 0..7 at kx = slot; slot 3: channel 8 at kx = lane 0..2
+                if (o >= cout) continue;
+                const int c8 = logical(ch.src, 8);
+                for (int jj = 0; jj < 8; ++jj) {
+                  const int li = slot < 3 ? logical(ch.src, jj) : jj < 3 ? c8 : -1;
+                  const int kx = slot < 3 ? slot : jj;
+                  if (li >= 0) f[lane * 8 + jj] = (_Float16)wat(o, 3 * ky + kx, li);
+                }
+                continue;
+              }
               if (o >= cout || slot >= 3 * ch.cg) continue;
               const int kx = slot / ch.cg, grp = slot % ch.cg;
               const int tap = 3 * ky + kx;
@@ -171,8 +183,9 @@ void pack_conv_host(const float* w, const float* b, int cin0, int cin1, int cout
 }
 
 // Shape fields of an fp16 conv launch (no pointers); cs0/cs1 as in run_conv.
-ConvF16Args f16_args(int cin0, int cin1, int cout, int h, int w, int cs0, int cs1, ConvLayout* L) {
-  conv_f16_layout(stored_channels(cin0), cin1 ? stored_channels(cin1) : 0, cout, L);
+ConvF16Args f16_args(int cin0, int cin1, int cout, int h, int w, int cs0, int cs1, ConvLayout* L,
+                     int tap_src = -1) {
+  conv_f16_layout(stored_channels(cin0), cin1 ? stored_channels(cin1) : 0, cout, L, tap_src);
   ConvF16Args a{};
   a.cs0 = cs0 ? cs0 : stored_channels(cin0);
   a.cs1 = cin1 ? (cs1 ? cs1 : stored_channels(cin1)) : 0;
@@ -183,6 +196,7 @@ ConvF16Args f16_args(int cin0, int cin1, int cout, int h, int w, int cs0, int cs
   a.nup4 = L->nup4;
   a.nup = L->nup;
   a.npl4 = L->npl4;
+  a.ntap = L->ntap;
   for (int i = 0; i < L->nchunks; ++i) a.chunk[i] = L->chunk[i];
   return a;
 }
@@ -191,12 +205,12 @@ ConvF16Args f16_args(int cin0, int cin1, int cout, int h, int w, int cs0, int cs
 // cs0/cs1: stored channels per pixel of the sources (0 = 4 * ceil(cin / 4)).
 int run_conv(const void* src0, int cin0, const void* src1, int cin1, bool upcat, int h, int w,
              const void* wpk, void* y, int cout, int in_dtype, int out_dtype, unsigned flags,
-             hipStream_t stream, int cs0 = 0, int cs1 = 0) {
+             hipStream_t stream, int cs0 = 0, int cs1 = 0, int tap_src = -1) {
   const bool pool = flags & OIDN_POOL2X2, relu = flags & OIDN_RELU;
   hipError_t e;
   if (in_dtype == OIDN_F16) {
     ConvLayout L;
-    ConvF16Args a = f16_args(cin0, cin1, cout, h, w, cs0, cs1, &L);
+    ConvF16Args a = f16_args(cin0, cin1, cout, h, w, cs0, cs1, &L, tap_src);
     a.src0 = src0;
     a.src1 = src1;
     a.bias = static_cast<const float*>(wpk);
@@ -258,9 +272,9 @@ bool pair_supported(int cin, int cs, int cout) {
 }
 
 int run_pair(const void* x, int cin, int cs, int h, int w, const void* wA, const void* wB, void* y,
-             int cout, int out_dtype, unsigned flags, hipStream_t stream) {
+             int cout, int out_dtype, unsigned flags, hipStream_t stream, bool tap = false) {
   ConvLayout LA, LB;
-  conv_f16_layout(stored_channels(cin), 0, 32, &LA);
+  conv_f16_layout(stored_channels(cin), 0, 32, &LA, tap ? 0 : -1);
   conv_f16_layout(32, 0, cout, &LB);
   PairArgs p{};
   p.x = x;
@@ -275,7 +289,7 @@ int run_pair(const void* x, int cin, int cs, int h, int w, const void* wA, const
   p.wB = static_cast<const unsigned char*>(wB) + LB.bias_bytes;
   p.y = y;
   p.cout_stored = stored_channels(cout);
-  hipError_t e = launch_conv_pair_f16(p, LA.chunk[0].cg, LB.nf, flags & OIDN_POOL2X2,
+  hipError_t e = launch_conv_pair_f16(p, LA.chunk[0].cg, LB.nf, tap, flags & OIDN_POOL2X2,
                                       flags & OIDN_RELU, out_dtype == OIDN_F32, stream);
   if (e != hipSuccess) return hip_fail(e, "conv3x3 pair launch");
   return OIDN_OK;
@@ -330,6 +344,36 @@ size_t unet_layer_offset(const LayerShape* s, int dtype, int layer) {
     off += align256(b);
   }
   return off;
+}
+
+// Tap variants.  With 9 input channels on the fp16 path the end-to-end call
+// packs the input with channel 8's row taps (PackArgs::taps), and the layers
+// that read the input (enc_conv0 from its source, dec_conv1a from its skip)
+// run that source as a tap chunk: half the MFMA K-steps for it.  Their
+// weights in that layout follow the sixteen plain ones in the packed blob;
+// the plain ones serve oidn_unet_forward_packed, whose input is packed by
+// the caller without taps.
+bool unet_taps(int in_channels, int dtype) { return dtype == OIDN_F16 && in_channels == 9; }
+
+// Source of layer i read as a tap chunk when the input carries taps, or -1.
+int unet_tap_src(int i) { return kUNet[i].src == 0 ? 0 : kUNet[i].skip == 0 ? 1 : -1; }
+
+// Offset of layer i's tap-variant weights (unet_tap_src(i) >= 0); with
+// layer = kLayers: the size of the whole blob.
+size_t unet_tap_offset(const LayerShape* s, int dtype, int layer) {
+  size_t off = unet_layer_offset(s, dtype, kLayers);
+  for (int i = 0; i < layer && i < kLayers; ++i) {
+    if (unet_tap_src(i) < 0) continue;
+    size_t b = 0;
+    conv_weights_bytes(s[i].cin0, s[i].cin1, s[i].cout, dtype, &b, unet_tap_src(i));
+    off += align256(b);
+  }
+  return off;
+}
+
+size_t unet_weights_total(const LayerShape* s, int in_channels, int dtype) {
+  return unet_taps(in_channels, dtype) ? unet_tap_offset(s, dtype, kLayers)
+                                       : unet_layer_offset(s, dtype, kLayers);
 }
 
 // Liveness-planned workspace ([web-0.4] NativeUNetExecutor._createExecution
@@ -454,15 +498,18 @@ int run_network(const unsigned char* weights, int in_channels, const void* packe
     const unsigned flags = (L.relu ? OIDN_RELU : 0u) | (L.pool ? OIDN_POOL2X2 : 0u);
     const int out_dtype = i == kLayers - 1 ? OIDN_F32 : dtype;
     const int in_cs = own_io ? internal_input_lanes(in_channels, dtype) : 0;
+    const int tap_src = own_io && unet_taps(in_channels, dtype) ? unet_tap_src(i) : -1;
+    const unsigned char* wl = tap_src >= 0 ? weights + unet_tap_offset(s, dtype, i) : weights + woff;
     if (fuse_with_next(in_channels, i, dtype, own_io)) {
       const Layer& B = kUNet[i + 1];
       const unsigned flags_b = (B.relu ? OIDN_RELU : 0u) | (B.pool ? OIDN_POOL2X2 : 0u);
       size_t ba = 0, bb = 0;
       conv_weights_bytes(s[i].cin0, 0, 32, dtype, &ba);
       conv_weights_bytes(32, 0, s[i + 1].cout, dtype, &bb);
-      int rc = run_pair(val[L.src], s[i].cin0, L.src == 0 ? in_cs : 0, h, w, weights + woff,
+      int rc = run_pair(val[L.src], s[i].cin0, L.src == 0 ? in_cs : 0, h, w, wl,
                         weights + woff + align256(ba), const_cast<void*>(val[i + 2]),
-                        s[i + 1].cout, i + 1 == kLayers - 1 ? OIDN_F32 : dtype, flags_b, stream);
+                        s[i + 1].cout, i + 1 == kLayers - 1 ? OIDN_F32 : dtype, flags_b, stream,
+                        tap_src == 0);
       if (rc) return rc;
       if (events && events[i + 1]) {   // the second layer's interval is empty
         hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[i + 1]), stream);
@@ -473,9 +520,9 @@ int run_network(const unsigned char* weights, int in_channels, const void* packe
       continue;
     }
     int rc = run_conv(val[L.src], s[i].cin0, L.skip >= 0 ? val[L.skip] : nullptr, s[i].cin1,
-                      L.skip >= 0, h, w, weights + woff, const_cast<void*>(val[i + 1]), s[i].cout,
-                      dtype, out_dtype, flags, stream, L.src == 0 ? in_cs : 0,
-                      L.skip == 0 ? in_cs : 0);
+                      L.skip >= 0, h, w, wl, const_cast<void*>(val[i + 1]), s[i].cout, dtype,
+                      out_dtype, flags, stream, L.src == 0 ? in_cs : 0, L.skip == 0 ? in_cs : 0,
+                      tap_src);
     if (rc) return rc;
     size_t b = 0;
     conv_weights_bytes(s[i].cin0, s[i].cin1, s[i].cout, dtype, &b);
@@ -555,6 +602,7 @@ int denoise(const void* d_weights, int in_channels, const float* color, const fl
     pa.input_scale = input_scale;
     pa.sources = sources;
     pa.lanes = internal_input_lanes(in_channels, dtype);
+    pa.taps = unet_taps(in_channels, dtype) && pa.lanes == 16;
     pa.packed = ws + P.offset[0];
     if ((e = launch_pack(pa, dtype == OIDN_F16, stream)) != hipSuccess) return hip_fail(e, "pack launch");
     rc = run_network(static_cast<const unsigned char*>(d_weights), in_channels, nullptr, t.in_w,
@@ -846,8 +894,10 @@ int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int dtype
     const int fh = th >> s[first].level, fw = tw >> s[first].level;
     const int st = stored_channels(s[first].cin0);
     const int cs = kUNet[first].src == 0 ? internal_input_lanes(in_channels, dtype) : st;
-    snprintf(buf, cap, "conv3x3_pair_f16<%d, %d, %s>", st > 16 ? 4 : 2,
-             cdiv(stored_channels(s[first + 1].cout), 16), first + 1 == kLayers - 1 ? "true" : "false");
+    const bool tap = unet_taps(in_channels, dtype) && unet_tap_src(first) == 0;
+    snprintf(buf, cap, "conv3x3_pair_f16<%d, %d, %s, %s>", st > 16 ? 4 : 2,
+             cdiv(stored_channels(s[first + 1].cout), 16), first + 1 == kLayers - 1 ? "true" : "false",
+             tap ? "true" : "false");
     (void)cs;
     nb = conv_pair_blocks(fh, fw);
   } else if (dtype == OIDN_F16) {
@@ -856,7 +906,8 @@ int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int dtype
     const Layer& L = kUNet[layer];
     ConvLayout lay;
     const ConvF16Args a = f16_args(s[layer].cin0, s[layer].cin1, s[layer].cout, h, w,
-                                   L.src == 0 ? in_cs : 0, L.skip == 0 ? in_cs : 0, &lay);
+                                   L.src == 0 ? in_cs : 0, L.skip == 0 ? in_cs : 0, &lay,
+                                   unet_taps(in_channels, dtype) ? unet_tap_src(layer) : -1);
     conv_f16_describe(a, lay.nf, final_layer, buf, cap, &nb);
   } else {
     snprintf(buf, cap, "conv3x3_f32_direct");
@@ -873,7 +924,7 @@ int oidn_unet_weights_bytes(int in_channels, int dtype, size_t* bytes) {
   if (rc) return rc;
   LayerShape s[kLayers];
   if (!unet_shapes(in_channels, s)) return fail(OIDN_E_INVALID, "input channels must be 3, 6 or 9");
-  *bytes = unet_layer_offset(s, dtype, kLayers);
+  *bytes = unet_weights_total(s, in_channels, dtype);
   return ok();
 }
 
@@ -887,7 +938,7 @@ int oidn_unet_pack_weights(const float* const* w_ohwi_host, const float* const* 
   if (!aligned16(d_weights)) return fail(OIDN_E_INVALID, "weights must be 16-byte aligned");
   for (int i = 0; i < kLayers; ++i)
     if (!w_ohwi_host[i] || !bias_host[i]) return fail(OIDN_E_INVALID, "null weights of layer %d", i);
-  std::vector<unsigned char> all(unet_layer_offset(s, dtype, kLayers), 0);
+  std::vector<unsigned char> all(unet_weights_total(s, in_channels, dtype), 0);
   size_t off = 0;
   for (int i = 0; i < kLayers; ++i) {
     size_t b = 0;
@@ -897,6 +948,16 @@ int oidn_unet_pack_weights(const float* const* w_ohwi_host, const float* const* 
     std::memcpy(all.data() + off, one.data(), b);
     off += align256(b);
   }
+  if (unet_taps(in_channels, dtype))
+    for (int i = 0; i < kLayers; ++i) {
+      const int ts = unet_tap_src(i);
+      if (ts < 0) continue;
+      size_t b = 0;
+      conv_weights_bytes(s[i].cin0, s[i].cin1, s[i].cout, dtype, &b, ts);
+      std::vector<unsigned char> one(b);
+      pack_conv_host(w_ohwi_host[i], bias_host[i], s[i].cin0, s[i].cin1, s[i].cout, dtype, one, ts);
+      std::memcpy(all.data() + unet_tap_offset(s, dtype, i), one.data(), b);
+    }
   rc = upload(all, d_weights, stream);
   return rc ? rc : ok();
 }

@@ -221,13 +221,16 @@ __device__ __forceinline__ void stage_patch(_Float16* lds, const _Float16* src, 
 // The wave's window starts at patch row row0 (even for UP) and column col0;
 // PWID is the full-resolution patch width in pixels; SW selects the
 // swizzled patch layout.  `wchunk` may point into LDS (weights staged there);
-// `nf` is then the fragment count of a staged weight row.
-template <int NFW, int R, int CG, bool PF, bool UP, int PWID = PW, bool SW = false, typename Hook>
+// `nf` is then the fragment count of a staged weight row.  TAP: a tap chunk
+// (CG 2; one column group, slot 3 = group 1 of the centre pixel).
+template <int NFW, int R, int CG, bool PF, bool UP, int PWID = PW, bool SW = false,
+          bool TAP = false, typename Hook>
 __device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], uint4 (&acur)[3][NFW],
                                           const _Float16* lds, int cur, int zero,
                                           const uint4* wchunk, const uint4* wnext, int nf,
                                           int row0, int col0, int g, int c, Hook&& hook) {
-  constexpr int NCG = (3 * CG + 3) / 4;
+  static_assert(!TAP || (CG == 2 && !UP), "tap chunks are plain 16-lane sources");
+  constexpr int NCG = TAP ? 1 : (3 * CG + 3) / 4;
 #pragma unroll 1
   for (int j = 0; j < NCG; ++j) {
     if constexpr (!PF) {
@@ -248,9 +251,9 @@ __device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], uint4 (&acur)[
     if (j == 0) hook();
     const int slot = 4 * j + g;
     int base = zero, rstride = 0;
-    if (slot < 3 * CG) {
-      const int kx = slot / CG;
-      const int grp = slot - kx * CG;
+    if (TAP || slot < 3 * CG) {
+      const int kx = TAP ? (slot < 3 ? slot : 1) : slot / CG;
+      const int grp = TAP ? (slot < 3 ? 0 : 1) : slot - kx * CG;
       constexpr int PS = pstride<CG, SW>();
       if constexpr (UP) {
         // patch row p of this wave's window is half-resolution row
@@ -490,10 +493,11 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
 #pragma unroll
       for (int q = 0; q < NFW; ++q) acur[ky][q] = w0[(ky * nf + q) * 64];
   }
-  // Chunks run in four loops of one shape each: upsampled source (32- then
-  // 16-channel chunks), then the plain source (32- then 16-channel chunks).
-  const int bounds[5] = {0, a.nup4, a.nup, a.nup + a.npl4, a.nchunks};
-#define OIDN_CHUNK_LOOP(K, CG, UP)                                                              \
+  // Chunks run in five loops of one shape each: upsampled source (32- then
+  // 16-channel chunks), then the plain source (32- then 16-channel chunks,
+  // then a tap chunk).
+  const int bounds[6] = {0, a.nup4, a.nup, a.nup + a.npl4, a.nchunks - a.ntap, a.nchunks};
+#define OIDN_CHUNK_LOOP(K, CG, UP, TAP)                                                         \
   _Pragma("unroll 1") for (int ci = bounds[K]; ci < bounds[K + 1]; ++ci) {                      \
     const ConvChunk ch = a.chunk[ci];                                                           \
     const _Float16* src = static_cast<const _Float16*>(ch.src ? a.src1 : a.src0);               \
@@ -506,20 +510,22 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
                                                              lane);                             \
     else                                                                                        \
       stage_patch<T::TH, CG, false, UP, SW>(lds, src, cs, ch.coff, a.h, a.w, y0, x0, tid);      \
-    if constexpr (WL) stage_weights<(3 * CG + 3) / 4 * 3 * FB>(lds + WOFF, wblk + (size_t)ch.wfrag * 64, \
-                                                              nf, FB, wave);                    \
+    if constexpr (WL) stage_weights<(TAP ? 1 : (3 * CG + 3) / 4) * 3 * FB>(                      \
+                          lds + WOFF, wblk + (size_t)ch.wfrag * 64, nf, FB, wave);              \
     __syncthreads();                                                                            \
     if constexpr (WL)                                                                           \
-      mma_chunk<NFW, R, CG, false, UP, PW, SW>(acc, acur, lds, 0, ZERO, wl, nullptr, FB, R * rg, \
-                                               0, g, c, [] {});                                 \
+      mma_chunk<NFW, R, CG, false, UP, PW, SW, TAP>(acc, acur, lds, 0, ZERO, wl, nullptr, FB,    \
+                                                    R * rg, 0, g, c, [] {});                    \
     else                                                                                        \
-      mma_chunk<NFW, R, CG, PF, UP>(acc, acur, lds, 0, ZERO, wf + (size_t)ch.wfrag * 64, wnext, \
-                                    nf, R * rg, 0, g, c, [] {});                                \
+      mma_chunk<NFW, R, CG, PF, UP, PW, false, TAP>(acc, acur, lds, 0, ZERO,                     \
+                                                    wf + (size_t)ch.wfrag * 64, wnext, nf,      \
+                                                    R * rg, 0, g, c, [] {});                    \
   }
-  OIDN_CHUNK_LOOP(0, 4, true)
-  OIDN_CHUNK_LOOP(1, 2, true)
-  OIDN_CHUNK_LOOP(2, 4, false)
-  OIDN_CHUNK_LOOP(3, 2, false)
+  OIDN_CHUNK_LOOP(0, 4, true, false)
+  OIDN_CHUNK_LOOP(1, 2, true, false)
+  OIDN_CHUNK_LOOP(2, 4, false, false)
+  OIDN_CHUNK_LOOP(3, 2, false, false)
+  OIDN_CHUNK_LOOP(4, 2, false, true)
 #undef OIDN_CHUNK_LOOP
   (void)upcat;
 
@@ -613,9 +619,11 @@ __device__ __forceinline__ void stage_pair_input(uint4* slots, const _Float16* s
 template <int CGA>
 constexpr int kPairWaves = CGA == 2 ? 3 : 2;
 
-template <int CGA, int NFB, bool OUTF32>
+// TAP: convA's one chunk is a tap chunk (16-lane packed network input).
+template <int CGA, int NFB, bool OUTF32, bool TAP>
 __global__ __launch_bounds__(THREADS, (kPairWaves<CGA>)) void conv3x3_pair_f16(PairArgs p, int pool,
                                                                               int relu) {
+  static_assert(!TAP || CGA == 2, "tap chunks are 16-lane sources");
   using L = PairLds<CGA>;
   constexpr bool WL = L::SW;                      // weights in LDS, swizzled layouts
   __shared__ __attribute__((aligned(16))) _Float16 lds[L::ZERO + 8];
@@ -672,8 +680,9 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA>)) void conv3x3_pair_f16(P
                                                            2, RA * rh, 16 * cf, g, c, [] {});
       } else {
         const uint4* wnext = ci + 1 < p.nchunks ? wf + (size_t)p.wfragA[ci + 1] * 64 : nullptr;
-        mma_chunk<2, RA, CGA, true, false, PAIR_PW>(acc, acur, lds, 0, L::ZERO, wchunk, wnext, 2,
-                                                    RA * rh, 16 * cf, g, c, [] {});
+        mma_chunk<2, RA, CGA, true, false, PAIR_PW, false, TAP>(acc, acur, lds, 0, L::ZERO, wchunk,
+                                                                wnext, 2, RA * rh, 16 * cf, g, c,
+                                                                [] {});
       }
     }
   }
@@ -751,17 +760,17 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA>)) void conv3x3_pair_f16(P
   store_tile<NFB, RB, OUTF32>(accb, a, 0, g, y0 + RB * rh, x0 + 16 * cf + c, c, pool, relu, xend);
 }
 
-template <int CGA, int NFB>
+template <int CGA, int NFB, bool TAP = false>
 hipError_t launch_pair_shape(PairArgs p, bool pool, bool relu, bool out_f32, hipStream_t stream) {
   p.tiles_x = cdiv(p.w, PAIR_TW);
   p.tiles_y = cdiv(p.h, PAIR_TH);
   const dim3 grid(cdiv(p.tiles_x * p.tiles_y, kXcds) * kXcds), block(THREADS);
   if (out_f32)
-    hipLaunchKernelGGL((conv3x3_pair_f16<CGA, NFB, true>), grid, block, 0, stream, p, (int)pool,
-                       (int)relu);
+    hipLaunchKernelGGL((conv3x3_pair_f16<CGA, NFB, true, TAP>), grid, block, 0, stream, p,
+                       (int)pool, (int)relu);
   else
-    hipLaunchKernelGGL((conv3x3_pair_f16<CGA, NFB, false>), grid, block, 0, stream, p, (int)pool,
-                       (int)relu);
+    hipLaunchKernelGGL((conv3x3_pair_f16<CGA, NFB, false, TAP>), grid, block, 0, stream, p,
+                       (int)pool, (int)relu);
   return hipGetLastError();
 }
 
@@ -842,16 +851,23 @@ int conv_f16_blocks(int h, int w, int nf, int nchunks) {
   return (int)plan_blocks(h, w, nf, conv_f16_plan(h, w, nf, nchunks));
 }
 
-bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out) {
+bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out,
+                     int tap_src) {
   ConvLayout L{};
   L.nf = cdiv(stored_channels(cout), 16);
   if (L.nf < 1 || L.nf > 8) return false;
+  // a tap chunk is the last source's only chunk: 12 or 16 stored channels
+  const int last_src = cin1_stored > 0 ? 1 : 0;
+  if (tap_src >= 0) {
+    const int st = last_src ? cin1_stored : cin0_stored;
+    if (tap_src != last_src || st < 12 || st > 16) return false;
+  }
   // Chunks of up to 32 channels, sources in order, channels in order; a chunk
   // is processed as 4 groups of 8 channels if it holds more than 16, else as
   // 2 (missing channels are zero).  With two sources the first is the
   // upsampled one.  Only a source's last chunk can be a 2-group chunk, so the
   // order is: upsampled 4-group, upsampled 2-group, plain 4-group, plain
-  // 2-group -- the kernel's four loops.
+  // 2-group, tap -- the kernel's five loops.
   const bool two = cin1_stored > 0;
   const int cs[2] = {cin0_stored, cin1_stored};
   int frag = 0, n = 0;
@@ -863,13 +879,14 @@ bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out
       ch.src = s;
       ch.coff = off;
       ch.cg = rem > 16 ? 4 : 2;
-      ch.ncg = cdiv(3 * ch.cg, 4);
+      ch.ncg = s == tap_src ? 1 : cdiv(3 * ch.cg, 4);
       ch.wfrag = frag;
       frag += ch.ncg * 3 * L.nf;
       const bool up = two && s == 0;
       if (up && ch.cg == 4) ++L.nup4;
       if (up) ++L.nup;
       if (!up && ch.cg == 4) ++L.npl4;
+      if (s == tap_src) ++L.ntap;
     }
   L.nchunks = n;
   L.total_frags = frag;
@@ -897,8 +914,13 @@ hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, 
   return launch_plan(b, P, nsplit, upcat, pool, relu, out_f32, stream);
 }
 
-hipError_t launch_conv_pair_f16(const PairArgs& p, int cga, int nfb, bool pool, bool relu,
-                                bool out_f32, hipStream_t stream) {
+hipError_t launch_conv_pair_f16(const PairArgs& p, int cga, int nfb, bool tap, bool pool,
+                                bool relu, bool out_f32, hipStream_t stream) {
+  if (tap) {
+    if (cga == 2 && nfb == 2) return launch_pair_shape<2, 2, true>(p, pool, relu, out_f32, stream);
+    if (cga == 2 && nfb == 1) return launch_pair_shape<2, 1, true>(p, pool, relu, out_f32, stream);
+    return hipErrorInvalidValue;
+  }
   if (cga == 2 && nfb == 2) return launch_pair_shape<2, 2>(p, pool, relu, out_f32, stream);
   if (cga == 2 && nfb == 1) return launch_pair_shape<2, 1>(p, pool, relu, out_f32, stream);
   if (cga == 4 && nfb == 2) return launch_pair_shape<4, 2>(p, pool, relu, out_f32, stream);

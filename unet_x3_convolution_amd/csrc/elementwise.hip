@@ -25,10 +25,15 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
 // native/denoise.ts): clamp-to-edge read, sanitize, HDR log transfer of the
 // scaled colour, normals to [0, 1], channels packed densely into 4-lane
 // blocks with zero lanes ([web-0.4] createInputPackShader lane rule).
+// With `taps` (fp16, 16 lanes, three images) lanes 8, 9, 10 hold channel 8
+// (the normal's z) of the pixels in tile columns x - 1, x, x + 1, zero
+// outside the tile -- the layout the first convs read as a tap chunk.
 template <bool F16>
 __global__ __launch_bounds__(THREADS) void pack_input_kernel(PackArgs a) {
-  const int t = blockIdx.x * THREADS + threadIdx.x;
-  if (t >= a.tile_w * a.tile_h) return;
+  const int n = a.tile_w * a.tile_h;
+  const int t0 = blockIdx.x * THREADS + threadIdx.x;
+  // lanes past the end compute the last pixel (for the tap shuffles) and store nothing
+  const int t = t0 < n ? t0 : n - 1;
   const int ty = t / a.tile_w, tx = t - ty * a.tile_w;
   const int sy = min(max(ty + a.tile_y, 0), a.img_h - 1);
   const int sx = min(max(tx + a.tile_x, 0), a.img_w - 1);
@@ -59,6 +64,27 @@ __global__ __launch_bounds__(THREADS) void pack_input_kernel(PackArgs a) {
     ch[7] = sanitize(nr.y, -1.f, 1.f) * 0.5f + 0.5f;
     ch[8] = sanitize(nr.z, -1.f, 1.f) * 0.5f + 0.5f;
   }
+  if (a.taps && a.sources > 2) {
+    // channel 8 of the row neighbours inside the tile: from the neighbouring
+    // lanes (consecutive pixels of a row), read directly at a wave's edge or
+    // where the neighbour lane holds another row
+    const int lane = threadIdx.x & 63;
+    const float c8 = ch[8];
+    float left = __shfl_up(c8, 1, 64), right = __shfl_down(c8, 1, 64);
+    const size_t row = (size_t)sy * a.img_w;
+    if (tx > 0 && (lane == 0 || t0 >= n)) {
+      left = sanitize(a.normal[row + min(max(tx - 1 + a.tile_x, 0), a.img_w - 1)].z, -1.f, 1.f) * 0.5f +
+             0.5f;
+    }
+    if (tx + 1 < a.tile_w && (lane == 63 || t0 + 1 >= n)) {
+      right = sanitize(a.normal[row + min(max(tx + 1 + a.tile_x, 0), a.img_w - 1)].z, -1.f, 1.f) * 0.5f +
+              0.5f;
+    }
+    ch[8] = tx > 0 ? left : 0.f;
+    ch[9] = c8;
+    ch[10] = tx + 1 < a.tile_w ? right : 0.f;
+  }
+  if (t0 >= n) return;
   const int nblk = a.lanes / 4;   // blocks past the data (lanes 12..15) are zero
   if constexpr (F16) {
     uint2* out = static_cast<uint2*>(a.packed) + (size_t)t * nblk;

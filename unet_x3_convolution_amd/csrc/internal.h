@@ -31,19 +31,28 @@ struct ConvChunk {
   int src;    // 0: first source (upsampled source for the decoder), 1: skip
   int coff;   // first stored channel of the chunk within its source
   int cg;     // 8-channel groups the chunk is processed as (2 or 4)
-  int ncg;    // column groups of the chunk: ceil(3 * cg / 4)
+  int ncg;    // column groups of the chunk: ceil(3 * cg / 4), 1 for a tap chunk
   int wfrag;  // index of the chunk's first weight fragment
 };
 
 // Weight fragment of (chunk, column group j, ky, output fragment q):
 //   chunk.wfrag + (j * 3 + ky) * nf + q
 // 64 lanes x 8 halves; lane l holds output row r = l % 16 and slot
-// 4 * j + l / 16 of the chunk, channels coff + 8 * group + 0..7.
+// 4 * j + l / 16 of the chunk.  Slot s is (kx, group) = (s / cg, s % cg),
+// channels coff + 8 * group + 0..7 of the pixel in column x + kx - 1.
+//
+// Tap chunk (a 9-channel source stored in 16 lanes whose lanes 8, 9, 10 hold
+// channel 8 of the pixels in columns x - 1, x, x + 1, zero past the image
+// edge -- the packed network input): one column group, slots 0..2 are
+// (kx, group 0) = channels 0..7, slot 3 is group 1 of the centre pixel, whose
+// lanes 0..2 carry the weights of channel 8 for kx = 0, 1, 2.  The chunk
+// takes 3 MFMA K-steps per output instead of 6.
 struct ConvLayout {           // shared by the weight packer and the launcher
   int nf;                     // 16-row output-channel fragments (N = 16 * nf)
   int nchunks;
   int nup4, nup;               // upsampled-source chunks (4-group ones, all)
   int npl4;                    // plain-source 4-group chunks
+  int ntap;                    // tap chunks (the last ones; 0 or 1)
   int total_frags;
   ConvChunk chunk[kMaxChunks];
   size_t bias_bytes;          // fp32 bias, 16 * nf floats, 256-aligned
@@ -51,7 +60,10 @@ struct ConvLayout {           // shared by the weight packer and the launcher
 };
 
 // Computes the fp16 layout; returns false if the shape exceeds the limits.
-bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out);
+// tap_src (0 or 1, the last source, stored as 12 or 16 channels of which 9
+// are data): that source is one tap chunk; -1: none.
+bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out,
+                     int tap_src = -1);
 
 // Output fragments go in pairs (2p, 2p + 1) that cover the 32 channels
 // [32 p, 32 p + 32).  Row r (0..15) of fragment q holds output channel
@@ -77,7 +89,8 @@ struct ConvF16Args {
   int nf;             // output fragments of the whole conv
   int tiles_x, tiles_y;
   int nchunks;
-  int nup4, nup, npl4;   // chunk ranges of the four loops (see ConvLayout)
+  int nup4, nup, npl4;   // chunk ranges of the kernel's loops (see ConvLayout)
+  int ntap;
   ConvChunk chunk[kMaxChunks];
 };
 
@@ -115,8 +128,9 @@ struct PairArgs {
   int cout_stored;
   int tiles_x, tiles_y;
 };
-hipError_t launch_conv_pair_f16(const PairArgs& p, int cga, int nfb, bool pool, bool relu,
-                                bool out_f32, hipStream_t stream);
+// tap: convA's one chunk is a tap chunk (cga 2).
+hipError_t launch_conv_pair_f16(const PairArgs& p, int cga, int nfb, bool tap, bool pool,
+                                bool relu, bool out_f32, hipStream_t stream);
 int conv_pair_blocks(int h, int w);
 
 // ---------------------------------------------------------------------------
@@ -152,6 +166,7 @@ struct PackArgs {
   float input_scale;
   int sources;       // 1, 2 or 3
   int lanes;         // stored channels per output pixel (>= 4 * ceil(3 * sources / 4))
+  int taps;          // fp16, 3 sources, 16 lanes: lanes 8..10 = channel 8 at x - 1, x, x + 1
   void* packed;
 };
 hipError_t launch_pack(const PackArgs& a, bool f16, hipStream_t stream);
