@@ -234,12 +234,19 @@ int oidn_unet_layer_info(int in_channels, int layer, int* cin0, int* cin1, int* 
 
 /* Name of the kernel instance that runs `layer` on a tw x th tile (for
  * matching per-kernel timings and profiles), written NUL-terminated into
- * buf (cap bytes), e.g. "conv3x3_f16_mfma<4, 8, false>"; *blocks receives the
- * launch's workgroup count.  Host only. */
+ * buf (cap bytes), e.g. "conv3x3_f16_mfma<2, 16, 2, false>" (fragments and
+ * rows per wave, row groups, fp32 output) or, for both layers of a fused
+ * pair, "conv3x3_pair_f16<2, 2, false, true>" (convA channel groups, convB
+ * fragments, fp32 output, tap-packed input); *blocks receives the launch's
+ * workgroup count.  Host only. */
 int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int dtype, char* buf,
                            int cap, int* blocks);
 
-/* Bytes of the packed weights of all sixteen layers. */
+/* Bytes of the packed weights of all sixteen layers.  With 9 input channels
+ * on the fp16 path the blob also holds a second copy of enc_conv0's and
+ * dec_conv1a's weights in the layout oidn_unet_forward uses for its
+ * tap-packed input (channel 8's row neighbours beside it: half the matrix
+ * steps for that source); oidn_unet_forward_packed uses the plain copies. */
 int oidn_unet_weights_bytes(int in_channels, int dtype, size_t* bytes);
 
 /* Packs all layers: w_ohwi_host[i] is cout x 3 x 3 x cin (cin = cin0 + cin1
