@@ -208,7 +208,10 @@ def main():
     for i in range(U.oidn_unet_layer_count()):
         name, c0, c1, co, level, flags = U.oidn_unet_layer_info(9, i)
         px = (tw >> level) * (th >> level)
-        flops = 2.0 * px * co * 9 * (c0 + c1)
+        # algorithmic work of the method: a decoder conv reads its nearest-2x
+        # upsampled source through 2 low-resolution rows per output row (the 3
+        # ky taps pre-summed per row parity), so 6 taps for those c0 channels
+        flops = 2.0 * px * co * ((6 * c0 + 9 * c1) if c1 else 9 * c0)
         ms = float(avg_ms[i + 1])
         sym, nblocks = U.oidn_unet_layer_kernel(9, i, tw, th, U.OIDN_F16)
         conv_flops += flops

@@ -76,65 +76,79 @@ def test_layer_table_matches_oracle(in_channels):
         assert bool(flags & U.OIDN_POOL2X2) == pool and bool(flags & U.OIDN_RELU) == relu
 
 
+COMBO_ROWS = [(0,), (1, 2), (0, 1), (2,)]   # ky rows summed into each upsampled-chunk combination
+
+
 def _decode_f16(packed, cin0, cin1, cout):
     """Decode the fp16 fragment layout from its documented description:
     bias (16 * nf floats, 256-aligned), then per chunk (<= 32 stored channels
     of one source, sources and channels in order, processed as cg = 4 groups
     of 8 channels if it holds more than 16, else cg = 2), per column group j,
-    per ky, per output
+    per row set (ky = 0, 1, 2; for the upsampled source of a two-source conv
+    the four combinations W0, W1 + W2, W0 + W1, W2 of ky rows), per output
     fragment q, a 1 KB fragment of 64 lanes x 8 halves; lane l holds row
     r = l % 16 (output channel 32 (q // 2) + 8 (r // 4) + 4 (q % 2) + r % 4
     when fragments q and q ^ 1 both exist, else 32 (q // 2) + r) and slot
     4 * j + l // 16 of the chunk, slot = kx * cg + group, channels
-    coff + 8 * group + 0..7."""
+    coff + 8 * group + 0..7.  Returns the plain weights (NaN for the
+    upsampled source), the combinations (NaN elsewhere) and the bias."""
     cs = [O.stored(cin0), O.stored(cin1) if cin1 else 0]
     nf = -(-O.stored(cout) // 16)
     bias_bytes = -(-(4 * 16 * nf) // 256) * 256
     bias = packed[:4 * cout].view(np.float32)
     frags = packed[bias_bytes:].view(np.float16).reshape(-1, 64, 8)
     w = np.full((cout, 3, 3, cin0 + cin1), np.nan, np.float32)
+    combos = np.full((cout, 4, 3, cin0 + cin1), np.nan, np.float32)
     chunks = [(s_idx, off, 4 if min(32, cs[s_idx] - off) > 16 else 2)
               for s_idx in range(2) for off in range(0, cs[s_idx], 32)]
     f = 0
     for s_idx, off, cg in chunks:
-        if True:
-            ncg = -(-3 * cg // 4)
-            for j in range(ncg):
-                for ky in range(3):
-                    for q in range(nf):
-                        frag = frags[f]
-                        f += 1
-                        for lane in range(64):
-                            r, slot = lane % 16, 4 * j + lane // 16
-                            o = (32 * (q // 2) + 8 * (r // 4) + 4 * (q % 2) + r % 4
-                                 if (q | 1) < nf else 32 * (q // 2) + r)
-                            vals = frag[lane].astype(np.float32)
-                            if o >= cout or slot >= 3 * cg:
-                                assert np.all(vals == 0)
-                                continue
-                            kx, grp = divmod(slot, cg)
-                            for jj in range(8):
-                                c = off + 8 * grp + jj
-                                logical = c if s_idx == 0 else cin0 + c
-                                limit = cin0 if s_idx == 0 else cin1
-                                if c < limit:
-                                    w[o, ky, kx, logical] = vals[jj]
-                                else:
-                                    assert vals[jj] == 0
+        up = s_idx == 0 and cin1 > 0
+        ncg = -(-3 * cg // 4)
+        for j in range(ncg):
+            for ky in range(4 if up else 3):
+                for q in range(nf):
+                    frag = frags[f]
+                    f += 1
+                    for lane in range(64):
+                        r, slot = lane % 16, 4 * j + lane // 16
+                        o = (32 * (q // 2) + 8 * (r // 4) + 4 * (q % 2) + r % 4
+                             if (q | 1) < nf else 32 * (q // 2) + r)
+                        vals = frag[lane].astype(np.float32)
+                        if o >= cout or slot >= 3 * cg:
+                            assert np.all(vals == 0)
+                            continue
+                        kx, grp = divmod(slot, cg)
+                        for jj in range(8):
+                            c = off + 8 * grp + jj
+                            logical = c if s_idx == 0 else cin0 + c
+                            limit = cin0 if s_idx == 0 else cin1
+                            if c >= limit:
+                                assert vals[jj] == 0
+                            elif up:
+                                combos[o, ky, kx, logical] = vals[jj]
+                            else:
+                                w[o, ky, kx, logical] = vals[jj]
     assert f == frags.shape[0]
-    return w, bias
+    return w, combos, bias
 
 
 @pytest.mark.parametrize("cin0,cin1,cout", [(9, 0, 32), (32, 0, 48), (64, 9, 64), (96, 64, 112),
-                                            (5, 0, 3), (36, 0, 20)])
+                                            (5, 0, 3), (36, 0, 20), (20, 12, 16)])
 def test_f16_weight_layout_round_trip(cin0, cin1, cout):
     r = np.random.default_rng(cin0 + cout)
     w = r.standard_normal((cout, 3, 3, cin0 + cin1)).astype(np.float32)
     b = r.standard_normal(cout).astype(np.float32)
     packed = U.oidn_conv3x3_pack_weights_host(w, b, cin0, cin1, cout, U.OIDN_F16)
-    wd, bd = _decode_f16(packed, cin0, cin1, cout)
-    assert not np.any(np.isnan(wd))
-    assert np.array_equal(wd, w.astype(np.float16).astype(np.float32))
+    wd, cd, bd = _decode_f16(packed, cin0, cin1, cout)
+    n_up = cin0 if cin1 else 0   # the upsampled source's channels come first
+    assert not np.any(np.isnan(wd[..., n_up:]))
+    assert np.array_equal(wd[..., n_up:], w[..., n_up:].astype(np.float16).astype(np.float32))
+    if n_up:
+        assert np.all(np.isnan(wd[..., :n_up])) and not np.any(np.isnan(cd[..., :n_up]))
+        for a, rows in enumerate(COMBO_ROWS):
+            want = sum(w[:, ky, :, :n_up].astype(np.float64) for ky in rows)
+            assert np.array_equal(cd[:, a, :, :n_up], want.astype(np.float16).astype(np.float32)), a
     assert np.array_equal(bd, b)
 
 
@@ -182,7 +196,8 @@ def test_weight_bytes_sum_per_layer():
     aligned); with 9 input channels on the fp16 path it ends with the tap
     variants of the two layers that read the network input (enc_conv0's
     source, dec_conv1a's skip): the same fragments except that the input's
-    chunk has one column group (3 K-steps per output) instead of two."""
+    chunk has one column group (3 K-steps per output) instead of two.  An
+    upsampled source's column group holds four row sets, others three."""
     for ic in (3, 6, 9):
         for dtype in (U.OIDN_F16, U.OIDN_F32):
             total = U.oidn_unet_weights_bytes(ic, dtype)
@@ -190,12 +205,12 @@ def test_weight_bytes_sum_per_layer():
             per = sum(_a256(U.oidn_conv3x3_weights_bytes(n[1], n[2], n[3], dtype)) for n in info)
             extra = 0
             if ic == 9 and dtype == U.OIDN_F16:
-                for i in (0, 13):   # fragments: (column groups x 3 ky x nf) of 1 KB, bias 16 nf floats
+                for i in (0, 13):   # 1 KB fragments per column group, row set and output fragment
                     name, c0, c1, co = info[i][:4]
                     nf = -(-co // 16)
-                    chunks = [3] * (c0 // 32) if c1 else []   # the upsampled source: 32-channel chunks
-                    ncg = sum(chunks) + 1                      # plus the tap chunk
-                    extra += _a256(_a256(16 * nf * 4) + ncg * 3 * nf * 1024)
+                    up_cgs = 3 * (c0 // 32) if c1 else 0   # upsampled 32-channel chunks: 4 row sets
+                    frags = (up_cgs * 4 + 1 * 3) * nf      # plus the tap chunk: 1 column group, 3 ky
+                    extra += _a256(_a256(16 * nf * 4) + frags * 1024)
             assert total == per + extra, (ic, dtype)
 
 

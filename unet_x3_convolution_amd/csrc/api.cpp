@@ -137,15 +137,34 @@ void pack_conv_host(const float* w, const float* b, int cin0, int cin1, int cout
     float* bias = reinterpret_cast<float*>(out.data());
     for (int o = 0; o < cout; ++o) bias[o] = b[o];
     _Float16* frag = reinterpret_cast<_Float16*>(out.data() + L.bias_bytes);
+    // Upsampled-source chunks hold four row combinations a per column group
+    // instead of the three ky rows: W0, W1 + W2, W0 + W1, W2 (the two rows
+    // of the low-resolution source an even / odd output row reads), each sum
+    // formed in double and rounded once to fp16.
+    static const int kCombo[4][2] = {{0, -1}, {1, 2}, {0, 1}, {2, -1}};
     for (int ci = 0; ci < L.nchunks; ++ci) {
       const ConvChunk& ch = L.chunk[ci];
+      const bool up = ci < L.nup;
+      const int rows = up ? 4 : 3;
       for (int j = 0; j < ch.ncg; ++j)
-        for (int ky = 0; ky < 3; ++ky)
+        for (int ky = 0; ky < rows; ++ky)
           for (int q = 0; q < L.nf; ++q) {
-            _Float16* f = frag + ((size_t)(ch.wfrag + (j * 3 + ky) * L.nf + q)) * (kFragBytes / 2);
+            _Float16* f = frag + ((size_t)(ch.wfrag + (j * rows + ky) * L.nf + q)) * (kFragBytes / 2);
             for (int lane = 0; lane < 64; ++lane) {
               const int r = lane & 15, slot = 4 * j + (lane >> 4);
               const int o = frag_row_to_cout(L.nf, q, r);
+              if (up) {
+                if (o >= cout || slot >= 3 * ch.cg) continue;
+                const int kx = slot / ch.cg, grp = slot % ch.cg;
+                for (int jj = 0; jj < 8; ++jj) {
+                  const int li = logical(ch.src, ch.coff + 8 * grp + jj);
+                  if (li < 0) continue;
+                  double v = wat(o, 3 * kCombo[ky][0] + kx, li);
+                  if (kCombo[ky][1] >= 0) v += wat(o, 3 * kCombo[ky][1] + kx, li);
+                  f[lane * 8 + jj] = (_Float16)v;
+                }
+                continue;
+              }
               if (ch.src == tap_src) {
                 // slots 0..2: channels 0..7 at kx = slot; slot 3: channel 8 at kx = lane 0..2
                 if (o >= cout) continue;

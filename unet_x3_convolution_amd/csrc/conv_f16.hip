@@ -66,6 +66,8 @@ constexpr int kXcds = 8;
 
 constexpr int LPW = TW / 2 + 2;               // half-resolution patch width
 
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
 template <int TH_, bool SW = false>
 struct Tile {
   static constexpr int TH = TH_;                // tile height (rows)
@@ -218,18 +220,18 @@ __device__ __forceinline__ void stage_patch(_Float16* lds, const _Float16* src, 
 // before its MFMAs, so weight loads overlap the matrix work, and on return
 // `acur` holds the next chunk's.  `hook` runs once, right after the first
 // of those prefetches is issued.
-// The wave's window starts at patch row row0 (even for UP) and column col0;
-// PWID is the full-resolution patch width in pixels; SW selects the
-// swizzled patch layout.  `wchunk` may point into LDS (weights staged there);
-// `nf` is then the fragment count of a staged weight row.  TAP: a tap chunk
-// (CG 2; one column group, slot 3 = group 1 of the centre pixel).
-template <int NFW, int R, int CG, bool PF, bool UP, int PWID = PW, bool SW = false,
-          bool TAP = false, typename Hook>
+// The wave's window starts at patch row row0 and column col0; PWID is the
+// patch width in pixels; SW selects the swizzled patch layout.  `wchunk` may
+// point into LDS (weights staged there); `nf` is then the fragment count of
+// a staged weight row.  TAP: a tap chunk (CG 2; one column group, slot 3 =
+// group 1 of the centre pixel).  (Upsampled-source chunks: mma_chunk_up.)
+template <int NFW, int R, int CG, bool PF, int PWID = PW, bool SW = false, bool TAP = false,
+          typename Hook>
 __device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], uint4 (&acur)[3][NFW],
                                           const _Float16* lds, int cur, int zero,
                                           const uint4* wchunk, const uint4* wnext, int nf,
                                           int row0, int col0, int g, int c, Hook&& hook) {
-  static_assert(!TAP || (CG == 2 && !UP), "tap chunks are plain 16-lane sources");
+  static_assert(!TAP || CG == 2, "tap chunks are 16-lane sources");
   constexpr int NCG = TAP ? 1 : (3 * CG + 3) / 4;
 #pragma unroll 1
   for (int j = 0; j < NCG; ++j) {
@@ -255,22 +257,13 @@ __device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], uint4 (&acur)[
       const int kx = TAP ? (slot < 3 ? slot : 1) : slot / CG;
       const int grp = TAP ? (slot < 3 ? 0 : 1) : slot - kx * CG;
       constexpr int PS = pstride<CG, SW>();
-      if constexpr (UP) {
-        // patch row p of this wave's window is half-resolution row
-        // row0 / 2 + (p + 1) / 2; column c + kx - 1 is (c + kx + 1) / 2
-        const int col = (col0 + c + kx + 1) >> 1;
-        base = cur + ((row0 >> 1) * LPW + col) * PS + 8 * gslot<CG, SW>(col, grp);
-        rstride = LPW * PS;
-      } else {
-        const int col = col0 + c + kx;
-        base = cur + (row0 * PWID + col) * PS + 8 * gslot<CG, SW>(col, grp);
-        rstride = PWID * PS;
-      }
+      const int col = col0 + c + kx;
+      base = cur + (row0 * PWID + col) * PS + 8 * gslot<CG, SW>(col, grp);
+      rstride = PWID * PS;
     }
 #pragma unroll
     for (int p = 0; p < R + 2; ++p) {
-      const int prow = UP ? (p + 1) >> 1 : p;
-      const half8 b = *reinterpret_cast<const half8*>(lds + base + prow * rstride);
+      const half8 b = *reinterpret_cast<const half8*>(lds + base + p * rstride);
 #pragma unroll
       for (int ky = 0; ky < 3; ++ky) {
         const int r = p - ky;
@@ -296,6 +289,64 @@ __device__ __forceinline__ float act(float v, int relu) { return relu ? fmaxf(v,
 __device__ __forceinline__ float swap_pair(float v) {
   // DPP quad_perm [1, 0, 3, 2]: exchange with the neighbouring lane.
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
+// MFMAs of one chunk of the nearest-2x-upsampled source, sub-pixel over
+// rows.  Through its three ky taps, an output row y = 2 Y + py of the
+// upsampled image reads only two low-resolution rows: Y - 1 (weight W0)
+// and Y (W1 + W2) when py = 0; Y (W0 + W1) and Y + 1 (W2) when py = 1 --
+// exact in real arithmetic (the zero padding of row -1 and row 2 H maps to
+// low-resolution rows -1 and H, which the patch holds as zeros).  The
+// chunk's weights hold these four row combinations a = 0..3 per column group
+// (A index (j * 4 + a) * nf + q), so an output row takes two MFMAs per
+// column group instead of three, and low-resolution patch row qr of the
+// wave's window serves output rows 2 qr (a = 0), 2 qr - 2 (a = 1),
+// 2 qr - 1 (a = 2) and 2 qr - 3 (a = 3): R / 2 + 2 B reads per column group
+// instead of R + 2.  Low-resolution patch column (c + kx + 1) / 2 holds
+// the full-resolution column c + kx - 1 of the wave's window (row0 even).
+// The A operands are loaded per column group and combination (from LDS or
+// global memory).
+template <int NFW, int R, int CG, bool SW>
+__device__ __forceinline__ void mma_chunk_up(floatx4 (&acc)[R][NFW], const _Float16* lds, int cur,
+                                             int zero, const uint4* wchunk, int nf, int row0,
+                                             int col0, int g, int c) {
+  static_assert(R % 2 == 0, "output rows come in pairs");
+  constexpr int NCG = (3 * CG + 3) / 4;
+#pragma unroll 1
+  for (int j = 0; j < NCG; ++j) {
+    const int slot = 4 * j + g;
+    int base = zero, rstride = 0;
+    if (slot < 3 * CG) {
+      const int kx = slot / CG;
+      const int grp = slot - kx * CG;
+      constexpr int PS = pstride<CG, SW>();
+      const int col = (col0 + c + kx + 1) >> 1;
+      base = cur + ((row0 >> 1) * LPW + col) * PS + 8 * gslot<CG, SW>(col, grp);
+      rstride = LPW * PS;
+    }
+    // the column group's R / 2 + 2 B fragments, then one row combination's
+    // A operands at a time (registers: B rows + NFW A, not 4 NFW A)
+    half8 b[R / 2 + 2];
+#pragma unroll
+    for (int qr = 0; qr < R / 2 + 2; ++qr)
+      b[qr] = *reinterpret_cast<const half8*>(lds + base + qr * rstride);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      uint4 aa[NFW];
+#pragma unroll
+      for (int q = 0; q < NFW; ++q) aa[q] = wchunk[((size_t)(j * 4 + a) * nf + q) * 64];
+#pragma unroll
+      for (int qr = 0; qr < R / 2 + 2; ++qr) {
+        const int r = a == 0 ? 2 * qr : a == 1 ? 2 * qr - 2 : a == 2 ? 2 * qr - 1 : 2 * qr - 3;
+        if (r >= 0 && r < R) {
+#pragma unroll
+          for (int q = 0; q < NFW; ++q)
+            acc[r][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(aa[q]), b[qr], acc[r][q],
+                                                               0, 0, 0);
+        }
+      }
+    }
+  }
 }
 
 template <bool OUTF32>
@@ -431,14 +482,18 @@ __device__ __forceinline__ void stage_weights(_Float16* dst, const uint4* w, int
 template <int NFW, int R>
 constexpr bool kPrefetch = 4 * R * NFW + 24 * NFW <= 176;
 
-// Staged weights: the workgroup's FB fragments of one chunk take
-// 9 FB KB (3 column groups x 3 ky x FB, 1 KB each).  They go to LDS where
-// the swizzled patch and those weights leave room for two workgroups per CU.
+// Staged weights: the workgroup's FB fragments of one chunk take 9 FB KB
+// (3 column groups x 3 ky x FB, 1 KB each), 12 FB KB for an upsampled
+// chunk (4 row combinations), which sits after that chunk's smaller
+// half-resolution patch.  They go to LDS where the swizzled patches and
+// those weights leave room for two workgroups per CU.
+template <int TH>
+constexpr int kUpPatch = ((TH / 2 + 2) * LPW * 32 + 511) / 512 * 512;   // halves (swizzled)
 template <int NFW, int R, int WR>
-constexpr int kWeightSlots = 9 * NFW * (4 / WR) * 64;
+constexpr int kWlHalves = cmax(Tile<WR * R, true>::PATCH + 8 * 9 * NFW * (4 / WR) * 64,
+                               kUpPatch<WR * R> + 8 * 12 * NFW * (4 / WR) * 64);
 template <int NFW, int R, int WR>
-constexpr bool kWeightsInLds =
-    2 * (2 * Tile<WR * R, true>::PATCH + 16 * kWeightSlots<NFW, R, WR> + 16) <= 160 * 1024;
+constexpr bool kWeightsInLds = 2 * (2 * kWlHalves<NFW, R, WR> + 16) <= 160 * 1024;
 
 // A workgroup of 4 waves covers a (WR R) x 16 tile for FB = NFW (4 / WR)
 // output fragments: wave w computes rows [R (w % WR), + R) for the NFW
@@ -457,8 +512,9 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
   constexpr bool SW = WL;
   constexpr int FB = NFW * (4 / WR);             // fragments per workgroup
   using T = Tile<WR * R, SW>;
-  constexpr int WOFF = T::PATCH;                 // staged weights (halves)
-  constexpr int ZERO = WOFF + (WL ? 8 * kWeightSlots<NFW, R, WR> : 0);
+  constexpr int WOFF = T::PATCH;                 // staged weights of a plain chunk (halves)
+  constexpr int WOFF_UP = kUpPatch<WR * R>;      // ... of an upsampled chunk
+  constexpr int ZERO = WL ? kWlHalves<NFW, R, WR> : T::PATCH;
   __shared__ __attribute__((aligned(16))) _Float16 lds[ZERO + 8];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -485,19 +541,43 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
   // the workgroup's weight rows (direct loads) and this wave's staged A operands
   const uint4* wblk = static_cast<const uint4*>(a.wfrag) + lane + blockIdx.y * FB * 64;
   const uint4* wl = reinterpret_cast<const uint4*>(lds + WOFF) + lane + (wave / WR) * NFW * 64;
+  const uint4* wl_up = reinterpret_cast<const uint4*>(lds + WOFF_UP) + lane + (wave / WR) * NFW * 64;
   uint4 acur[3][NFW];
-  if (PF) {
-    const uint4* w0 = wf + (size_t)a.chunk[0].wfrag * 64;
+  // PF: acur holds the first plain chunk's column-group-0 weights on entry
+  // to the plain loops (upsampled chunks load theirs per column group)
+  auto preload = [&](int ci) {
 #pragma unroll
     for (int ky = 0; ky < 3; ++ky)
 #pragma unroll
-      for (int q = 0; q < NFW; ++q) acur[ky][q] = w0[(ky * nf + q) * 64];
-  }
+      for (int q = 0; q < NFW; ++q)
+        acur[ky][q] = wf[((size_t)a.chunk[ci].wfrag + ky * nf + q) * 64];
+  };
+  if (PF && a.nup == 0) preload(0);
   // Chunks run in five loops of one shape each: upsampled source (32- then
   // 16-channel chunks), then the plain source (32- then 16-channel chunks,
   // then a tap chunk).
   const int bounds[6] = {0, a.nup4, a.nup, a.nup + a.npl4, a.nchunks - a.ntap, a.nchunks};
-#define OIDN_CHUNK_LOOP(K, CG, UP, TAP)                                                         \
+#define OIDN_UP_LOOP(K, CG)                                                                     \
+  _Pragma("unroll 1") for (int ci = bounds[K]; ci < bounds[K + 1]; ++ci) {                      \
+    const ConvChunk ch = a.chunk[ci];                                                           \
+    const _Float16* src = static_cast<const _Float16*>(a.src0);                                 \
+    __syncthreads();                                                                            \
+    if ((a.cs0 & 7) == 0)                                                                       \
+      stage_patch_direct<T::TH, 4, T::PATCH / 8, CG, true, SW>(reinterpret_cast<uint4*>(lds),    \
+                                                               src, a.cs0, ch.coff, a.h, a.w,   \
+                                                               y0, x0, wave, lane);             \
+    else                                                                                        \
+      stage_patch<T::TH, CG, false, true, SW>(lds, src, a.cs0, ch.coff, a.h, a.w, y0, x0, tid);  \
+    if constexpr (WL) stage_weights<(3 * CG + 3) / 4 * 4 * FB>(                                 \
+                          lds + WOFF_UP, wblk + (size_t)ch.wfrag * 64, nf, FB, wave);           \
+    __syncthreads();                                                                            \
+    if constexpr (WL)                                                                           \
+      mma_chunk_up<NFW, R, CG, SW>(acc, lds, 0, ZERO, wl_up, FB, R * rg, 0, g, c);              \
+    else                                                                                        \
+      mma_chunk_up<NFW, R, CG, SW>(acc, lds, 0, ZERO, wf + (size_t)ch.wfrag * 64, nf, R * rg, 0, \
+                                   g, c);                                                       \
+  }
+#define OIDN_CHUNK_LOOP(K, CG, TAP)                                                             \
   _Pragma("unroll 1") for (int ci = bounds[K]; ci < bounds[K + 1]; ++ci) {                      \
     const ConvChunk ch = a.chunk[ci];                                                           \
     const _Float16* src = static_cast<const _Float16*>(ch.src ? a.src1 : a.src0);               \
@@ -505,28 +585,30 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
     const uint4* wnext = ci + 1 < a.nchunks ? wf + (size_t)a.chunk[ci + 1].wfrag * 64 : nullptr; \
     __syncthreads();                                                                            \
     if ((cs & 7) == 0)                                                                          \
-      stage_patch_direct<T::TH, 4, T::PATCH / 8, CG, UP, SW>(reinterpret_cast<uint4*>(lds), src, \
-                                                             cs, ch.coff, a.h, a.w, y0, x0, wave, \
-                                                             lane);                             \
+      stage_patch_direct<T::TH, 4, T::PATCH / 8, CG, false, SW>(reinterpret_cast<uint4*>(lds),   \
+                                                                src, cs, ch.coff, a.h, a.w, y0, \
+                                                                x0, wave, lane);                \
     else                                                                                        \
-      stage_patch<T::TH, CG, false, UP, SW>(lds, src, cs, ch.coff, a.h, a.w, y0, x0, tid);      \
+      stage_patch<T::TH, CG, false, false, SW>(lds, src, cs, ch.coff, a.h, a.w, y0, x0, tid);   \
     if constexpr (WL) stage_weights<(TAP ? 1 : (3 * CG + 3) / 4) * 3 * FB>(                      \
                           lds + WOFF, wblk + (size_t)ch.wfrag * 64, nf, FB, wave);              \
     __syncthreads();                                                                            \
     if constexpr (WL)                                                                           \
-      mma_chunk<NFW, R, CG, false, UP, PW, SW, TAP>(acc, acur, lds, 0, ZERO, wl, nullptr, FB,    \
-                                                    R * rg, 0, g, c, [] {});                    \
+      mma_chunk<NFW, R, CG, false, PW, SW, TAP>(acc, acur, lds, 0, ZERO, wl, nullptr, FB,        \
+                                                R * rg, 0, g, c, [] {});                        \
     else                                                                                        \
-      mma_chunk<NFW, R, CG, PF, UP, PW, false, TAP>(acc, acur, lds, 0, ZERO,                     \
-                                                    wf + (size_t)ch.wfrag * 64, wnext, nf,      \
-                                                    R * rg, 0, g, c, [] {});                    \
+      mma_chunk<NFW, R, CG, PF, PW, false, TAP>(acc, acur, lds, 0, ZERO,                         \
+                                                wf + (size_t)ch.wfrag * 64, wnext, nf, R * rg,  \
+                                                0, g, c, [] {});                                \
   }
-  OIDN_CHUNK_LOOP(0, 4, true, false)
-  OIDN_CHUNK_LOOP(1, 2, true, false)
-  OIDN_CHUNK_LOOP(2, 4, false, false)
-  OIDN_CHUNK_LOOP(3, 2, false, false)
-  OIDN_CHUNK_LOOP(4, 2, false, true)
+  OIDN_UP_LOOP(0, 4)
+  OIDN_UP_LOOP(1, 2)
+  if (PF && a.nup > 0 && a.nup < a.nchunks) preload(a.nup);
+  OIDN_CHUNK_LOOP(2, 4, false)
+  OIDN_CHUNK_LOOP(3, 2, false)
+  OIDN_CHUNK_LOOP(4, 2, true)
 #undef OIDN_CHUNK_LOOP
+#undef OIDN_UP_LOOP
   (void)upcat;
 
   store_tile<NFW, R, OUTF32>(acc, a, q0, g, y0 + R * rg, x0 + c, c, pool, relu, a.w);
@@ -676,13 +758,12 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA>)) void conv3x3_pair_f16(P
       if constexpr (WL) stage_weights<(3 * CGA + 3) / 4 * 3 * 2>(lds + L::WOFF, wchunk, 2, 2, wave);
       __syncthreads();
       if constexpr (WL) {
-        mma_chunk<2, RA, CGA, false, false, PAIR_PW, true>(acc, acur, lds, 0, L::ZERO, wl, nullptr,
-                                                           2, RA * rh, 16 * cf, g, c, [] {});
+        mma_chunk<2, RA, CGA, false, PAIR_PW, true>(acc, acur, lds, 0, L::ZERO, wl, nullptr, 2,
+                                                    RA * rh, 16 * cf, g, c, [] {});
       } else {
         const uint4* wnext = ci + 1 < p.nchunks ? wf + (size_t)p.wfragA[ci + 1] * 64 : nullptr;
-        mma_chunk<2, RA, CGA, true, false, PAIR_PW, false, TAP>(acc, acur, lds, 0, L::ZERO, wchunk,
-                                                                wnext, 2, RA * rh, 16 * cf, g, c,
-                                                                [] {});
+        mma_chunk<2, RA, CGA, true, PAIR_PW, false, TAP>(acc, acur, lds, 0, L::ZERO, wchunk, wnext,
+                                                         2, RA * rh, 16 * cf, g, c, [] {});
       }
     }
   }
@@ -738,15 +819,15 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA>)) void conv3x3_pair_f16(P
     uint4 acur[3][NFB];
     if constexpr (WL) {
       const uint4* wl = reinterpret_cast<const uint4*>(lds + L::WOFF) + lane;
-      mma_chunk<NFB, RB, 4, false, false, PAIR_PW, true>(accb, acur, lds, 0, L::ZERO, wl, nullptr,
-                                                         NFB, RB * rh, 16 * cf, g, c, [] {});
+      mma_chunk<NFB, RB, 4, false, PAIR_PW, true>(accb, acur, lds, 0, L::ZERO, wl, nullptr, NFB,
+                                                  RB * rh, 16 * cf, g, c, [] {});
     } else {
 #pragma unroll
       for (int ky = 0; ky < 3; ++ky)
 #pragma unroll
         for (int q = 0; q < NFB; ++q) acur[ky][q] = wf[(ky * NFB + q) * 64];
-      mma_chunk<NFB, RB, 4, true, false, PAIR_PW>(accb, acur, lds, 0, L::ZERO, wf, nullptr, NFB,
-                                                  RB * rh, 16 * cf, g, c, [] {});
+      mma_chunk<NFB, RB, 4, true, PAIR_PW>(accb, acur, lds, 0, L::ZERO, wf, nullptr, NFB, RB * rh,
+                                           16 * cf, g, c, [] {});
     }
   }
   ConvF16Args a{};
@@ -881,8 +962,8 @@ bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out
       ch.cg = rem > 16 ? 4 : 2;
       ch.ncg = s == tap_src ? 1 : cdiv(3 * ch.cg, 4);
       ch.wfrag = frag;
-      frag += ch.ncg * 3 * L.nf;
       const bool up = two && s == 0;
+      frag += ch.ncg * (up ? 4 : 3) * L.nf;   // an upsampled chunk has 4 row combinations
       if (up && ch.cg == 4) ++L.nup4;
       if (up) ++L.nup;
       if (!up && ch.cg == 4) ++L.npl4;
