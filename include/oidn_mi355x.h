@@ -98,8 +98,11 @@ int oidn_conv3x3_weights_bytes(int cin0, int cin1, int cout, int dtype, size_t* 
 
 /* Packs OHWI float32 weights (cout x 3 x 3 x (cin0 + cin1), host) and a
  * float32 bias (cout, host) into the device layout of the chosen dtype
- * (fp16: MFMA A-operand fragments in K-major chunk order, pad lanes 0; fp32:
- * [out block][tap][stored input channel][4 out lanes]).  d_packed must hold
+ * (fp16: MFMA A-operand fragments in K-major chunk order, pad lanes 0, the
+ * upsampled source of a two-source conv as four sums of ky rows -- W0,
+ * W1 + W2, W0 + W1, W2, each rounded once to fp16 -- because an output row
+ * reads only two low-resolution rows of it; fp32: [out block][tap][stored
+ * input channel][4 out lanes]).  d_packed must hold
  * oidn_conv3x3_weights_bytes() bytes.  Blocks until the upload finished.
  * Two sources need cin0 % 4 == 0 (each source keeps its own 4-lane blocks,
  * [web-0.4] createTiledDecoderShader). */

@@ -35,8 +35,12 @@ struct ConvChunk {
   int wfrag;  // index of the chunk's first weight fragment
 };
 
-// Weight fragment of (chunk, column group j, ky, output fragment q):
-//   chunk.wfrag + (j * 3 + ky) * nf + q
+// Weight fragment of (chunk, column group j, row set t, output fragment q):
+//   chunk.wfrag + (j * T + t) * nf + q
+// with T = 3 row sets, the ky rows, for a plain source and T = 4 for the
+// nearest-2x-upsampled source: the row combinations W0, W1 + W2, W0 + W1,
+// W2 (an output row of parity 0 reads low-resolution rows Y - 1, Y with the
+// first two, one of parity 1 reads Y, Y + 1 with the last two).
 // 64 lanes x 8 halves; lane l holds output row r = l % 16 and slot
 // 4 * j + l / 16 of the chunk.  Slot s is (kx, group) = (s / cg, s % cg),
 // channels coff + 8 * group + 0..7 of the pixel in column x + kx - 1.
