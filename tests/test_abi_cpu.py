@@ -281,7 +281,8 @@ def test_conv_kernel_selection():
     with all fragments in one workgroup for large layers, output channels
     split across workgroups and shorter tiles for small ones."""
     F, F32, R, P = U.OIDN_F16, U.OIDN_F32, U.OIDN_RELU, U.OIDN_POOL2X2
-    assert U.oidn_conv3x3_kernel(544, 960, 64, 16, 64, F, F, R) == ("conv3x3_f16_mfma<2, 16, 2, false>", 1024)
+    assert U.oidn_conv3x3_kernel(544, 960, 64, 16, 64, F, F, R) == ("conv3x3_f16_mfma<4, 8, 4, false>", 1024)
+    assert U.oidn_conv3x3_kernel(544, 960, 64, 0, 64, F, F, R) == ("conv3x3_f16_mfma<2, 16, 2, false>", 1024)
     assert U.oidn_conv3x3_kernel(1088, 1920, 32, 0, 3, F, F32, 0) == ("conv3x3_f16_mfma<1, 4, 4, true>", 8160)
     assert U.oidn_conv3x3_kernel(136, 240, 160, 0, 112, F, F, R) == ("conv3x3_f16_mfma<1, 4, 4, false>", 952)
     assert U.oidn_conv3x3_kernel(40, 52, 32, 0, 64, F, F, R) == ("conv3x3_f16_mfma<1, 2, 4, false>", 96)
@@ -292,8 +293,9 @@ def test_conv_kernel_selection():
 
 # Launch plans of the 1920x1088 network tile (fragments per wave, rows per
 # wave, row groups): the first candidate of each fragment count that gives
-# at least 480 workgroups, else the one with the most (4 fragments with four
-# or more K chunks per tile: a list led by 4-fragment waves).  enc_conv0 ->
+# at least 480 workgroups, else the one with the most (4 fragments with an
+# upsampled source or four or more K chunks per tile: a list led by
+# 4-fragment waves).  enc_conv0 ->
 # enc_conv1 and dec_conv1b -> dec_conv0 run as fused pairs (both layers
 # report the pair kernel: convA chunk groups, convB fragments, fp32 output,
 # convA reads the tap-packed network input).
@@ -304,7 +306,7 @@ UNET_1080P_PLANS = {
     "enc_conv5b": ("<1, 2, 4, false>", 432), "dec_conv4a": ("<1, 4, 4, false>", 952),
     "dec_conv4b": ("<1, 4, 4, false>", 952), "dec_conv3a": ("<3, 8, 2, false>", 512),
     "dec_conv3b": ("<3, 8, 2, false>", 512), "dec_conv2a": ("<4, 8, 4, false>", 1024),
-    "dec_conv2b": ("<2, 16, 2, false>", 1024), "dec_conv1a": ("<2, 16, 2, false>", 4080),
+    "dec_conv2b": ("<2, 16, 2, false>", 1024), "dec_conv1a": ("<4, 8, 4, false>", 4080),
     "dec_conv1b": ("pair<4, 1, true, false>", 4352), "dec_conv0": ("pair<4, 1, true, false>", 4352),
 }
 

@@ -165,10 +165,19 @@ UPCAT_CASES = [
     (18, 26, 112, 48, 96, "f16"),
     (12, 10, 16, 9, 8, "f32"),
     (512, 1024, 64, 9, 64, "f16"),                              # 32-row tiles
-    (544, 960, 64, 16, 64, "f16"),                              # 16-channel skip, 3 chunks
+    (544, 960, 64, 16, 64, "f16"),                              # <4, 8, 4>: 16-channel skip, 3 chunks
     (546, 1002, 96, 32, 64, "f16"),                             # <4, 8, 4>, ragged, 4 chunks
     (514, 1026, 32, 16, 32, "f16"),                             # ragged
     (272, 480, 112, 48, 96, "f16"),                             # <3, 8, 2>: 2 row groups
+    # one ragged case for every other instance an upsampled source can reach
+    (238, 242, 96, 48, 24, "f16"),                              # <1, 4, 2>
+    (130, 242, 112, 64, 120, "f16"),                            # <2, 4, 2>
+    (466, 242, 48, 32, 56, "f16"),                              # <2, 8, 2>
+    (466, 242, 64, 9, 40, "f16"),                               # <3, 4, 4>
+    (226, 966, 32, 16, 40, "f16"),                              # <3, 8, 4>
+    (466, 242, 32, 16, 120, "f16"),                             # <4, 8, 2>
+    (466, 242, 96, 48, 72, "f16"),                              # <5, 4, 4>
+    (466, 242, 48, 32, 104, "f16"),                             # <7, 4, 4>
 ]
 
 

@@ -897,8 +897,8 @@ const ConvPlan kPlanCandidates[9][kMaxCandidates] = {
 };
 const ConvPlan kPlanManyChunks[kMaxCandidates] = {{8, 4, 4}, {8, 2, 2}, {8, 1, 1}, {2, 1, 4}};
 
-const ConvPlan* plan_candidates(int nf, int nchunks) {
-  if (nf == 4 && nchunks >= 4) return kPlanManyChunks;
+const ConvPlan* plan_candidates(int nf, int nchunks, int nup) {
+  if (nf == 4 && (nup > 0 || nchunks >= 4)) return kPlanManyChunks;
   return kPlanCandidates[nf < 1 ? 1 : nf > 8 ? 8 : nf];
 }
 
@@ -907,10 +907,10 @@ long plan_blocks(int h, int w, int nf, const ConvPlan& P) {
   return (long)cdiv(cdiv(w, TW) * cdiv(h, P.wr * P.rows), kXcds) * kXcds * (nf / frags);
 }
 
-ConvPlan conv_f16_plan(int h, int w, int nf, int nchunks) {
+ConvPlan conv_f16_plan(int h, int w, int nf, int nchunks, int nup) {
   ConvPlan best{};
   long most = -1;
-  const ConvPlan* cand = plan_candidates(nf, nchunks);
+  const ConvPlan* cand = plan_candidates(nf, nchunks, nup);
   for (int i = 0; i < kMaxCandidates; ++i) {
     const ConvPlan& P = cand[i];
     if (P.rows == 0) break;
@@ -928,8 +928,8 @@ ConvPlan conv_f16_plan(int h, int w, int nf, int nchunks) {
 int plan_block_frags(const ConvPlan& P) { return P.nfw * (4 / P.wr); }
 
 // Workgroups of the launch (for reporting).
-int conv_f16_blocks(int h, int w, int nf, int nchunks) {
-  return (int)plan_blocks(h, w, nf, conv_f16_plan(h, w, nf, nchunks));
+int conv_f16_blocks(int h, int w, int nf, int nchunks, int nup) {
+  return (int)plan_blocks(h, w, nf, conv_f16_plan(h, w, nf, nchunks, nup));
 }
 
 bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out,
@@ -980,17 +980,17 @@ bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out
 void conv_f16_describe(const ConvF16Args& a, int nf, bool out_f32, char* buf, int cap,
                        int* blocks) {
   const int h = a.h, w = a.w;
-  const ConvPlan P = conv_f16_plan(h, w, nf, a.nchunks);
+  const ConvPlan P = conv_f16_plan(h, w, nf, a.nchunks, a.nup);
   snprintf(buf, cap, "conv3x3_f16_mfma<%d, %d, %d, %s>", P.nfw, P.rows, P.wr,
            out_f32 ? "true" : "false");
-  *blocks = conv_f16_blocks(h, w, nf, a.nchunks);
+  *blocks = conv_f16_blocks(h, w, nf, a.nchunks, a.nup);
 }
 
 hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, bool relu,
                            bool out_f32, hipStream_t stream) {
   ConvF16Args b = a;
   b.nf = nf;
-  const ConvPlan P = conv_f16_plan(a.h, a.w, nf, a.nchunks);
+  const ConvPlan P = conv_f16_plan(a.h, a.w, nf, a.nchunks, a.nup);
   const int nsplit = nf / plan_block_frags(P);
   return launch_plan(b, P, nsplit, upcat, pool, relu, out_f32, stream);
 }
