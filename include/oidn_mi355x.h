@@ -239,9 +239,10 @@ int oidn_unet_layer_info(int in_channels, int layer, int* cin0, int* cin1, int* 
  * matching per-kernel timings and profiles), written NUL-terminated into
  * buf (cap bytes), e.g. "conv3x3_f16_mfma<2, 16, 2, false>" (fragments and
  * rows per wave, row groups, fp32 output) or, for both layers of a fused
- * pair, "conv3x3_pair_f16<2, 2, false, true>" (convA channel groups, convB
- * fragments, fp32 output, tap-packed input); *blocks receives the launch's
- * workgroup count.  Host only. */
+ * pair, "conv3x3_pair_f16<2, 2, 0, true>" (convA channel groups, convB
+ * fragments, output: 0 fp16, 1 fp32, 2 straight through the output pass,
+ * tap-packed input); *blocks receives the launch's workgroup count.  Host
+ * only. */
 int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int dtype, char* buf,
                            int cap, int* blocks);
 
@@ -249,7 +250,11 @@ int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int dtype
  * on the fp16 path the blob also holds a second copy of enc_conv0's and
  * dec_conv1a's weights in the layout oidn_unet_forward uses for its
  * tap-packed input (channel 8's row neighbours beside it: half the matrix
- * steps for that source); oidn_unet_forward_packed uses the plain copies. */
+ * steps for that source); oidn_unet_forward_packed uses the plain copies.
+ * On the fp16 path dec_conv0's one output fragment holds its three output
+ * channels' weights and biases in each of its four 4-channel groups (lanes
+ * 4g .. 4g + 2, lane 4g + 3 zero), so the output pass fused into that
+ * layer's kernel can spread its rows over all lanes; the size is unchanged. */
 int oidn_unet_weights_bytes(int in_channels, int dtype, size_t* bytes);
 
 /* Packs all layers: w_ohwi_host[i] is cout x 3 x 3 x cin (cin = cin0 + cin1
@@ -275,7 +280,8 @@ int oidn_unet_workspace_bytes(int in_channels, int w, int h, int max_tile, int o
 
 /* End-to-end denoise ([webgpu-0.6] recordDenoiseExecution): plan the tile
  * grid, then for each tile in order: input pass, network, output pass into
- * the tile's output rectangle of out_rgba (h x w RGBA float32).  in_channels
+ * the tile's output rectangle of out_rgba (h x w RGBA float32; on the fp16
+ * path the network's last fused pair writes that rectangle itself).  in_channels
  * must match the non-NULL images (color; + albedo; + normal). */
 int oidn_unet_forward(const void* d_weights, int in_channels, const float* color,
                       const float* albedo, const float* normal, int w, int h, int hdr,
@@ -285,7 +291,9 @@ int oidn_unet_forward(const void* d_weights, int in_channels, const float* color
 
 /* Same as oidn_unet_forward, and records events[k] on the stream before the
  * k-th kernel of the FIRST tile (k = 0: input pass, 1..16: layers, 17: output
- * pass) and events[18] after it, for per-kernel timing.  n_events >= 19;
+ * pass) and events[18] after it, for per-kernel timing.  Where the last
+ * layer's kernel runs the output pass itself (layer kernel output field 2),
+ * events[17] and events[18] are recorded back to back.  n_events >= 19;
  * events are hipEvent_t handles (see oidn_event_create). */
 int oidn_unet_forward_timed(const void* d_weights, int in_channels, const float* color,
                             const float* albedo, const float* normal, int w, int h, int hdr,

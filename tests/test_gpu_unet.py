@@ -96,6 +96,38 @@ def test_tiled_equals_untiled_at_default_overlap():
     assert np.array_equal(tiled, untiled)
 
 
+def test_fused_output_pass_equals_separate_pass_bit_exact():
+    """On the fp16 path the last fused pair writes the image through the output
+    pass itself.  With 6 input channels (no tap-packed weights) the end-to-end
+    call must give the same bits as the three separate calls per tile:
+    input pass, network with a float32 output, output pass; 12 tiles with
+    ragged output rectangles."""
+    color, albedo, normal, ws, bs = make_case(200, 150, in_channels=6, seed=8)
+    F = DT["f16"]
+    name = U.oidn_unet_layer_kernel(6, 15, 128, 128, F)[0]
+    assert name.startswith("conv3x3_pair_f16<") and name.split(", ")[2] == "2", name
+    got = gpu_denoise(ws, bs, color, albedo, normal, "f16", 128, 32, scale=0.75)
+    tiles = U.oidn_plan_tiles(200, 150, 128, 32)
+    assert len(tiles) == 12
+    wd = packed_unet(ws, bs, 6, "f16")
+    d_color, d_albedo = dev(color), dev(albedo)
+    ref = empty((150, 200, 4), np.float32, fill=float("nan"))
+    for ix, iy, iw, ih, ox, oy, ow, oh in tiles:
+        packed = empty((ih, iw, 8), np.float16)
+        U.oidn_pack_input(d_color, d_albedo, None, 200, 150, ix, iy, iw, ih, True,
+                          U.OIDN_TRANSFER_LOG, 0.75, packed, F)
+        nbytes = U.oidn_unet_packed_workspace_bytes(6, iw, ih, F)
+        work = empty((nbytes,), np.uint8)
+        net = empty((ih, iw, 4), np.float32, fill=float("nan"))
+        U.oidn_unet_forward_packed(wd, 6, packed, iw, ih, work, nbytes, net, F)
+        U.oidn_unpack_output(net, iw, ih, ox - ix, oy - iy, d_color, 200, 150, ox, oy, ow, oh,
+                             True, U.OIDN_TRANSFER_LOG, 0.75, ref)
+    ref = host(ref)
+    assert not np.any(np.isnan(got))
+    assert np.array_equal(got, ref)
+    say("fused output pass == pack + network + unpack, 12 tiles: bit-exact")
+
+
 def _oracle_rect(ws, bs, color, albedo, normal, out_rect, precision):
     """Oracle output of one output rectangle, computed on a 16-aligned input
     window with >= 96 px of context (or the image's aligned edge) per side."""

@@ -290,8 +290,10 @@ bool pair_supported(int cin, int cs, int cout) {
          st <= 8 * kChunkChannels && cout >= 1 && cout <= 32;
 }
 
+// img: the network's last pair writes through the output pass instead of y.
 int run_pair(const void* x, int cin, int cs, int h, int w, const void* wA, const void* wB, void* y,
-             int cout, int out_dtype, unsigned flags, hipStream_t stream, bool tap = false) {
+             int cout, int out_dtype, unsigned flags, hipStream_t stream, bool tap = false,
+             const OutputPass* img = nullptr) {
   ConvLayout LA, LB;
   conv_f16_layout(stored_channels(cin), 0, 32, &LA, tap ? 0 : -1);
   conv_f16_layout(32, 0, cout, &LB);
@@ -306,10 +308,12 @@ int run_pair(const void* x, int cin, int cs, int h, int w, const void* wA, const
   p.wA = static_cast<const unsigned char*>(wA) + LA.bias_bytes;
   p.biasB = static_cast<const float*>(wB);
   p.wB = static_cast<const unsigned char*>(wB) + LB.bias_bytes;
-  p.y = y;
+  p.y = img ? nullptr : y;
   p.cout_stored = stored_channels(cout);
+  if (img) p.img = *img;
+  const int out = img ? kPairImage : out_dtype == OIDN_F32 ? kPairF32 : kPairF16;
   hipError_t e = launch_conv_pair_f16(p, LA.chunk[0].cg, LB.nf, tap, flags & OIDN_POOL2X2,
-                                      flags & OIDN_RELU, out_dtype == OIDN_F32, stream);
+                                      flags & OIDN_RELU, out, stream);
   if (e != hipSuccess) return hip_fail(e, "conv3x3 pair launch");
   return OIDN_OK;
 }
@@ -430,6 +434,13 @@ bool fuse_with_next(int in_channels, int i, int dtype, bool own_io) {
   return pair_supported(s[i].cin0, cs, s[i + 1].cout);
 }
 
+// The end-to-end path runs the output pass in the epilogue of the network's
+// last conv when that conv is the second layer of a fused pair (fp16); the
+// network output is then never stored.
+bool output_fused(int in_channels, int dtype) {
+  return fuse_with_next(in_channels, kLayers - 2, dtype, true);
+}
+
 void plan_workspace(int in_channels, int tw, int th, int dtype, bool own_io, Plan* p) {
   LayerShape s[kLayers];
   unet_shapes(in_channels, s);
@@ -453,6 +464,7 @@ void plan_workspace(int in_channels, int tw, int th, int dtype, bool own_io, Pla
     if (kUNet[i].skip >= 0) last[kUNet[i].skip] = i > last[kUNet[i].skip] ? i : last[kUNet[i].skip];
   }
   last[kLayers] = kLayers;  // consumed by the output pass
+  if (own_io && output_fused(in_channels, dtype)) size[kLayers] = 0;
   // A fused pair (layers i, i + 1) reads layer i's source while it writes
   // layer i + 1's output, so that source lives through layer i + 1; the
   // intermediate between them is never stored.
@@ -495,10 +507,11 @@ void plan_workspace(int in_channels, int tw, int th, int dtype, bool own_io, Pla
 }
 
 // Runs the sixteen convs of one tile.  events: optional, events[k] recorded
-// before layer k and events[16] after the last layer.
+// before layer k and events[16] after the last layer.  img (own_io, with
+// output_fused): the output pass of this tile, run by the last pair.
 int run_network(const unsigned char* weights, int in_channels, const void* packed_in, int tw,
                 int th, unsigned char* ws, const Plan& P, bool own_io, float* net_out, int dtype,
-                hipStream_t stream, void* const* events) {
+                hipStream_t stream, void* const* events, const OutputPass* img = nullptr) {
   LayerShape s[kLayers];
   unet_shapes(in_channels, s);
   const void* val[kLayers + 1];
@@ -528,7 +541,7 @@ int run_network(const unsigned char* weights, int in_channels, const void* packe
       int rc = run_pair(val[L.src], s[i].cin0, L.src == 0 ? in_cs : 0, h, w, wl,
                         weights + woff + align256(ba), const_cast<void*>(val[i + 2]),
                         s[i + 1].cout, i + 1 == kLayers - 1 ? OIDN_F32 : dtype, flags_b, stream,
-                        tap_src == 0);
+                        tap_src == 0, i + 1 == kLayers - 1 ? img : nullptr);
       if (rc) return rc;
       if (events && events[i + 1]) {   // the second layer's interval is empty
         hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[i + 1]), stream);
@@ -624,24 +637,30 @@ int denoise(const void* d_weights, int in_channels, const float* color, const fl
     pa.taps = unet_taps(in_channels, dtype) && pa.lanes == 16;
     pa.packed = ws + P.offset[0];
     if ((e = launch_pack(pa, dtype == OIDN_F16, stream)) != hipSuccess) return hip_fail(e, "pack launch");
+    OutputPass op{};
+    op.color = reinterpret_cast<const float4*>(color);
+    op.out = reinterpret_cast<float4*>(out_rgba);
+    op.img_w = w;
+    op.in_off_x = t.out_x - t.in_x;
+    op.in_off_y = t.out_y - t.in_y;
+    op.out_x = t.out_x;
+    op.out_y = t.out_y;
+    op.out_w = t.out_w;
+    op.out_h = t.out_h;
+    op.hdr = hdr;
+    op.input_scale = input_scale;
+    const bool fused = output_fused(in_channels, dtype);
     rc = run_network(static_cast<const unsigned char*>(d_weights), in_channels, nullptr, t.in_w,
-                     t.in_h, ws, P, true, nullptr, dtype, stream, ev ? ev + 1 : nullptr);
+                     t.in_h, ws, P, true, nullptr, dtype, stream, ev ? ev + 1 : nullptr,
+                     fused ? &op : nullptr);
     if (rc) return rc;
-    UnpackArgs ua{};
-    ua.net = reinterpret_cast<const float4*>(ws + P.offset[kLayers]);
-    ua.tile_w = t.in_w;
-    ua.in_off_x = t.out_x - t.in_x;
-    ua.in_off_y = t.out_y - t.in_y;
-    ua.color = reinterpret_cast<const float4*>(color);
-    ua.img_w = w;
-    ua.out_x = t.out_x;
-    ua.out_y = t.out_y;
-    ua.out_w = t.out_w;
-    ua.out_h = t.out_h;
-    ua.hdr = hdr;
-    ua.input_scale = input_scale;
-    ua.out = reinterpret_cast<float4*>(out_rgba);
-    if ((e = launch_unpack(ua, stream)) != hipSuccess) return hip_fail(e, "unpack launch");
+    if (!fused) {
+      UnpackArgs ua{};
+      ua.net = reinterpret_cast<const float4*>(ws + P.offset[kLayers]);
+      ua.tile_w = t.in_w;
+      ua.o = op;
+      if ((e = launch_unpack(ua, stream)) != hipSuccess) return hip_fail(e, "unpack launch");
+    }
     if (ev && ev[kLayers + 2] && (e = hipEventRecord(static_cast<hipEvent_t>(ev[kLayers + 2]), stream)) != hipSuccess)
       return hip_fail(e, "hipEventRecord");
   }
@@ -863,17 +882,17 @@ int oidn_unpack_output(const float* net_rgba, int tile_w, int tile_h, int in_off
   UnpackArgs a{};
   a.net = reinterpret_cast<const float4*>(net_rgba);
   a.tile_w = tile_w;
-  a.in_off_x = in_off_x;
-  a.in_off_y = in_off_y;
-  a.color = reinterpret_cast<const float4*>(color);
-  a.img_w = img_w;
-  a.out_x = out_x;
-  a.out_y = out_y;
-  a.out_w = out_w;
-  a.out_h = out_h;
-  a.hdr = hdr;
-  a.input_scale = input_scale;
-  a.out = reinterpret_cast<float4*>(out_rgba);
+  a.o.in_off_x = in_off_x;
+  a.o.in_off_y = in_off_y;
+  a.o.color = reinterpret_cast<const float4*>(color);
+  a.o.img_w = img_w;
+  a.o.out_x = out_x;
+  a.o.out_y = out_y;
+  a.o.out_w = out_w;
+  a.o.out_h = out_h;
+  a.o.hdr = hdr;
+  a.o.input_scale = input_scale;
+  a.o.out = reinterpret_cast<float4*>(out_rgba);
   hipError_t e = launch_unpack(a, stream);
   if (e != hipSuccess) return hip_fail(e, "unpack launch");
   return ok();
@@ -914,9 +933,10 @@ int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int dtype
     const int st = stored_channels(s[first].cin0);
     const int cs = kUNet[first].src == 0 ? internal_input_lanes(in_channels, dtype) : st;
     const bool tap = unet_taps(in_channels, dtype) && unet_tap_src(first) == 0;
-    snprintf(buf, cap, "conv3x3_pair_f16<%d, %d, %s, %s>", st > 16 ? 4 : 2,
-             cdiv(stored_channels(s[first + 1].cout), 16), first + 1 == kLayers - 1 ? "true" : "false",
-             tap ? "true" : "false");
+    // output: 0 fp16, 1 fp32, 2 through the output pass (last layer, fused)
+    const int out = first + 1 == kLayers - 1 ? (output_fused(in_channels, dtype) ? 2 : 1) : 0;
+    snprintf(buf, cap, "conv3x3_pair_f16<%d, %d, %d, %s>", st > 16 ? 4 : 2,
+             cdiv(stored_channels(s[first + 1].cout), 16), out, tap ? "true" : "false");
     (void)cs;
     nb = conv_pair_blocks(fh, fw);
   } else if (dtype == OIDN_F16) {
@@ -963,7 +983,25 @@ int oidn_unet_pack_weights(const float* const* w_ohwi_host, const float* const* 
     size_t b = 0;
     conv_weights_bytes(s[i].cin0, s[i].cin1, s[i].cout, dtype, &b);
     std::vector<unsigned char> one(b);
-    pack_conv_host(w_ohwi_host[i], bias_host[i], s[i].cin0, s[i].cin1, s[i].cout, dtype, one);
+    if (i == kLayers - 1 && dtype == OIDN_F16) {
+      // fp16: the last layer's RGB in all four 4-channel lane groups of its
+      // output fragment (lane 3 of each zero), for the output pass in its
+      // epilogue; the same bytes as the plain 3-channel packing
+      const int cin = s[i].cin0 + s[i].cin1;
+      std::vector<float> wr((size_t)16 * 9 * cin, 0.f), br(16, 0.f);
+      for (int g = 0; g < 4; ++g)
+        for (int o = 0; o < s[i].cout; ++o) {
+          std::memcpy(&wr[(size_t)(4 * g + o) * 9 * cin], w_ohwi_host[i] + (size_t)o * 9 * cin,
+                      sizeof(float) * 9 * cin);
+          br[4 * g + o] = bias_host[i][o];
+        }
+      size_t b16 = 0;
+      conv_weights_bytes(s[i].cin0, s[i].cin1, 16, dtype, &b16);
+      if (b16 != b) return fail(OIDN_E_UNSUPPORTED, "last layer packing size mismatch");
+      pack_conv_host(wr.data(), br.data(), s[i].cin0, s[i].cin1, 16, dtype, one);
+    } else {
+      pack_conv_host(w_ohwi_host[i], bias_host[i], s[i].cin0, s[i].cin1, s[i].cout, dtype, one);
+    }
     std::memcpy(all.data() + off, one.data(), b);
     off += align256(b);
   }

@@ -37,6 +37,7 @@
 #include <cstdio>
 
 #include "internal.h"
+#include "output_pass.h"
 
 namespace oidn {
 namespace {
@@ -701,11 +702,61 @@ __device__ __forceinline__ void stage_pair_input(uint4* slots, const _Float16* s
 template <int CGA>
 constexpr int kPairWaves = CGA == 2 ? 3 : 2;
 
+// The output pass in convB's epilogue (the network's last conv, one output
+// fragment whose RGB weights and biases are replicated in all four 4-channel
+// lane groups, lane 3 of each zero): lane group g of column x takes the rows
+// r = g, g + 4, ... of the wave's R rows, so the transfer's arithmetic runs
+// on every lane.  Each value is the one store_tile would have written as
+// fp32 from lane group 0.  `alpha` holds the input colour's alpha of those
+// rows, loaded at the start of the kernel (see image_alpha).
+template <int R>
+__device__ __forceinline__ bool image_index(const PairArgs& p, int g, int k, int yb, int x, int xend,
+                                            size_t& i) {
+  const OutputPass& o = p.img;
+  const int y = yb + g + 4 * k;
+  const int lx = x - o.in_off_x, ly = y - o.in_off_y;
+  if (x >= xend || y >= p.h || lx < 0 || lx >= o.out_w || ly < 0 || ly >= o.out_h) return false;
+  i = (size_t)(ly + o.out_y) * o.img_w + lx + o.out_x;
+  return true;
+}
+
+template <int R>
+__device__ __forceinline__ void image_alpha(float (&alpha)[R / 4], const PairArgs& p, int g, int yb,
+                                            int x, int xend) {
+#pragma unroll
+  for (int k = 0; k < R / 4; ++k) {
+    size_t i;
+    alpha[k] = image_index<R>(p, g, k, yb, x, xend, i) ? p.img.color[i].w : 0.f;
+  }
+}
+
+template <int R>
+__device__ __forceinline__ void store_image(const floatx4 (&acc)[R][1], const float (&alpha)[R / 4],
+                                            const PairArgs& p, int g, int yb, int x, int xend,
+                                            int relu) {
+  static_assert(R % 4 == 0, "rows are spread over the four lane groups");
+  const OutputPass& o = p.img;
+  const float b0 = p.biasB[4 * g], b1 = p.biasB[4 * g + 1], b2 = p.biasB[4 * g + 2];
+#pragma unroll
+  for (int k = 0; k < R / 4; ++k) {
+    // row g + 4 k of this lane's column, chosen by selects (a loop of
+    // conditional copies becomes a dynamic index into acc, i.e. scratch)
+    const floatx4 v = g == 0 ? acc[4 * k][0] : g == 1 ? acc[4 * k + 1][0]
+                    : g == 2 ? acc[4 * k + 2][0] : acc[4 * k + 3][0];
+    size_t i;
+    if (!image_index<R>(p, g, k, yb, x, xend, i)) continue;
+    o.out[i] = output_pixel(act(v[0] + b0, relu), act(v[1] + b1, relu), act(v[2] + b2, relu),
+                            alpha[k], o.hdr, o.input_scale);
+  }
+}
+
 // TAP: convA's one chunk is a tap chunk (16-lane packed network input).
-template <int CGA, int NFB, bool OUTF32, bool TAP>
+// OUT: a PairOut (convB's result as fp16, fp32, or through the output pass).
+template <int CGA, int NFB, int OUT, bool TAP>
 __global__ __launch_bounds__(THREADS, (kPairWaves<CGA>)) void conv3x3_pair_f16(PairArgs p, int pool,
                                                                               int relu) {
   static_assert(!TAP || CGA == 2, "tap chunks are 16-lane sources");
+  static_assert(OUT != kPairImage || NFB == 1, "the output pass reads one fragment");
   using L = PairLds<CGA>;
   constexpr bool WL = L::SW;                      // weights in LDS, swizzled layouts
   __shared__ __attribute__((aligned(16))) _Float16 lds[L::ZERO + 8];
@@ -718,6 +769,10 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA>)) void conv3x3_pair_f16(P
   if (!tile_of_block(blockIdx.x, p.tiles_x, p.tiles_y, tx, ty)) return;
   const int y0 = ty * PAIR_TH, x0 = tx * PAIR_TW;
   if (tid < 2) reinterpret_cast<uint2*>(lds + L::ZERO)[tid] = make_uint2(0u, 0u);
+  constexpr int RB = PAIR_TH / 2;                 // convB rows per wave
+  const int xend = x0 + PAIR_TW < p.w ? x0 + PAIR_TW : p.w;
+  float alpha[OUT == kPairImage ? RB / 4 : 1];
+  if constexpr (OUT == kPairImage) image_alpha<RB>(alpha, p, g, y0 + RB * rh, x0 + 16 * cf + c, xend);
 
   // convA's biases for this lane: lane group g of the pair of fragments owns
   // channels 8 g .. 8 g + 7 (one 16-byte slot of the intermediate).  Read
@@ -808,7 +863,6 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA>)) void conv3x3_pair_f16(P
   if constexpr (WL) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // convB's weight copy
   __syncthreads();
   // convB: output rows [8 rh, 8 rh + 8), columns [16 cf, 16 cf + 16).
-  constexpr int RB = PAIR_TH / 2;
   floatx4 accb[RB][NFB];
 #pragma unroll
   for (int r = 0; r < RB; ++r)
@@ -830,28 +884,42 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA>)) void conv3x3_pair_f16(P
                                            16 * cf, g, c, [] {});
     }
   }
-  ConvF16Args a{};
-  a.h = p.h;
-  a.w = p.w;
-  a.bias = p.biasB;
-  a.y = p.y;
-  a.cout_stored = p.cout_stored;
-  a.nf = NFB;
-  const int xend = x0 + PAIR_TW < p.w ? x0 + PAIR_TW : p.w;
-  store_tile<NFB, RB, OUTF32>(accb, a, 0, g, y0 + RB * rh, x0 + 16 * cf + c, c, pool, relu, xend);
+  if constexpr (OUT == kPairImage) {
+    store_image<RB>(accb, alpha, p, g, y0 + RB * rh, x0 + 16 * cf + c, xend, relu);
+  } else {
+    ConvF16Args a{};
+    a.h = p.h;
+    a.w = p.w;
+    a.bias = p.biasB;
+    a.y = p.y;
+    a.cout_stored = p.cout_stored;
+    a.nf = NFB;
+    store_tile<NFB, RB, OUT == kPairF32>(accb, a, 0, g, y0 + RB * rh, x0 + 16 * cf + c, c, pool,
+                                         relu, xend);
+  }
 }
 
 template <int CGA, int NFB, bool TAP = false>
-hipError_t launch_pair_shape(PairArgs p, bool pool, bool relu, bool out_f32, hipStream_t stream) {
+hipError_t launch_pair_shape(PairArgs p, bool pool, bool relu, int out, hipStream_t stream) {
   p.tiles_x = cdiv(p.w, PAIR_TW);
   p.tiles_y = cdiv(p.h, PAIR_TH);
   const dim3 grid(cdiv(p.tiles_x * p.tiles_y, kXcds) * kXcds), block(THREADS);
-  if (out_f32)
-    hipLaunchKernelGGL((conv3x3_pair_f16<CGA, NFB, true, TAP>), grid, block, 0, stream, p,
+  if (out == kPairF32) {
+    hipLaunchKernelGGL((conv3x3_pair_f16<CGA, NFB, kPairF32, TAP>), grid, block, 0, stream, p,
                        (int)pool, (int)relu);
-  else
-    hipLaunchKernelGGL((conv3x3_pair_f16<CGA, NFB, false, TAP>), grid, block, 0, stream, p,
+  } else if (out == kPairF16) {
+    hipLaunchKernelGGL((conv3x3_pair_f16<CGA, NFB, kPairF16, TAP>), grid, block, 0, stream, p,
                        (int)pool, (int)relu);
+  } else {
+    // the network's last pair only: 64 -> 32 -> one fragment, no pool
+    if constexpr (CGA == 4 && NFB == 1 && !TAP) {
+      if (out != kPairImage || pool || !p.img.color || !p.img.out) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((conv3x3_pair_f16<CGA, NFB, kPairImage, TAP>), grid, block, 0, stream,
+                         p, (int)pool, (int)relu);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   return hipGetLastError();
 }
 
@@ -996,16 +1064,16 @@ hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, 
 }
 
 hipError_t launch_conv_pair_f16(const PairArgs& p, int cga, int nfb, bool tap, bool pool,
-                                bool relu, bool out_f32, hipStream_t stream) {
+                                bool relu, int out, hipStream_t stream) {
   if (tap) {
-    if (cga == 2 && nfb == 2) return launch_pair_shape<2, 2, true>(p, pool, relu, out_f32, stream);
-    if (cga == 2 && nfb == 1) return launch_pair_shape<2, 1, true>(p, pool, relu, out_f32, stream);
+    if (cga == 2 && nfb == 2) return launch_pair_shape<2, 2, true>(p, pool, relu, out, stream);
+    if (cga == 2 && nfb == 1) return launch_pair_shape<2, 1, true>(p, pool, relu, out, stream);
     return hipErrorInvalidValue;
   }
-  if (cga == 2 && nfb == 2) return launch_pair_shape<2, 2>(p, pool, relu, out_f32, stream);
-  if (cga == 2 && nfb == 1) return launch_pair_shape<2, 1>(p, pool, relu, out_f32, stream);
-  if (cga == 4 && nfb == 2) return launch_pair_shape<4, 2>(p, pool, relu, out_f32, stream);
-  if (cga == 4 && nfb == 1) return launch_pair_shape<4, 1>(p, pool, relu, out_f32, stream);
+  if (cga == 2 && nfb == 2) return launch_pair_shape<2, 2>(p, pool, relu, out, stream);
+  if (cga == 2 && nfb == 1) return launch_pair_shape<2, 1>(p, pool, relu, out, stream);
+  if (cga == 4 && nfb == 2) return launch_pair_shape<4, 2>(p, pool, relu, out, stream);
+  if (cga == 4 && nfb == 1) return launch_pair_shape<4, 1>(p, pool, relu, out, stream);
   return hipErrorInvalidValue;
 }
 

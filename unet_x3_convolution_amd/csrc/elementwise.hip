@@ -3,18 +3,12 @@
 // per 4-channel block), consecutive threads on consecutive addresses, 16-byte
 // loads where the layout allows.
 #include "internal.h"
+#include "output_pass.h"
 
 namespace oidn {
 namespace {
 
 constexpr int THREADS = 256;
-constexpr float kFltMax = 3.402823466e+38f;
-
-// NaN -> 0, otherwise clamp to [lo, hi] (reading of the pages' sanitize()).
-__device__ __forceinline__ float sanitize(float v, float lo, float hi) {
-  if (v != v) return 0.f;
-  return fminf(fmaxf(v, lo), hi);
-}
 
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
   const _Float16 ha = (_Float16)a, hb = (_Float16)b;
@@ -106,25 +100,13 @@ __global__ __launch_bounds__(THREADS) void pack_input_kernel(PackArgs a) {
 // [webgpu-0.6] outputShader: sanitize the network RGB, invert the transfer and
 // the input scale, alpha from the input colour; only the output rectangle.
 __global__ __launch_bounds__(THREADS) void unpack_output_kernel(UnpackArgs a) {
+  const OutputPass& p = a.o;
   const int t = blockIdx.x * THREADS + threadIdx.x;
-  if (t >= a.out_w * a.out_h) return;
-  const int y = t / a.out_w, x = t - y * a.out_w;
-  const float4 net = a.net[(size_t)(y + a.in_off_y) * a.tile_w + x + a.in_off_x];
-  const size_t o = (size_t)(y + a.out_y) * a.img_w + x + a.out_x;
-  const float alpha = a.color[o].w;
-  float4 r;
-  if (a.hdr) {
-    const float s = a.input_scale;
-    r.x = expm1f(sanitize(net.x, 0.f, kFltMax)) / s;
-    r.y = expm1f(sanitize(net.y, 0.f, kFltMax)) / s;
-    r.z = expm1f(sanitize(net.z, 0.f, kFltMax)) / s;
-  } else {
-    r.x = sanitize(net.x, 0.f, 1.f);
-    r.y = sanitize(net.y, 0.f, 1.f);
-    r.z = sanitize(net.z, 0.f, 1.f);
-  }
-  r.w = alpha;
-  a.out[o] = r;
+  if (t >= p.out_w * p.out_h) return;
+  const int y = t / p.out_w, x = t - y * p.out_w;
+  const float4 net = a.net[(size_t)(y + p.in_off_y) * a.tile_w + x + p.in_off_x];
+  const size_t o = (size_t)(y + p.out_y) * p.img_w + x + p.out_x;
+  p.out[o] = output_pixel(net.x, net.y, net.z, p.color[o].w, p.hdr, p.input_scale);
 }
 
 // [web-0.4] createMaxPoolShader / [web-0.5] coalesced "channels" pool: one
@@ -202,7 +184,7 @@ hipError_t launch_pack(const PackArgs& a, bool f16, hipStream_t stream) {
 }
 
 hipError_t launch_unpack(const UnpackArgs& a, hipStream_t stream) {
-  const size_t n = (size_t)a.out_w * a.out_h;
+  const size_t n = (size_t)a.o.out_w * a.o.out_h;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(unpack_output_kernel, grid_for(n), dim3(THREADS), 0, stream, a);
   return hipGetLastError();

@@ -116,9 +116,27 @@ int conv_f16_blocks(int h, int w, int nf, int nchunks, int nup);
 void conv_f16_describe(const ConvF16Args& a, int nf, bool out_f32, char* buf, int cap,
                        int* blocks);
 
+// Output pass of one tile ([webgpu-0.6] outputShader): the network's pixel
+// (y, x) in tile coordinates lands on image pixel (y - in_off_y + out_y,
+// x - in_off_x + out_x) when 0 <= y - in_off_y < out_h and
+// 0 <= x - in_off_x < out_w; RGB sanitized and (hdr) taken back through the
+// transfer and the input scale, alpha copied from the input colour.
+struct OutputPass {
+  const float4* color;     // h x img_w RGBA float32 (alpha source)
+  float4* out;             // h x img_w RGBA float32
+  int img_w;
+  int in_off_x, in_off_y;
+  int out_x, out_y, out_w, out_h;
+  int hdr;
+  float input_scale;
+};
+
 // Fused pair y = convB(relu(convA(x))) through a 32-channel intermediate kept
 // in LDS (both fp16 layouts as above; convA: one source whose stored channel
 // count is a multiple of 8, all chunks of one kind; convB: 32 -> cout <= 32).
+// convB's result goes to `y` as fp16 or fp32 (cout_stored lanes), or, for the
+// network's last two layers, straight through the output pass into `img`.
+enum PairOut { kPairF16 = 0, kPairF32 = 1, kPairImage = 2 };
 struct PairArgs {
   const void* x;           // fp16, h x w x cs
   int cs, h, w;
@@ -131,10 +149,11 @@ struct PairArgs {
   void* y;
   int cout_stored;
   int tiles_x, tiles_y;
+  OutputPass img;          // out == kPairImage (cga 4, nfb 1, convB without ReLU)
 };
-// tap: convA's one chunk is a tap chunk (cga 2).
+// tap: convA's one chunk is a tap chunk (cga 2); out: a PairOut.
 hipError_t launch_conv_pair_f16(const PairArgs& p, int cga, int nfb, bool tap, bool pool,
-                                bool relu, bool out_f32, hipStream_t stream);
+                                bool relu, int out, hipStream_t stream);
 int conv_pair_blocks(int h, int w);
 
 // ---------------------------------------------------------------------------
@@ -176,15 +195,9 @@ struct PackArgs {
 hipError_t launch_pack(const PackArgs& a, bool f16, hipStream_t stream);
 
 struct UnpackArgs {
-  const float4* net;
+  const float4* net;       // tile of RGBA float32 network output, tile_w wide
   int tile_w;
-  int in_off_x, in_off_y;
-  const float4* color;
-  int img_w;
-  int out_x, out_y, out_w, out_h;
-  int hdr;
-  float input_scale;
-  float4* out;
+  OutputPass o;
 };
 hipError_t launch_unpack(const UnpackArgs& a, hipStream_t stream);
 
