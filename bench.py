@@ -240,11 +240,19 @@ def main():
     px0 = tw * th
     pack_bytes = W * H * 48 + px0 * 16 * 2 if len(tiles) == 1 else None   # 16 lanes fp16 out
     unpack_bytes = W * H * (32 + 16)
-    # the last pair may run the output pass in its epilogue (output field 2)
-    last_sym = U.oidn_unet_layer_kernel(9, U.oidn_unet_layer_count() - 1, tw, th, U.OIDN_F16)[0]
-    out_fused = last_sym.startswith("conv3x3_pair_f16<") and last_sym.split(", ")[2] == "2"
-    for j, nm in ((0, "input pass"), (nk - 1, "output pass")):
-        note = "  (in the last conv's epilogue)" if j == nk - 1 and out_fused else ""
+    # the first pair may run the input pass in its staging (input bit 1), the
+    # last the output pass in its epilogue (output field 2)
+    def pair_fields(layer):
+        sym = U.oidn_unet_layer_kernel(9, layer, tw, th, U.OIDN_F16)[0]
+        if not sym.startswith("conv3x3_pair_f16<"):
+            return None
+        return [int(f) for f in sym[len("conv3x3_pair_f16<"):-1].split(", ")]
+    first, last = pair_fields(0), pair_fields(U.oidn_unet_layer_count() - 1)
+    in_fused = first is not None and (first[3] & 2) != 0
+    out_fused = last is not None and last[2] == 2
+    for j, nm, fused, where in ((0, "input pass", in_fused, "first conv's staging"),
+                                (nk - 1, "output pass", out_fused, "last conv's epilogue")):
+        note = f"  (in the {where})" if fused else ""
         print(f"  {nm:11s} {avg_ms[j] * 1e3:8.1f} us{note}", file=sys.stderr)
     sym, g = max(groups.items(), key=lambda kv: kv[1]["ms"])
     achieved = g["flops"] / g["ms"] / 1e9  # TFLOP/s
@@ -277,8 +285,10 @@ def main():
                      "frac": round(achieved / PEAK_F16_TFLOPS, 4),
                      "traffic": recorded_traffic(sym)},
         "elementwise": {
+            "input_pass_fused": in_fused,
             "input_pass_us": round(float(avg_ms[0]) * 1e3, 2),
-            "input_pass_gbs": round(pack_bytes / avg_ms[0] / 1e6, 1) if pack_bytes else None,
+            "input_pass_gbs": (round(pack_bytes / avg_ms[0] / 1e6, 1)
+                               if pack_bytes and not in_fused else None),
             "output_pass_fused": out_fused,
             "output_pass_us": round(float(avg_ms[nk - 1]) * 1e3, 2),
             "output_pass_gbs": (round(unpack_bytes / avg_ms[nk - 1] / 1e6, 1)

@@ -239,10 +239,10 @@ int oidn_unet_layer_info(int in_channels, int layer, int* cin0, int* cin1, int* 
  * matching per-kernel timings and profiles), written NUL-terminated into
  * buf (cap bytes), e.g. "conv3x3_f16_mfma<2, 16, 2, false>" (fragments and
  * rows per wave, row groups, fp32 output) or, for both layers of a fused
- * pair, "conv3x3_pair_f16<2, 2, 0, true>" (convA channel groups, convB
- * fragments, output: 0 fp16, 1 fp32, 2 straight through the output pass,
- * tap-packed input); *blocks receives the launch's workgroup count.  Host
- * only. */
+ * pair, "conv3x3_pair_f16<2, 2, 0, 3>" (convA channel groups, convB
+ * fragments, output: 0 fp16, 1 fp32, 2 straight through the output pass;
+ * input: bit 0 tap-packed, bit 1 the caller's images through the input pass);
+ * *blocks receives the launch's workgroup count.  Host only. */
 int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int dtype, char* buf,
                            int cap, int* blocks);
 
@@ -281,7 +281,8 @@ int oidn_unet_workspace_bytes(int in_channels, int w, int h, int max_tile, int o
 /* End-to-end denoise ([webgpu-0.6] recordDenoiseExecution): plan the tile
  * grid, then for each tile in order: input pass, network, output pass into
  * the tile's output rectangle of out_rgba (h x w RGBA float32; on the fp16
- * path the network's last fused pair writes that rectangle itself).  in_channels
+ * path the network's first fused pair runs the input pass on the images and
+ * the last writes that rectangle itself).  in_channels
  * must match the non-NULL images (color; + albedo; + normal). */
 int oidn_unet_forward(const void* d_weights, int in_channels, const float* color,
                       const float* albedo, const float* normal, int w, int h, int hdr,
@@ -291,10 +292,11 @@ int oidn_unet_forward(const void* d_weights, int in_channels, const float* color
 
 /* Same as oidn_unet_forward, and records events[k] on the stream before the
  * k-th kernel of the FIRST tile (k = 0: input pass, 1..16: layers, 17: output
- * pass) and events[18] after it, for per-kernel timing.  Where the last
- * layer's kernel runs the output pass itself (layer kernel output field 2),
- * events[17] and events[18] are recorded back to back.  n_events >= 19;
- * events are hipEvent_t handles (see oidn_event_create). */
+ * pass) and events[18] after it, for per-kernel timing.  Where the first
+ * layer's kernel runs the input pass itself (layer kernel input bit 1),
+ * events[0] and events[1] are recorded back to back; where the last layer's
+ * runs the output pass (output field 2), events[17] and events[18].
+ * n_events >= 19; events are hipEvent_t handles (see oidn_event_create). */
 int oidn_unet_forward_timed(const void* d_weights, int in_channels, const float* color,
                             const float* albedo, const float* normal, int w, int h, int hdr,
                             int transfer, float input_scale, int max_tile, int overlap,

@@ -298,17 +298,18 @@ def test_conv_kernel_selection():
 # 4-fragment waves).  enc_conv0 ->
 # enc_conv1 and dec_conv1b -> dec_conv0 run as fused pairs (both layers
 # report the pair kernel: convA chunk groups, convB fragments, output (0 fp16,
-# 2 through the output pass: the last pair writes the image itself), convA
-# reads the tap-packed network input).
+# 2 through the output pass: the last pair writes the image itself), input
+# (1 taps | 2 images through the input pass: the first pair reads the caller's
+# images and writes the tap-packed network input)).
 UNET_1080P_PLANS = {
-    "enc_conv0": ("pair<2, 2, 0, true>", 4352), "enc_conv1": ("pair<2, 2, 0, true>", 4352),
+    "enc_conv0": ("pair<2, 2, 0, 3>", 4352), "enc_conv1": ("pair<2, 2, 0, 3>", 4352),
     "enc_conv2": ("<3, 8, 4, false>", 1024), "enc_conv3": ("<2, 8, 2, false>", 512),
     "enc_conv4": ("<1, 2, 4, false>", 1280), "enc_conv5a": ("<1, 2, 4, false>", 432),
     "enc_conv5b": ("<1, 2, 4, false>", 432), "dec_conv4a": ("<1, 4, 4, false>", 952),
     "dec_conv4b": ("<1, 4, 4, false>", 952), "dec_conv3a": ("<3, 8, 2, false>", 512),
     "dec_conv3b": ("<3, 8, 2, false>", 512), "dec_conv2a": ("<4, 8, 4, false>", 1024),
     "dec_conv2b": ("<2, 16, 2, false>", 1024), "dec_conv1a": ("<4, 8, 4, false>", 4080),
-    "dec_conv1b": ("pair<4, 1, 2, false>", 4352), "dec_conv0": ("pair<4, 1, 2, false>", 4352),
+    "dec_conv1b": ("pair<4, 1, 2, 0>", 4352), "dec_conv0": ("pair<4, 1, 2, 0>", 4352),
 }
 
 

@@ -96,16 +96,18 @@ def test_tiled_equals_untiled_at_default_overlap():
     assert np.array_equal(tiled, untiled)
 
 
-def test_fused_output_pass_equals_separate_pass_bit_exact():
-    """On the fp16 path the last fused pair writes the image through the output
-    pass itself.  With 6 input channels (no tap-packed weights) the end-to-end
-    call must give the same bits as the three separate calls per tile:
-    input pass, network with a float32 output, output pass; 12 tiles with
-    ragged output rectangles."""
+def test_fused_io_passes_equal_separate_passes_bit_exact():
+    """On the fp16 path the first fused pair reads the images through the input
+    pass and the last writes the image through the output pass.  With 6 input
+    channels (no tap-packed weights) the end-to-end call must give the same
+    bits as the three separate calls per tile: input pass, network with a
+    float32 output, output pass; 12 tiles with ragged output rectangles."""
     color, albedo, normal, ws, bs = make_case(200, 150, in_channels=6, seed=8)
     F = DT["f16"]
     name = U.oidn_unet_layer_kernel(6, 15, 128, 128, F)[0]
     assert name.startswith("conv3x3_pair_f16<") and name.split(", ")[2] == "2", name
+    first = U.oidn_unet_layer_kernel(6, 0, 128, 128, F)[0]
+    assert first == "conv3x3_pair_f16<2, 2, 0, 2>", first
     got = gpu_denoise(ws, bs, color, albedo, normal, "f16", 128, 32, scale=0.75)
     tiles = U.oidn_plan_tiles(200, 150, 128, 32)
     assert len(tiles) == 12
@@ -125,7 +127,7 @@ def test_fused_output_pass_equals_separate_pass_bit_exact():
     ref = host(ref)
     assert not np.any(np.isnan(got))
     assert np.array_equal(got, ref)
-    say("fused output pass == pack + network + unpack, 12 tiles: bit-exact")
+    say("fused input/output passes == pack + network + unpack, 12 tiles: bit-exact")
 
 
 def _oracle_rect(ws, bs, color, albedo, normal, out_rect, precision):

@@ -291,9 +291,11 @@ bool pair_supported(int cin, int cs, int cout) {
 }
 
 // img: the network's last pair writes through the output pass instead of y.
+// in_pass: the network's first pair reads the images through the input pass
+// (instead of x) and writes the packed tile to in_pass->packed.
 int run_pair(const void* x, int cin, int cs, int h, int w, const void* wA, const void* wB, void* y,
              int cout, int out_dtype, unsigned flags, hipStream_t stream, bool tap = false,
-             const OutputPass* img = nullptr) {
+             const OutputPass* img = nullptr, const PackArgs* in_pass = nullptr) {
   ConvLayout LA, LB;
   conv_f16_layout(stored_channels(cin), 0, 32, &LA, tap ? 0 : -1);
   conv_f16_layout(32, 0, cout, &LB);
@@ -311,8 +313,10 @@ int run_pair(const void* x, int cin, int cs, int h, int w, const void* wA, const
   p.y = img ? nullptr : y;
   p.cout_stored = stored_channels(cout);
   if (img) p.img = *img;
+  if (in_pass) p.in = *in_pass;
   const int out = img ? kPairImage : out_dtype == OIDN_F32 ? kPairF32 : kPairF16;
-  hipError_t e = launch_conv_pair_f16(p, LA.chunk[0].cg, LB.nf, tap, flags & OIDN_POOL2X2,
+  const int in = (tap ? kPairInTaps : 0) | (in_pass ? kPairInImages : 0);
+  hipError_t e = launch_conv_pair_f16(p, LA.chunk[0].cg, LB.nf, in, flags & OIDN_POOL2X2,
                                       flags & OIDN_RELU, out, stream);
   if (e != hipSuccess) return hip_fail(e, "conv3x3 pair launch");
   return OIDN_OK;
@@ -441,6 +445,14 @@ bool output_fused(int in_channels, int dtype) {
   return fuse_with_next(in_channels, kLayers - 2, dtype, true);
 }
 
+// Likewise the input pass runs in the staging of the network's first conv
+// when that conv is the first layer of a fused pair (fp16, a 16-lane chunk).
+// The packed input is still written (the decoder's last skip reads it).
+bool input_fused(int in_channels, int dtype) {
+  return fuse_with_next(in_channels, 0, dtype, true) && dtype == OIDN_F16 &&
+         stored_channels(in_channels) <= 16;
+}
+
 void plan_workspace(int in_channels, int tw, int th, int dtype, bool own_io, Plan* p) {
   LayerShape s[kLayers];
   unet_shapes(in_channels, s);
@@ -508,10 +520,12 @@ void plan_workspace(int in_channels, int tw, int th, int dtype, bool own_io, Pla
 
 // Runs the sixteen convs of one tile.  events: optional, events[k] recorded
 // before layer k and events[16] after the last layer.  img (own_io, with
-// output_fused): the output pass of this tile, run by the last pair.
+// output_fused): the output pass of this tile, run by the last pair;
+// in_pass (own_io, with input_fused): the input pass, run by the first.
 int run_network(const unsigned char* weights, int in_channels, const void* packed_in, int tw,
                 int th, unsigned char* ws, const Plan& P, bool own_io, float* net_out, int dtype,
-                hipStream_t stream, void* const* events, const OutputPass* img = nullptr) {
+                hipStream_t stream, void* const* events, const OutputPass* img = nullptr,
+                const PackArgs* in_pass = nullptr) {
   LayerShape s[kLayers];
   unet_shapes(in_channels, s);
   const void* val[kLayers + 1];
@@ -541,7 +555,8 @@ int run_network(const unsigned char* weights, int in_channels, const void* packe
       int rc = run_pair(val[L.src], s[i].cin0, L.src == 0 ? in_cs : 0, h, w, wl,
                         weights + woff + align256(ba), const_cast<void*>(val[i + 2]),
                         s[i + 1].cout, i + 1 == kLayers - 1 ? OIDN_F32 : dtype, flags_b, stream,
-                        tap_src == 0, i + 1 == kLayers - 1 ? img : nullptr);
+                        tap_src == 0, i + 1 == kLayers - 1 ? img : nullptr,
+                        i == 0 ? in_pass : nullptr);
       if (rc) return rc;
       if (events && events[i + 1]) {   // the second layer's interval is empty
         hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[i + 1]), stream);
@@ -636,7 +651,9 @@ int denoise(const void* d_weights, int in_channels, const float* color, const fl
     pa.lanes = internal_input_lanes(in_channels, dtype);
     pa.taps = unet_taps(in_channels, dtype) && pa.lanes == 16;
     pa.packed = ws + P.offset[0];
-    if ((e = launch_pack(pa, dtype == OIDN_F16, stream)) != hipSuccess) return hip_fail(e, "pack launch");
+    const bool in_fused = input_fused(in_channels, dtype);
+    if (!in_fused && (e = launch_pack(pa, dtype == OIDN_F16, stream)) != hipSuccess)
+      return hip_fail(e, "pack launch");
     OutputPass op{};
     op.color = reinterpret_cast<const float4*>(color);
     op.out = reinterpret_cast<float4*>(out_rgba);
@@ -652,7 +669,7 @@ int denoise(const void* d_weights, int in_channels, const float* color, const fl
     const bool fused = output_fused(in_channels, dtype);
     rc = run_network(static_cast<const unsigned char*>(d_weights), in_channels, nullptr, t.in_w,
                      t.in_h, ws, P, true, nullptr, dtype, stream, ev ? ev + 1 : nullptr,
-                     fused ? &op : nullptr);
+                     fused ? &op : nullptr, in_fused ? &pa : nullptr);
     if (rc) return rc;
     if (!fused) {
       UnpackArgs ua{};
@@ -933,10 +950,12 @@ int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int dtype
     const int st = stored_channels(s[first].cin0);
     const int cs = kUNet[first].src == 0 ? internal_input_lanes(in_channels, dtype) : st;
     const bool tap = unet_taps(in_channels, dtype) && unet_tap_src(first) == 0;
-    // output: 0 fp16, 1 fp32, 2 through the output pass (last layer, fused)
+    // output: 0 fp16, 1 fp32, 2 through the output pass (last layer, fused);
+    // input: 1 taps | 2 images through the input pass (first layer, fused)
     const int out = first + 1 == kLayers - 1 ? (output_fused(in_channels, dtype) ? 2 : 1) : 0;
-    snprintf(buf, cap, "conv3x3_pair_f16<%d, %d, %d, %s>", st > 16 ? 4 : 2,
-             cdiv(stored_channels(s[first + 1].cout), 16), out, tap ? "true" : "false");
+    const int in = (tap ? 1 : 0) | (first == 0 && input_fused(in_channels, dtype) ? 2 : 0);
+    snprintf(buf, cap, "conv3x3_pair_f16<%d, %d, %d, %d>", st > 16 ? 4 : 2,
+             cdiv(stored_channels(s[first + 1].cout), 16), out, in);
     (void)cs;
     nb = conv_pair_blocks(fh, fw);
   } else if (dtype == OIDN_F16) {

@@ -37,7 +37,7 @@
 #include <cstdio>
 
 #include "internal.h"
-#include "output_pass.h"
+#include "image_io.h"
 
 namespace oidn {
 namespace {
@@ -653,13 +653,14 @@ constexpr int PAIR_PW = 34;                        // patch width (input and int
 // fragments) while the intermediate is written -- the four waves share one
 // copy instead of each reading every A operand from global memory.  That
 // still leaves two workgroups per CU.  16-channel convA chunks (three
-// workgroups per CU, no LDS to spare) keep the padded layout and global
-// weights.
-template <int CGA>
+// workgroups per CU, no LDS to spare) keep the padded input patch and
+// global weights; their intermediate is swizzled (MSW) where the input pass
+// runs in the staging: 39 KB, four workgroups per CU.
+template <int CGA, bool MSW = CGA == 4>
 struct PairLds {
   static constexpr bool SW = CGA == 4;
   static constexpr int IN = PAIR_IH * PAIR_PW * pstride<CGA, SW>();     // halves
-  static constexpr int MID = PAIR_MH * PAIR_PW * pstride<4, SW>();
+  static constexpr int MID = PAIR_MH * PAIR_PW * pstride<4, MSW>();
   static constexpr int REGION = ((IN > MID ? IN : MID) + 511) / 512 * 512;
   static constexpr int WSLOTS = SW ? 9 * 2 * 64 : 0;                 // weight rows (16 B slots)
   static constexpr int WOFF = REGION;
@@ -697,10 +698,97 @@ __device__ __forceinline__ void stage_pair_input(uint4* slots, const _Float16* s
   }
 }
 
+// The input pass fused into convA's staging (one 16-channel chunk, padded
+// layout): patch pixel (py, px) of the window at (y0 - 2, x0 - 2) is network
+// tile pixel (y, x).  Inside the tile it holds the packed input as the input
+// pass computes it (clamp-to-edge image read, the same per-channel
+// arithmetic; with TAPS channel 8 of the row neighbours in lanes 8..10, zero
+// outside the tile), outside the tile zero (the conv's padding).  The
+// pixels of the workgroup's own output tile are also stored to `in.packed`
+// (in.lanes per pixel) for the decoder's later skip read.  Every image load
+// is issued before the first value is used.
+template <bool TAPS>
+__device__ __forceinline__ void stage_pair_images(uint4* slots, const PackArgs& in, int h, int w,
+                                                  int y0, int x0, int tid) {
+  constexpr int NPIX = PAIR_IH * PAIR_PW;
+  constexpr int NIT = (NPIX + THREADS - 1) / THREADS;
+  constexpr int SPP = pstride<2, false>() / 8;     // 16-byte slots per pixel
+  // RGB only (alpha is not an input channel): 3 dwords per image pixel
+  float3 col[NIT], alb[NIT], nrm[NIT];
+  float zl[NIT], zr[NIT];
+  auto rgb = [](const float4* img, size_t i) { return *reinterpret_cast<const float3*>(img + i); };
+#pragma unroll
+  for (int i = 0; i < NIT; ++i) {
+    const int pp = tid + THREADS * i;
+    const int py = pp / PAIR_PW, px = pp - py * PAIR_PW;
+    const int y = y0 - 2 + py, x = x0 - 2 + px;
+    col[i] = alb[i] = nrm[i] = make_float3(0.f, 0.f, 0.f);
+    zl[i] = zr[i] = 0.f;
+    if (pp < NPIX && y >= 0 && y < h && x >= 0 && x < w) {
+      const size_t row = (size_t)min(max(y + in.tile_y, 0), in.img_h - 1) * in.img_w;
+      const size_t src = row + min(max(x + in.tile_x, 0), in.img_w - 1);
+      col[i] = rgb(in.color, src);
+      if (in.sources > 1) alb[i] = rgb(in.albedo, src);
+      if (in.sources > 2) nrm[i] = rgb(in.normal, src);
+      if (TAPS) {
+        if (x > 0) zl[i] = in.normal[row + min(max(x - 1 + in.tile_x, 0), in.img_w - 1)].z;
+        if (x + 1 < w) zr[i] = in.normal[row + min(max(x + 1 + in.tile_x, 0), in.img_w - 1)].z;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NIT; ++i) {
+    const int pp = tid + THREADS * i;
+    if (pp >= NPIX) break;
+    const int py = pp / PAIR_PW, px = pp - py * PAIR_PW;
+    const int y = y0 - 2 + py, x = x0 - 2 + px;
+    const bool inside = y >= 0 && y < h && x >= 0 && x < w;
+    float ch[12];
+#pragma unroll
+    for (int k = 0; k < 12; ++k) ch[k] = 0.f;
+    ch[0] = in_color(col[i].x, in.hdr, in.input_scale);
+    ch[1] = in_color(col[i].y, in.hdr, in.input_scale);
+    ch[2] = in_color(col[i].z, in.hdr, in.input_scale);
+    if (in.sources > 1) {
+      ch[3] = in_albedo(alb[i].x);
+      ch[4] = in_albedo(alb[i].y);
+      ch[5] = in_albedo(alb[i].z);
+    }
+    if (in.sources > 2) {
+      ch[6] = in_normal(nrm[i].x);
+      ch[7] = in_normal(nrm[i].y);
+      ch[8] = in_normal(nrm[i].z);
+    }
+    if (TAPS) {
+      ch[9] = ch[8];
+      ch[8] = x > 0 ? in_normal(zl[i]) : 0.f;
+      ch[10] = x + 1 < w ? in_normal(zr[i]) : 0.f;
+    }
+    uint4 g0 = make_uint4(0u, 0u, 0u, 0u), g1 = g0;
+    if (inside) {
+      g0 = make_uint4(pack_h2(ch[0], ch[1]), pack_h2(ch[2], ch[3]), pack_h2(ch[4], ch[5]),
+                      pack_h2(ch[6], ch[7]));
+      if (in.lanes > 8) g1 = make_uint4(pack_h2(ch[8], ch[9]), pack_h2(ch[10], ch[11]), 0u, 0u);
+      if (py >= 2 && py < 2 + PAIR_TH && px >= 2 && px < 2 + PAIR_TW) {
+        // 32-bit offset formed here (a hoisted 64-bit address is spilled)
+        int o = (y * w + x) * (in.lanes / 8);
+        asm volatile("" : "+v"(o));
+        uint4* out = static_cast<uint4*>(in.packed) + o;
+        out[0] = g0;
+        if (in.lanes > 8) out[1] = g1;
+      }
+    }
+    slots[pp * SPP] = g0;
+    slots[pp * SPP + 1] = g1;
+  }
+}
+
 // A 16-channel convA source leaves LDS for three workgroups per CU; the
-// registers are held to that.  32-channel chunks need more LDS: two.
-template <int CGA>
-constexpr int kPairWaves = CGA == 2 ? 3 : 2;
+// registers are held to that.  32-channel chunks need more LDS: two.  With
+// the input pass in the staging and a tap chunk (no chunk loop, one column
+// group, swizzled intermediate: 126 VGPRs, 39 KB) four.
+template <int CGA, int IN>
+constexpr int kPairWaves = IN == (kPairInImages | kPairInTaps) ? 4 : CGA == 2 ? 3 : 2;
 
 // The output pass in convB's epilogue (the network's last conv, one output
 // fragment whose RGB weights and biases are replicated in all four 4-channel
@@ -750,14 +838,18 @@ __device__ __forceinline__ void store_image(const floatx4 (&acc)[R][1], const fl
   }
 }
 
-// TAP: convA's one chunk is a tap chunk (16-lane packed network input).
+// IN: a PairIn (convA reads packed fp16, the tap-packed network input, or
+// the images through the fused input pass, with or without taps).
 // OUT: a PairOut (convB's result as fp16, fp32, or through the output pass).
-template <int CGA, int NFB, int OUT, bool TAP>
-__global__ __launch_bounds__(THREADS, (kPairWaves<CGA>)) void conv3x3_pair_f16(PairArgs p, int pool,
+template <int CGA, int NFB, int OUT, int IN>
+__global__ __launch_bounds__(THREADS, (kPairWaves<CGA, IN>)) void conv3x3_pair_f16(PairArgs p, int pool,
                                                                               int relu) {
+  constexpr bool TAP = (IN & kPairInTaps) != 0, IMG = (IN & kPairInImages) != 0;
   static_assert(!TAP || CGA == 2, "tap chunks are 16-lane sources");
+  static_assert(!IMG || CGA == 2, "the input pass writes one 16-lane chunk");
   static_assert(OUT != kPairImage || NFB == 1, "the output pass reads one fragment");
-  using L = PairLds<CGA>;
+  constexpr bool MSW = CGA == 4 || IMG;           // swizzled intermediate
+  using L = PairLds<CGA, MSW>;
   constexpr bool WL = L::SW;                      // weights in LDS, swizzled layouts
   __shared__ __attribute__((aligned(16))) _Float16 lds[L::ZERO + 8];
   const int tid = threadIdx.x;
@@ -796,16 +888,27 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA>)) void conv3x3_pair_f16(P
   {
     const uint4* wf = static_cast<const uint4*>(p.wA) + lane;
     uint4 acur[3][2];
-    if constexpr (!WL) {
+    auto load_a = [&] {
 #pragma unroll
       for (int ky = 0; ky < 3; ++ky)
 #pragma unroll
         for (int q = 0; q < 2; ++q) acur[ky][q] = wf[(ky * 2 + q) * 64];
-    }
+    };
+    // (with the input pass the image registers come first)
+    if constexpr (!WL && !IMG) load_a();
     const _Float16* src = static_cast<const _Float16*>(p.x);
     const uint4* wl = reinterpret_cast<const uint4*>(lds + L::WOFF) + lane;
+    if constexpr (IMG) {
+      // one chunk: straight-line code (in the chunk loop the compiler keeps
+      // the staging's addresses live across it and spills them)
+      stage_pair_images<TAP>(reinterpret_cast<uint4*>(lds), p.in, p.h, p.w, y0, x0, tid);
+      load_a();
+      __syncthreads();
+      mma_chunk<2, RA, CGA, true, PAIR_PW, false, TAP>(acc, acur, lds, 0, L::ZERO, wf, nullptr, 2,
+                                                       RA * rh, 16 * cf, g, c, [] {});
+    }
 #pragma unroll 1
-    for (int ci = 0; ci < p.nchunks; ++ci) {
+    for (int ci = 0; ci < (IMG ? 0 : p.nchunks); ++ci) {
       __syncthreads();
       stage_pair_input<CGA, WL>(reinterpret_cast<uint4*>(lds), src, p.cs, ci * kChunkChannels,
                                 p.h, p.w, y0, x0, wave, lane);
@@ -857,7 +960,7 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA>)) void conv3x3_pair_f16(P
       }
       const int col = 16 * cf + c;
       const int px = (RA * rh + r) * PAIR_PW + col;
-      *reinterpret_cast<uint4*>(lds + px * pstride<4, WL>() + 8 * gslot<4, WL>(col, g)) = v;
+      *reinterpret_cast<uint4*>(lds + px * pstride<4, MSW>() + 8 * gslot<4, MSW>(col, g)) = v;
     }
   }
   if constexpr (WL) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // convB's weight copy
@@ -880,7 +983,7 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA>)) void conv3x3_pair_f16(P
       for (int ky = 0; ky < 3; ++ky)
 #pragma unroll
         for (int q = 0; q < NFB; ++q) acur[ky][q] = wf[(ky * NFB + q) * 64];
-      mma_chunk<NFB, RB, 4, true, PAIR_PW>(accb, acur, lds, 0, L::ZERO, wf, nullptr, NFB, RB * rh,
+      mma_chunk<NFB, RB, 4, true, PAIR_PW, MSW>(accb, acur, lds, 0, L::ZERO, wf, nullptr, NFB, RB * rh,
                                            16 * cf, g, c, [] {});
     }
   }
@@ -899,22 +1002,22 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA>)) void conv3x3_pair_f16(P
   }
 }
 
-template <int CGA, int NFB, bool TAP = false>
+template <int CGA, int NFB, int IN>
 hipError_t launch_pair_shape(PairArgs p, bool pool, bool relu, int out, hipStream_t stream) {
   p.tiles_x = cdiv(p.w, PAIR_TW);
   p.tiles_y = cdiv(p.h, PAIR_TH);
   const dim3 grid(cdiv(p.tiles_x * p.tiles_y, kXcds) * kXcds), block(THREADS);
   if (out == kPairF32) {
-    hipLaunchKernelGGL((conv3x3_pair_f16<CGA, NFB, kPairF32, TAP>), grid, block, 0, stream, p,
+    hipLaunchKernelGGL((conv3x3_pair_f16<CGA, NFB, kPairF32, IN>), grid, block, 0, stream, p,
                        (int)pool, (int)relu);
   } else if (out == kPairF16) {
-    hipLaunchKernelGGL((conv3x3_pair_f16<CGA, NFB, kPairF16, TAP>), grid, block, 0, stream, p,
+    hipLaunchKernelGGL((conv3x3_pair_f16<CGA, NFB, kPairF16, IN>), grid, block, 0, stream, p,
                        (int)pool, (int)relu);
   } else {
     // the network's last pair only: 64 -> 32 -> one fragment, no pool
-    if constexpr (CGA == 4 && NFB == 1 && !TAP) {
+    if constexpr (CGA == 4 && NFB == 1 && IN == kPairInPacked) {
       if (out != kPairImage || pool || !p.img.color || !p.img.out) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((conv3x3_pair_f16<CGA, NFB, kPairImage, TAP>), grid, block, 0, stream,
+      hipLaunchKernelGGL((conv3x3_pair_f16<CGA, NFB, kPairImage, IN>), grid, block, 0, stream,
                          p, (int)pool, (int)relu);
     } else {
       return hipErrorInvalidValue;
@@ -1063,17 +1166,26 @@ hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, 
   return launch_plan(b, P, nsplit, upcat, pool, relu, out_f32, stream);
 }
 
-hipError_t launch_conv_pair_f16(const PairArgs& p, int cga, int nfb, bool tap, bool pool,
+hipError_t launch_conv_pair_f16(const PairArgs& p, int cga, int nfb, int in, bool pool,
                                 bool relu, int out, hipStream_t stream) {
-  if (tap) {
-    if (cga == 2 && nfb == 2) return launch_pair_shape<2, 2, true>(p, pool, relu, out, stream);
-    if (cga == 2 && nfb == 1) return launch_pair_shape<2, 1, true>(p, pool, relu, out, stream);
+  if (in & kPairInImages) {
+    // the network's first pair: 16-lane input chunk, 32 -> 32 (pool)
+    if (cga != 2 || nfb != 2 || !p.in.color || !p.in.packed) return hipErrorInvalidValue;
+    if (in == kPairInImages) return launch_pair_shape<2, 2, kPairInImages>(p, pool, relu, out, stream);
+    if (in == (kPairInImages | kPairInTaps))
+      return launch_pair_shape<2, 2, kPairInImages | kPairInTaps>(p, pool, relu, out, stream);
     return hipErrorInvalidValue;
   }
-  if (cga == 2 && nfb == 2) return launch_pair_shape<2, 2>(p, pool, relu, out, stream);
-  if (cga == 2 && nfb == 1) return launch_pair_shape<2, 1>(p, pool, relu, out, stream);
-  if (cga == 4 && nfb == 2) return launch_pair_shape<4, 2>(p, pool, relu, out, stream);
-  if (cga == 4 && nfb == 1) return launch_pair_shape<4, 1>(p, pool, relu, out, stream);
+  if (in == kPairInTaps) {
+    if (cga == 2 && nfb == 2) return launch_pair_shape<2, 2, kPairInTaps>(p, pool, relu, out, stream);
+    if (cga == 2 && nfb == 1) return launch_pair_shape<2, 1, kPairInTaps>(p, pool, relu, out, stream);
+    return hipErrorInvalidValue;
+  }
+  if (in != kPairInPacked) return hipErrorInvalidValue;
+  if (cga == 2 && nfb == 2) return launch_pair_shape<2, 2, kPairInPacked>(p, pool, relu, out, stream);
+  if (cga == 2 && nfb == 1) return launch_pair_shape<2, 1, kPairInPacked>(p, pool, relu, out, stream);
+  if (cga == 4 && nfb == 2) return launch_pair_shape<4, 2, kPairInPacked>(p, pool, relu, out, stream);
+  if (cga == 4 && nfb == 1) return launch_pair_shape<4, 1, kPairInPacked>(p, pool, relu, out, stream);
   return hipErrorInvalidValue;
 }
 

@@ -3,17 +3,13 @@
 // per 4-channel block), consecutive threads on consecutive addresses, 16-byte
 // loads where the layout allows.
 #include "internal.h"
-#include "output_pass.h"
+#include "image_io.h"
 
 namespace oidn {
 namespace {
 
 constexpr int THREADS = 256;
 
-__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
-  const _Float16 ha = (_Float16)a, hb = (_Float16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
-}
 
 // [webgpu-0.6] inputShader ("oidn-webgpu 0.0.0-stage -> 0.6.0",
 // native/denoise.ts): clamp-to-edge read, sanitize, HDR log transfer of the
@@ -36,27 +32,20 @@ __global__ __launch_bounds__(THREADS) void pack_input_kernel(PackArgs a) {
 #pragma unroll
   for (int i = 0; i < 12; ++i) ch[i] = 0.f;
   const float4 col = a.color[src];
-  if (a.hdr) {
-    const float s = a.input_scale;
-    ch[0] = log1pf(sanitize(col.x * s, 0.f, kFltMax));
-    ch[1] = log1pf(sanitize(col.y * s, 0.f, kFltMax));
-    ch[2] = log1pf(sanitize(col.z * s, 0.f, kFltMax));
-  } else {
-    ch[0] = sanitize(col.x, 0.f, 1.f);
-    ch[1] = sanitize(col.y, 0.f, 1.f);
-    ch[2] = sanitize(col.z, 0.f, 1.f);
-  }
+  ch[0] = in_color(col.x, a.hdr, a.input_scale);
+  ch[1] = in_color(col.y, a.hdr, a.input_scale);
+  ch[2] = in_color(col.z, a.hdr, a.input_scale);
   if (a.sources > 1) {
     const float4 al = a.albedo[src];
-    ch[3] = sanitize(al.x, 0.f, 1.f);
-    ch[4] = sanitize(al.y, 0.f, 1.f);
-    ch[5] = sanitize(al.z, 0.f, 1.f);
+    ch[3] = in_albedo(al.x);
+    ch[4] = in_albedo(al.y);
+    ch[5] = in_albedo(al.z);
   }
   if (a.sources > 2) {
     const float4 nr = a.normal[src];
-    ch[6] = sanitize(nr.x, -1.f, 1.f) * 0.5f + 0.5f;
-    ch[7] = sanitize(nr.y, -1.f, 1.f) * 0.5f + 0.5f;
-    ch[8] = sanitize(nr.z, -1.f, 1.f) * 0.5f + 0.5f;
+    ch[6] = in_normal(nr.x);
+    ch[7] = in_normal(nr.y);
+    ch[8] = in_normal(nr.z);
   }
   if (a.taps && a.sources > 2) {
     // channel 8 of the row neighbours inside the tile: from the neighbouring
@@ -66,14 +55,10 @@ __global__ __launch_bounds__(THREADS) void pack_input_kernel(PackArgs a) {
     const float c8 = ch[8];
     float left = __shfl_up(c8, 1, 64), right = __shfl_down(c8, 1, 64);
     const size_t row = (size_t)sy * a.img_w;
-    if (tx > 0 && (lane == 0 || t0 >= n)) {
-      left = sanitize(a.normal[row + min(max(tx - 1 + a.tile_x, 0), a.img_w - 1)].z, -1.f, 1.f) * 0.5f +
-             0.5f;
-    }
-    if (tx + 1 < a.tile_w && (lane == 63 || t0 + 1 >= n)) {
-      right = sanitize(a.normal[row + min(max(tx + 1 + a.tile_x, 0), a.img_w - 1)].z, -1.f, 1.f) * 0.5f +
-              0.5f;
-    }
+    if (tx > 0 && (lane == 0 || t0 >= n))
+      left = in_normal(a.normal[row + min(max(tx - 1 + a.tile_x, 0), a.img_w - 1)].z);
+    if (tx + 1 < a.tile_w && (lane == 63 || t0 + 1 >= n))
+      right = in_normal(a.normal[row + min(max(tx + 1 + a.tile_x, 0), a.img_w - 1)].z);
     ch[8] = tx > 0 ? left : 0.f;
     ch[9] = c8;
     ch[10] = tx + 1 < a.tile_w ? right : 0.f;

@@ -137,6 +137,23 @@ struct OutputPass {
 // convB's result goes to `y` as fp16 or fp32 (cout_stored lanes), or, for the
 // network's last two layers, straight through the output pass into `img`.
 enum PairOut { kPairF16 = 0, kPairF32 = 1, kPairImage = 2 };
+// convA's source: packed fp16 (optionally the tap-packed network input), or
+// the caller's images through the input pass run in convA's staging (bits).
+enum PairIn { kPairInPacked = 0, kPairInTaps = 1, kPairInImages = 2 };
+struct PackArgs {
+  const float4* color;
+  const float4* albedo;
+  const float4* normal;
+  int img_w, img_h;
+  int tile_x, tile_y, tile_w, tile_h;
+  int hdr;
+  float input_scale;
+  int sources;       // 1, 2 or 3
+  int lanes;         // stored channels per output pixel (>= 4 * ceil(3 * sources / 4))
+  int taps;          // fp16, 3 sources, 16 lanes: lanes 8..10 = channel 8 at x - 1, x, x + 1
+  void* packed;
+};
+
 struct PairArgs {
   const void* x;           // fp16, h x w x cs
   int cs, h, w;
@@ -150,9 +167,12 @@ struct PairArgs {
   int cout_stored;
   int tiles_x, tiles_y;
   OutputPass img;          // out == kPairImage (cga 4, nfb 1, convB without ReLU)
+  PackArgs in;             // in & kPairInImages (cga 2, nfb 2): x is not read, the
+                           // packed tile is written to in.packed
 };
-// tap: convA's one chunk is a tap chunk (cga 2); out: a PairOut.
-hipError_t launch_conv_pair_f16(const PairArgs& p, int cga, int nfb, bool tap, bool pool,
+// in: PairIn bits (kPairInTaps: convA's one chunk is a tap chunk, cga 2);
+// out: a PairOut.
+hipError_t launch_conv_pair_f16(const PairArgs& p, int cga, int nfb, int in, bool pool,
                                 bool relu, int out, hipStream_t stream);
 int conv_pair_blocks(int h, int w);
 
@@ -179,19 +199,6 @@ hipError_t launch_conv_f32(const ConvF32Args& a, bool upcat, bool pool, bool rel
 // ---------------------------------------------------------------------------
 // Elementwise / gather passes.
 // ---------------------------------------------------------------------------
-struct PackArgs {
-  const float4* color;
-  const float4* albedo;
-  const float4* normal;
-  int img_w, img_h;
-  int tile_x, tile_y, tile_w, tile_h;
-  int hdr;
-  float input_scale;
-  int sources;       // 1, 2 or 3
-  int lanes;         // stored channels per output pixel (>= 4 * ceil(3 * sources / 4))
-  int taps;          // fp16, 3 sources, 16 lanes: lanes 8..10 = channel 8 at x - 1, x, x + 1
-  void* packed;
-};
 hipError_t launch_pack(const PackArgs& a, bool f16, hipStream_t stream);
 
 struct UnpackArgs {
