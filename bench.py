@@ -161,6 +161,8 @@ def main():
     out = torch.empty((H, W, 4), dtype=torch.float32, device="cuda")
     tiles = U.oidn_plan_tiles(W, H, args.max_tile, args.overlap)
     tw, th = tiles[0][2], tiles[0][3]
+    # tiles per launch: the per-kernel events cover the first batch
+    nbatch = U.oidn_unet_tile_batch(9, W, H, args.max_tile, args.overlap, U.OIDN_F16)
 
     def step(events=None):
         if events is None:
@@ -207,13 +209,14 @@ def main():
     prev_sym = None
     for i in range(U.oidn_unet_layer_count()):
         name, c0, c1, co, level, flags = U.oidn_unet_layer_info(9, i)
-        px = (tw >> level) * (th >> level)
+        px = (tw >> level) * (th >> level) * nbatch
         # algorithmic work of the method: a decoder conv reads its nearest-2x
         # upsampled source through 2 low-resolution rows per output row (the 3
         # ky taps pre-summed per row parity), so 6 taps for those c0 channels
         flops = 2.0 * px * co * ((6 * c0 + 9 * c1) if c1 else 9 * c0)
         ms = float(avg_ms[i + 1])
         sym, nblocks = U.oidn_unet_layer_kernel(9, i, tw, th, U.OIDN_F16)
+        nblocks *= nbatch
         conv_flops += flops
         conv_ms += ms
         g = groups.setdefault(sym, {"flops": 0.0, "ms": 0.0, "launches": 0})
@@ -275,8 +278,8 @@ def main():
                                   f"{every}-th timed step; the other steps run without markers"},
         "config": {"workload": f"UNet denoise {W}x{H}, {len(tiles)} tile(s) of {tw}x{th}, HDR log "
                                "transfer, 9-channel input, fp16 storage / fp32 accumulate",
-                   "width": W, "height": H, "tiles": len(tiles), "max_tile": args.max_tile,
-                   "overlap": args.overlap},
+                   "width": W, "height": H, "tiles": len(tiles), "tiles_per_launch": nbatch,
+                   "max_tile": args.max_tile, "overlap": args.overlap},
         "conv_tflops": round(conv_flops / conv_ms / 1e9, 1),
         "conv_mfma_frac": round(conv_flops / conv_ms / 1e9 / PEAK_F16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "kernel": sym, "launches_per_step": g["launches"],

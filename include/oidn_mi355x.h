@@ -274,9 +274,19 @@ int oidn_unet_forward_packed(const void* d_weights, int in_channels, const void*
                              int tw, int th, void* workspace, size_t ws_bytes,
                              float* net_out_rgba, int dtype, hipStream_t stream);
 
-/* Workspace for oidn_unet_forward on a w x h image with this tile plan. */
+/* Workspace for oidn_unet_forward on a w x h image with this tile plan
+ * (on the fp16 path one copy of the per-tile plan for each tile of a batch,
+ * see oidn_unet_tile_batch). */
 int oidn_unet_workspace_bytes(int in_channels, int w, int h, int max_tile, int overlap,
                               int dtype, size_t* bytes);
+
+/* Tiles of this plan that oidn_unet_forward runs through the network
+ * together: on the fp16 path, where both image passes run inside the first
+ * and last convs, up to 16 consecutive tiles of one size share one launch
+ * per layer (tile index in grid z); else 1.  The per-kernel events of
+ * oidn_unet_forward_timed cover the first such batch.  Host only. */
+int oidn_unet_tile_batch(int in_channels, int w, int h, int max_tile, int overlap, int dtype,
+                         int* batch);
 
 /* End-to-end denoise ([webgpu-0.6] recordDenoiseExecution): plan the tile
  * grid, then for each tile in order: input pass, network, output pass into
@@ -291,7 +301,7 @@ int oidn_unet_forward(const void* d_weights, int in_channels, const float* color
                       hipStream_t stream);
 
 /* Same as oidn_unet_forward, and records events[k] on the stream before the
- * k-th kernel of the FIRST tile (k = 0: input pass, 1..16: layers, 17: output
+ * k-th kernel of the FIRST tile or tile batch (k = 0: input pass, 1..16: layers, 17: output
  * pass) and events[18] after it, for per-kernel timing.  Where the first
  * layer's kernel runs the input pass itself (layer kernel input bit 1),
  * events[0] and events[1] are recorded back to back; where the last layer's

@@ -187,6 +187,23 @@ def test_workspace_plan_is_liveness_bounded():
     assert full >= 1920 * 1088 * (12 * 2 + 16)
 
 
+def test_tile_batch_and_its_workspace():
+    """The fp16 end-to-end path runs up to 16 same-size tiles per launch, each
+    with its own copy of the per-tile plan; fp32 runs tiles one by one."""
+    F, F32 = U.OIDN_F16, U.OIDN_F32
+    cases = [((3840, 2160, 1024, 32), 12), ((1920, 1080, 0, 32), 1), ((400, 272, 224, 96), 16),
+             ((200, 150, 128, 32), 12)]
+    for (w, h, mt, ov), want in cases:
+        tiles = U.oidn_plan_tiles(w, h, mt, ov)
+        assert U.oidn_unet_tile_batch(9, w, h, mt, ov, F) == min(len(tiles), 16) == want
+        assert U.oidn_unet_tile_batch(9, w, h, mt, ov, F32) == 1
+        one = U.oidn_unet_workspace_bytes(9, w, h, mt, ov, F) // want
+        assert U.oidn_unet_workspace_bytes(9, w, h, mt, ov, F) == one * want
+        assert one % 256 == 0 and one >= tiles[0][2] * tiles[0][3] * 16 * 2
+    with pytest.raises(U.OidnError):
+        U.oidn_unet_tile_batch(7, 64, 64, 0, 32, F)
+
+
 def _a256(n):
     return -(-n // 256) * 256
 

@@ -41,7 +41,8 @@ EXPORTS = (
     "oidn_conv3x3_pair", "oidn_conv3x3_kernel", "oidn_unet_layer_count", "oidn_unet_layer_info", "oidn_unet_layer_kernel",
     "oidn_unet_weights_bytes",
     "oidn_unet_pack_weights", "oidn_unet_packed_workspace_bytes", "oidn_unet_forward_packed",
-    "oidn_unet_workspace_bytes", "oidn_unet_forward", "oidn_unet_forward_timed",
+    "oidn_unet_workspace_bytes", "oidn_unet_tile_batch", "oidn_unet_forward",
+    "oidn_unet_forward_timed",
     "oidn_event_create", "oidn_event_destroy", "oidn_event_elapsed_ms",
 )
 
@@ -89,6 +90,7 @@ _SIGS = {
     "oidn_unet_packed_workspace_bytes": ([_i, _i, _i, _i, ctypes.POINTER(_sz)], _i),
     "oidn_unet_forward_packed": ([_vp, _i, _vp, _i, _i, _vp, _sz, _vp, _i, _vp], _i),
     "oidn_unet_workspace_bytes": ([_i, _i, _i, _i, _i, _i, ctypes.POINTER(_sz)], _i),
+    "oidn_unet_tile_batch": ([_i, _i, _i, _i, _i, _i, ctypes.POINTER(_i)], _i),
     "oidn_unet_forward": ([_vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp, _i,
                            _vp], _i),
     "oidn_unet_forward_timed": ([_vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp,
@@ -327,6 +329,13 @@ def oidn_unet_workspace_bytes(in_channels: int, w: int, h: int, max_tile: int, o
     n = _sz()
     _check(lib().oidn_unet_workspace_bytes(in_channels, w, h, max_tile, overlap, dtype,
                                            ctypes.byref(n)))
+    return n.value
+
+
+def oidn_unet_tile_batch(in_channels: int, w: int, h: int, max_tile: int, overlap: int,
+                         dtype: int) -> int:
+    n = _i()
+    _check(lib().oidn_unet_tile_batch(in_channels, w, h, max_tile, overlap, dtype, ctypes.byref(n)))
     return n.value
 
 

@@ -222,9 +222,11 @@ ConvF16Args f16_args(int cin0, int cin1, int cout, int h, int w, int cs0, int cs
 
 // Validates and launches one conv.  Pointers already checked by the caller.
 // cs0/cs1: stored channels per pixel of the sources (0 = 4 * ceil(cin / 4)).
+// batch, bstride (fp16): that many tiles, each at + b * bstride bytes.
 int run_conv(const void* src0, int cin0, const void* src1, int cin1, bool upcat, int h, int w,
              const void* wpk, void* y, int cout, int in_dtype, int out_dtype, unsigned flags,
-             hipStream_t stream, int cs0 = 0, int cs1 = 0, int tap_src = -1) {
+             hipStream_t stream, int cs0 = 0, int cs1 = 0, int tap_src = -1, int batch = 1,
+             size_t bstride = 0) {
   const bool pool = flags & OIDN_POOL2X2, relu = flags & OIDN_RELU;
   hipError_t e;
   if (in_dtype == OIDN_F16) {
@@ -235,8 +237,11 @@ int run_conv(const void* src0, int cin0, const void* src1, int cin1, bool upcat,
     a.bias = static_cast<const float*>(wpk);
     a.wfrag = static_cast<const unsigned char*>(wpk) + L.bias_bytes;
     a.y = y;
+    a.batch = batch;
+    a.bstride = bstride;
     e = launch_conv_f16(a, L.nf, upcat, pool, relu, out_dtype == OIDN_F32, stream);
   } else {
+    if (batch != 1) return fail(OIDN_E_UNSUPPORTED, "batched fp32 convs");
     ConvF32Args a{};
     a.src0 = static_cast<const float*>(src0);
     a.src1 = static_cast<const float*>(src1);
@@ -293,9 +298,12 @@ bool pair_supported(int cin, int cs, int cout) {
 // img: the network's last pair writes through the output pass instead of y.
 // in_pass: the network's first pair reads the images through the input pass
 // (instead of x) and writes the packed tile to in_pass->packed.
+// batch, bstride, rects: that many tiles, activations at + b * bstride bytes,
+// rects[b] the input pass origin / output pass rectangle of tile b.
 int run_pair(const void* x, int cin, int cs, int h, int w, const void* wA, const void* wB, void* y,
              int cout, int out_dtype, unsigned flags, hipStream_t stream, bool tap = false,
-             const OutputPass* img = nullptr, const PackArgs* in_pass = nullptr) {
+             const OutputPass* img = nullptr, const PackArgs* in_pass = nullptr, int batch = 1,
+             size_t bstride = 0, const TileRect* rects = nullptr) {
   ConvLayout LA, LB;
   conv_f16_layout(stored_channels(cin), 0, 32, &LA, tap ? 0 : -1);
   conv_f16_layout(32, 0, cout, &LB);
@@ -314,6 +322,11 @@ int run_pair(const void* x, int cin, int cs, int h, int w, const void* wA, const
   p.cout_stored = stored_channels(cout);
   if (img) p.img = *img;
   if (in_pass) p.in = *in_pass;
+  if (batch < 1 || batch > kMaxBatch || ((img || in_pass) && !rects))
+    return fail(OIDN_E_INVALID, "bad tile batch");
+  p.batch = batch;
+  p.bstride = bstride;
+  for (int b = 0; rects && b < batch; ++b) p.rect[b] = rects[b];
   const int out = img ? kPairImage : out_dtype == OIDN_F32 ? kPairF32 : kPairF16;
   const int in = (tap ? kPairInTaps : 0) | (in_pass ? kPairInImages : 0);
   hipError_t e = launch_conv_pair_f16(p, LA.chunk[0].cg, LB.nf, in, flags & OIDN_POOL2X2,
@@ -453,6 +466,14 @@ bool input_fused(int in_channels, int dtype) {
          stored_channels(in_channels) <= 16;
 }
 
+// Tiles the end-to-end path runs through the network together: up to
+// kMaxBatch tiles of one size when both image passes run inside the convs
+// (the fp16 path), else one.
+int tile_batch(int in_channels, int dtype, size_t ntiles) {
+  if (!input_fused(in_channels, dtype) || !output_fused(in_channels, dtype)) return 1;
+  return ntiles < (size_t)kMaxBatch ? (int)ntiles : kMaxBatch;
+}
+
 void plan_workspace(int in_channels, int tw, int th, int dtype, bool own_io, Plan* p) {
   LayerShape s[kLayers];
   unet_shapes(in_channels, s);
@@ -518,14 +539,17 @@ void plan_workspace(int in_channels, int tw, int th, int dtype, bool own_io, Pla
   p->bytes = end;
 }
 
-// Runs the sixteen convs of one tile.  events: optional, events[k] recorded
-// before layer k and events[16] after the last layer.  img (own_io, with
-// output_fused): the output pass of this tile, run by the last pair;
+// Runs the sixteen convs of one tile, or of `batch` tiles of one size
+// together (each with its own copy of the plan at + b * P.bytes; needs both
+// image passes fused, rects[b] their rectangles).  events: optional,
+// events[k] recorded before layer k and events[16] after the last layer.
+// img (own_io, with output_fused): the output pass, run by the last pair;
 // in_pass (own_io, with input_fused): the input pass, run by the first.
 int run_network(const unsigned char* weights, int in_channels, const void* packed_in, int tw,
                 int th, unsigned char* ws, const Plan& P, bool own_io, float* net_out, int dtype,
                 hipStream_t stream, void* const* events, const OutputPass* img = nullptr,
-                const PackArgs* in_pass = nullptr) {
+                const PackArgs* in_pass = nullptr, int batch = 1, const TileRect* rects = nullptr) {
+  const size_t bstride = batch > 1 ? P.bytes : 0;   // each tile has its own copy of the plan
   LayerShape s[kLayers];
   unet_shapes(in_channels, s);
   const void* val[kLayers + 1];
@@ -556,7 +580,7 @@ int run_network(const unsigned char* weights, int in_channels, const void* packe
                         weights + woff + align256(ba), const_cast<void*>(val[i + 2]),
                         s[i + 1].cout, i + 1 == kLayers - 1 ? OIDN_F32 : dtype, flags_b, stream,
                         tap_src == 0, i + 1 == kLayers - 1 ? img : nullptr,
-                        i == 0 ? in_pass : nullptr);
+                        i == 0 ? in_pass : nullptr, batch, bstride, rects);
       if (rc) return rc;
       if (events && events[i + 1]) {   // the second layer's interval is empty
         hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[i + 1]), stream);
@@ -569,7 +593,7 @@ int run_network(const unsigned char* weights, int in_channels, const void* packe
     int rc = run_conv(val[L.src], s[i].cin0, L.skip >= 0 ? val[L.skip] : nullptr, s[i].cin1,
                       L.skip >= 0, h, w, wl, const_cast<void*>(val[i + 1]), s[i].cout, dtype,
                       out_dtype, flags, stream, L.src == 0 ? in_cs : 0, L.skip == 0 ? in_cs : 0,
-                      tap_src);
+                      tap_src, batch, bstride);
     if (rc) return rc;
     size_t b = 0;
     conv_weights_bytes(s[i].cin0, s[i].cin1, s[i].cout, dtype, &b);
@@ -626,9 +650,58 @@ int denoise(const void* d_weights, int in_channels, const float* color, const fl
   if (rc) return rc;
   Plan P;
   plan_workspace(in_channels, tw, th, dtype, true, &P);
-  if (ws_bytes < P.bytes)
-    return fail(OIDN_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, P.bytes);
+  const int nb = tile_batch(in_channels, dtype, tiles.size());
+  if (ws_bytes < P.bytes * nb)
+    return fail(OIDN_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
+                P.bytes * nb);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
+  if (input_fused(in_channels, dtype) && output_fused(in_channels, dtype)) {
+    // batches of up to nb consecutive tiles of one size, both image passes
+    // in the convs (the fp16 path)
+    PackArgs pa{};
+    pa.color = reinterpret_cast<const float4*>(color);
+    pa.albedo = reinterpret_cast<const float4*>(albedo);
+    pa.normal = reinterpret_cast<const float4*>(normal);
+    pa.img_w = w;
+    pa.img_h = h;
+    pa.hdr = hdr;
+    pa.input_scale = input_scale;
+    pa.sources = sources;
+    pa.lanes = internal_input_lanes(in_channels, dtype);
+    pa.taps = unet_taps(in_channels, dtype) && pa.lanes == 16;
+    pa.packed = ws + P.offset[0];
+    OutputPass op{};
+    op.color = reinterpret_cast<const float4*>(color);
+    op.out = reinterpret_cast<float4*>(out_rgba);
+    op.img_w = w;
+    op.hdr = hdr;
+    op.input_scale = input_scale;
+    for (size_t k = 0; k < tiles.size();) {
+      const oidn_tile& t0 = tiles[k];
+      TileRect rects[kMaxBatch];
+      int n = 0;
+      while (k + n < tiles.size() && n < nb && tiles[k + n].in_w == t0.in_w &&
+             tiles[k + n].in_h == t0.in_h) {
+        const oidn_tile& t = tiles[k + n];
+        rects[n++] = TileRect{t.in_x, t.in_y, t.out_x, t.out_y, t.out_w, t.out_h};
+      }
+      void* const* ev = (events && k == 0) ? events : nullptr;
+      hipError_t e;
+      if (ev && ev[0] && (e = hipEventRecord(static_cast<hipEvent_t>(ev[0]), stream)) != hipSuccess)
+        return hip_fail(e, "hipEventRecord");
+      pa.tile_w = t0.in_w;
+      pa.tile_h = t0.in_h;
+      rc = run_network(static_cast<const unsigned char*>(d_weights), in_channels, nullptr, t0.in_w,
+                       t0.in_h, ws, P, true, nullptr, dtype, stream, ev ? ev + 1 : nullptr, &op,
+                       &pa, n, rects);
+      if (rc) return rc;
+      if (ev && ev[kLayers + 2] &&
+          (e = hipEventRecord(static_cast<hipEvent_t>(ev[kLayers + 2]), stream)) != hipSuccess)
+        return hip_fail(e, "hipEventRecord");
+      k += n;
+    }
+    return ok();
+  }
   for (size_t k = 0; k < tiles.size(); ++k) {
     const oidn_tile& t = tiles[k];
     void* const* ev = (events && k == 0) ? events : nullptr;
@@ -651,33 +724,26 @@ int denoise(const void* d_weights, int in_channels, const float* color, const fl
     pa.lanes = internal_input_lanes(in_channels, dtype);
     pa.taps = unet_taps(in_channels, dtype) && pa.lanes == 16;
     pa.packed = ws + P.offset[0];
-    const bool in_fused = input_fused(in_channels, dtype);
-    if (!in_fused && (e = launch_pack(pa, dtype == OIDN_F16, stream)) != hipSuccess)
-      return hip_fail(e, "pack launch");
-    OutputPass op{};
-    op.color = reinterpret_cast<const float4*>(color);
-    op.out = reinterpret_cast<float4*>(out_rgba);
-    op.img_w = w;
-    op.in_off_x = t.out_x - t.in_x;
-    op.in_off_y = t.out_y - t.in_y;
-    op.out_x = t.out_x;
-    op.out_y = t.out_y;
-    op.out_w = t.out_w;
-    op.out_h = t.out_h;
-    op.hdr = hdr;
-    op.input_scale = input_scale;
-    const bool fused = output_fused(in_channels, dtype);
+    // input pass, network with a stored float32 output, output pass (fp32)
+    if ((e = launch_pack(pa, dtype == OIDN_F16, stream)) != hipSuccess) return hip_fail(e, "pack launch");
     rc = run_network(static_cast<const unsigned char*>(d_weights), in_channels, nullptr, t.in_w,
-                     t.in_h, ws, P, true, nullptr, dtype, stream, ev ? ev + 1 : nullptr,
-                     fused ? &op : nullptr, in_fused ? &pa : nullptr);
+                     t.in_h, ws, P, true, nullptr, dtype, stream, ev ? ev + 1 : nullptr);
     if (rc) return rc;
-    if (!fused) {
-      UnpackArgs ua{};
-      ua.net = reinterpret_cast<const float4*>(ws + P.offset[kLayers]);
-      ua.tile_w = t.in_w;
-      ua.o = op;
-      if ((e = launch_unpack(ua, stream)) != hipSuccess) return hip_fail(e, "unpack launch");
-    }
+    UnpackArgs ua{};
+    ua.net = reinterpret_cast<const float4*>(ws + P.offset[kLayers]);
+    ua.tile_w = t.in_w;
+    ua.o.color = reinterpret_cast<const float4*>(color);
+    ua.o.out = reinterpret_cast<float4*>(out_rgba);
+    ua.o.img_w = w;
+    ua.o.in_off_x = t.out_x - t.in_x;
+    ua.o.in_off_y = t.out_y - t.in_y;
+    ua.o.out_x = t.out_x;
+    ua.o.out_y = t.out_y;
+    ua.o.out_w = t.out_w;
+    ua.o.out_h = t.out_h;
+    ua.o.hdr = hdr;
+    ua.o.input_scale = input_scale;
+    if ((e = launch_unpack(ua, stream)) != hipSuccess) return hip_fail(e, "unpack launch");
     if (ev && ev[kLayers + 2] && (e = hipEventRecord(static_cast<hipEvent_t>(ev[kLayers + 2]), stream)) != hipSuccess)
       return hip_fail(e, "hipEventRecord");
   }
@@ -1080,7 +1146,21 @@ int oidn_unet_workspace_bytes(int in_channels, int w, int h, int max_tile, int o
   if (rc) return rc;
   Plan P;
   plan_workspace(in_channels, tw, th, dtype, true, &P);
-  *bytes = P.bytes;
+  *bytes = P.bytes * tile_batch(in_channels, dtype, tiles.size());
+  return ok();
+}
+
+int oidn_unet_tile_batch(int in_channels, int w, int h, int max_tile, int overlap, int dtype,
+                         int* batch) {
+  if (!batch) return fail(OIDN_E_INVALID, "null batch pointer");
+  std::vector<oidn_tile> tiles;
+  int rc = plan(w, h, max_tile, overlap, tiles);
+  if (rc) return rc;
+  LayerShape s[kLayers];
+  if (!unet_shapes(in_channels, s)) return fail(OIDN_E_INVALID, "input channels must be 3, 6 or 9");
+  rc = check_dtype(dtype);
+  if (rc) return rc;
+  *batch = tile_batch(in_channels, dtype, tiles.size());
   return ok();
 }
 

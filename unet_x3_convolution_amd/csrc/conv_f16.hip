@@ -409,7 +409,7 @@ __device__ __forceinline__ void store_pixel(void* y, size_t pix, const int (&cha
 // Pixels at or past column xend (<= the image width) are not stored.
 template <int NFW, int R, bool OUTF32>
 __device__ __forceinline__ void store_tile(const floatx4 (&acc)[R][NFW], const ConvF16Args& a,
-                                           int q0, int g, int yb, int x, int c, int pool,
+                                           void* y, int q0, int g, int yb, int x, int c, int pool,
                                            int relu, int xend) {
   const int nf = a.nf;
   int chan[NFW];
@@ -435,7 +435,7 @@ __device__ __forceinline__ void store_tile(const floatx4 (&acc)[R][NFW], const C
         for (int q = 0; q < NFW; ++q)
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[q][i] = act(acc[r][q][i] + bv[q][i], relu);
-        store_pixel<NFW, OUTF32>(a.y, ((size_t)yy * a.w + x) * a.cout_stored, chan, lead, tail,
+        store_pixel<NFW, OUTF32>(y, ((size_t)yy * a.w + x) * a.cout_stored, chan, lead, tail,
                                  a.cout_stored, v);
       }
     }
@@ -453,7 +453,7 @@ __device__ __forceinline__ void store_tile(const floatx4 (&acc)[R][NFW], const C
         }
       const int yy = yb + 2 * rp;
       if ((c & 1) == 0 && yy < a.h && x < xend)
-        store_pixel<NFW, OUTF32>(a.y, ((size_t)(yy >> 1) * ow + (x >> 1)) * a.cout_stored, chan,
+        store_pixel<NFW, OUTF32>(y, ((size_t)(yy >> 1) * ow + (x >> 1)) * a.cout_stored, chan,
                                  lead, tail, a.cout_stored, m);
     }
   }
@@ -529,6 +529,13 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
   int tx, ty;
   if (!tile_of_block(blockIdx.x, a.tiles_x, a.tiles_y, tx, ty)) return;
   const int y0 = ty * T::TH, x0 = tx * TW;
+  // this tile of the batch (locals: writing to `a` would copy all of it,
+  // chunk table included, to scratch)
+  const size_t boff = (size_t)blockIdx.z * a.bstride;
+  const _Float16* const src0 = reinterpret_cast<const _Float16*>(static_cast<const char*>(a.src0) + boff);
+  const _Float16* const src1 =
+      a.src1 ? reinterpret_cast<const _Float16*>(static_cast<const char*>(a.src1) + boff) : nullptr;
+  void* const ydst = static_cast<char*>(a.y) + boff;
 
   if (tid < 2) reinterpret_cast<uint2*>(lds + ZERO)[tid] = make_uint2(0u, 0u);
 
@@ -561,7 +568,7 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
 #define OIDN_UP_LOOP(K, CG)                                                                     \
   _Pragma("unroll 1") for (int ci = bounds[K]; ci < bounds[K + 1]; ++ci) {                      \
     const ConvChunk ch = a.chunk[ci];                                                           \
-    const _Float16* src = static_cast<const _Float16*>(a.src0);                                 \
+    const _Float16* src = src0;                                                                 \
     __syncthreads();                                                                            \
     if ((a.cs0 & 7) == 0)                                                                       \
       stage_patch_direct<T::TH, 4, T::PATCH / 8, CG, true, SW>(reinterpret_cast<uint4*>(lds),    \
@@ -581,7 +588,7 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
 #define OIDN_CHUNK_LOOP(K, CG, TAP)                                                             \
   _Pragma("unroll 1") for (int ci = bounds[K]; ci < bounds[K + 1]; ++ci) {                      \
     const ConvChunk ch = a.chunk[ci];                                                           \
-    const _Float16* src = static_cast<const _Float16*>(ch.src ? a.src1 : a.src0);               \
+    const _Float16* src = ch.src ? src1 : src0;                                                 \
     const int cs = ch.src ? a.cs1 : a.cs0;                                                      \
     const uint4* wnext = ci + 1 < a.nchunks ? wf + (size_t)a.chunk[ci + 1].wfrag * 64 : nullptr; \
     __syncthreads();                                                                            \
@@ -612,7 +619,7 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
 #undef OIDN_UP_LOOP
   (void)upcat;
 
-  store_tile<NFW, R, OUTF32>(acc, a, q0, g, y0 + R * rg, x0 + c, c, pool, relu, a.w);
+  store_tile<NFW, R, OUTF32>(acc, a, ydst, q0, g, y0 + R * rg, x0 + c, c, pool, relu, a.w);
 }
 
 template <int NFW, int R, int WR>
@@ -621,7 +628,7 @@ hipError_t launch_shape(ConvF16Args a, int nsplit, bool upcat, bool pool, bool r
   a.tiles_x = cdiv(a.w, TW);
   a.tiles_y = cdiv(a.h, WR * R);
   const int ntiles = a.tiles_x * a.tiles_y;
-  const dim3 grid(cdiv(ntiles, kXcds) * kXcds, nsplit), block(THREADS);
+  const dim3 grid(cdiv(ntiles, kXcds) * kXcds, nsplit, a.batch > 1 ? a.batch : 1), block(THREADS);
   if (out_f32)
     hipLaunchKernelGGL((conv3x3_f16_mfma<NFW, R, WR, true>), grid, block, 0, stream, a,
                        (int)upcat, (int)pool, (int)relu);
@@ -798,33 +805,31 @@ constexpr int kPairWaves = IN == (kPairInImages | kPairInTaps) ? 4 : CGA == 2 ? 
 // fp32 from lane group 0.  `alpha` holds the input colour's alpha of those
 // rows, loaded at the start of the kernel (see image_alpha).
 template <int R>
-__device__ __forceinline__ bool image_index(const PairArgs& p, int g, int k, int yb, int x, int xend,
-                                            size_t& i) {
-  const OutputPass& o = p.img;
+__device__ __forceinline__ bool image_index(const OutputPass& o, int h, int g, int k, int yb, int x,
+                                            int xend, size_t& i) {
   const int y = yb + g + 4 * k;
   const int lx = x - o.in_off_x, ly = y - o.in_off_y;
-  if (x >= xend || y >= p.h || lx < 0 || lx >= o.out_w || ly < 0 || ly >= o.out_h) return false;
+  if (x >= xend || y >= h || lx < 0 || lx >= o.out_w || ly < 0 || ly >= o.out_h) return false;
   i = (size_t)(ly + o.out_y) * o.img_w + lx + o.out_x;
   return true;
 }
 
 template <int R>
-__device__ __forceinline__ void image_alpha(float (&alpha)[R / 4], const PairArgs& p, int g, int yb,
-                                            int x, int xend) {
+__device__ __forceinline__ void image_alpha(float (&alpha)[R / 4], const OutputPass& o, int h, int g,
+                                            int yb, int x, int xend) {
 #pragma unroll
   for (int k = 0; k < R / 4; ++k) {
     size_t i;
-    alpha[k] = image_index<R>(p, g, k, yb, x, xend, i) ? p.img.color[i].w : 0.f;
+    alpha[k] = image_index<R>(o, h, g, k, yb, x, xend, i) ? o.color[i].w : 0.f;
   }
 }
 
 template <int R>
 __device__ __forceinline__ void store_image(const floatx4 (&acc)[R][1], const float (&alpha)[R / 4],
-                                            const PairArgs& p, int g, int yb, int x, int xend,
-                                            int relu) {
+                                            const OutputPass& o, const float* bias, int h, int g,
+                                            int yb, int x, int xend, int relu) {
   static_assert(R % 4 == 0, "rows are spread over the four lane groups");
-  const OutputPass& o = p.img;
-  const float b0 = p.biasB[4 * g], b1 = p.biasB[4 * g + 1], b2 = p.biasB[4 * g + 2];
+  const float b0 = bias[4 * g], b1 = bias[4 * g + 1], b2 = bias[4 * g + 2];
 #pragma unroll
   for (int k = 0; k < R / 4; ++k) {
     // row g + 4 k of this lane's column, chosen by selects (a loop of
@@ -832,7 +837,7 @@ __device__ __forceinline__ void store_image(const floatx4 (&acc)[R][1], const fl
     const floatx4 v = g == 0 ? acc[4 * k][0] : g == 1 ? acc[4 * k + 1][0]
                     : g == 2 ? acc[4 * k + 2][0] : acc[4 * k + 3][0];
     size_t i;
-    if (!image_index<R>(p, g, k, yb, x, xend, i)) continue;
+    if (!image_index<R>(o, h, g, k, yb, x, xend, i)) continue;
     o.out[i] = output_pixel(act(v[0] + b0, relu), act(v[1] + b1, relu), act(v[2] + b2, relu),
                             alpha[k], o.hdr, o.input_scale);
   }
@@ -863,8 +868,22 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA, IN>)) void conv3x3_pair_f
   if (tid < 2) reinterpret_cast<uint2*>(lds + L::ZERO)[tid] = make_uint2(0u, 0u);
   constexpr int RB = PAIR_TH / 2;                 // convB rows per wave
   const int xend = x0 + PAIR_TW < p.w ? x0 + PAIR_TW : p.w;
+  // this tile of the batch: activations at its offset, its image rectangle
+  const int bt = blockIdx.z;
+  const size_t boff = (size_t)bt * p.bstride;
+  OutputPass img = p.img;
+  if constexpr (OUT == kPairImage) {
+    const TileRect& t = p.rect[bt];
+    img.in_off_x = t.out_x - t.in_x;
+    img.in_off_y = t.out_y - t.in_y;
+    img.out_x = t.out_x;
+    img.out_y = t.out_y;
+    img.out_w = t.out_w;
+    img.out_h = t.out_h;
+  }
   float alpha[OUT == kPairImage ? RB / 4 : 1];
-  if constexpr (OUT == kPairImage) image_alpha<RB>(alpha, p, g, y0 + RB * rh, x0 + 16 * cf + c, xend);
+  if constexpr (OUT == kPairImage)
+    image_alpha<RB>(alpha, img, p.h, g, y0 + RB * rh, x0 + 16 * cf + c, xend);
 
   // convA's biases for this lane: lane group g of the pair of fragments owns
   // channels 8 g .. 8 g + 7 (one 16-byte slot of the intermediate).  Read
@@ -896,12 +915,16 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA, IN>)) void conv3x3_pair_f
     };
     // (with the input pass the image registers come first)
     if constexpr (!WL && !IMG) load_a();
-    const _Float16* src = static_cast<const _Float16*>(p.x);
+    const _Float16* src = reinterpret_cast<const _Float16*>(static_cast<const char*>(p.x) + boff);
     const uint4* wl = reinterpret_cast<const uint4*>(lds + L::WOFF) + lane;
     if constexpr (IMG) {
       // one chunk: straight-line code (in the chunk loop the compiler keeps
       // the staging's addresses live across it and spills them)
-      stage_pair_images<TAP>(reinterpret_cast<uint4*>(lds), p.in, p.h, p.w, y0, x0, tid);
+      PackArgs in = p.in;
+      in.tile_x = p.rect[bt].in_x;
+      in.tile_y = p.rect[bt].in_y;
+      in.packed = static_cast<char*>(in.packed) + boff;
+      stage_pair_images<TAP>(reinterpret_cast<uint4*>(lds), in, p.h, p.w, y0, x0, tid);
       load_a();
       __syncthreads();
       mma_chunk<2, RA, CGA, true, PAIR_PW, false, TAP>(acc, acur, lds, 0, L::ZERO, wf, nullptr, 2,
@@ -988,16 +1011,17 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA, IN>)) void conv3x3_pair_f
     }
   }
   if constexpr (OUT == kPairImage) {
-    store_image<RB>(accb, alpha, p, g, y0 + RB * rh, x0 + 16 * cf + c, xend, relu);
+    store_image<RB>(accb, alpha, img, p.biasB, p.h, g, y0 + RB * rh, x0 + 16 * cf + c, xend, relu);
   } else {
     ConvF16Args a{};
     a.h = p.h;
     a.w = p.w;
     a.bias = p.biasB;
-    a.y = p.y;
+    a.y = nullptr;
     a.cout_stored = p.cout_stored;
     a.nf = NFB;
-    store_tile<NFB, RB, OUT == kPairF32>(accb, a, 0, g, y0 + RB * rh, x0 + 16 * cf + c, c, pool,
+    store_tile<NFB, RB, OUT == kPairF32>(accb, a, static_cast<char*>(p.y) + boff, 0, g,
+                                         y0 + RB * rh, x0 + 16 * cf + c, c, pool,
                                          relu, xend);
   }
 }
@@ -1006,7 +1030,8 @@ template <int CGA, int NFB, int IN>
 hipError_t launch_pair_shape(PairArgs p, bool pool, bool relu, int out, hipStream_t stream) {
   p.tiles_x = cdiv(p.w, PAIR_TW);
   p.tiles_y = cdiv(p.h, PAIR_TH);
-  const dim3 grid(cdiv(p.tiles_x * p.tiles_y, kXcds) * kXcds), block(THREADS);
+  const dim3 grid(cdiv(p.tiles_x * p.tiles_y, kXcds) * kXcds, 1, p.batch > 1 ? p.batch : 1),
+      block(THREADS);
   if (out == kPairF32) {
     hipLaunchKernelGGL((conv3x3_pair_f16<CGA, NFB, kPairF32, IN>), grid, block, 0, stream, p,
                        (int)pool, (int)relu);
@@ -1159,6 +1184,7 @@ void conv_f16_describe(const ConvF16Args& a, int nf, bool out_f32, char* buf, in
 
 hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, bool relu,
                            bool out_f32, hipStream_t stream) {
+  if (a.batch > 65535) return hipErrorInvalidValue;
   ConvF16Args b = a;
   b.nf = nf;
   const ConvPlan P = conv_f16_plan(a.h, a.w, nf, a.nchunks, a.nup);
@@ -1168,6 +1194,7 @@ hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, 
 
 hipError_t launch_conv_pair_f16(const PairArgs& p, int cga, int nfb, int in, bool pool,
                                 bool relu, int out, hipStream_t stream) {
+  if (p.batch > kMaxBatch) return hipErrorInvalidValue;
   if (in & kPairInImages) {
     // the network's first pair: 16-lane input chunk, 32 -> 32 (pool)
     if (cga != 2 || nfb != 2 || !p.in.color || !p.in.packed) return hipErrorInvalidValue;

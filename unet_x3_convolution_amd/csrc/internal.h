@@ -95,6 +95,8 @@ struct ConvF16Args {
   int nchunks;
   int nup4, nup, npl4;   // chunk ranges of the kernel's loops (see ConvLayout)
   int ntap;
+  int batch;          // tiles in the launch (grid z), >= 1
+  size_t bstride;     // bytes between tiles for src0, src1 and y (0 if batch == 1)
   ConvChunk chunk[kMaxChunks];
 };
 
@@ -115,6 +117,17 @@ int conv_f16_blocks(int h, int w, int nf, int nchunks, int nup);
 // cs0, cs1 and the chunk fields set) and its grid.
 void conv_f16_describe(const ConvF16Args& a, int nf, bool out_f32, char* buf, int cap,
                        int* blocks);
+
+// Tiles of one size run through the network together: one launch per layer
+// with the tile index in grid z, each tile's activations at its own byte
+// offset (batch stride) in the workspace.
+constexpr int kMaxBatch = 16;
+
+// A tile's input window origin and output rectangle in the image.
+struct TileRect {
+  int in_x, in_y;
+  int out_x, out_y, out_w, out_h;
+};
 
 // Output pass of one tile ([webgpu-0.6] outputShader): the network's pixel
 // (y, x) in tile coordinates lands on image pixel (y - in_off_y + out_y,
@@ -169,6 +182,9 @@ struct PairArgs {
   OutputPass img;          // out == kPairImage (cga 4, nfb 1, convB without ReLU)
   PackArgs in;             // in & kPairInImages (cga 2, nfb 2): x is not read, the
                            // packed tile is written to in.packed
+  int batch;               // tiles in the launch (grid z), >= 1
+  size_t bstride;          // bytes between tiles for x, y and in.packed
+  TileRect rect[kMaxBatch];  // per tile: in.tile_x/y and img's rectangle (images only)
 };
 // in: PairIn bits (kPairInTaps: convA's one chunk is a tap chunk, cga 2);
 // out: a PairOut.
