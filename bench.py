@@ -124,6 +124,8 @@ def main():
     ap.add_argument("--height", type=int, default=1080)
     ap.add_argument("--max-tile", type=int, default=0)
     ap.add_argument("--overlap", type=int, default=32)
+    ap.add_argument("--dtype", choices=["f16", "bf16"], default="f16",
+                    help="16-bit storage of the network (the metric is quoted on f16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--events-every", type=int, default=10,
                     help="record per-kernel HIP events on every N-th timed step (event markers "
@@ -154,25 +156,26 @@ def main():
     ws, bs = S.layer_params(r, U.unet_layer_shapes(9))
     dev = lambda a: torch.from_numpy(a).cuda()
     d_color, d_albedo, d_normal = dev(color), dev(albedo), dev(normal)
-    wbuf = torch.empty(U.oidn_unet_weights_bytes(9, U.OIDN_F16), dtype=torch.uint8, device="cuda")
-    U.oidn_unet_pack_weights(ws, bs, 9, U.OIDN_F16, wbuf)
-    nbytes = U.oidn_unet_workspace_bytes(9, W, H, args.max_tile, args.overlap, U.OIDN_F16)
+    DTYPE = {"f16": U.OIDN_F16, "bf16": U.OIDN_BF16}[args.dtype]
+    wbuf = torch.empty(U.oidn_unet_weights_bytes(9, DTYPE), dtype=torch.uint8, device="cuda")
+    U.oidn_unet_pack_weights(ws, bs, 9, DTYPE, wbuf)
+    nbytes = U.oidn_unet_workspace_bytes(9, W, H, args.max_tile, args.overlap, DTYPE)
     work = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     out = torch.empty((H, W, 4), dtype=torch.float32, device="cuda")
     tiles = U.oidn_plan_tiles(W, H, args.max_tile, args.overlap)
     tw, th = tiles[0][2], tiles[0][3]
     # tiles per launch: the per-kernel events cover the first batch
-    nbatch = U.oidn_unet_tile_batch(9, W, H, args.max_tile, args.overlap, U.OIDN_F16)
+    nbatch = U.oidn_unet_tile_batch(9, W, H, args.max_tile, args.overlap, DTYPE)
 
     def step(events=None):
         if events is None:
             U.oidn_unet_forward(wbuf, 9, d_color, d_albedo, d_normal, W, H, True,
                                 U.OIDN_TRANSFER_LOG, 1.0, args.max_tile, args.overlap, work,
-                                nbytes, out, U.OIDN_F16)
+                                nbytes, out, DTYPE)
         else:
             U.oidn_unet_forward_timed(wbuf, 9, d_color, d_albedo, d_normal, W, H, True,
                                       U.OIDN_TRANSFER_LOG, 1.0, args.max_tile, args.overlap, work,
-                                      nbytes, out, U.OIDN_F16, events)
+                                      nbytes, out, DTYPE, events)
 
     nk = 18  # input pass, 16 convs, output pass
     every = max(1, args.events_every)
@@ -215,7 +218,7 @@ def main():
         # ky taps pre-summed per row parity), so 6 taps for those c0 channels
         flops = 2.0 * px * co * ((6 * c0 + 9 * c1) if c1 else 9 * c0)
         ms = float(avg_ms[i + 1])
-        sym, nblocks = U.oidn_unet_layer_kernel(9, i, tw, th, U.OIDN_F16)
+        sym, nblocks = U.oidn_unet_layer_kernel(9, i, tw, th, DTYPE)
         nblocks *= nbatch
         conv_flops += flops
         conv_ms += ms
@@ -246,10 +249,10 @@ def main():
     # the first pair may run the input pass in its staging (input bit 1), the
     # last the output pass in its epilogue (output field 2)
     def pair_fields(layer):
-        sym = U.oidn_unet_layer_kernel(9, layer, tw, th, U.OIDN_F16)[0]
-        if not sym.startswith("conv3x3_pair_f16<"):
+        sym = U.oidn_unet_layer_kernel(9, layer, tw, th, DTYPE)[0]
+        if not sym.startswith("conv3x3_pair_"):
             return None
-        return [int(f) for f in sym[len("conv3x3_pair_f16<"):-1].split(", ")]
+        return [int(f) for f in sym[sym.index("<") + 1:-1].split(", ")]
     first, last = pair_fields(0), pair_fields(U.oidn_unet_layer_count() - 1)
     in_fused = first is not None and (first[3] & 2) != 0
     out_fused = last is not None and last[2] == 2
@@ -271,13 +274,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "kernel_timing": {"instrumented_steps": len(inst), "of_steps": args.steps,
                           "note": "HIP events between the launches of every "
                                   f"{every}-th timed step; the other steps run without markers"},
         "config": {"workload": f"UNet denoise {W}x{H}, {len(tiles)} tile(s) of {tw}x{th}, HDR log "
-                               "transfer, 9-channel input, fp16 storage / fp32 accumulate",
+                               f"transfer, 9-channel input, {args.dtype} storage / fp32 accumulate",
                    "width": W, "height": H, "tiles": len(tiles), "tiles_per_launch": nbatch,
                    "max_tile": args.max_tile, "overlap": args.overlap},
         "conv_tflops": round(conv_flops / conv_ms / 1e9, 1),
@@ -313,13 +316,13 @@ def main():
         import threadpoolctl
         t = time.perf_counter()
         O.unet_forward(ws, bs, color, albedo, normal, True, 1.0, args.max_tile, args.overlap,
-                       "f16")
+                       args.dtype)
         dt = time.perf_counter() - t
         threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
         result["cpu_baseline"] = {"value": round(W * H / 1e6 / dt, 4), "unit": "MP/s",
                                   "cores": threads, "kind": "oracle",
                                   "sample": f"the same {W}x{H} frame once, end to end (pack, "
-                                            f"network, unpack), fp16 storage emulated, float64 "
+                                            f"network, unpack), {args.dtype} storage emulated, float64 "
                                             f"sums; {dt:.1f} s"}
     print(json.dumps(result), flush=True)
 

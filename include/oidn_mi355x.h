@@ -21,8 +21,11 @@
  *     any error nothing is enqueued and outputs are untouched;
  *     oidn_last_error() returns the message (thread-local).
  *   - dtype selects the storage type of activations and weights: OIDN_F16
- *     (fp16 storage, fp32 accumulate, MFMA path) or OIDN_F32 (fp32 storage and
- *     arithmetic).  OIDN_BF16 is reserved and returns OIDN_E_UNSUPPORTED.
+ *     (fp16 storage, fp32 accumulate, MFMA path), OIDN_BF16 (bf16 storage,
+ *     the same kernels with the bf16 MFMA; every stored value rounded to
+ *     nearest even from fp32, as fp16 is) or OIDN_F32 (fp32 storage and
+ *     arithmetic).  A conv's 16-bit output has its input's type; any 16-bit
+ *     path may write fp32 instead.  Weights are packed for one dtype.
  *     Biases are always fp32 ([web-0.4] packConvTensors keeps the bias in f32).
  *   - Overlapping calls on different streams that share buffers race; the
  *     caller orders them.
@@ -47,7 +50,7 @@ extern "C" {
 /* ---- storage types ----------------------------------------------------- */
 #define OIDN_F32   0
 #define OIDN_F16   1
-#define OIDN_BF16  2   /* reserved */
+#define OIDN_BF16  2
 
 /* ---- conv flags -------------------------------------------------------- */
 #define OIDN_RELU     1u  /* y = max(y, 0) ([web-0.4] activationExpression)            */
@@ -98,9 +101,9 @@ int oidn_conv3x3_weights_bytes(int cin0, int cin1, int cout, int dtype, size_t* 
 
 /* Packs OHWI float32 weights (cout x 3 x 3 x (cin0 + cin1), host) and a
  * float32 bias (cout, host) into the device layout of the chosen dtype
- * (fp16: MFMA A-operand fragments in K-major chunk order, pad lanes 0, the
+ * (fp16 and bf16: MFMA A-operand fragments in K-major chunk order, pad lanes 0, the
  * upsampled source of a two-source conv as four sums of ky rows -- W0,
- * W1 + W2, W0 + W1, W2, each rounded once to fp16 -- because an output row
+ * W1 + W2, W0 + W1, W2, each rounded once to the storage type -- because an output row
  * reads only two low-resolution rows of it; fp32: [out block][tap][stored
  * input channel][4 out lanes]).  d_packed must hold
  * oidn_conv3x3_weights_bytes() bytes.  Blocks until the upload finished.
@@ -240,18 +243,19 @@ int oidn_unet_layer_info(int in_channels, int layer, int* cin0, int* cin1, int* 
  * buf (cap bytes), e.g. "conv3x3_f16_mfma<2, 16, 2, false>" (fragments and
  * rows per wave, row groups, fp32 output) or, for both layers of a fused
  * pair, "conv3x3_pair_f16<2, 2, 0, 3>" (convA channel groups, convB
- * fragments, output: 0 fp16, 1 fp32, 2 straight through the output pass;
+ * fragments, output: 0 16-bit, 1 fp32, 2 straight through the output pass;
  * input: bit 0 tap-packed, bit 1 the caller's images through the input pass);
- * *blocks receives the launch's workgroup count.  Host only. */
+ * with bf16 storage "conv3x3_bf16_mfma" and "conv3x3_pair_bf16".  *blocks
+ * receives the launch's workgroup count.  Host only. */
 int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int dtype, char* buf,
                            int cap, int* blocks);
 
 /* Bytes of the packed weights of all sixteen layers.  With 9 input channels
- * on the fp16 path the blob also holds a second copy of enc_conv0's and
+ * on the 16-bit paths the blob also holds a second copy of enc_conv0's and
  * dec_conv1a's weights in the layout oidn_unet_forward uses for its
  * tap-packed input (channel 8's row neighbours beside it: half the matrix
  * steps for that source); oidn_unet_forward_packed uses the plain copies.
- * On the fp16 path dec_conv0's one output fragment holds its three output
+ * On the 16-bit paths dec_conv0's one output fragment holds its three output
  * channels' weights and biases in each of its four 4-channel groups (lanes
  * 4g .. 4g + 2, lane 4g + 3 zero), so the output pass fused into that
  * layer's kernel can spread its rows over all lanes; the size is unchanged. */
@@ -275,13 +279,13 @@ int oidn_unet_forward_packed(const void* d_weights, int in_channels, const void*
                              float* net_out_rgba, int dtype, hipStream_t stream);
 
 /* Workspace for oidn_unet_forward on a w x h image with this tile plan
- * (on the fp16 path one copy of the per-tile plan for each tile of a batch,
+ * (on the 16-bit paths one copy of the per-tile plan for each tile of a batch,
  * see oidn_unet_tile_batch). */
 int oidn_unet_workspace_bytes(int in_channels, int w, int h, int max_tile, int overlap,
                               int dtype, size_t* bytes);
 
 /* Tiles of this plan that oidn_unet_forward runs through the network
- * together: on the fp16 path, where both image passes run inside the first
+ * together: on the 16-bit paths, where both image passes run inside the first
  * and last convs, up to 16 consecutive tiles of one size share one launch
  * per layer (tile index in grid z); else 1.  The per-kernel events of
  * oidn_unet_forward_timed cover the first such batch.  Host only. */
@@ -290,7 +294,7 @@ int oidn_unet_tile_batch(int in_channels, int w, int h, int max_tile, int overla
 
 /* End-to-end denoise ([webgpu-0.6] recordDenoiseExecution): plan the tile
  * grid, then for each tile in order: input pass, network, output pass into
- * the tile's output rectangle of out_rgba (h x w RGBA float32; on the fp16
+ * the tile's output rectangle of out_rgba (h x w RGBA float32; on the 16-bit
  * path the network's first fused pair runs the input pass on the images and
  * the last writes that rectangle itself).  in_channels
  * must match the non-NULL images (color; + albedo; + normal). */

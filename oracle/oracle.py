@@ -13,12 +13,14 @@ Pages cited (by title and symbol):
 * [web-0.5] "oidn-web 0.4.0 -> 0.5.0", nativeUNet.ts (hunks over [web-0.4])
 * [webgpu-0.6] "oidn-webgpu 0.0.0-stage -> 0.6.0", native/denoise.ts
 
-Storage model.  A compute precision ``'f16'`` or ``'f32'`` says how every
-stored tensor is rounded: weights are rounded to it ([web-0.4]
+Storage model.  A compute precision ``'f16'``, ``'bf16'`` or ``'f32'`` says how
+every stored tensor is rounded: weights are rounded to it ([web-0.4]
 packConvTensors converts weights to the activation precision), the bias stays
 float32 ([web-0.4] packConvTensors: bias stays f32 because convolution
 accumulates in f32), every activation is rounded after bias and ReLU (float64
--> float32 -> float16 with round-to-nearest-even), and the last convolution
+-> float32 -> float16 or bfloat16 with round-to-nearest-even; bfloat16 is
+not on the pages: it is read as the same model with the 16-bit format
+swapped), and the last convolution
 stores float32 ([web-0.4] NativeUNetExecutor._nodePipelineSpec and
 _createExecution: the final node writes an f32 buffer).  Sums are taken in
 float64, so only accumulation order separates this from an fp32-accumulating
@@ -60,19 +62,39 @@ def stored(c: int) -> int:
 
 
 def np_storage(precision: str):
+    """numpy dtype holding stored values; bfloat16 values are held exactly in
+    float32 (numpy has no bfloat16)."""
     if precision == "f16":
         return np.float16
-    if precision == "f32":
+    if precision in ("f32", "bf16"):
         return np.float32
     raise ValueError(f"unknown precision {precision!r}")
 
 
+def float32_to_bfloat16(v32) -> np.ndarray:
+    """float32 -> bfloat16 (8 significant bits, float32's exponent range),
+    round to nearest, ties to even, written out on the bit pattern: keep the
+    upper 16 bits after adding 0x7FFF plus the lowest kept bit; NaN stays NaN
+    (the addition could carry a NaN payload into the exponent).  Overflow
+    rounds to infinity.  Returned as float32."""
+    v32 = np.ascontiguousarray(v32, dtype=np.float32)
+    u = v32.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    out = (r & 0xFFFFFFFF).astype(np.uint32).view(np.float32)
+    return np.where(np.isnan(v32), np.float32(np.nan), out)
+
+
 def round_to(values, precision: str) -> np.ndarray:
     """Round float64 values to a stored precision: to float32 (RNE), then, for
-    'f16', float32 -> float16 (RNE; overflow -> inf; subnormals kept)."""
+    'f16', float32 -> float16 (RNE; overflow -> inf; subnormals kept), for
+    'bf16', float32 -> bfloat16 (RNE, held in float32)."""
     with np.errstate(over="ignore"):
         v32 = np.asarray(values, dtype=np.float64).astype(np.float32)
-        return v32.astype(np.float16) if precision == "f16" else v32
+        if precision == "f16":
+            return v32.astype(np.float16)
+        if precision == "bf16":
+            return float32_to_bfloat16(v32)
+        return v32
 
 
 # ----------------------------------------------------------------------------

@@ -1,6 +1,10 @@
 """Helpers for the GPU parity tests: host <-> device copies and packing
 through the C ABI.  Tolerances follow the contract: max_i |g - o| / max |o|
-within 1e-5 (fp32 storage) or 2e-2 (fp16 storage, fp32 accumulate)."""
+within 1e-5 (fp32 storage) or 2e-2 (fp16 storage, fp32 accumulate).  bf16
+storage has no stated bound: the fp16 one scaled by the ratio of the two
+formats' unit roundoffs, 2^-8 / 2^-11 = 8, since both sides round every
+stored value the same way and differ only where fp32 and float64 sums round
+to different neighbours."""
 import os
 import sys
 
@@ -13,8 +17,8 @@ if ROOT not in sys.path:
 
 import unet_x3_convolution_amd as U  # noqa: E402
 
-TOL = {"f32": 1e-5, "f16": 2e-2}
-DT = {"f32": U.OIDN_F32, "f16": U.OIDN_F16}
+TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 8 * 2e-2}
+DT = {"f32": U.OIDN_F32, "f16": U.OIDN_F16, "bf16": U.OIDN_BF16}
 
 
 def torch_cuda():
@@ -42,7 +46,29 @@ def empty(shape, np_dtype, fill=None):
 def host(t):
     torch = torch_cuda()
     torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy()   # exact
     return t.cpu().numpy()
+
+
+def to_dev(a, precision):
+    """Stored values (the oracle's storage arrays) to a device tensor of the
+    precision's storage type; bf16 values are exact in both."""
+    if precision == "bf16":
+        torch = torch_cuda()
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).cuda()
+    return dev(np.asarray(a, {"f16": np.float16, "f32": np.float32}[precision]))
+
+
+def alloc(shape, precision, fill=None):
+    """Device buffer of the precision's storage type."""
+    if precision == "bf16":
+        torch = torch_cuda()
+        t = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        if fill is not None:
+            t.fill_(fill)
+        return t
+    return empty(shape, {"f16": np.float16, "f32": np.float32}[precision], fill)
 
 
 def packed_conv(w, b, cin0, cin1, cout, precision):
@@ -72,6 +98,19 @@ def ulp_diff_f16(a, b):
         i = np.asarray(x, np.float16).view(np.int16).astype(np.int32)
         return np.where(i < 0, -(i & 0x7FFF), i)
     return np.abs(key(a) - key(b))
+
+
+def ulp_diff_bf16(a, b):
+    """|difference| in units of bf16 ordering, for float32 arrays holding
+    bf16 values (0 = identical bits)."""
+    def key(x):
+        i = (np.ascontiguousarray(x, np.float32).view(np.uint32) >> 16).astype(np.int32)
+        return np.where(i >= 0x8000, -(i & 0x7FFF), i)
+    return np.abs(key(a) - key(b))
+
+
+def ulp_diff(a, b, precision):
+    return ulp_diff_bf16(a, b) if precision == "bf16" else ulp_diff_f16(a, b)
 
 
 def say(*args):

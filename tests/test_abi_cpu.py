@@ -248,7 +248,8 @@ def test_conv_argument_errors():
     assert _code(c, FAKE, 0, 8, 12, FAKE, FAKE, 32, U.OIDN_F16, U.OIDN_F16, 1, 0) == E    # h = 0
     assert _code(c, FAKE, 7, 8, 12, FAKE, FAKE, 32, U.OIDN_F16, U.OIDN_F16, 3, 0) == E    # odd pool
     assert _code(c, FAKE, 8, 8, 12, FAKE, FAKE, 32, U.OIDN_F32, U.OIDN_F16, 1, 0) == N    # f32 -> f16
-    assert _code(c, FAKE, 8, 8, 12, FAKE, FAKE, 32, U.OIDN_BF16, U.OIDN_BF16, 1, 0) == N  # bf16
+    assert _code(c, FAKE, 8, 8, 12, FAKE, FAKE, 32, U.OIDN_BF16, U.OIDN_F16, 1, 0) == N   # bf16 -> f16
+    assert _code(c, FAKE, 8, 8, 12, FAKE, FAKE, 32, U.OIDN_F16, U.OIDN_BF16, 1, 0) == N   # f16 -> bf16
     assert _code(c, FAKE, 8, 8, 12, FAKE, FAKE, 32, 7, U.OIDN_F16, 1, 0) == E             # dtype
     assert _code(c, FAKE, 8, 8, 12, FAKE, FAKE, 32, U.OIDN_F16, U.OIDN_F16, 8, 0) == E    # flags
     assert _code(c, FAKE, 8, 8, 300, FAKE, FAKE, 32, U.OIDN_F16, U.OIDN_F16, 1, 0) == N   # cin

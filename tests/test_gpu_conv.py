@@ -5,7 +5,7 @@ import pytest
 
 import synthetic as S
 import unet_x3_convolution_amd as U
-from helpers import DT, TOL, dev, empty, host, packed_conv, rel_err, say, ulp_diff_f16
+from helpers import DT, TOL, alloc, dev, empty, host, packed_conv, rel_err, say, to_dev, ulp_diff_f16
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -16,8 +16,9 @@ def run_conv(x_np, cin, w, b, cout, precision, flags, out_precision=None):
     h, wd = x_np.shape[:2]
     pk = packed_conv(w, b, cin, 0, cout, precision)
     oh, ow = (h // 2, wd // 2) if flags & U.OIDN_POOL2X2 else (h, wd)
-    y = empty((oh, ow, O.stored(cout)), O.np_storage(out_precision), fill=float("nan"))
-    U.oidn_conv3x3(dev(x_np), h, wd, cin, pk, y, cout, DT[precision], DT[out_precision], flags)
+    y = alloc((oh, ow, O.stored(cout)), out_precision, fill=float("nan"))
+    U.oidn_conv3x3(to_dev(x_np, precision), h, wd, cin, pk, y, cout, DT[precision],
+                   DT[out_precision], flags)
     return host(y)
 
 
@@ -107,6 +108,19 @@ def test_conv_f16_matches_oracle(h, w, cin, cout, flags, outp):
           f"conv f16 {h}x{w} {cin}->{cout} flags={flags} out={outp}")
 
 
+@pytest.mark.parametrize("h,w,cin,cout,flags,outp", F16_CASES)
+def test_conv_bf16_matches_oracle(h, w, cin, cout, flags, outp):
+    """The same shapes with bf16 storage (every launch plan instance)."""
+    r = np.random.default_rng(2000 + h * 7 + cin)
+    x = O.round_to(S.relu_normal_activation(r, h, w, cin, O.stored(cin)), "bf16")
+    wt = S.he_normal(r, cout, cin)
+    b = S.bias(r, cout)
+    outp = "bf16" if outp == "f16" else outp
+    got = run_conv(x, cin, wt, b, cout, "bf16", flags, outp)
+    check(got, oracle_conv(x, cin, wt, b, cout, "bf16", flags, outp), cout, "bf16",
+          f"conv bf16 {h}x{w} {cin}->{cout} flags={flags} out={outp}")
+
+
 @pytest.mark.parametrize("h,w,cin,cout,flags", [(20, 18, 12, 8, U.OIDN_RELU),
                                                 (10, 14, 40, 20, U.OIDN_RELU | U.OIDN_POOL2X2),
                                                 (9, 5, 3, 3, 0)])
@@ -181,6 +195,10 @@ UPCAT_CASES = [
 ]
 
 
+# every fp16 case again with bf16 storage
+UPCAT_CASES += [c[:5] + ("bf16",) for c in UPCAT_CASES if c[5] == "f16"]
+
+
 @pytest.mark.parametrize("h,w,c_low,c_skip,cout,precision", UPCAT_CASES)
 def test_decoder_conv_matches_oracle(h, w, c_low, c_skip, cout, precision):
     r = np.random.default_rng(h * w + c_low)
@@ -189,9 +207,9 @@ def test_decoder_conv_matches_oracle(h, w, c_low, c_skip, cout, precision):
     wt = S.he_normal(r, cout, c_low + c_skip)
     b = S.bias(r, cout)
     pk = packed_conv(wt, b, c_low, c_skip, cout, precision)
-    y = empty((h, w, O.stored(cout)), O.np_storage(precision), fill=float("nan"))
-    U.oidn_conv3x3_upcat(dev(low), c_low, dev(skip), c_skip, h, w, pk, y, cout, DT[precision],
-                         DT[precision], U.OIDN_RELU)
+    y = alloc((h, w, O.stored(cout)), precision, fill=float("nan"))
+    U.oidn_conv3x3_upcat(to_dev(low, precision), c_low, to_dev(skip, precision), c_skip, h, w, pk,
+                         y, cout, DT[precision], DT[precision], U.OIDN_RELU)
     got = host(y)
     z = O.upsample_concat(low, c_low, skip, c_skip)
     ref = O.conv3x3(z, c_low + c_skip, wt, b, True, precision)

@@ -7,33 +7,36 @@ import pytest
 
 import synthetic as S
 import unet_x3_convolution_amd as U
-from helpers import DT, dev, empty, host, say, ulp_diff_f16
+from helpers import DT, alloc, dev, empty, host, say, to_dev, ulp_diff, ulp_diff_f16
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("h,w,c,precision", [(6, 10, 12, "f16"), (128, 64, 48, "f16"),
-                                             (2, 2, 4, "f32"), (40, 18, 9, "f32")])
+                                             (2, 2, 4, "f32"), (40, 18, 9, "f32"),
+                                             (6, 10, 12, "bf16"), (128, 64, 48, "bf16")])
 def test_pool_bit_exact(h, w, c, precision):
     r = np.random.default_rng(h * w)
     x = np.zeros((h, w, O.stored(c)), O.np_storage(precision))
-    x[..., :c] = r.standard_normal((h, w, c))
-    y = empty((h // 2, w // 2, O.stored(c)), O.np_storage(precision), fill=float("nan"))
-    U.oidn_pool2x2(dev(x), h, w, c, y, DT[precision])
+    x[..., :c] = O.round_to(r.standard_normal((h, w, c)), precision)
+    y = alloc((h // 2, w // 2, O.stored(c)), precision, fill=float("nan"))
+    U.oidn_pool2x2(to_dev(x, precision), h, w, c, y, DT[precision])
     assert np.array_equal(host(y), O.pool2x2(x))
 
 
 @pytest.mark.parametrize("h,w,c_low,c_skip,precision", [(16, 16, 96, 64, "f16"),
                                                         (6, 10, 8, 9, "f16"),
-                                                        (4, 2, 4, 3, "f32")])
+                                                        (4, 2, 4, 3, "f32"),
+                                                        (6, 10, 8, 9, "bf16")])
 def test_upsample_concat_bit_exact(h, w, c_low, c_skip, precision):
     r = np.random.default_rng(h + c_low)
-    low = r.standard_normal((h // 2, w // 2, c_low)).astype(O.np_storage(precision))
+    low = O.round_to(r.standard_normal((h // 2, w // 2, c_low)), precision)
     skip = np.zeros((h, w, O.stored(c_skip)), O.np_storage(precision))
-    skip[..., :c_skip] = r.standard_normal((h, w, c_skip))
-    z = empty((h, w, c_low + O.stored(c_skip)), O.np_storage(precision), fill=float("nan"))
-    U.oidn_upsample_concat(dev(low), c_low, dev(skip), c_skip, h, w, z, DT[precision])
+    skip[..., :c_skip] = O.round_to(r.standard_normal((h, w, c_skip)), precision)
+    z = alloc((h, w, c_low + O.stored(c_skip)), precision, fill=float("nan"))
+    U.oidn_upsample_concat(to_dev(low, precision), c_low, to_dev(skip, precision), c_skip, h, w,
+                           z, DT[precision])
     assert np.array_equal(host(z), O.upsample_concat(low, c_low, skip, c_skip))
 
 
@@ -41,7 +44,7 @@ def _gpu_pack(color, albedo, normal, rect, hdr, scale, precision):
     img_h, img_w = color.shape[:2]
     tx, ty, tw, th = rect
     ch = 3 * (1 + (albedo is not None) + (normal is not None))
-    out = empty((th, tw, O.stored(ch)), O.np_storage(precision), fill=float("nan"))
+    out = alloc((th, tw, O.stored(ch)), precision, fill=float("nan"))
     U.oidn_pack_input(dev(color), None if albedo is None else dev(albedo),
                       None if normal is None else dev(normal), img_w, img_h, tx, ty, tw, th, hdr,
                       U.OIDN_TRANSFER_LOG, scale, out, DT[precision])
@@ -49,7 +52,7 @@ def _gpu_pack(color, albedo, normal, rect, hdr, scale, precision):
 
 
 @pytest.mark.parametrize("sources", [1, 2, 3])
-@pytest.mark.parametrize("precision", ["f16", "f32"])
+@pytest.mark.parametrize("precision", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("hdr", [True, False])
 def test_pack_matches_oracle(sources, precision, hdr):
     r = S.rng(sources)
@@ -69,8 +72,8 @@ def test_pack_matches_oracle(sources, precision, hdr):
             exact[..., :3] = ref[..., :3]
         assert np.array_equal(exact, ref), rect
         if hdr:  # log1p on the device vs float64 on the host: <= 1 ulp of the stored type
-            if precision == "f16":
-                assert ulp_diff_f16(got[..., :3], ref[..., :3]).max() <= 1
+            if precision != "f32":
+                assert ulp_diff(got[..., :3], ref[..., :3], precision).max() <= 1
             else:
                 np.testing.assert_allclose(got[..., :3], ref[..., :3], rtol=3e-7, atol=0)
 
@@ -80,14 +83,13 @@ def test_pack_special_values():
     color = np.array([[[nan, -1.0, inf, 0.5], [0.0, 1e30, 3.0, 0.25]]], np.float32)
     albedo = np.array([[[nan, 2.0, -3.0, 1.0], [0.5, 0.25, 1.0, 0.0]]], np.float32)
     normal = np.array([[[nan, -5.0, 5.0, 0.0], [-1.0, 0.0, 1.0, 0.0]]], np.float32)
-    for precision in ["f16", "f32"]:
+    for precision in ["f16", "bf16", "f32"]:
         got = _gpu_pack(color, albedo, normal, (0, 0, 2, 1), True, 1.0, precision)
         ref = O.pack_input(color, albedo, normal, 0, 0, 2, 1, True, 1.0, precision)
         assert got[0, 0, 0] == 0 and got[0, 0, 1] == 0
         assert np.array_equal(got[..., 3:], ref[..., 3:])
-        tol = 1 if precision == "f16" else 0
-        if precision == "f16":
-            assert ulp_diff_f16(got[..., :3], ref[..., :3]).max() <= tol
+        if precision != "f32":
+            assert ulp_diff(got[..., :3], ref[..., :3], precision).max() <= 1
         else:
             np.testing.assert_allclose(got[..., :3], ref[..., :3], rtol=3e-7)
     assert math.isclose(float(got[0, 0, 2]), math.log1p(O.FLT_MAX), rel_tol=1e-6)

@@ -6,7 +6,7 @@ import pytest
 
 import synthetic as S
 import unet_x3_convolution_amd as U
-from helpers import DT, TOL, dev, empty, host, packed_unet, rel_err, say
+from helpers import DT, TOL, dev, empty, host, packed_unet, rel_err, say, to_dev
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -29,7 +29,8 @@ def gpu_forward_packed(ws, bs, packed, in_channels, precision):
     nbytes = U.oidn_unet_packed_workspace_bytes(in_channels, tw, th, DT[precision])
     work = empty((nbytes,), np.uint8)
     out = empty((th, tw, 4), np.float32, fill=float("nan"))
-    U.oidn_unet_forward_packed(wd, in_channels, dev(packed), tw, th, work, nbytes, out, DT[precision])
+    U.oidn_unet_forward_packed(wd, in_channels, to_dev(packed, precision), tw, th, work, nbytes, out,
+                               DT[precision])
     return host(out)
 
 
@@ -48,7 +49,8 @@ def gpu_denoise(ws, bs, color, albedo, normal, precision, max_tile, overlap, hdr
 
 
 @pytest.mark.parametrize("tw,th,in_channels,precision", [(64, 48, 9, "f16"), (80, 32, 3, "f16"),
-                                                         (48, 64, 6, "f16"), (64, 64, 9, "f32")])
+                                                         (48, 64, 6, "f16"), (64, 64, 9, "f32"),
+                                                         (64, 48, 9, "bf16"), (80, 32, 3, "bf16")])
 def test_network_on_packed_tile(tw, th, in_channels, precision):
     color, albedo, normal, ws, bs = make_case(tw, th, in_channels, seed=tw + th)
     packed = O.pack_input(color, albedo, normal, 0, 0, tw, th, True, 1.0, precision)
@@ -71,7 +73,7 @@ def test_config3_network_512_fp16():
     assert err <= TOL["f16"]
 
 
-@pytest.mark.parametrize("precision", ["f16", "f32"])
+@pytest.mark.parametrize("precision", ["f16", "bf16", "f32"])
 def test_end_to_end_tiled_matches_oracle(precision):
     """200x150 image, 128-pixel tiles, overlap 32 -> a 4x3 grid with ragged
     output spans; GPU and oracle run the same plan."""
@@ -148,19 +150,20 @@ def _oracle_rect(ws, bs, color, albedo, normal, out_rect, precision):
     return out[oy:oy + oh, ox:ox + ow]
 
 
-def test_config4_1080p_end_to_end_sampled():
-    """1920x1080 fp16, one 1920x1088 tile, HDR log with input scale 1:
-    the whole frame on the GPU; the oracle on sampled output rectangles."""
+@pytest.mark.parametrize("precision", ["f16", "bf16"])
+def test_config4_1080p_end_to_end_sampled(precision):
+    """1920x1080, one 1920x1088 tile, HDR log with input scale 1: the whole
+    frame on the GPU; the oracle on sampled output rectangles."""
     color, albedo, normal, ws, bs = make_case(1920, 1080)
-    got = gpu_denoise(ws, bs, color, albedo, normal, "f16", 0, 32)
+    got = gpu_denoise(ws, bs, color, albedo, normal, precision, 0, 32)
     assert not np.any(np.isnan(got))
     assert np.array_equal(got[..., 3], color[..., 3])
     for rect in [(0, 0, 48, 48), (1872, 1032, 48, 48), (944, 520, 32, 40), (1900, 300, 20, 16)]:
-        ref = _oracle_rect(ws, bs, color, albedo, normal, rect, "f16")
+        ref = _oracle_rect(ws, bs, color, albedo, normal, rect, precision)
         ox, oy, ow, oh = rect
         err = rel_err(got[oy:oy + oh, ox:ox + ow], ref)
-        say(f"config4 rect {rect}: max_rel_err={err:.3e}")
-        assert err <= TOL["f16"]
+        say(f"config4 {precision} rect {rect}: max_rel_err={err:.3e}")
+        assert err <= TOL[precision]
 
 
 def test_config5_4k_tiled_sampled():

@@ -35,6 +35,44 @@ def test_f16_rounding_closed_forms():
         assert got == expected, (value, got, expected)
 
 
+def test_bf16_rounding_closed_forms():
+    # bfloat16 = float32's sign and exponent with 7 stored fraction bits:
+    # ulp(1) = 2^-7, max finite (2 - 2^-7) 2^127, smallest subnormal 2^-133.
+    bmax = (2.0 - 2.0 ** -7) * 2.0 ** 127
+    cases = [
+        (1.0 + 2.0 ** -8, 1.0),                   # exact tie -> even (fraction 0)
+        (1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -6),   # tie between odd and even -> even
+        (1.0 + 2.0 ** -8 + 2.0 ** -20, 1.0 + 2.0 ** -7),   # above the tie -> up
+        (-(3.0 + 2.0 ** -7), -3.0),               # tie below 4: ulp 2^-6, even is 3
+        (bmax, bmax),
+        (bmax + 2.0 ** 119, math.inf),            # tie at the top rounds to overflow
+        (2.0 ** -133, 2.0 ** -133),               # subnormals kept
+        (3 * 2.0 ** -134, 2.0 ** -132),           # tie -> even
+        (1.0 / 3.0, 0.333984375),                 # 0x3EAB
+    ]
+    for value, expected in cases:
+        got = float(O.round_to(np.array([value]), "bf16")[0])
+        assert got == expected, (value, got, expected)
+    assert np.isnan(O.round_to(np.array([np.nan]), "bf16")[0])
+
+
+def test_bf16_rounding_matches_torch():
+    """float32 -> bfloat16 against torch's CPU conversion (a library
+    routine), over normals, subnormals, ties and the overflow edge."""
+    torch = pytest.importorskip("torch")
+    r = np.random.default_rng(3)
+    with np.errstate(invalid="ignore", over="ignore"):
+        v = np.concatenate([
+            r.standard_normal(20000) * 10.0 ** r.integers(-40, 38, 20000),
+            (r.integers(0, 2 ** 16, 5000).astype(np.uint32) << 16 | 0x8000).view(np.float32),
+            np.array([3.3961e38, -3.3961e38, 1e-45, 0.0, -0.0], np.float64)])
+        v32 = v.astype(np.float32)
+    v32 = v32[np.isfinite(v32)]
+    got = O.round_to(v32, "bf16")
+    want = torch.from_numpy(v32).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
 # ------------------------------------------------------------- conv pins
 def brute_conv(x, cin, w, b, relu):
     """Six nested loops, float64, taps outside the image skipped."""
@@ -383,3 +421,7 @@ def test_f16_storage_stays_within_tolerance_of_f32(small_unet):
     assert n16.dtype == np.float32 and np.all(n32[..., 3] == 0)
     err = O.max_rel_error(n16, n32)
     assert 0 < err < 2e-2
+    pb = O.pack_input(color, albedo, normal, 0, 0, 400, 64, True, 1.0, "bf16")
+    nb = O.unet_forward_packed(ws, bs, pb, 9, "bf16")
+    errb = O.max_rel_error(nb, n32)
+    assert err < errb < 0.2      # 3 fewer significand bits than fp16

@@ -2,6 +2,7 @@
 // planner, weight packing, the liveness-planned UNet workspace and the
 // per-tile launch sequence.  Every device step is one of the HIP kernels in
 // this directory; nothing here computes on the host except packing weights.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -39,12 +40,38 @@ int hip_fail(hipError_t e, const char* what) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_dtype(int dtype) {
-  if (dtype == OIDN_F32 || dtype == OIDN_F16) return OIDN_OK;
-  if (dtype == OIDN_BF16) return fail(OIDN_E_UNSUPPORTED, "bf16 storage is not supported by this build");
+  if (dtype == OIDN_F32 || dtype == OIDN_F16 || dtype == OIDN_BF16) return OIDN_OK;
   return fail(OIDN_E_INVALID, "unknown dtype %d", dtype);
 }
 
 size_t esize(int dtype) { return dtype == OIDN_F32 ? 4 : 2; }
+
+// fp16 and bf16 storage run the same MFMA kernels (16-bit path).
+bool b16(int dtype) { return dtype == OIDN_F16 || dtype == OIDN_BF16; }
+
+// double -> bf16 bits, rounded to nearest even once (8 significant bits;
+// subnormals below 2^-126 at a fixed 2^-133 step; overflow to infinity).
+uint16_t bf16_bits(double v) {
+  if (std::isnan(v)) return 0x7fc0;
+  if (v == 0.0) return std::signbit(v) ? 0x8000 : 0x0000;
+  int e = 0;
+  std::frexp(v, &e);                       // |v| = m 2^e, 0.5 <= m < 1
+  const int shift = e >= -125 ? 8 - e : 133;
+  const double r = std::nearbyint(std::ldexp(v, shift));   // ties to even
+  const float f = (float)std::ldexp(r, -shift);            // exact, or +-inf past the range
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return (uint16_t)(u >> 16);
+}
+
+// One stored weight value: fp16 (rounded once from double) or bf16.
+void put16(void* frag, size_t i, double v, int dtype) {
+  if (dtype == OIDN_BF16) {
+    static_cast<uint16_t*>(frag)[i] = bf16_bits(v);
+  } else {
+    static_cast<_Float16*>(frag)[i] = (_Float16)v;
+  }
+}
 
 // ------------------------------------------------------------ tile planner
 struct Span { int in0, in_size, out0, out_size; };
@@ -105,7 +132,7 @@ int conv_weights_bytes(int cin0, int cin1, int cout, int dtype, size_t* bytes, i
                 OIDN_MAX_SOURCE_CHANNELS, OIDN_MAX_OUT_CHANNELS);
   if (cin1 > 0 && cin0 % 4)
     return fail(OIDN_E_INVALID, "the upsampled source needs a multiple of 4 channels (got %d)", cin0);
-  if (dtype == OIDN_F16) {
+  if (b16(dtype)) {
     ConvLayout L;
     if (!conv_f16_layout(stored_channels(cin0), cin1 ? stored_channels(cin1) : 0, cout, &L, tap_src))
       return fail(OIDN_E_UNSUPPORTED, "conv shape exceeds the fp16 kernel limits");
@@ -117,7 +144,8 @@ int conv_weights_bytes(int cin0, int cin1, int cout, int dtype, size_t* bytes, i
 }
 
 // Host-side packing into `out` (sized by conv_weights_bytes).  tap_src: the
-// source packed as a tap chunk (fp16 only; see ConvChunk), -1 for none.
+// source packed as a tap chunk (16-bit storage only; see ConvChunk), -1 for
+// none.  fp16 and bf16 share the layout.
 void pack_conv_host(const float* w, const float* b, int cin0, int cin1, int cout, int dtype,
                     std::vector<unsigned char>& out, int tap_src = -1) {
   const int cin = cin0 + cin1;
@@ -131,16 +159,16 @@ void pack_conv_host(const float* w, const float* b, int cin0, int cin1, int cout
     return c < cin1 ? cin0 + c : -1;
   };
   std::fill(out.begin(), out.end(), 0);
-  if (dtype == OIDN_F16) {
+  if (b16(dtype)) {
     ConvLayout L;
     conv_f16_layout(cs0, cs1, cout, &L, tap_src);
     float* bias = reinterpret_cast<float*>(out.data());
     for (int o = 0; o < cout; ++o) bias[o] = b[o];
-    _Float16* frag = reinterpret_cast<_Float16*>(out.data() + L.bias_bytes);
+    unsigned char* frag = out.data() + L.bias_bytes;
     // Upsampled-source chunks hold four row combinations a per column group
     // instead of the three ky rows: W0, W1 + W2, W0 + W1, W2 (the two rows
     // of the low-resolution source an even / odd output row reads), each sum
-    // formed in double and rounded once to fp16.
+    // formed in double and rounded once to the storage type.
     static const int kCombo[4][2] = {{0, -1}, {1, 2}, {0, 1}, {2, -1}};
     for (int ci = 0; ci < L.nchunks; ++ci) {
       const ConvChunk& ch = L.chunk[ci];
@@ -149,7 +177,7 @@ void pack_conv_host(const float* w, const float* b, int cin0, int cin1, int cout
       for (int j = 0; j < ch.ncg; ++j)
         for (int ky = 0; ky < rows; ++ky)
           for (int q = 0; q < L.nf; ++q) {
-            _Float16* f = frag + ((size_t)(ch.wfrag + (j * rows + ky) * L.nf + q)) * (kFragBytes / 2);
+            unsigned char* f = frag + ((size_t)(ch.wfrag + (j * rows + ky) * L.nf + q)) * kFragBytes;
             for (int lane = 0; lane < 64; ++lane) {
               const int r = lane & 15, slot = 4 * j + (lane >> 4);
               const int o = frag_row_to_cout(L.nf, q, r);
@@ -161,7 +189,7 @@ void pack_conv_host(const float* w, const float* b, int cin0, int cin1, int cout
                   if (li < 0) continue;
                   double v = wat(o, 3 * kCombo[ky][0] + kx, li);
                   if (kCombo[ky][1] >= 0) v += wat(o, 3 * kCombo[ky][1] + kx, li);
-                  f[lane * 8 + jj] = (_Float16)v;
+                  put16(f, lane * 8 + jj, v, dtype);
                 }
                 continue;
               }
@@ -172,7 +200,7 @@ void pack_conv_host(const float* w, const float* b, int cin0, int cin1, int cout
                 for (int jj = 0; jj < 8; ++jj) {
                   const int li = slot < 3 ? logical(ch.src, jj) : jj < 3 ? c8 : -1;
                   const int kx = slot < 3 ? slot : jj;
-                  if (li >= 0) f[lane * 8 + jj] = (_Float16)wat(o, 3 * ky + kx, li);
+                  if (li >= 0) put16(f, lane * 8 + jj, wat(o, 3 * ky + kx, li), dtype);
                 }
                 continue;
               }
@@ -181,7 +209,7 @@ void pack_conv_host(const float* w, const float* b, int cin0, int cin1, int cout
               const int tap = 3 * ky + kx;
               for (int jj = 0; jj < 8; ++jj) {
                 const int li = logical(ch.src, ch.coff + 8 * grp + jj);
-                if (li >= 0) f[lane * 8 + jj] = (_Float16)wat(o, tap, li);
+                if (li >= 0) put16(f, lane * 8 + jj, wat(o, tap, li), dtype);
               }
             }
           }
@@ -229,7 +257,7 @@ int run_conv(const void* src0, int cin0, const void* src1, int cin1, bool upcat,
              size_t bstride = 0) {
   const bool pool = flags & OIDN_POOL2X2, relu = flags & OIDN_RELU;
   hipError_t e;
-  if (in_dtype == OIDN_F16) {
+  if (b16(in_dtype)) {
     ConvLayout L;
     ConvF16Args a = f16_args(cin0, cin1, cout, h, w, cs0, cs1, &L, tap_src);
     a.src0 = src0;
@@ -239,7 +267,8 @@ int run_conv(const void* src0, int cin0, const void* src1, int cin1, bool upcat,
     a.y = y;
     a.batch = batch;
     a.bstride = bstride;
-    e = launch_conv_f16(a, L.nf, upcat, pool, relu, out_dtype == OIDN_F32, stream);
+    e = launch_conv_f16(a, L.nf, upcat, pool, relu, out_dtype == OIDN_F32, in_dtype == OIDN_BF16,
+                        stream);
   } else {
     if (batch != 1) return fail(OIDN_E_UNSUPPORTED, "batched fp32 convs");
     ConvF32Args a{};
@@ -268,6 +297,8 @@ int check_conv(int h, int w, int cin0, int cin1, int cout, int in_dtype, int out
   if (rc) return rc;
   if (in_dtype == OIDN_F32 && out_dtype != OIDN_F32)
     return fail(OIDN_E_UNSUPPORTED, "fp32 input needs fp32 output");
+  if (b16(out_dtype) && out_dtype != in_dtype)
+    return fail(OIDN_E_UNSUPPORTED, "a 16-bit output needs the same 16-bit input type");
   if (h <= 0 || w <= 0 || h > 65536 || w > 65536)
     return fail(OIDN_E_INVALID, "conv size %dx%d out of range", w, h);
   if (flags & ~(OIDN_RELU | OIDN_POOL2X2)) return fail(OIDN_E_INVALID, "unknown conv flags 0x%x", flags);
@@ -300,10 +331,11 @@ bool pair_supported(int cin, int cs, int cout) {
 // (instead of x) and writes the packed tile to in_pass->packed.
 // batch, bstride, rects: that many tiles, activations at + b * bstride bytes,
 // rects[b] the input pass origin / output pass rectangle of tile b.
+// bf16: the 16-bit storage (x, the intermediate, a 16-bit y) is bf16.
 int run_pair(const void* x, int cin, int cs, int h, int w, const void* wA, const void* wB, void* y,
              int cout, int out_dtype, unsigned flags, hipStream_t stream, bool tap = false,
              const OutputPass* img = nullptr, const PackArgs* in_pass = nullptr, int batch = 1,
-             size_t bstride = 0, const TileRect* rects = nullptr) {
+             size_t bstride = 0, const TileRect* rects = nullptr, bool bf16 = false) {
   ConvLayout LA, LB;
   conv_f16_layout(stored_channels(cin), 0, 32, &LA, tap ? 0 : -1);
   conv_f16_layout(32, 0, cout, &LB);
@@ -330,7 +362,7 @@ int run_pair(const void* x, int cin, int cs, int h, int w, const void* wA, const
   const int out = img ? kPairImage : out_dtype == OIDN_F32 ? kPairF32 : kPairF16;
   const int in = (tap ? kPairInTaps : 0) | (in_pass ? kPairInImages : 0);
   hipError_t e = launch_conv_pair_f16(p, LA.chunk[0].cg, LB.nf, in, flags & OIDN_POOL2X2,
-                                      flags & OIDN_RELU, out, stream);
+                                      flags & OIDN_RELU, out, bf16, stream);
   if (e != hipSuccess) return hip_fail(e, "conv3x3 pair launch");
   return OIDN_OK;
 }
@@ -393,7 +425,7 @@ size_t unet_layer_offset(const LayerShape* s, int dtype, int layer) {
 // weights in that layout follow the sixteen plain ones in the packed blob;
 // the plain ones serve oidn_unet_forward_packed, whose input is packed by
 // the caller without taps.
-bool unet_taps(int in_channels, int dtype) { return dtype == OIDN_F16 && in_channels == 9; }
+bool unet_taps(int in_channels, int dtype) { return b16(dtype) && in_channels == 9; }
 
 // Source of layer i read as a tap chunk when the input carries taps, or -1.
 int unet_tap_src(int i) { return kUNet[i].src == 0 ? 0 : kUNet[i].skip == 0 ? 1 : -1; }
@@ -430,7 +462,7 @@ struct Plan {
 // multiple of 8, so the conv's patch loads move whole 16-byte channel groups.
 int internal_input_lanes(int in_channels, int dtype) {
   const int cs = stored_channels(in_channels);
-  return dtype == OIDN_F16 ? (cs + 7) / 8 * 8 : cs;
+  return b16(dtype) ? (cs + 7) / 8 * 8 : cs;
 }
 
 // Layer i runs fused with layer i + 1 (y = conv_{i+1}(conv_i(x)) through LDS)
@@ -439,7 +471,7 @@ int internal_input_lanes(int in_channels, int dtype) {
 // conv_i's source.  In this network: enc_conv0 -> enc_conv1 and
 // dec_conv1b -> dec_conv0 on the fp16 path.
 bool fuse_with_next(int in_channels, int i, int dtype, bool own_io) {
-  if (dtype != OIDN_F16 || i + 1 >= kLayers) return false;
+  if (!b16(dtype) || i + 1 >= kLayers) return false;
   LayerShape s[kLayers];
   unet_shapes(in_channels, s);
   const Layer &A = kUNet[i], &B = kUNet[i + 1];
@@ -462,7 +494,7 @@ bool output_fused(int in_channels, int dtype) {
 // when that conv is the first layer of a fused pair (fp16, a 16-lane chunk).
 // The packed input is still written (the decoder's last skip reads it).
 bool input_fused(int in_channels, int dtype) {
-  return fuse_with_next(in_channels, 0, dtype, true) && dtype == OIDN_F16 &&
+  return fuse_with_next(in_channels, 0, dtype, true) && b16(dtype) &&
          stored_channels(in_channels) <= 16;
 }
 
@@ -580,7 +612,7 @@ int run_network(const unsigned char* weights, int in_channels, const void* packe
                         weights + woff + align256(ba), const_cast<void*>(val[i + 2]),
                         s[i + 1].cout, i + 1 == kLayers - 1 ? OIDN_F32 : dtype, flags_b, stream,
                         tap_src == 0, i + 1 == kLayers - 1 ? img : nullptr,
-                        i == 0 ? in_pass : nullptr, batch, bstride, rects);
+                        i == 0 ? in_pass : nullptr, batch, bstride, rects, dtype == OIDN_BF16);
       if (rc) return rc;
       if (events && events[i + 1]) {   // the second layer's interval is empty
         hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[i + 1]), stream);
@@ -725,7 +757,7 @@ int denoise(const void* d_weights, int in_channels, const float* color, const fl
     pa.taps = unet_taps(in_channels, dtype) && pa.lanes == 16;
     pa.packed = ws + P.offset[0];
     // input pass, network with a stored float32 output, output pass (fp32)
-    if ((e = launch_pack(pa, dtype == OIDN_F16, stream)) != hipSuccess) return hip_fail(e, "pack launch");
+    if ((e = launch_pack(pa, dtype, stream)) != hipSuccess) return hip_fail(e, "pack launch");
     rc = run_network(static_cast<const unsigned char*>(d_weights), in_channels, nullptr, t.in_w,
                      t.in_h, ws, P, true, nullptr, dtype, stream, ev ? ev + 1 : nullptr);
     if (rc) return rc;
@@ -862,10 +894,10 @@ int oidn_conv3x3_kernel(int h, int w, int cin0, int cin1, int cout, int in_dtype
   int rc = check_conv(h, w, cin0, cin1, cout, in_dtype, out_dtype, flags, cin1 > 0);
   if (rc) return rc;
   int nb = 0;
-  if (in_dtype == OIDN_F16) {
+  if (b16(in_dtype)) {
     ConvLayout L;
     const ConvF16Args a = f16_args(cin0, cin1, cout, h, w, 0, 0, &L);
-    conv_f16_describe(a, L.nf, out_dtype == OIDN_F32, buf, cap, &nb);
+    conv_f16_describe(a, L.nf, out_dtype == OIDN_F32, in_dtype == OIDN_BF16, buf, cap, &nb);
   } else {
     snprintf(buf, cap, "conv3x3_f32_direct");
     const bool pool = flags & OIDN_POOL2X2;
@@ -883,7 +915,7 @@ int oidn_pool2x2(const void* x, int h, int w, int c, void* y, int dtype, hipStre
     return fail(OIDN_E_INVALID, "pool2x2 needs positive even sizes and channels (got %dx%dx%d)", w, h, c);
   if (!aligned16(x) || !aligned16(y)) return fail(OIDN_E_INVALID, "device pointers must be 16-byte aligned");
   if ((double)h * w * stored_channels(c) > 4.0e9) return fail(OIDN_E_UNSUPPORTED, "tensor too large");
-  hipError_t e = launch_pool(x, h, w, stored_channels(c), y, dtype == OIDN_F16, stream);
+  hipError_t e = launch_pool(x, h, w, stored_channels(c), y, dtype, stream);
   if (e != hipSuccess) return hip_fail(e, "pool launch");
   return ok();
 }
@@ -899,7 +931,7 @@ int oidn_upsample_concat(const void* low, int c_low, const void* skip, int c_ski
   if (!aligned16(low) || !aligned16(skip) || !aligned16(z))
     return fail(OIDN_E_INVALID, "device pointers must be 16-byte aligned");
   if ((double)h * w * (c_low + stored_channels(c_skip)) > 4.0e9) return fail(OIDN_E_UNSUPPORTED, "tensor too large");
-  hipError_t e = launch_upcat(low, c_low, skip, stored_channels(c_skip), h, w, z, dtype == OIDN_F16, stream);
+  hipError_t e = launch_upcat(low, c_low, skip, stored_channels(c_skip), h, w, z, b16(dtype), stream);
   if (e != hipSuccess) return hip_fail(e, "upsample-concat launch");
   return ok();
 }
@@ -938,7 +970,7 @@ int oidn_pack_input(const float* color, const float* albedo, const float* normal
   a.sources = 1 + (albedo != nullptr) + (normal != nullptr);
   a.lanes = stored_channels(3 * a.sources);
   a.packed = packed;
-  hipError_t e = launch_pack(a, dtype == OIDN_F16, stream);
+  hipError_t e = launch_pack(a, dtype, stream);
   if (e != hipSuccess) return hip_fail(e, "pack launch");
   return ok();
 }
@@ -1008,7 +1040,7 @@ int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int dtype
   const int h = th >> s[layer].level, w = tw >> s[layer].level;
   const bool final_layer = layer == kLayers - 1;
   int nb = 0;
-  if (dtype == OIDN_F16 && (fuse_with_next(in_channels, layer, dtype, true) ||
+  if (b16(dtype) && (fuse_with_next(in_channels, layer, dtype, true) ||
                             (layer > 0 && fuse_with_next(in_channels, layer - 1, dtype, true)))) {
     // both layers of a fused pair report the pair kernel (sized by the first)
     const int first = fuse_with_next(in_channels, layer, dtype, true) ? layer : layer - 1;
@@ -1020,11 +1052,11 @@ int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int dtype
     // input: 1 taps | 2 images through the input pass (first layer, fused)
     const int out = first + 1 == kLayers - 1 ? (output_fused(in_channels, dtype) ? 2 : 1) : 0;
     const int in = (tap ? 1 : 0) | (first == 0 && input_fused(in_channels, dtype) ? 2 : 0);
-    snprintf(buf, cap, "conv3x3_pair_f16<%d, %d, %d, %d>", st > 16 ? 4 : 2,
-             cdiv(stored_channels(s[first + 1].cout), 16), out, in);
+    snprintf(buf, cap, "conv3x3_pair_%s<%d, %d, %d, %d>", dtype == OIDN_BF16 ? "bf16" : "f16",
+             st > 16 ? 4 : 2, cdiv(stored_channels(s[first + 1].cout), 16), out, in);
     (void)cs;
     nb = conv_pair_blocks(fh, fw);
-  } else if (dtype == OIDN_F16) {
+  } else if (b16(dtype)) {
     // as oidn_unet_forward runs it: the input packed with a multiple of 8 lanes
     const int in_cs = internal_input_lanes(in_channels, dtype);
     const Layer& L = kUNet[layer];
@@ -1032,7 +1064,7 @@ int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int dtype
     const ConvF16Args a = f16_args(s[layer].cin0, s[layer].cin1, s[layer].cout, h, w,
                                    L.src == 0 ? in_cs : 0, L.skip == 0 ? in_cs : 0, &lay,
                                    unet_taps(in_channels, dtype) ? unet_tap_src(layer) : -1);
-    conv_f16_describe(a, lay.nf, final_layer, buf, cap, &nb);
+    conv_f16_describe(a, lay.nf, final_layer, dtype == OIDN_BF16, buf, cap, &nb);
   } else {
     snprintf(buf, cap, "conv3x3_f32_direct");
     const int oh = kUNet[layer].pool ? h / 2 : h, ow = kUNet[layer].pool ? w / 2 : w;
@@ -1068,7 +1100,7 @@ int oidn_unet_pack_weights(const float* const* w_ohwi_host, const float* const* 
     size_t b = 0;
     conv_weights_bytes(s[i].cin0, s[i].cin1, s[i].cout, dtype, &b);
     std::vector<unsigned char> one(b);
-    if (i == kLayers - 1 && dtype == OIDN_F16) {
+    if (i == kLayers - 1 && b16(dtype)) {
       // fp16: the last layer's RGB in all four 4-channel lane groups of its
       // output fragment (lane 3 of each zero), for the output pass in its
       // epilogue; the same bytes as the plain 3-channel packing

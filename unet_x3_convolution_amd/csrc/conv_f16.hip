@@ -43,7 +43,22 @@ namespace oidn {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// Activations and weights are stored as fp16 or (BF) bf16, both rounded to
+// nearest even from fp32; the matching MFMA multiplies them with fp32
+// accumulate.  Operands travel as raw 16-byte groups of 8 values.
+template <bool BF>
+__device__ __forceinline__ floatx4 mfma16(uint4 a, uint4 b, floatx4 c) {
+  if constexpr (BF)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
+                                                   __builtin_bit_cast(half8, b), c, 0, 0, 0);
+}
+
 
 constexpr int TW = 16;                        // tile width (one B fragment)
 constexpr int PW = TW + 2;                    // patch width
@@ -103,7 +118,6 @@ __device__ __forceinline__ void dma16(const void* gp, uint4* lds) {
 // Zero block that padding lanes of the direct patch loads read from.
 __device__ __attribute__((aligned(16))) unsigned int g_zero16[4] = {0u, 0u, 0u, 0u};
 
-__device__ __forceinline__ half8 as_half8(uint4 v) { return __builtin_bit_cast(half8, v); }
 
 // Tile order.  Tiles are walked in super-tiles of kSuperW x kSuperH tiles
 // (row-major inside a super-tile, super-tiles row-major), and XCD x takes
@@ -227,7 +241,7 @@ __device__ __forceinline__ void stage_patch(_Float16* lds, const _Float16* src, 
 // a staged weight row.  TAP: a tap chunk (CG 2; one column group, slot 3 =
 // group 1 of the centre pixel).  (Upsampled-source chunks: mma_chunk_up.)
 template <int NFW, int R, int CG, bool PF, int PWID = PW, bool SW = false, bool TAP = false,
-          typename Hook>
+          bool BF = false, typename Hook>
 __device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], uint4 (&acur)[3][NFW],
                                           const _Float16* lds, int cur, int zero,
                                           const uint4* wchunk, const uint4* wnext, int nf,
@@ -264,15 +278,14 @@ __device__ __forceinline__ void mma_chunk(floatx4 (&acc)[R][NFW], uint4 (&acur)[
     }
 #pragma unroll
     for (int p = 0; p < R + 2; ++p) {
-      const half8 b = *reinterpret_cast<const half8*>(lds + base + p * rstride);
+      const uint4 b = *reinterpret_cast<const uint4*>(lds + base + p * rstride);
 #pragma unroll
       for (int ky = 0; ky < 3; ++ky) {
         const int r = p - ky;
         if (r >= 0 && r < R) {
 #pragma unroll
           for (int q = 0; q < NFW; ++q)
-            acc[r][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(acur[ky][q]), b,
-                                                               acc[r][q], 0, 0, 0);
+            acc[r][q] = mfma16<BF>(acur[ky][q], b, acc[r][q]);
         }
       }
     }
@@ -307,7 +320,7 @@ __device__ __forceinline__ float swap_pair(float v) {
 // the full-resolution column c + kx - 1 of the wave's window (row0 even).
 // The A operands are loaded per column group and combination (from LDS or
 // global memory).
-template <int NFW, int R, int CG, bool SW>
+template <int NFW, int R, int CG, bool SW, bool BF = false>
 __device__ __forceinline__ void mma_chunk_up(floatx4 (&acc)[R][NFW], const _Float16* lds, int cur,
                                              int zero, const uint4* wchunk, int nf, int row0,
                                              int col0, int g, int c) {
@@ -327,10 +340,10 @@ __device__ __forceinline__ void mma_chunk_up(floatx4 (&acc)[R][NFW], const _Floa
     }
     // the column group's R / 2 + 2 B fragments, then one row combination's
     // A operands at a time (registers: B rows + NFW A, not 4 NFW A)
-    half8 b[R / 2 + 2];
+    uint4 b[R / 2 + 2];
 #pragma unroll
     for (int qr = 0; qr < R / 2 + 2; ++qr)
-      b[qr] = *reinterpret_cast<const half8*>(lds + base + qr * rstride);
+      b[qr] = *reinterpret_cast<const uint4*>(lds + base + qr * rstride);
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       uint4 aa[NFW];
@@ -342,41 +355,33 @@ __device__ __forceinline__ void mma_chunk_up(floatx4 (&acc)[R][NFW], const _Floa
         if (r >= 0 && r < R) {
 #pragma unroll
           for (int q = 0; q < NFW; ++q)
-            acc[r][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(aa[q]), b[qr], acc[r][q],
-                                                               0, 0, 0);
+            acc[r][q] = mfma16<BF>(aa[q], b[qr], acc[r][q]);
         }
       }
     }
   }
 }
 
-template <bool OUTF32>
+template <bool OUTF32, bool BF>
 __device__ __forceinline__ void store4(void* y, size_t idx, float v0, float v1, float v2, float v3) {
   if constexpr (OUTF32) {
     *reinterpret_cast<float4*>(static_cast<float*>(y) + idx) = make_float4(v0, v1, v2, v3);
   } else {
-    const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1, h2 = (_Float16)v2, h3 = (_Float16)v3;
-    uint2 p;
-    p.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-    p.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
-    *reinterpret_cast<uint2*>(static_cast<_Float16*>(y) + idx) = p;
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + idx) =
+        make_uint2(pack2<BF>(v0, v1), pack2<BF>(v2, v3));
   }
 }
 
-template <bool OUTF32>
+template <bool OUTF32, bool BF>
 __device__ __forceinline__ void store8(void* y, size_t idx, const float (&v)[8]) {
   if constexpr (OUTF32) {
     float4* p = reinterpret_cast<float4*>(static_cast<float*>(y) + idx);
     p[0] = make_float4(v[0], v[1], v[2], v[3]);
     p[1] = make_float4(v[4], v[5], v[6], v[7]);
   } else {
-    uint4 p;
-    uint32_t* w = reinterpret_cast<uint32_t*>(&p);
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      w[k] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2 * k]) |
-             ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2 * k + 1]) << 16);
-    *reinterpret_cast<uint4*>(static_cast<_Float16*>(y) + idx) = p;
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + idx) =
+        make_uint4(pack2<BF>(v[0], v[1]), pack2<BF>(v[2], v[3]), pack2<BF>(v[4], v[5]),
+                   pack2<BF>(v[6], v[7]));
   }
 }
 
@@ -385,7 +390,7 @@ __device__ __forceinline__ void store8(void* y, size_t idx, const float (&v)[8])
 // by the same lane are 8 consecutive channels and go out as one 16-byte
 // store when all 8 are stored channels; others as 8-byte stores.  Channels
 // at or past cout_stored (a multiple of 4) are never written.
-template <int NFW, bool OUTF32>
+template <int NFW, bool OUTF32, bool BF>
 __device__ __forceinline__ void store_pixel(void* y, size_t pix, const int (&chan)[NFW],
                                             const bool (&lead)[NFW], const bool (&tail)[NFW],
                                             int cout_stored, const float (&v)[NFW][4]) {
@@ -396,9 +401,9 @@ __device__ __forceinline__ void store_pixel(void* y, size_t pix, const int (&cha
     if (q + 1 < NFW && lead[q] && chan[q] + 8 <= cout_stored) {
       const float w8[8] = {v[q][0], v[q][1], v[q][2], v[q][3],
                            v[q + 1][0], v[q + 1][1], v[q + 1][2], v[q + 1][3]};
-      store8<OUTF32>(y, pix + chan[q], w8);
+      store8<OUTF32, BF>(y, pix + chan[q], w8);
     } else {
-      store4<OUTF32>(y, pix + chan[q], v[q][0], v[q][1], v[q][2], v[q][3]);
+      store4<OUTF32, BF>(y, pix + chan[q], v[q][0], v[q][1], v[q][2], v[q][3]);
     }
   }
 }
@@ -407,7 +412,7 @@ __device__ __forceinline__ void store_pixel(void* y, size_t pix, const int (&cha
 // acc[r][q] holds, for this lane (16-lane group g), rows 4 g .. 4 g + 3 of
 // fragment q0 + q for pixel (yb + r, x); c is the pixel column in the tile.
 // Pixels at or past column xend (<= the image width) are not stored.
-template <int NFW, int R, bool OUTF32>
+template <int NFW, int R, bool OUTF32, bool BF>
 __device__ __forceinline__ void store_tile(const floatx4 (&acc)[R][NFW], const ConvF16Args& a,
                                            void* y, int q0, int g, int yb, int x, int c, int pool,
                                            int relu, int xend) {
@@ -435,7 +440,7 @@ __device__ __forceinline__ void store_tile(const floatx4 (&acc)[R][NFW], const C
         for (int q = 0; q < NFW; ++q)
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[q][i] = act(acc[r][q][i] + bv[q][i], relu);
-        store_pixel<NFW, OUTF32>(y, ((size_t)yy * a.w + x) * a.cout_stored, chan, lead, tail,
+        store_pixel<NFW, OUTF32, BF>(y, ((size_t)yy * a.w + x) * a.cout_stored, chan, lead, tail,
                                  a.cout_stored, v);
       }
     }
@@ -453,7 +458,7 @@ __device__ __forceinline__ void store_tile(const floatx4 (&acc)[R][NFW], const C
         }
       const int yy = yb + 2 * rp;
       if ((c & 1) == 0 && yy < a.h && x < xend)
-        store_pixel<NFW, OUTF32>(y, ((size_t)(yy >> 1) * ow + (x >> 1)) * a.cout_stored, chan,
+        store_pixel<NFW, OUTF32, BF>(y, ((size_t)(yy >> 1) * ow + (x >> 1)) * a.cout_stored, chan,
                                  lead, tail, a.cout_stored, m);
     }
   }
@@ -505,9 +510,8 @@ constexpr bool kWeightsInLds = 2 * (2 * kWlHalves<NFW, R, WR> + 16) <= 160 * 102
 // the A operands come from LDS; the patch uses the swizzled layout.  Else
 // every wave reads its A operands from global memory (L1/L2), with the next
 // column group's prefetched into registers where they fit.
-template <int NFW, int R, int WR, bool OUTF32>
-__global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
-    ConvF16Args a, int upcat, int pool, int relu) {
+template <int NFW, int R, int WR, bool OUTF32, bool BF>
+__device__ __forceinline__ void conv3x3_body(const ConvF16Args& __restrict__ a, int upcat, int pool, int relu) {
   static_assert(WR == 1 || WR == 2 || WR == 4, "row groups");
   constexpr bool WL = kWeightsInLds<NFW, R, WR>;
   constexpr bool SW = WL;
@@ -580,9 +584,9 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
                           lds + WOFF_UP, wblk + (size_t)ch.wfrag * 64, nf, FB, wave);           \
     __syncthreads();                                                                            \
     if constexpr (WL)                                                                           \
-      mma_chunk_up<NFW, R, CG, SW>(acc, lds, 0, ZERO, wl_up, FB, R * rg, 0, g, c);              \
+      mma_chunk_up<NFW, R, CG, SW, BF>(acc, lds, 0, ZERO, wl_up, FB, R * rg, 0, g, c);          \
     else                                                                                        \
-      mma_chunk_up<NFW, R, CG, SW>(acc, lds, 0, ZERO, wf + (size_t)ch.wfrag * 64, nf, R * rg, 0, \
+      mma_chunk_up<NFW, R, CG, SW, BF>(acc, lds, 0, ZERO, wf + (size_t)ch.wfrag * 64, nf, R * rg, 0, \
                                    g, c);                                                       \
   }
 #define OIDN_CHUNK_LOOP(K, CG, TAP)                                                             \
@@ -602,10 +606,10 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
                           lds + WOFF, wblk + (size_t)ch.wfrag * 64, nf, FB, wave);              \
     __syncthreads();                                                                            \
     if constexpr (WL)                                                                           \
-      mma_chunk<NFW, R, CG, false, PW, SW, TAP>(acc, acur, lds, 0, ZERO, wl, nullptr, FB,        \
+      mma_chunk<NFW, R, CG, false, PW, SW, TAP, BF>(acc, acur, lds, 0, ZERO, wl, nullptr, FB,    \
                                                 R * rg, 0, g, c, [] {});                        \
     else                                                                                        \
-      mma_chunk<NFW, R, CG, PF, PW, false, TAP>(acc, acur, lds, 0, ZERO,                         \
+      mma_chunk<NFW, R, CG, PF, PW, false, TAP, BF>(acc, acur, lds, 0, ZERO,                     \
                                                 wf + (size_t)ch.wfrag * 64, wnext, nf, R * rg,  \
                                                 0, g, c, [] {});                                \
   }
@@ -619,17 +623,35 @@ __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(
 #undef OIDN_UP_LOOP
   (void)upcat;
 
-  store_tile<NFW, R, OUTF32>(acc, a, ydst, q0, g, y0 + R * rg, x0 + c, c, pool, relu, a.w);
+  store_tile<NFW, R, OUTF32, BF>(acc, a, ydst, q0, g, y0 + R * rg, x0 + c, c, pool, relu, a.w);
+}
+
+// The kernels: fp16 and bf16 storage.
+template <int NFW, int R, int WR, bool OUTF32>
+__global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(ConvF16Args a, int upcat, int pool,
+                                                               int relu) {
+  conv3x3_body<NFW, R, WR, OUTF32, false>(a, upcat, pool, relu);
+}
+template <int NFW, int R, int WR, bool OUTF32>
+__global__ __launch_bounds__(THREADS, 2) void conv3x3_bf16_mfma(ConvF16Args a, int upcat, int pool,
+                                                                int relu) {
+  conv3x3_body<NFW, R, WR, OUTF32, true>(a, upcat, pool, relu);
 }
 
 template <int NFW, int R, int WR>
 hipError_t launch_shape(ConvF16Args a, int nsplit, bool upcat, bool pool, bool relu,
-                        bool out_f32, hipStream_t stream) {
+                        bool out_f32, bool bf16, hipStream_t stream) {
   a.tiles_x = cdiv(a.w, TW);
   a.tiles_y = cdiv(a.h, WR * R);
   const int ntiles = a.tiles_x * a.tiles_y;
   const dim3 grid(cdiv(ntiles, kXcds) * kXcds, nsplit, a.batch > 1 ? a.batch : 1), block(THREADS);
-  if (out_f32)
+  if (bf16 && out_f32)
+    hipLaunchKernelGGL((conv3x3_bf16_mfma<NFW, R, WR, true>), grid, block, 0, stream, a,
+                       (int)upcat, (int)pool, (int)relu);
+  else if (bf16)
+    hipLaunchKernelGGL((conv3x3_bf16_mfma<NFW, R, WR, false>), grid, block, 0, stream, a,
+                       (int)upcat, (int)pool, (int)relu);
+  else if (out_f32)
     hipLaunchKernelGGL((conv3x3_f16_mfma<NFW, R, WR, true>), grid, block, 0, stream, a,
                        (int)upcat, (int)pool, (int)relu);
   else
@@ -714,7 +736,7 @@ __device__ __forceinline__ void stage_pair_input(uint4* slots, const _Float16* s
 // pixels of the workgroup's own output tile are also stored to `in.packed`
 // (in.lanes per pixel) for the decoder's later skip read.  Every image load
 // is issued before the first value is used.
-template <bool TAPS>
+template <bool TAPS, bool BF>
 __device__ __forceinline__ void stage_pair_images(uint4* slots, const PackArgs& in, int h, int w,
                                                   int y0, int x0, int tid) {
   constexpr int NPIX = PAIR_IH * PAIR_PW;
@@ -773,9 +795,9 @@ __device__ __forceinline__ void stage_pair_images(uint4* slots, const PackArgs& 
     }
     uint4 g0 = make_uint4(0u, 0u, 0u, 0u), g1 = g0;
     if (inside) {
-      g0 = make_uint4(pack_h2(ch[0], ch[1]), pack_h2(ch[2], ch[3]), pack_h2(ch[4], ch[5]),
-                      pack_h2(ch[6], ch[7]));
-      if (in.lanes > 8) g1 = make_uint4(pack_h2(ch[8], ch[9]), pack_h2(ch[10], ch[11]), 0u, 0u);
+      g0 = make_uint4(pack2<BF>(ch[0], ch[1]), pack2<BF>(ch[2], ch[3]), pack2<BF>(ch[4], ch[5]),
+                      pack2<BF>(ch[6], ch[7]));
+      if (in.lanes > 8) g1 = make_uint4(pack2<BF>(ch[8], ch[9]), pack2<BF>(ch[10], ch[11]), 0u, 0u);
       if (py >= 2 && py < 2 + PAIR_TH && px >= 2 && px < 2 + PAIR_TW) {
         // 32-bit offset formed here (a hoisted 64-bit address is spilled)
         int o = (y * w + x) * (in.lanes / 8);
@@ -846,9 +868,8 @@ __device__ __forceinline__ void store_image(const floatx4 (&acc)[R][1], const fl
 // IN: a PairIn (convA reads packed fp16, the tap-packed network input, or
 // the images through the fused input pass, with or without taps).
 // OUT: a PairOut (convB's result as fp16, fp32, or through the output pass).
-template <int CGA, int NFB, int OUT, int IN>
-__global__ __launch_bounds__(THREADS, (kPairWaves<CGA, IN>)) void conv3x3_pair_f16(PairArgs p, int pool,
-                                                                              int relu) {
+template <int CGA, int NFB, int OUT, int IN, bool BF>
+__device__ __forceinline__ void conv3x3_pair_body(const PairArgs& __restrict__ p, int pool, int relu) {
   constexpr bool TAP = (IN & kPairInTaps) != 0, IMG = (IN & kPairInImages) != 0;
   static_assert(!TAP || CGA == 2, "tap chunks are 16-lane sources");
   static_assert(!IMG || CGA == 2, "the input pass writes one 16-lane chunk");
@@ -924,10 +945,10 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA, IN>)) void conv3x3_pair_f
       in.tile_x = p.rect[bt].in_x;
       in.tile_y = p.rect[bt].in_y;
       in.packed = static_cast<char*>(in.packed) + boff;
-      stage_pair_images<TAP>(reinterpret_cast<uint4*>(lds), in, p.h, p.w, y0, x0, tid);
+      stage_pair_images<TAP, BF>(reinterpret_cast<uint4*>(lds), in, p.h, p.w, y0, x0, tid);
       load_a();
       __syncthreads();
-      mma_chunk<2, RA, CGA, true, PAIR_PW, false, TAP>(acc, acur, lds, 0, L::ZERO, wf, nullptr, 2,
+      mma_chunk<2, RA, CGA, true, PAIR_PW, false, TAP, BF>(acc, acur, lds, 0, L::ZERO, wf, nullptr, 2,
                                                        RA * rh, 16 * cf, g, c, [] {});
     }
 #pragma unroll 1
@@ -939,11 +960,11 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA, IN>)) void conv3x3_pair_f
       if constexpr (WL) stage_weights<(3 * CGA + 3) / 4 * 3 * 2>(lds + L::WOFF, wchunk, 2, 2, wave);
       __syncthreads();
       if constexpr (WL) {
-        mma_chunk<2, RA, CGA, false, PAIR_PW, true>(acc, acur, lds, 0, L::ZERO, wl, nullptr, 2,
+        mma_chunk<2, RA, CGA, false, PAIR_PW, true, false, BF>(acc, acur, lds, 0, L::ZERO, wl, nullptr, 2,
                                                     RA * rh, 16 * cf, g, c, [] {});
       } else {
         const uint4* wnext = ci + 1 < p.nchunks ? wf + (size_t)p.wfragA[ci + 1] * 64 : nullptr;
-        mma_chunk<2, RA, CGA, true, PAIR_PW, false, TAP>(acc, acur, lds, 0, L::ZERO, wchunk, wnext,
+        mma_chunk<2, RA, CGA, true, PAIR_PW, false, TAP, BF>(acc, acur, lds, 0, L::ZERO, wchunk, wnext,
                                                          2, RA * rh, 16 * cf, g, c, [] {});
       }
     }
@@ -976,10 +997,8 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA, IN>)) void conv3x3_pair_f
         const int i0 = 2 * k, i1 = 2 * k + 1;
         const float f0 = (i0 < 4 ? acc[r][0][i0] : acc[r][1][i0 - 4]) + bA[i0];
         const float f1 = (i1 < 4 ? acc[r][0][i1] : acc[r][1][i1 - 4]) + bA[i1];
-        const _Float16 h0 = inside ? (_Float16)fmaxf(f0, 0.f) : (_Float16)0.f;
-        const _Float16 h1 = inside ? (_Float16)fmaxf(f1, 0.f) : (_Float16)0.f;
-        wv[k] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-                ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        // mask, not a conditional: the compiler branches around the conversion
+        wv[k] = pack2<BF>(fmaxf(f0, 0.f), fmaxf(f1, 0.f)) & (0u - (uint32_t)inside);
       }
       const int col = 16 * cf + c;
       const int px = (RA * rh + r) * PAIR_PW + col;
@@ -999,14 +1018,14 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA, IN>)) void conv3x3_pair_f
     uint4 acur[3][NFB];
     if constexpr (WL) {
       const uint4* wl = reinterpret_cast<const uint4*>(lds + L::WOFF) + lane;
-      mma_chunk<NFB, RB, 4, false, PAIR_PW, true>(accb, acur, lds, 0, L::ZERO, wl, nullptr, NFB,
+      mma_chunk<NFB, RB, 4, false, PAIR_PW, true, false, BF>(accb, acur, lds, 0, L::ZERO, wl, nullptr, NFB,
                                                   RB * rh, 16 * cf, g, c, [] {});
     } else {
 #pragma unroll
       for (int ky = 0; ky < 3; ++ky)
 #pragma unroll
         for (int q = 0; q < NFB; ++q) acur[ky][q] = wf[(ky * NFB + q) * 64];
-      mma_chunk<NFB, RB, 4, true, PAIR_PW, MSW>(accb, acur, lds, 0, L::ZERO, wf, nullptr, NFB, RB * rh,
+      mma_chunk<NFB, RB, 4, true, PAIR_PW, MSW, false, BF>(accb, acur, lds, 0, L::ZERO, wf, nullptr, NFB, RB * rh,
                                            16 * cf, g, c, [] {});
     }
   }
@@ -1020,35 +1039,78 @@ __global__ __launch_bounds__(THREADS, (kPairWaves<CGA, IN>)) void conv3x3_pair_f
     a.y = nullptr;
     a.cout_stored = p.cout_stored;
     a.nf = NFB;
-    store_tile<NFB, RB, OUT == kPairF32>(accb, a, static_cast<char*>(p.y) + boff, 0, g,
+    store_tile<NFB, RB, OUT == kPairF32, BF>(accb, a, static_cast<char*>(p.y) + boff, 0, g,
                                          y0 + RB * rh, x0 + 16 * cf + c, c, pool,
                                          relu, xend);
   }
 }
 
-template <int CGA, int NFB, int IN>
+// The kernels: fp16 and bf16 storage.
+template <int CGA, int NFB, int OUT, int IN>
+__global__ __launch_bounds__(THREADS, (kPairWaves<CGA, IN>)) void conv3x3_pair_f16(PairArgs p, int pool,
+                                                                                  int relu) {
+  conv3x3_pair_body<CGA, NFB, OUT, IN, false>(p, pool, relu);
+}
+template <int CGA, int NFB, int OUT, int IN>
+__global__ __launch_bounds__(THREADS, (kPairWaves<CGA, IN>)) void conv3x3_pair_bf16(PairArgs p, int pool,
+                                                                                   int relu) {
+  conv3x3_pair_body<CGA, NFB, OUT, IN, true>(p, pool, relu);
+}
+
+template <int CGA, int NFB, int OUT, int IN, bool BF>
+void launch_pair_kernel(const PairArgs& p, dim3 grid, bool pool, bool relu, hipStream_t stream) {
+  if constexpr (BF)
+    hipLaunchKernelGGL((conv3x3_pair_bf16<CGA, NFB, OUT, IN>), grid, dim3(THREADS), 0, stream, p,
+                       (int)pool, (int)relu);
+  else
+    hipLaunchKernelGGL((conv3x3_pair_f16<CGA, NFB, OUT, IN>), grid, dim3(THREADS), 0, stream, p,
+                       (int)pool, (int)relu);
+}
+
+template <int CGA, int NFB, int IN, bool BF>
 hipError_t launch_pair_shape(PairArgs p, bool pool, bool relu, int out, hipStream_t stream) {
   p.tiles_x = cdiv(p.w, PAIR_TW);
   p.tiles_y = cdiv(p.h, PAIR_TH);
-  const dim3 grid(cdiv(p.tiles_x * p.tiles_y, kXcds) * kXcds, 1, p.batch > 1 ? p.batch : 1),
-      block(THREADS);
+  const dim3 grid(cdiv(p.tiles_x * p.tiles_y, kXcds) * kXcds, 1, p.batch > 1 ? p.batch : 1);
   if (out == kPairF32) {
-    hipLaunchKernelGGL((conv3x3_pair_f16<CGA, NFB, kPairF32, IN>), grid, block, 0, stream, p,
-                       (int)pool, (int)relu);
+    launch_pair_kernel<CGA, NFB, kPairF32, IN, BF>(p, grid, pool, relu, stream);
   } else if (out == kPairF16) {
-    hipLaunchKernelGGL((conv3x3_pair_f16<CGA, NFB, kPairF16, IN>), grid, block, 0, stream, p,
-                       (int)pool, (int)relu);
+    launch_pair_kernel<CGA, NFB, kPairF16, IN, BF>(p, grid, pool, relu, stream);
   } else {
     // the network's last pair only: 64 -> 32 -> one fragment, no pool
     if constexpr (CGA == 4 && NFB == 1 && IN == kPairInPacked) {
       if (out != kPairImage || pool || !p.img.color || !p.img.out) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((conv3x3_pair_f16<CGA, NFB, kPairImage, IN>), grid, block, 0, stream,
-                         p, (int)pool, (int)relu);
+      launch_pair_kernel<CGA, NFB, kPairImage, IN, BF>(p, grid, pool, relu, stream);
     } else {
       return hipErrorInvalidValue;
     }
   }
   return hipGetLastError();
+}
+
+template <bool BF>
+hipError_t launch_pair_typed(const PairArgs& p, int cga, int nfb, int in, bool pool, bool relu,
+                             int out, hipStream_t stream) {
+  if (in & kPairInImages) {
+    // the network's first pair: 16-lane input chunk, 32 -> 32 (pool)
+    if (cga != 2 || nfb != 2 || !p.in.color || !p.in.packed) return hipErrorInvalidValue;
+    if (in == kPairInImages)
+      return launch_pair_shape<2, 2, kPairInImages, BF>(p, pool, relu, out, stream);
+    if (in == (kPairInImages | kPairInTaps))
+      return launch_pair_shape<2, 2, kPairInImages | kPairInTaps, BF>(p, pool, relu, out, stream);
+    return hipErrorInvalidValue;
+  }
+  if (in == kPairInTaps) {
+    if (cga == 2 && nfb == 2) return launch_pair_shape<2, 2, kPairInTaps, BF>(p, pool, relu, out, stream);
+    if (cga == 2 && nfb == 1) return launch_pair_shape<2, 1, kPairInTaps, BF>(p, pool, relu, out, stream);
+    return hipErrorInvalidValue;
+  }
+  if (in != kPairInPacked) return hipErrorInvalidValue;
+  if (cga == 2 && nfb == 2) return launch_pair_shape<2, 2, kPairInPacked, BF>(p, pool, relu, out, stream);
+  if (cga == 2 && nfb == 1) return launch_pair_shape<2, 1, kPairInPacked, BF>(p, pool, relu, out, stream);
+  if (cga == 4 && nfb == 2) return launch_pair_shape<4, 2, kPairInPacked, BF>(p, pool, relu, out, stream);
+  if (cga == 4 && nfb == 1) return launch_pair_shape<4, 1, kPairInPacked, BF>(p, pool, relu, out, stream);
+  return hipErrorInvalidValue;
 }
 
 // The instances the planner can choose (see kPlanCandidates).
@@ -1058,10 +1120,10 @@ hipError_t launch_pair_shape(PairArgs p, bool pool, bool relu, int out, hipStrea
   X(5, 4, 4) X(7, 4, 4)
 
 hipError_t launch_plan(const ConvF16Args& a, const ConvPlan& P, int nsplit, bool upcat, bool pool,
-                       bool relu, bool out_f32, hipStream_t stream) {
+                       bool relu, bool out_f32, bool bf16, hipStream_t stream) {
 #define OIDN_TRY(NFW, R, WR)                                                                \
   if (P.nfw == NFW && P.rows == R && P.wr == WR)                                            \
-    return launch_shape<NFW, R, WR>(a, nsplit, upcat, pool, relu, out_f32, stream);
+    return launch_shape<NFW, R, WR>(a, nsplit, upcat, pool, relu, out_f32, bf16, stream);
   OIDN_PLAN_INSTANCES(OIDN_TRY)
 #undef OIDN_TRY
   return hipErrorInvalidValue;
@@ -1173,47 +1235,30 @@ bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out
   return true;
 }
 
-void conv_f16_describe(const ConvF16Args& a, int nf, bool out_f32, char* buf, int cap,
+void conv_f16_describe(const ConvF16Args& a, int nf, bool out_f32, bool bf16, char* buf, int cap,
                        int* blocks) {
   const int h = a.h, w = a.w;
   const ConvPlan P = conv_f16_plan(h, w, nf, a.nchunks, a.nup);
-  snprintf(buf, cap, "conv3x3_f16_mfma<%d, %d, %d, %s>", P.nfw, P.rows, P.wr,
+  snprintf(buf, cap, "conv3x3_%s_mfma<%d, %d, %d, %s>", bf16 ? "bf16" : "f16", P.nfw, P.rows, P.wr,
            out_f32 ? "true" : "false");
   *blocks = conv_f16_blocks(h, w, nf, a.nchunks, a.nup);
 }
 
 hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, bool relu,
-                           bool out_f32, hipStream_t stream) {
+                           bool out_f32, bool bf16, hipStream_t stream) {
   if (a.batch > 65535) return hipErrorInvalidValue;
   ConvF16Args b = a;
   b.nf = nf;
   const ConvPlan P = conv_f16_plan(a.h, a.w, nf, a.nchunks, a.nup);
   const int nsplit = nf / plan_block_frags(P);
-  return launch_plan(b, P, nsplit, upcat, pool, relu, out_f32, stream);
+  return launch_plan(b, P, nsplit, upcat, pool, relu, out_f32, bf16, stream);
 }
 
 hipError_t launch_conv_pair_f16(const PairArgs& p, int cga, int nfb, int in, bool pool,
-                                bool relu, int out, hipStream_t stream) {
+                                bool relu, int out, bool bf16, hipStream_t stream) {
   if (p.batch > kMaxBatch) return hipErrorInvalidValue;
-  if (in & kPairInImages) {
-    // the network's first pair: 16-lane input chunk, 32 -> 32 (pool)
-    if (cga != 2 || nfb != 2 || !p.in.color || !p.in.packed) return hipErrorInvalidValue;
-    if (in == kPairInImages) return launch_pair_shape<2, 2, kPairInImages>(p, pool, relu, out, stream);
-    if (in == (kPairInImages | kPairInTaps))
-      return launch_pair_shape<2, 2, kPairInImages | kPairInTaps>(p, pool, relu, out, stream);
-    return hipErrorInvalidValue;
-  }
-  if (in == kPairInTaps) {
-    if (cga == 2 && nfb == 2) return launch_pair_shape<2, 2, kPairInTaps>(p, pool, relu, out, stream);
-    if (cga == 2 && nfb == 1) return launch_pair_shape<2, 1, kPairInTaps>(p, pool, relu, out, stream);
-    return hipErrorInvalidValue;
-  }
-  if (in != kPairInPacked) return hipErrorInvalidValue;
-  if (cga == 2 && nfb == 2) return launch_pair_shape<2, 2, kPairInPacked>(p, pool, relu, out, stream);
-  if (cga == 2 && nfb == 1) return launch_pair_shape<2, 1, kPairInPacked>(p, pool, relu, out, stream);
-  if (cga == 4 && nfb == 2) return launch_pair_shape<4, 2, kPairInPacked>(p, pool, relu, out, stream);
-  if (cga == 4 && nfb == 1) return launch_pair_shape<4, 1, kPairInPacked>(p, pool, relu, out, stream);
-  return hipErrorInvalidValue;
+  return bf16 ? launch_pair_typed<true>(p, cga, nfb, in, pool, relu, out, stream)
+              : launch_pair_typed<false>(p, cga, nfb, in, pool, relu, out, stream);
 }
 
 int conv_pair_blocks(int h, int w) {

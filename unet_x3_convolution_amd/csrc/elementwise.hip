@@ -18,7 +18,8 @@ constexpr int THREADS = 256;
 // With `taps` (fp16, 16 lanes, three images) lanes 8, 9, 10 hold channel 8
 // (the normal's z) of the pixels in tile columns x - 1, x, x + 1, zero
 // outside the tile -- the layout the first convs read as a tap chunk.
-template <bool F16>
+// DT: the storage type (OIDN_F32, OIDN_F16 or OIDN_BF16).
+template <int DT>
 __global__ __launch_bounds__(THREADS) void pack_input_kernel(PackArgs a) {
   const int n = a.tile_w * a.tile_h;
   const int t0 = blockIdx.x * THREADS + threadIdx.x;
@@ -65,12 +66,14 @@ __global__ __launch_bounds__(THREADS) void pack_input_kernel(PackArgs a) {
   }
   if (t0 >= n) return;
   const int nblk = a.lanes / 4;   // blocks past the data (lanes 12..15) are zero
-  if constexpr (F16) {
+  if constexpr (DT != OIDN_F32) {
+    constexpr bool BF = DT == OIDN_BF16;
     uint2* out = static_cast<uint2*>(a.packed) + (size_t)t * nblk;
 #pragma unroll
     for (int b = 0; b < 4; ++b)
       if (b < nblk)
-        out[b] = b < 3 ? make_uint2(pack_h2(ch[4 * b], ch[4 * b + 1]), pack_h2(ch[4 * b + 2], ch[4 * b + 3]))
+        out[b] = b < 3 ? make_uint2(pack2<BF>(ch[4 * b], ch[4 * b + 1]),
+                                    pack2<BF>(ch[4 * b + 2], ch[4 * b + 3]))
                        : make_uint2(0u, 0u);
   } else {
     float4* out = static_cast<float4*>(a.packed) + (size_t)t * nblk;
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(THREADS) void unpack_output_kernel(UnpackArgs a) {
 // [web-0.4] createMaxPoolShader / [web-0.5] coalesced "channels" pool: one
 // thread per (output pixel, 4-channel block), threads of a wave walk the
 // blocks of consecutive pixels.
-template <bool F16>
+template <int DT>
 __global__ __launch_bounds__(THREADS) void pool2x2_kernel(const void* x, int h, int w, int cs,
                                                           void* y) {
   const int nb = cs / 4;
@@ -111,7 +114,19 @@ __global__ __launch_bounds__(THREADS) void pool2x2_kernel(const void* x, int h, 
   const size_t i01 = i00 + nb;
   const size_t i10 = i00 + (size_t)w * nb;
   const size_t i11 = i10 + nb;
-  if constexpr (F16) {
+  if constexpr (DT == OIDN_BF16) {
+    // bf16 -> fp32 is exact (the high half of the fp32 bits)
+    const uint2* in = static_cast<const uint2*>(x);
+    const uint2 a0 = in[i00], a1 = in[i01], a2 = in[i10], a3 = in[i11];
+    auto lo = [](uint32_t u) { return __uint_as_float(u << 16); };
+    auto hi = [](uint32_t u) { return __uint_as_float(u & 0xffff0000u); };
+    const float m0 = fmaxf(fmaxf(lo(a0.x), lo(a1.x)), fmaxf(lo(a2.x), lo(a3.x)));
+    const float m1 = fmaxf(fmaxf(hi(a0.x), hi(a1.x)), fmaxf(hi(a2.x), hi(a3.x)));
+    const float m2 = fmaxf(fmaxf(lo(a0.y), lo(a1.y)), fmaxf(lo(a2.y), lo(a3.y)));
+    const float m3 = fmaxf(fmaxf(hi(a0.y), hi(a1.y)), fmaxf(hi(a2.y), hi(a3.y)));
+    // exact: each maximum is one of the bf16 inputs
+    static_cast<uint2*>(y)[t] = make_uint2(pack_bf2(m0, m1), pack_bf2(m2, m3));
+  } else if constexpr (DT == OIDN_F16) {
     typedef _Float16 half4 __attribute__((ext_vector_type(4)));
     const half4* in = static_cast<const half4*>(x);
     const half4 a0 = in[i00], a1 = in[i01], a2 = in[i10], a3 = in[i11];
@@ -158,13 +173,15 @@ inline dim3 grid_for(size_t n) { return dim3((unsigned)((n + THREADS - 1) / THRE
 
 }  // namespace
 
-hipError_t launch_pack(const PackArgs& a, bool f16, hipStream_t stream) {
+hipError_t launch_pack(const PackArgs& a, int dtype, hipStream_t stream) {
   const size_t n = (size_t)a.tile_w * a.tile_h;
   if (n == 0) return hipSuccess;
-  if (f16)
-    hipLaunchKernelGGL(pack_input_kernel<true>, grid_for(n), dim3(THREADS), 0, stream, a);
+  if (dtype == OIDN_BF16)
+    hipLaunchKernelGGL(pack_input_kernel<OIDN_BF16>, grid_for(n), dim3(THREADS), 0, stream, a);
+  else if (dtype == OIDN_F16)
+    hipLaunchKernelGGL(pack_input_kernel<OIDN_F16>, grid_for(n), dim3(THREADS), 0, stream, a);
   else
-    hipLaunchKernelGGL(pack_input_kernel<false>, grid_for(n), dim3(THREADS), 0, stream, a);
+    hipLaunchKernelGGL(pack_input_kernel<OIDN_F32>, grid_for(n), dim3(THREADS), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -175,22 +192,24 @@ hipError_t launch_unpack(const UnpackArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_pool(const void* x, int h, int w, int cs, void* y, bool f16, hipStream_t stream) {
+hipError_t launch_pool(const void* x, int h, int w, int cs, void* y, int dtype, hipStream_t stream) {
   const size_t n = (size_t)(w / 2) * (h / 2) * (cs / 4);
   if (n == 0) return hipSuccess;
-  if (f16)
-    hipLaunchKernelGGL(pool2x2_kernel<true>, grid_for(n), dim3(THREADS), 0, stream, x, h, w, cs, y);
+  if (dtype == OIDN_BF16)
+    hipLaunchKernelGGL(pool2x2_kernel<OIDN_BF16>, grid_for(n), dim3(THREADS), 0, stream, x, h, w, cs, y);
+  else if (dtype == OIDN_F16)
+    hipLaunchKernelGGL(pool2x2_kernel<OIDN_F16>, grid_for(n), dim3(THREADS), 0, stream, x, h, w, cs, y);
   else
-    hipLaunchKernelGGL(pool2x2_kernel<false>, grid_for(n), dim3(THREADS), 0, stream, x, h, w, cs, y);
+    hipLaunchKernelGGL(pool2x2_kernel<OIDN_F32>, grid_for(n), dim3(THREADS), 0, stream, x, h, w, cs, y);
   return hipGetLastError();
 }
 
 hipError_t launch_upcat(const void* low, int cs_low, const void* skip, int cs_skip, int h, int w,
-                        void* z, bool f16, hipStream_t stream) {
+                        void* z, bool b16, hipStream_t stream) {
   const int nb = (cs_low + cs_skip) / 4;
   const size_t n = (size_t)h * w * nb;
   if (n == 0) return hipSuccess;
-  if (f16)
+  if (b16)
     hipLaunchKernelGGL(upcat_kernel<uint2>, grid_for(n), dim3(THREADS), 0, stream,
                        static_cast<const uint2*>(low), cs_low / 4, static_cast<const uint2*>(skip),
                        cs_skip / 4, h, w, static_cast<uint2*>(z));

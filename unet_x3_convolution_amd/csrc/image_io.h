@@ -30,6 +30,21 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
 }
 
+// Two channels as bf16 (round to nearest even), the first in the low half.
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+}
+
+// ... in the 16-bit storage type: fp16, or bf16 (BF).
+template <bool BF>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (BF)
+    return pack_bf2(a, b);
+  else
+    return pack_h2(a, b);
+}
+
 // Network RGB -> image RGBA: sanitize, invert the HDR log transfer and the
 // input scale (hdr), else clamp to [0, 1]; alpha from the input colour.
 __device__ __forceinline__ float4 output_pixel(float r, float g, float b, float alpha, int hdr,

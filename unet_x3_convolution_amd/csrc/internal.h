@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "oidn_mi355x.h"
+
 namespace oidn {
 
 constexpr int kMaxChunks = 20;        // 32-channel K chunks per conv (two sources)
@@ -100,8 +102,9 @@ struct ConvF16Args {
   ConvChunk chunk[kMaxChunks];
 };
 
+// bf16: the 16-bit storage is bf16 (conv3x3_bf16_mfma), else fp16.
 hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, bool relu,
-                           bool out_f32, hipStream_t stream);
+                           bool out_f32, bool bf16, hipStream_t stream);
 
 // Launch plan of a conv: a workgroup of 4 waves covers a (wr * rows) x 16
 // tile; each wave computes `rows` rows of `nfw` output fragments, the waves
@@ -115,7 +118,7 @@ int conv_f16_blocks(int h, int w, int nf, int nchunks, int nup);
 
 // Name of the kernel instance launch_conv_f16 would run for `a` (h, w,
 // cs0, cs1 and the chunk fields set) and its grid.
-void conv_f16_describe(const ConvF16Args& a, int nf, bool out_f32, char* buf, int cap,
+void conv_f16_describe(const ConvF16Args& a, int nf, bool out_f32, bool bf16, char* buf, int cap,
                        int* blocks);
 
 // Tiles of one size run through the network together: one launch per layer
@@ -189,7 +192,7 @@ struct PairArgs {
 // in: PairIn bits (kPairInTaps: convA's one chunk is a tap chunk, cga 2);
 // out: a PairOut.
 hipError_t launch_conv_pair_f16(const PairArgs& p, int cga, int nfb, int in, bool pool,
-                                bool relu, int out, hipStream_t stream);
+                                bool relu, int out, bool bf16, hipStream_t stream);
 int conv_pair_blocks(int h, int w);
 
 // ---------------------------------------------------------------------------
@@ -215,7 +218,9 @@ hipError_t launch_conv_f32(const ConvF32Args& a, bool upcat, bool pool, bool rel
 // ---------------------------------------------------------------------------
 // Elementwise / gather passes.
 // ---------------------------------------------------------------------------
-hipError_t launch_pack(const PackArgs& a, bool f16, hipStream_t stream);
+// dtype: OIDN_F32, OIDN_F16 or OIDN_BF16 storage of the packed / pooled /
+// concatenated tensors.
+hipError_t launch_pack(const PackArgs& a, int dtype, hipStream_t stream);
 
 struct UnpackArgs {
   const float4* net;       // tile of RGBA float32 network output, tile_w wide
@@ -224,8 +229,9 @@ struct UnpackArgs {
 };
 hipError_t launch_unpack(const UnpackArgs& a, hipStream_t stream);
 
-hipError_t launch_pool(const void* x, int h, int w, int cs, void* y, bool f16, hipStream_t stream);
+hipError_t launch_pool(const void* x, int h, int w, int cs, void* y, int dtype, hipStream_t stream);
+// b16: 16-bit storage (fp16 or bf16: a bit copy either way), else fp32.
 hipError_t launch_upcat(const void* low, int cs_low, const void* skip, int cs_skip, int h, int w,
-                        void* z, bool f16, hipStream_t stream);
+                        void* z, bool b16, hipStream_t stream);
 
 }  // namespace oidn
