@@ -2,6 +2,7 @@
 host-only logic (tile planner, layer table, weight packing, workspace plan)
 matches the oracle or the documented layout, and every argument error is
 rejected before any device work.  No GPU is touched."""
+import math
 import os
 import re
 
@@ -79,7 +80,7 @@ def test_layer_table_matches_oracle(in_channels):
 COMBO_ROWS = [(0,), (1, 2), (0, 1), (2,)]   # ky rows summed into each upsampled-chunk combination
 
 
-def _decode_f16(packed, cin0, cin1, cout):
+def _decode_f16(packed, cin0, cin1, cout, bf16=False):
     """Decode the fp16 fragment layout from its documented description:
     bias (16 * nf floats, 256-aligned), then per chunk (<= 32 stored channels
     of one source, sources and channels in order, processed as cg = 4 groups
@@ -96,7 +97,11 @@ def _decode_f16(packed, cin0, cin1, cout):
     nf = -(-O.stored(cout) // 16)
     bias_bytes = -(-(4 * 16 * nf) // 256) * 256
     bias = packed[:4 * cout].view(np.float32)
-    frags = packed[bias_bytes:].view(np.float16).reshape(-1, 64, 8)
+    if bf16:   # bf16 bits are the upper half of the float32 bits
+        u = packed[bias_bytes:].view(np.uint16).astype(np.uint32) << 16
+        frags = u.view(np.float32).reshape(-1, 64, 8)
+    else:
+        frags = packed[bias_bytes:].view(np.float16).reshape(-1, 64, 8)
     w = np.full((cout, 3, 3, cin0 + cin1), np.nan, np.float32)
     combos = np.full((cout, 4, 3, cin0 + cin1), np.nan, np.float32)
     chunks = [(s_idx, off, 4 if min(32, cs[s_idx] - off) > 16 else 2)
@@ -133,22 +138,37 @@ def _decode_f16(packed, cin0, cin1, cout):
     return w, combos, bias
 
 
+def _bf16_once(v):
+    """float64 -> nearest bfloat16 (8 significant bits, ties to even), one
+    rounding: scale the value so its last kept bit is the units bit and let
+    Python's round() (half to even) do it.  Normal range only."""
+    def one(x):
+        if x == 0.0:
+            return x
+        e = math.frexp(x)[1]
+        return round(x * 2.0 ** (8 - e)) * 2.0 ** (e - 8)
+    return np.vectorize(one, otypes=[np.float64])(np.asarray(v, np.float64)).astype(np.float32)
+
+
+@pytest.mark.parametrize("precision", ["f16", "bf16"])
 @pytest.mark.parametrize("cin0,cin1,cout", [(9, 0, 32), (32, 0, 48), (64, 9, 64), (96, 64, 112),
                                             (5, 0, 3), (36, 0, 20), (20, 12, 16)])
-def test_f16_weight_layout_round_trip(cin0, cin1, cout):
+def test_f16_weight_layout_round_trip(cin0, cin1, cout, precision):
     r = np.random.default_rng(cin0 + cout)
     w = r.standard_normal((cout, 3, 3, cin0 + cin1)).astype(np.float32)
     b = r.standard_normal(cout).astype(np.float32)
-    packed = U.oidn_conv3x3_pack_weights_host(w, b, cin0, cin1, cout, U.OIDN_F16)
-    wd, cd, bd = _decode_f16(packed, cin0, cin1, cout)
+    dt = U.OIDN_BF16 if precision == "bf16" else U.OIDN_F16
+    packed = U.oidn_conv3x3_pack_weights_host(w, b, cin0, cin1, cout, dt)
+    wd, cd, bd = _decode_f16(packed, cin0, cin1, cout, precision == "bf16")
+    once = _bf16_once if precision == "bf16" else (lambda v: np.asarray(v).astype(np.float16).astype(np.float32))
     n_up = cin0 if cin1 else 0   # the upsampled source's channels come first
     assert not np.any(np.isnan(wd[..., n_up:]))
-    assert np.array_equal(wd[..., n_up:], w[..., n_up:].astype(np.float16).astype(np.float32))
+    assert np.array_equal(wd[..., n_up:], once(w[..., n_up:]))
     if n_up:
         assert np.all(np.isnan(wd[..., :n_up])) and not np.any(np.isnan(cd[..., :n_up]))
         for a, rows in enumerate(COMBO_ROWS):
             want = sum(w[:, ky, :, :n_up].astype(np.float64) for ky in rows)
-            assert np.array_equal(cd[:, a, :, :n_up], want.astype(np.float16).astype(np.float32)), a
+            assert np.array_equal(cd[:, a, :, :n_up], once(want)), a
     assert np.array_equal(bd, b)
 
 
