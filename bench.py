@@ -124,6 +124,8 @@ def main():
     ap.add_argument("--height", type=int, default=1080)
     ap.add_argument("--max-tile", type=int, default=0)
     ap.add_argument("--overlap", type=int, default=32)
+    ap.add_argument("--cold-frames", type=int, default=20,
+                    help="frames timed one by one after an Infinity Cache flush (0: none)")
     ap.add_argument("--dtype", choices=["f16", "bf16"], default="f16",
                     help="16-bit storage of the network (the metric is quoted on f16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -196,6 +198,21 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
+    # cold Infinity Cache (256 MB): frames timed one by one, each after a
+    # 512 MB buffer was written outside its timed interval (not `value`)
+    cold = []
+    if args.cold_frames > 0:
+        flush = torch.empty(512 * 2 ** 20 // 4, dtype=torch.float32, device="cuda")
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(args.cold_frames):
+            flush.fill_(1.0)
+            c0.record()
+            step()
+            c1.record()
+            torch.cuda.synchronize()
+            cold.append(c0.elapsed_time(c1))
+        del flush
+
     # per-kernel durations (first tile of each instrumented step)
     dur = np.zeros((len(inst), nk))
     for n, k in enumerate(inst):
@@ -205,6 +222,43 @@ def main():
         for e in evs:
             U.oidn_event_destroy(e)
     avg_ms = dur.mean(axis=0)
+
+    # the first pair may run the input pass in its staging (input bit 1), the
+    # last the output pass in its epilogue (output field 2)
+    def pair_fields(layer):
+        sym = U.oidn_unet_layer_kernel(9, layer, tw, th, DTYPE)[0]
+        if not sym.startswith("conv3x3_pair_"):
+            return None
+        return [int(f) for f in sym[sym.index("<") + 1:-1].split(", ")]
+    first, last = pair_fields(0), pair_fields(U.oidn_unet_layer_count() - 1)
+    in_fused = first is not None and (first[3] & 2) != 0
+    out_fused = last is not None and last[2] == 2
+
+    def layer_bytes(i, c0, c1, co, level, flags, px):
+        """Algorithmic HBM bytes of one layer at 16-bit storage: its sources
+        once (an upsampled source at half resolution; the network input as
+        the three RGBA images plus the packed tile the input pass writes, or
+        the packed tile) and its output once (pooled if the layer pools; the
+        last layer's image write plus the alpha read when it runs the output
+        pass, else its fp32 RGBA)."""
+        st = lambda c: 4 * -(-c // 4)
+        lanes = lambda c: 8 * -(-st(c) // 8)         # 16-byte channel groups
+        if i == 0:
+            b_in = px * (48 + 2 * lanes(c0)) if in_fused else px * 2 * lanes(c0)
+        else:
+            b_in = (px / 4 if c1 else px) * 2 * st(c0)
+        if c1:
+            b_in += px * 2 * lanes(c1)
+        px_out = px / 4 if flags & U.OIDN_POOL2X2 else px
+        if i == U.oidn_unet_layer_count() - 1:
+            b_out = px_out * (32 if out_fused else 16)
+        else:
+            b_out = px_out * 2 * st(co)
+        return b_in, b_out
+
+    def roof_frac(flops, nbytes, ms):
+        roof = min(PEAK_F16_TFLOPS, flops / nbytes * PEAK_HBM_GBS / 1e3)   # TFLOP/s
+        return round(flops / ms / 1e9 / roof, 4), ("mfma" if roof == PEAK_F16_TFLOPS else "hbm")
 
     layers = []
     groups = {}
@@ -220,6 +274,7 @@ def main():
         ms = float(avg_ms[i + 1])
         sym, nblocks = U.oidn_unet_layer_kernel(9, i, tw, th, DTYPE)
         nblocks *= nbatch
+        b_in, b_out = layer_bytes(i, c0, c1, co, level, flags, px)
         conv_flops += flops
         conv_ms += ms
         g = groups.setdefault(sym, {"flops": 0.0, "ms": 0.0, "launches": 0})
@@ -232,30 +287,26 @@ def main():
             prev["flops"] += flops
             prev["us"] = round(prev["us"] + ms * 1e3, 2)
             prev["tflops"] = round(prev["flops"] / (prev["us"] / 1e3) / 1e9, 1)
+            prev["bytes"] = prev["b_in"] + b_out     # the intermediate stays on chip
+            prev["roof_frac"], prev["roof"] = roof_frac(prev["flops"], prev["bytes"],
+                                                        prev["us"] / 1e3)
             print(f"  {name:11s}  (fused into the previous launch)", file=sys.stderr)
             prev_sym = None
             continue
         g["launches"] += 1
         prev_sym = sym
+        fr, bound = roof_frac(flops, b_in + b_out, ms)
         layers.append({"layer": name, "us": round(ms * 1e3, 2), "flops": flops,
-                       "tflops": round(flops / ms / 1e9, 1), "kernel": sym, "blocks": nblocks})
+                       "tflops": round(flops / ms / 1e9, 1), "roof": bound, "roof_frac": fr,
+                       "bytes": b_in + b_out, "b_in": b_in, "kernel": sym, "blocks": nblocks})
         print(f"  {name:11s} {ms * 1e3:8.1f} us  {flops / ms / 1e9:7.1f} TFLOP/s  {sym} x{nblocks}",
               file=sys.stderr)
     for L in layers:
-        del L["flops"]
+        L["mb"] = round(L.pop("bytes") / 1e6, 1)
+        del L["flops"], L["b_in"]
     px0 = tw * th
     pack_bytes = W * H * 48 + px0 * 16 * 2 if len(tiles) == 1 else None   # 16 lanes fp16 out
     unpack_bytes = W * H * (32 + 16)
-    # the first pair may run the input pass in its staging (input bit 1), the
-    # last the output pass in its epilogue (output field 2)
-    def pair_fields(layer):
-        sym = U.oidn_unet_layer_kernel(9, layer, tw, th, DTYPE)[0]
-        if not sym.startswith("conv3x3_pair_"):
-            return None
-        return [int(f) for f in sym[sym.index("<") + 1:-1].split(", ")]
-    first, last = pair_fields(0), pair_fields(U.oidn_unet_layer_count() - 1)
-    in_fused = first is not None and (first[3] & 2) != 0
-    out_fused = last is not None and last[2] == 2
     for j, nm, fused, where in ((0, "input pass", in_fused, "first conv's staging"),
                                 (nk - 1, "output pass", out_fused, "last conv's epilogue")):
         note = f"  (in the {where})" if fused else ""
@@ -302,6 +353,12 @@ def main():
             "peak_gbs": PEAK_HBM_GBS},
         "layers": layers,
     }
+    if cold:
+        result["cold_cache"] = {"frames": len(cold), "flush_mb": 512,
+                                "ms_median": round(float(np.median(cold)), 4),
+                                "ms_p10": round(float(np.percentile(cold, 10)), 4),
+                                "ms_p90": round(float(np.percentile(cold, 90)), 4),
+                                "note": "each frame timed alone after writing 512 MB; not value"}
 
     if args.copy_calibration:
         a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
