@@ -88,6 +88,29 @@ def test_end_to_end_tiled_matches_oracle(precision):
     assert err <= TOL[precision]
 
 
+@pytest.mark.parametrize("in_channels,hdr,precision", [(3, False, "f16"), (6, False, "bf16"),
+                                                      (3, True, "bf16"), (6, True, "f16")])
+def test_end_to_end_input_variants(in_channels, hdr, precision):
+    """Colour only or colour + albedo, HDR log or LDR clamp, through the
+    fused input and output passes: 160x96, 64-pixel tiles, overlap 16 (15
+    tiles of 64x64, one batch), against the oracle on the same plan."""
+    assert len(U.oidn_plan_tiles(160, 96, 64, 16)) == 15
+    color, albedo, normal, ws, bs = make_case(160, 96, in_channels, seed=in_channels + 10 * hdr)
+    if not hdr:
+        r = np.random.default_rng(5)
+        color[..., :3] = r.uniform(-0.1, 1.1, color[..., :3].shape).astype(np.float32)
+    scale = 0.8 if hdr else 1.0
+    got = gpu_denoise(ws, bs, color, albedo, normal, precision, 64, 16, hdr=hdr, scale=scale)
+    ref = O.unet_forward(ws, bs, color, albedo, normal, hdr, scale, 64, 16, precision)
+    assert not np.any(np.isnan(got))
+    assert np.array_equal(got[..., 3], color[..., 3])
+    if not hdr:
+        assert got[..., :3].min() >= 0.0 and got[..., :3].max() <= 1.0
+    err = rel_err(got, ref)
+    say(f"end-to-end in={in_channels} hdr={hdr} {precision}: max_rel_err={err:.3e}")
+    assert err <= TOL[precision]
+
+
 def test_tiled_equals_untiled_at_default_overlap():
     """At overlap 96 (>= the receptive reach) tiling does not change the result;
     the kernels' reduction order does not depend on position, so it is bit-exact."""
