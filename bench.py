@@ -226,7 +226,7 @@ def main():
     # the first pair may run the input pass in its staging (input bit 1), the
     # last the output pass in its epilogue (output field 2)
     def pair_fields(layer):
-        sym = U.oidn_unet_layer_kernel(9, layer, tw, th, DTYPE)[0]
+        sym = U.oidn_unet_layer_kernel(9, layer, tw, th, DTYPE, nbatch)[0]
         if not sym.startswith("conv3x3_pair_"):
             return None
         return [int(f) for f in sym[sym.index("<") + 1:-1].split(", ")]
@@ -272,8 +272,7 @@ def main():
         # ky taps pre-summed per row parity), so 6 taps for those c0 channels
         flops = 2.0 * px * co * ((6 * c0 + 9 * c1) if c1 else 9 * c0)
         ms = float(avg_ms[i + 1])
-        sym, nblocks = U.oidn_unet_layer_kernel(9, i, tw, th, DTYPE)
-        nblocks *= nbatch
+        sym, nblocks = U.oidn_unet_layer_kernel(9, i, tw, th, DTYPE, nbatch)
         b_in, b_out = layer_bytes(i, c0, c1, co, level, flags, px)
         conv_flops += flops
         conv_ms += ms

@@ -238,8 +238,9 @@ int oidn_unet_layer_count(void);
 int oidn_unet_layer_info(int in_channels, int layer, int* cin0, int* cin1, int* cout,
                          int* level, unsigned* flags, const char** name);
 
-/* Name of the kernel instance that runs `layer` on a tw x th tile (for
- * matching per-kernel timings and profiles), written NUL-terminated into
+/* Name of the kernel instance that runs `layer` on `batch` tw x th tiles per
+ * launch (oidn_unet_tile_batch; the launch plan counts the whole launch's
+ * workgroups) (for matching per-kernel timings and profiles), written NUL-terminated into
  * buf (cap bytes), e.g. "conv3x3_f16_mfma<2, 16, 2, false>" (fragments and
  * rows per wave, row groups, fp32 output) or, for both layers of a fused
  * pair, "conv3x3_pair_f16<2, 2, 0, 3>" (convA channel groups, convB
@@ -247,8 +248,8 @@ int oidn_unet_layer_info(int in_channels, int layer, int* cin0, int* cin1, int* 
  * input: bit 0 tap-packed, bit 1 the caller's images through the input pass);
  * with bf16 storage "conv3x3_bf16_mfma" and "conv3x3_pair_bf16".  *blocks
  * receives the launch's workgroup count.  Host only. */
-int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int dtype, char* buf,
-                           int cap, int* blocks);
+int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int batch, int dtype,
+                           char* buf, int cap, int* blocks);
 
 /* Bytes of the packed weights of all sixteen layers.  With 9 input channels
  * on the 16-bit paths the blob also holds a second copy of enc_conv0's and

@@ -207,6 +207,22 @@ def test_workspace_plan_is_liveness_bounded():
     assert full >= 1920 * 1088 * (12 * 2 + 16)
 
 
+def test_batched_launch_plans_count_the_whole_launch():
+    """With 12 tiles of 1024x784 per launch the planner sees 12x the
+    workgroups: the deep and middle layers take the larger plans a single
+    big tile gets, and the reported workgroups are the launch's."""
+    F = U.OIDN_F16
+    for i in range(U.oidn_unet_layer_count()):
+        one, nb1 = U.oidn_unet_layer_kernel(9, i, 1024, 784, F)
+        bat, nb12 = U.oidn_unet_layer_kernel(9, i, 1024, 784, F, 12)
+        if one == bat:
+            assert nb12 == 12 * nb1, (i, one)
+    assert U.oidn_unet_layer_kernel(9, 11, 1024, 784, F, 12)[0] == "conv3x3_f16_mfma<4, 8, 4, false>"
+    assert U.oidn_unet_layer_kernel(9, 11, 1024, 784, F)[0] != "conv3x3_f16_mfma<4, 8, 4, false>"
+    with pytest.raises(U.OidnError):
+        U.oidn_unet_layer_kernel(9, 0, 1024, 784, F, 17)
+
+
 def test_tile_batch_and_its_workspace():
     """The fp16 end-to-end path runs up to 16 same-size tiles per launch, each
     with its own copy of the per-tile plan; fp32 runs tiles one by one."""

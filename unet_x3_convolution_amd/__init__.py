@@ -81,7 +81,7 @@ _SIGS = {
     "oidn_unet_layer_info": ([_i, _i, ctypes.POINTER(_i), ctypes.POINTER(_i), ctypes.POINTER(_i),
                               ctypes.POINTER(_i), ctypes.POINTER(_u),
                               ctypes.POINTER(ctypes.c_char_p)], _i),
-    "oidn_unet_layer_kernel": ([_i, _i, _i, _i, _i, ctypes.c_char_p, _i, ctypes.POINTER(_i)], _i),
+    "oidn_unet_layer_kernel": ([_i, _i, _i, _i, _i, _i, ctypes.c_char_p, _i, ctypes.POINTER(_i)], _i),
     "oidn_conv3x3_pair": ([_vp, _i, _i, _i, _vp, _vp, _vp, _i, _i, _u, _vp], _i),
     "oidn_conv3x3_kernel": ([_i, _i, _i, _i, _i, _i, _i, _u, ctypes.c_char_p, _i,
                              ctypes.POINTER(_i)], _i),
@@ -271,11 +271,13 @@ def oidn_conv3x3_kernel(h: int, w: int, cin0: int, cin1: int, cout: int, in_dtyp
     return buf.value.decode(), nb.value
 
 
-def oidn_unet_layer_kernel(in_channels: int, layer: int, tw: int, th: int, dtype: int):
-    """(kernel instance name, workgroups) of a layer on a tw x th tile."""
+def oidn_unet_layer_kernel(in_channels: int, layer: int, tw: int, th: int, dtype: int,
+                           batch: int = 1):
+    """(kernel instance name, workgroups) of a layer on `batch` tw x th tiles
+    per launch."""
     buf = ctypes.create_string_buffer(128)
     nb = _i()
-    _check(lib().oidn_unet_layer_kernel(in_channels, layer, tw, th, dtype, buf, 128,
+    _check(lib().oidn_unet_layer_kernel(in_channels, layer, tw, th, batch, dtype, buf, 128,
                                         ctypes.byref(nb)))
     return buf.value.decode(), nb.value
 

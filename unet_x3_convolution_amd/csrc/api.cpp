@@ -1029,9 +1029,10 @@ int oidn_unet_layer_info(int in_channels, int layer, int* cin0, int* cin1, int* 
   return ok();
 }
 
-int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int dtype, char* buf,
-                           int cap, int* blocks) {
+int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int batch, int dtype,
+                           char* buf, int cap, int* blocks) {
   if (!buf || cap <= 0) return fail(OIDN_E_INVALID, "null or empty name buffer");
+  if (batch < 1 || batch > kMaxBatch) return fail(OIDN_E_INVALID, "batch %d out of range", batch);
   int rc = check_network_tile(in_channels, tw, th, dtype);
   if (rc) return rc;
   if (layer < 0 || layer >= kLayers) return fail(OIDN_E_INVALID, "layer %d out of range", layer);
@@ -1055,20 +1056,21 @@ int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int dtype
     snprintf(buf, cap, "conv3x3_pair_%s<%d, %d, %d, %d>", dtype == OIDN_BF16 ? "bf16" : "f16",
              st > 16 ? 4 : 2, cdiv(stored_channels(s[first + 1].cout), 16), out, in);
     (void)cs;
-    nb = conv_pair_blocks(fh, fw);
+    nb = conv_pair_blocks(fh, fw) * batch;
   } else if (b16(dtype)) {
     // as oidn_unet_forward runs it: the input packed with a multiple of 8 lanes
     const int in_cs = internal_input_lanes(in_channels, dtype);
     const Layer& L = kUNet[layer];
     ConvLayout lay;
-    const ConvF16Args a = f16_args(s[layer].cin0, s[layer].cin1, s[layer].cout, h, w,
-                                   L.src == 0 ? in_cs : 0, L.skip == 0 ? in_cs : 0, &lay,
-                                   unet_taps(in_channels, dtype) ? unet_tap_src(layer) : -1);
+    ConvF16Args a = f16_args(s[layer].cin0, s[layer].cin1, s[layer].cout, h, w,
+                             L.src == 0 ? in_cs : 0, L.skip == 0 ? in_cs : 0, &lay,
+                             unet_taps(in_channels, dtype) ? unet_tap_src(layer) : -1);
+    a.batch = batch;
     conv_f16_describe(a, lay.nf, final_layer, dtype == OIDN_BF16, buf, cap, &nb);
   } else {
     snprintf(buf, cap, "conv3x3_f32_direct");
     const int oh = kUNet[layer].pool ? h / 2 : h, ow = kUNet[layer].pool ? w / 2 : w;
-    nb = (int)cdiv(ow * oh * (stored_channels(s[layer].cout) / 4), 256);
+    nb = (int)cdiv(ow * oh * (stored_channels(s[layer].cout) / 4), 256) * batch;
   }
   if (blocks) *blocks = nb;
   return ok();

@@ -1165,14 +1165,14 @@ long plan_blocks(int h, int w, int nf, const ConvPlan& P) {
   return (long)cdiv(cdiv(w, TW) * cdiv(h, P.wr * P.rows), kXcds) * kXcds * (nf / frags);
 }
 
-ConvPlan conv_f16_plan(int h, int w, int nf, int nchunks, int nup) {
+ConvPlan conv_f16_plan(int h, int w, int nf, int nchunks, int nup, int batch) {
   ConvPlan best{};
   long most = -1;
   const ConvPlan* cand = plan_candidates(nf, nchunks, nup);
   for (int i = 0; i < kMaxCandidates; ++i) {
     const ConvPlan& P = cand[i];
     if (P.rows == 0) break;
-    const long b = plan_blocks(h, w, nf, P);
+    const long b = plan_blocks(h, w, nf, P) * (batch > 1 ? batch : 1);   // the whole launch
     if (b >= kMinBlocks) return P;
     if (b > most) {
       most = b;
@@ -1186,8 +1186,9 @@ ConvPlan conv_f16_plan(int h, int w, int nf, int nchunks, int nup) {
 int plan_block_frags(const ConvPlan& P) { return P.nfw * (4 / P.wr); }
 
 // Workgroups of the launch (for reporting).
-int conv_f16_blocks(int h, int w, int nf, int nchunks, int nup) {
-  return (int)plan_blocks(h, w, nf, conv_f16_plan(h, w, nf, nchunks, nup));
+int conv_f16_blocks(int h, int w, int nf, int nchunks, int nup, int batch) {
+  return (int)plan_blocks(h, w, nf, conv_f16_plan(h, w, nf, nchunks, nup, batch)) *
+         (batch > 1 ? batch : 1);
 }
 
 bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out,
@@ -1238,10 +1239,10 @@ bool conv_f16_layout(int cin0_stored, int cin1_stored, int cout, ConvLayout* out
 void conv_f16_describe(const ConvF16Args& a, int nf, bool out_f32, bool bf16, char* buf, int cap,
                        int* blocks) {
   const int h = a.h, w = a.w;
-  const ConvPlan P = conv_f16_plan(h, w, nf, a.nchunks, a.nup);
+  const ConvPlan P = conv_f16_plan(h, w, nf, a.nchunks, a.nup, a.batch);
   snprintf(buf, cap, "conv3x3_%s_mfma<%d, %d, %d, %s>", bf16 ? "bf16" : "f16", P.nfw, P.rows, P.wr,
            out_f32 ? "true" : "false");
-  *blocks = conv_f16_blocks(h, w, nf, a.nchunks, a.nup);
+  *blocks = conv_f16_blocks(h, w, nf, a.nchunks, a.nup, a.batch);
 }
 
 hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, bool relu,
@@ -1249,7 +1250,7 @@ hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, 
   if (a.batch > 65535) return hipErrorInvalidValue;
   ConvF16Args b = a;
   b.nf = nf;
-  const ConvPlan P = conv_f16_plan(a.h, a.w, nf, a.nchunks, a.nup);
+  const ConvPlan P = conv_f16_plan(a.h, a.w, nf, a.nchunks, a.nup, a.batch);
   const int nsplit = nf / plan_block_frags(P);
   return launch_plan(b, P, nsplit, upcat, pool, relu, out_f32, bf16, stream);
 }

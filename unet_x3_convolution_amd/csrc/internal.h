@@ -113,8 +113,9 @@ hipError_t launch_conv_f16(const ConvF16Args& a, int nf, bool upcat, bool pool, 
 struct ConvPlan {
   int rows, nfw, wr;
 };
-ConvPlan conv_f16_plan(int h, int w, int nf, int nchunks, int nup);
-int conv_f16_blocks(int h, int w, int nf, int nchunks, int nup);
+// batch: tiles in the launch; the plan counts the whole launch's workgroups.
+ConvPlan conv_f16_plan(int h, int w, int nf, int nchunks, int nup, int batch = 1);
+int conv_f16_blocks(int h, int w, int nf, int nchunks, int nup, int batch = 1);
 
 // Name of the kernel instance launch_conv_f16 would run for `a` (h, w,
 // cs0, cs1 and the chunk fields set) and its grid.
