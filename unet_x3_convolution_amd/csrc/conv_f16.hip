@@ -1141,6 +1141,11 @@ hipError_t launch_plan(const ConvF16Args& a, const ConvPlan& P, int nsplit, bool
 // in one workgroup, small deep layers split the output channels.  For
 // nf = 4 with four or more K chunks per tile, waves of four fragments win.
 constexpr long kMinBlocks = 480;
+// Tiles of a batched launch the count above takes in: at most 4.  Counting
+// all of them (12 at 4K) lets plans through whose workgroups run long serial
+// chains (dec_conv4a at 4K: 7 fragments x 5 chunks per workgroup, 114 vs
+// 66 us); 3 to 8 measured alike.
+constexpr int kPlanBatchCap = 4;
 constexpr int kMaxCandidates = 4;
 const ConvPlan kPlanCandidates[9][kMaxCandidates] = {
     {},
@@ -1172,7 +1177,8 @@ ConvPlan conv_f16_plan(int h, int w, int nf, int nchunks, int nup, int batch) {
   for (int i = 0; i < kMaxCandidates; ++i) {
     const ConvPlan& P = cand[i];
     if (P.rows == 0) break;
-    const long b = plan_blocks(h, w, nf, P) * (batch > 1 ? batch : 1);   // the whole launch
+    const long b = plan_blocks(h, w, nf, P) * (batch > kPlanBatchCap ? kPlanBatchCap
+                                                : batch > 1 ? batch : 1);
     if (b >= kMinBlocks) return P;
     if (b > most) {
       most = b;
