@@ -216,6 +216,55 @@ def test_decoder_conv_matches_oracle(h, w, c_low, c_skip, cout, precision):
     check(got, ref, cout, precision, f"upcat conv {precision} {h}x{w} [{c_low}|{c_skip}]->{cout}")
 
 
+def _random_cases(seed, n):
+    """Seeded conv shapes across the kernel's regimes: ragged sizes, channel
+    counts off the 4-, 8- and 16-lane grids, pooled or fp32 outputs, an
+    upsampled source with a skip."""
+    r = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        upcat = bool(r.random() < 0.35)
+        h = 2 * int(r.integers(1, 150))
+        w = 2 * int(r.integers(1, 200))
+        cin = 4 * int(r.integers(1, 33)) if upcat else int(r.integers(1, 161))
+        cskip = int(r.integers(1, 65)) if upcat else 0
+        cin = min(cin, 160 - cskip) if upcat else cin
+        cout = int(r.integers(1, 129))
+        pool = (not upcat) and bool(r.random() < 0.4)
+        outp = "f32" if r.random() < 0.2 else None
+        cases.append((h, w, cin, cskip, cout, pool, outp))
+    return cases
+
+
+@pytest.mark.parametrize("precision", ["f16", "bf16"])
+@pytest.mark.parametrize("idx", range(12))
+def test_conv_random_shapes(precision, idx):
+    h, w, cin, cskip, cout, pool, outp = _random_cases(77 if precision == "f16" else 78, 12)[idx]
+    outp = outp or precision
+    r = np.random.default_rng(idx)
+    wt = S.he_normal(r, cout, cin + cskip)
+    b = S.bias(r, cout)
+    flags = U.OIDN_RELU | (U.OIDN_POOL2X2 if pool else 0)
+    name = U.oidn_conv3x3_kernel(h, w, cin, cskip, cout, DT[precision], DT[outp], flags)[0]
+    label = f"random conv {precision} {h}x{w} [{cin}|{cskip}]->{cout} pool={pool} out={outp} {name}"
+    say(label)
+    if cskip:
+        low = O.round_to(S.relu_normal_activation(r, h // 2, w // 2, cin, cin), precision)
+        skip = O.round_to(S.relu_normal_activation(r, h, w, cskip, O.stored(cskip)), precision)
+        pk = packed_conv(wt, b, cin, cskip, cout, precision)
+        y = alloc((h, w, O.stored(cout)), outp, fill=float("nan"))
+        U.oidn_conv3x3_upcat(to_dev(low, precision), cin, to_dev(skip, precision), cskip, h, w, pk,
+                             y, cout, DT[precision], DT[outp], flags)
+        got = host(y)
+        ref = O.conv3x3(O.upsample_concat(low, cin, skip, cskip), cin + cskip, wt, b, True,
+                        precision, outp)
+    else:
+        x = O.round_to(S.relu_normal_activation(r, h, w, cin, O.stored(cin)), precision)
+        got = run_conv(x, cin, wt, b, cout, precision, flags, outp)
+        ref = oracle_conv(x, cin, wt, b, cout, precision, flags, outp)
+    check(got, ref, cout, precision, label)
+
+
 def test_conv_ladder_config2():
     """256x256 fp16: 32->48->64->80->96->96, conv+ReLU then 2x2 pool per stage;
     each stage is checked against the oracle on the GPU's own stage input."""
