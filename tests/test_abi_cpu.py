@@ -222,7 +222,8 @@ def test_batched_launch_plans_count_the_whole_launch():
     # at most 4 tiles count: dec_conv4a keeps one fragment per wave rather
     # than 7-fragment workgroups
     assert U.oidn_unet_layer_kernel(9, 7, 1024, 784, F, 12)[0] == "conv3x3_f16_mfma<1, 4, 4, false>"
-    assert U.oidn_unet_layer_kernel(9, 7, 1024, 784, F, 4) == U.oidn_unet_layer_kernel(9, 7, 1024, 784, F, 12)[:1] + (U.oidn_unet_layer_kernel(9, 7, 1024, 784, F, 4)[1],)
+    assert (U.oidn_unet_layer_kernel(9, 7, 1024, 784, F, 4)[0] ==
+            U.oidn_unet_layer_kernel(9, 7, 1024, 784, F, 12)[0])
     with pytest.raises(U.OidnError):
         U.oidn_unet_layer_kernel(9, 0, 1024, 784, F, 17)
 
