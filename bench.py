@@ -141,8 +141,9 @@ def main():
         traffic_summary(*args.traffic_summary)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(tiles would shard across GPUs; see the design notes)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the tiles of a frame, or whole frames, would be dealt out to one process "
+              "per GPU)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -43,7 +43,7 @@ extern "C" {
 /* ---- status codes ------------------------------------------------------ */
 #define OIDN_OK              0
 #define OIDN_E_INVALID      -1  /* null pointer, bad size, bad enum          */
-#define OIDN_E_UNSUPPORTED  -2  /* valid request this build does not handle */
+#define OIDN_E_UNSUPPORTED  -2  /* valid request the library does not handle */
 #define OIDN_E_WORKSPACE    -3  /* workspace or output capacity too small    */
 #define OIDN_E_HIP          -4  /* a HIP runtime call or launch failed       */
 

@@ -26,7 +26,7 @@ _createExecution: the final node writes an f32 buffer).  Sums are taken in
 float64, so only accumulation order separates this from an fp32-accumulating
 GPU path.
 
-Readings where the pages are silent (each is also listed in the design notes):
+Readings where the pages are silent:
 
 * the UNet wiring (the ``modelSpec`` module is not on the pages): skips are the
   pool outputs pool1..pool3 and the packed network input; the decoder concat
