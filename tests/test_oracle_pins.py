@@ -44,6 +44,8 @@ def test_bf16_rounding_closed_forms():
         (1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -6),   # tie between odd and even -> even
         (1.0 + 2.0 ** -8 + 2.0 ** -20, 1.0 + 2.0 ** -7),   # above the tie -> up
         (-(3.0 + 2.0 ** -7), -3.0),               # tie below 4: ulp 2^-6, even is 3
+        (2.0 - 2.0 ** -9, 2.0),                   # rounding up carries into the exponent
+        (2.0 - 2.0 ** -8, 2.0),                   # tie: fraction 0x7F is odd -> 2.0
         (bmax, bmax),
         (bmax + 2.0 ** 119, math.inf),            # tie at the top rounds to overflow
         (2.0 ** -133, 2.0 ** -133),               # subnormals kept
