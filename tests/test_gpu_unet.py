@@ -111,6 +111,42 @@ def test_end_to_end_input_variants(in_channels, hdr, precision):
     assert err <= TOL[precision]
 
 
+@pytest.mark.parametrize("w,h,precision", [(1, 1, "f16"), (5, 3, "bf16"), (17, 2, "f32"),
+                                           (2, 33, "f16"), (31, 17, "bf16"), (1, 40, "f32")])
+def test_end_to_end_tiny_images(w, h, precision):
+    """Images smaller than one 16-pixel alignment step or one pair tile, one
+    pixel wide or high: the plan pads them to a 16-aligned tile whose deepest
+    level is 1 x 1 (or 1 x 3); every pass must still match the oracle and
+    write exactly the image."""
+    color, albedo, normal, ws, bs = make_case(w, h, seed=w * 100 + h)
+    got = gpu_denoise(ws, bs, color, albedo, normal, precision, 0, 16)
+    ref = O.unet_forward(ws, bs, color, albedo, normal, True, 1.0, 0, 16, precision)
+    assert got.shape == (h, w, 4) and not np.any(np.isnan(got))
+    assert np.array_equal(got[..., 3], color[..., 3])
+    err = rel_err(got, ref)
+    say(f"tiny {w}x{h} {precision}: max_rel_err={err:.3e}")
+    assert err <= TOL[precision]
+
+
+@pytest.mark.parametrize("w,h,tile,precision", [(240, 144, 64, "f16"), (208, 208, 48, "bf16")])
+def test_end_to_end_several_batches(w, h, tile, precision):
+    """More same-size tiles than one launch takes (40 tiles: batches of 16,
+    16 and 8; 169 tiles of 48 x 48: ten full batches and one of 9), overlap
+    16: every batch, the partial last one included, against the oracle on
+    the same plan."""
+    ntiles = len(U.oidn_plan_tiles(w, h, tile, 16))
+    batch = U.oidn_unet_tile_batch(9, w, h, tile, 16, DT[precision])
+    assert ntiles > batch > 1 and ntiles % batch != 0
+    color, albedo, normal, ws, bs = make_case(w, h, seed=w + h)
+    got = gpu_denoise(ws, bs, color, albedo, normal, precision, tile, 16)
+    ref = O.unet_forward(ws, bs, color, albedo, normal, True, 1.0, tile, 16, precision)
+    assert not np.any(np.isnan(got))
+    assert np.array_equal(got[..., 3], color[..., 3])
+    err = rel_err(got, ref)
+    say(f"{ntiles} tiles in batches of {batch}, {precision}: max_rel_err={err:.3e}")
+    assert err <= TOL[precision]
+
+
 def test_tiled_equals_untiled_at_default_overlap():
     """At overlap 96 (>= the receptive reach) tiling does not change the result;
     the kernels' reduction order does not depend on position, so it is bit-exact."""
@@ -121,26 +157,28 @@ def test_tiled_equals_untiled_at_default_overlap():
     assert np.array_equal(tiled, untiled)
 
 
-def test_fused_io_passes_equal_separate_passes_bit_exact():
-    """On the fp16 path the first fused pair reads the images through the input
-    pass and the last writes the image through the output pass.  With 6 input
-    channels (no tap-packed weights) the end-to-end call must give the same
-    bits as the three separate calls per tile: input pass, network with a
-    float32 output, output pass; 12 tiles with ragged output rectangles."""
+@pytest.mark.parametrize("precision", ["f16", "bf16"])
+def test_fused_io_passes_equal_separate_passes_bit_exact(precision):
+    """On the 16-bit paths the first fused pair reads the images through the
+    input pass and the last writes the image through the output pass.  With 6
+    input channels (no tap-packed weights) the end-to-end call must give the
+    same bits as the three separate calls per tile: input pass, network with
+    a float32 output, output pass; 12 tiles with ragged output rectangles."""
     color, albedo, normal, ws, bs = make_case(200, 150, in_channels=6, seed=8)
-    F = DT["f16"]
+    F = DT[precision]
+    kind = "pair_" + precision
     name = U.oidn_unet_layer_kernel(6, 15, 128, 128, F)[0]
-    assert name.startswith("conv3x3_pair_f16<") and name.split(", ")[2] == "2", name
+    assert name.startswith(f"conv3x3_{kind}<") and name.split(", ")[2] == "2", name
     first = U.oidn_unet_layer_kernel(6, 0, 128, 128, F)[0]
-    assert first == "conv3x3_pair_f16<2, 2, 0, 2>", first
-    got = gpu_denoise(ws, bs, color, albedo, normal, "f16", 128, 32, scale=0.75)
+    assert first == f"conv3x3_{kind}<2, 2, 0, 2>", first
+    got = gpu_denoise(ws, bs, color, albedo, normal, precision, 128, 32, scale=0.75)
     tiles = U.oidn_plan_tiles(200, 150, 128, 32)
     assert len(tiles) == 12
-    wd = packed_unet(ws, bs, 6, "f16")
+    wd = packed_unet(ws, bs, 6, precision)
     d_color, d_albedo = dev(color), dev(albedo)
     ref = empty((150, 200, 4), np.float32, fill=float("nan"))
     for ix, iy, iw, ih, ox, oy, ow, oh in tiles:
-        packed = empty((ih, iw, 8), np.float16)
+        packed = empty((ih, iw, 8), np.float16)   # 16-bit storage (fp16 or bf16 bits)
         U.oidn_pack_input(d_color, d_albedo, None, 200, 150, ix, iy, iw, ih, True,
                           U.OIDN_TRANSFER_LOG, 0.75, packed, F)
         nbytes = U.oidn_unet_packed_workspace_bytes(6, iw, ih, F)
@@ -152,7 +190,7 @@ def test_fused_io_passes_equal_separate_passes_bit_exact():
     ref = host(ref)
     assert not np.any(np.isnan(got))
     assert np.array_equal(got, ref)
-    say("fused input/output passes == pack + network + unpack, 12 tiles: bit-exact")
+    say(f"fused input/output passes == pack + network + unpack, 12 tiles, {precision}: bit-exact")
 
 
 def _oracle_rect(ws, bs, color, albedo, normal, out_rect, precision):
