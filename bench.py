@@ -115,6 +115,64 @@ def traffic_summary(fetch_dir, write_dir):
     print("\n".join(lines))
 
 
+def standalone_passes(U, torch, W, H, tw, th, dtype, d_color, d_albedo, d_normal, launches):
+    """The library's standalone bandwidth-bound passes at the 1080p shapes of
+    the network (fp16 / bf16 storage): the input pass of the whole image into
+    a tw x th tile, the output pass back, the 2x2 pool of enc_conv1's output
+    and the materialised upsample + concat that dec_conv1a would read.  Each
+    launch is timed alone with events on the stream it runs on, after 512 MB
+    of other data were read (inputs not in the 256 MB Infinity Cache, which
+    holds only clean lines, so the pass pays for no one else's write-back);
+    reported: the median, its algorithmic bytes (inputs read once, outputs
+    written once) and GB/s against the HBM peak."""
+    import numpy as np
+    dev = "cuda"
+    h16 = torch.float16
+    packed = torch.empty((th, tw, 12), dtype=h16, device=dev)
+    net = torch.rand((th, tw, 4), dtype=torch.float32, device=dev)
+    out = torch.empty((H, W, 4), dtype=torch.float32, device=dev)
+    x32 = torch.rand((th, tw, 32), device=dev).to(h16)          # enc_conv1 output
+    y32 = torch.empty((th // 2, tw // 2, 32), dtype=h16, device=dev)
+    low = torch.rand((th // 2, tw // 2, 64), device=dev).to(h16)   # dec_conv2b output
+    skip = torch.rand((th, tw, 12), device=dev).to(h16)          # packed input
+    z = torch.empty((th, tw, 76), dtype=h16, device=dev)
+    px, opx = tw * th, W * H
+    cases = [
+        ("input pass", "pack_input_kernel", opx * 48 + px * 24,
+         lambda: U.oidn_pack_input(d_color, d_albedo, d_normal, W, H, 0, 0, tw, th, True,
+                                   U.OIDN_TRANSFER_LOG, 1.0, packed, dtype)),
+        ("output pass", "unpack_output_kernel", opx * (16 + 16 + 16),
+         lambda: U.oidn_unpack_output(net, tw, th, 0, 0, d_color, W, H, 0, 0, W, H, True,
+                                      U.OIDN_TRANSFER_LOG, 1.0, out)),
+        ("pool2x2 32ch", "pool2x2_kernel", px * 64 + px // 4 * 64,
+         lambda: U.oidn_pool2x2(x32, th, tw, 32, y32, dtype)),
+        ("upsample+concat 64+12ch", "upcat_kernel", px // 4 * 128 + px * 24 + px * 152,
+         lambda: U.oidn_upsample_concat(low, 64, skip, 12, th, tw, z, dtype)),
+    ]
+    flush = torch.ones(512 * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = []
+    for name, kernel, nbytes, launch in cases:
+        launch()
+        times = []
+        for _ in range(launches):
+            flush.sum()
+            e0.record()
+            launch()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = float(np.median(times))
+        gbs = nbytes / ms / 1e6
+        res.append({"pass": name, "kernel": kernel, "us": round(ms * 1e3, 2),
+                    "mb": round(nbytes / 1e6, 1), "gbs": round(gbs, 1),
+                    "frac": round(gbs / PEAK_HBM_GBS, 4)})
+        print(f"  {name:24s} {ms * 1e3:8.1f} us  {gbs:7.1f} GB/s  ({kernel}, inputs not cached)",
+              file=sys.stderr)
+    del flush
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +187,8 @@ def main():
     ap.add_argument("--dtype", choices=["f16", "bf16"], default="f16",
                     help="16-bit storage of the network (the metric is quoted on f16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass-launches", type=int, default=10,
+                    help="cold-cache launches of each standalone bandwidth-bound pass (0: skip)")
     ap.add_argument("--events-every", type=int, default=10,
                     help="record per-kernel HIP events on every N-th timed step (event markers "
                          "between launches cost ~4 us each, so they are kept off the other steps)")
@@ -213,6 +273,10 @@ def main():
             torch.cuda.synchronize()
             cold.append(c0.elapsed_time(c1))
         del flush
+
+    passes = (standalone_passes(U, torch, W, H, tw, th, DTYPE, d_color, d_albedo, d_normal,
+                                args.pass_launches)
+              if args.pass_launches > 0 and len(tiles) == 1 else [])
 
     # per-kernel durations (first tile of each instrumented step)
     dur = np.zeros((len(inst), nk))
@@ -350,7 +414,8 @@ def main():
             "output_pass_us": round(float(avg_ms[nk - 1]) * 1e3, 2),
             "output_pass_gbs": (round(unpack_bytes / avg_ms[nk - 1] / 1e6, 1)
                                 if len(tiles) == 1 and not out_fused else None),
-            "peak_gbs": PEAK_HBM_GBS},
+            "peak_gbs": PEAK_HBM_GBS,
+            "standalone": passes},
         "layers": layers,
     }
     if cold:

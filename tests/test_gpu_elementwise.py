@@ -15,7 +15,10 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("h,w,c,precision", [(6, 10, 12, "f16"), (128, 64, 48, "f16"),
                                              (2, 2, 4, "f32"), (40, 18, 9, "f32"),
-                                             (6, 10, 12, "bf16"), (128, 64, 48, "bf16")])
+                                             (6, 10, 12, "bf16"), (128, 64, 48, "bf16"),
+                                             # more output rows than one launch's grid
+                                             # holds: the kernel steps over the rest
+                                             (70002, 4, 8, "f16"), (65540, 2, 4, "bf16")])
 def test_pool_bit_exact(h, w, c, precision):
     r = np.random.default_rng(h * w)
     x = np.zeros((h, w, O.stored(c)), O.np_storage(precision))
@@ -28,7 +31,10 @@ def test_pool_bit_exact(h, w, c, precision):
 @pytest.mark.parametrize("h,w,c_low,c_skip,precision", [(16, 16, 96, 64, "f16"),
                                                         (6, 10, 8, 9, "f16"),
                                                         (4, 2, 4, 3, "f32"),
-                                                        (6, 10, 8, 9, "bf16")])
+                                                        (6, 10, 8, 9, "bf16"),
+                                                        # rows past one launch's grid
+                                                        (70000, 4, 4, 3, "f16"),
+                                                        (66000, 2, 8, 9, "f32")])
 def test_upsample_concat_bit_exact(h, w, c_low, c_skip, precision):
     r = np.random.default_rng(h + c_low)
     low = O.round_to(r.standard_normal((h // 2, w // 2, c_low)), precision)

@@ -2,6 +2,8 @@
 // materialised nearest-2x upsample + concat.  One thread per output pixel (or
 // per 4-channel block), consecutive threads on consecutive addresses, 16-byte
 // loads where the layout allows.
+#include <type_traits>
+
 #include "internal.h"
 #include "image_io.h"
 
@@ -9,6 +11,33 @@ namespace oidn {
 namespace {
 
 constexpr int THREADS = 256;
+
+// Streaming accesses.  Inputs that a wave reads in whole 64-byte lines and
+// nothing reads again are loaded non-temporally, and outputs written in
+// whole lines are stored non-temporally: cold reads of a just-written cache
+// then do not have to evict its dirty lines first (a 150 MB copy moves
+// 5.6 TB/s instead of 3.5 on one MI355X).  Partial-line accesses (the input
+// pass's 8-byte channel blocks at a 24-byte pixel stride, the skip blocks of
+// the concat) stay cached, so that the neighbouring lanes' and waves' pieces
+// of a line meet in L2.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld_stream(const float4* p) {
+  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_stream(const uint2* p) {
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ float ld_stream(const float* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void st_stream(float4* p, float4 v) {
+  __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4*>(p));
+}
+__device__ __forceinline__ void st_stream(uint2* p, uint2 v) {
+  __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(p));
+}
 
 
 // [webgpu-0.6] inputShader ("oidn-webgpu 0.0.0-stage -> 0.6.0",
@@ -32,18 +61,18 @@ __global__ __launch_bounds__(THREADS) void pack_input_kernel(PackArgs a) {
   float ch[12];
 #pragma unroll
   for (int i = 0; i < 12; ++i) ch[i] = 0.f;
-  const float4 col = a.color[src];
+  const float4 col = ld_stream(a.color + src);
   ch[0] = in_color(col.x, a.hdr, a.input_scale);
   ch[1] = in_color(col.y, a.hdr, a.input_scale);
   ch[2] = in_color(col.z, a.hdr, a.input_scale);
   if (a.sources > 1) {
-    const float4 al = a.albedo[src];
+    const float4 al = ld_stream(a.albedo + src);
     ch[3] = in_albedo(al.x);
     ch[4] = in_albedo(al.y);
     ch[5] = in_albedo(al.z);
   }
   if (a.sources > 2) {
-    const float4 nr = a.normal[src];
+    const float4 nr = ld_stream(a.normal + src);
     ch[6] = in_normal(nr.x);
     ch[7] = in_normal(nr.y);
     ch[8] = in_normal(nr.z);
@@ -87,89 +116,146 @@ __global__ __launch_bounds__(THREADS) void pack_input_kernel(PackArgs a) {
 
 // [webgpu-0.6] outputShader: sanitize the network RGB, invert the transfer and
 // the input scale, alpha from the input colour; only the output rectangle.
+// A block covers 2 x 256 pixels: each thread loads both of its pixels (256
+// apart, so every load and store instruction stays lane-contiguous) before
+// storing either.
+constexpr int kUnpackPerThread = 2;
 __global__ __launch_bounds__(THREADS) void unpack_output_kernel(UnpackArgs a) {
   const OutputPass& p = a.o;
-  const int t = blockIdx.x * THREADS + threadIdx.x;
-  if (t >= p.out_w * p.out_h) return;
-  const int y = t / p.out_w, x = t - y * p.out_w;
-  const float4 net = a.net[(size_t)(y + p.in_off_y) * a.tile_w + x + p.in_off_x];
-  const size_t o = (size_t)(y + p.out_y) * p.img_w + x + p.out_x;
-  p.out[o] = output_pixel(net.x, net.y, net.z, p.color[o].w, p.hdr, p.input_scale);
+  const int n = p.out_w * p.out_h;
+  const int t0 = blockIdx.x * THREADS * kUnpackPerThread + threadIdx.x;
+  float4 net[kUnpackPerThread];
+  float alpha[kUnpackPerThread];
+  size_t o[kUnpackPerThread];
+#pragma unroll
+  for (int k = 0; k < kUnpackPerThread; ++k) {
+    const int t = t0 + k * THREADS;
+    if (t >= n) break;
+    const int y = t / p.out_w, x = t - y * p.out_w;
+    net[k] = ld_stream(a.net + (size_t)(y + p.in_off_y) * a.tile_w + x + p.in_off_x);
+    o[k] = (size_t)(y + p.out_y) * p.img_w + x + p.out_x;
+    alpha[k] = ld_stream(reinterpret_cast<const float*>(p.color + o[k]) + 3);
+  }
+#pragma unroll
+  for (int k = 0; k < kUnpackPerThread; ++k) {
+    if (t0 + k * THREADS >= n) break;
+    st_stream(p.out + o[k], output_pixel(net[k].x, net[k].y, net[k].z, alpha[k], p.hdr, p.input_scale));
+  }
 }
 
 // [web-0.4] createMaxPoolShader / [web-0.5] coalesced "channels" pool: one
-// thread per (output pixel, 4-channel block), threads of a wave walk the
-// blocks of consecutive pixels.
+// thread per two (output pixel, 4-channel block) items of an output row,
+// 256 apart (threads of a wave walk the blocks of consecutive pixels, every
+// instruction stays lane-contiguous); all eight loads are issued before the
+// maxima.  blockIdx.y is the output row, so the index arithmetic stays in
+// 32 bits.
+constexpr int kPoolPerThread = 2;
 template <int DT>
 __global__ __launch_bounds__(THREADS) void pool2x2_kernel(const void* x, int h, int w, int cs,
                                                           void* y) {
+  // a 4-channel block: fp32 x 4, fp16 x 4, or bf16 x 4 as two 32-bit words
+  typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+  using Blk = std::conditional_t<DT == OIDN_F32, float4,
+                                 std::conditional_t<DT == OIDN_F16, half4, uint2>>;
+  const Blk* in = static_cast<const Blk*>(x);
+  Blk* out = static_cast<Blk*>(y);
   const int nb = cs / 4;
   const int ow = w >> 1, oh = h >> 1;
-  const size_t t = (size_t)blockIdx.x * THREADS + threadIdx.x;
-  if (t >= (size_t)ow * oh * nb) return;
-  const int b = (int)(t % nb);
-  const size_t pix = t / nb;
-  const int ox = (int)(pix % ow), oy = (int)(pix / ow);
-  const size_t i00 = ((size_t)(2 * oy) * w + 2 * ox) * nb + b;
-  const size_t i01 = i00 + nb;
-  const size_t i10 = i00 + (size_t)w * nb;
-  const size_t i11 = i10 + nb;
-  if constexpr (DT == OIDN_BF16) {
-    // bf16 -> fp32 is exact (the high half of the fp32 bits)
-    const uint2* in = static_cast<const uint2*>(x);
-    const uint2 a0 = in[i00], a1 = in[i01], a2 = in[i10], a3 = in[i11];
-    auto lo = [](uint32_t u) { return __uint_as_float(u << 16); };
-    auto hi = [](uint32_t u) { return __uint_as_float(u & 0xffff0000u); };
-    const float m0 = fmaxf(fmaxf(lo(a0.x), lo(a1.x)), fmaxf(lo(a2.x), lo(a3.x)));
-    const float m1 = fmaxf(fmaxf(hi(a0.x), hi(a1.x)), fmaxf(hi(a2.x), hi(a3.x)));
-    const float m2 = fmaxf(fmaxf(lo(a0.y), lo(a1.y)), fmaxf(lo(a2.y), lo(a3.y)));
-    const float m3 = fmaxf(fmaxf(hi(a0.y), hi(a1.y)), fmaxf(hi(a2.y), hi(a3.y)));
-    // exact: each maximum is one of the bf16 inputs
-    static_cast<uint2*>(y)[t] = make_uint2(pack_bf2(m0, m1), pack_bf2(m2, m3));
-  } else if constexpr (DT == OIDN_F16) {
-    typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-    const half4* in = static_cast<const half4*>(x);
-    const half4 a0 = in[i00], a1 = in[i01], a2 = in[i10], a3 = in[i11];
-    half4 m;
+  const int r0 = blockIdx.x * THREADS * kPoolPerThread + threadIdx.x;
+  for (int oy = blockIdx.y; oy < oh; oy += gridDim.y) {
+    Blk v[kPoolPerThread][4];
+    size_t t[kPoolPerThread];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = fmaxf(fmaxf((float)a0[i], (float)a1[i]), fmaxf((float)a2[i], (float)a3[i]));
-      m[i] = (_Float16)v;  // exact: v is one of the fp16 inputs
+    for (int k = 0; k < kPoolPerThread; ++k) {
+      const int r = r0 + k * THREADS;   // (pixel, block) within the row
+      if (r >= ow * nb) break;
+      const int ox = r / nb, b = r - ox * nb;
+      t[k] = (size_t)oy * ow * nb + r;
+      const size_t i00 = ((size_t)(2 * oy) * w + 2 * ox) * nb + b;
+      const size_t i10 = i00 + (size_t)w * nb;
+      if constexpr (DT == OIDN_F16) {
+        v[k][0] = __builtin_nontemporal_load(in + i00);
+        v[k][1] = __builtin_nontemporal_load(in + i00 + nb);
+        v[k][2] = __builtin_nontemporal_load(in + i10);
+        v[k][3] = __builtin_nontemporal_load(in + i10 + nb);
+      } else {
+        v[k][0] = ld_stream(in + i00);
+        v[k][1] = ld_stream(in + i00 + nb);
+        v[k][2] = ld_stream(in + i10);
+        v[k][3] = ld_stream(in + i10 + nb);
+      }
     }
-    static_cast<half4*>(y)[t] = m;
-  } else {
-    const float4* in = static_cast<const float4*>(x);
-    const float4 a0 = in[i00], a1 = in[i01], a2 = in[i10], a3 = in[i11];
-    float4 m;
-    m.x = fmaxf(fmaxf(a0.x, a1.x), fmaxf(a2.x, a3.x));
-    m.y = fmaxf(fmaxf(a0.y, a1.y), fmaxf(a2.y, a3.y));
-    m.z = fmaxf(fmaxf(a0.z, a1.z), fmaxf(a2.z, a3.z));
-    m.w = fmaxf(fmaxf(a0.w, a1.w), fmaxf(a2.w, a3.w));
-    static_cast<float4*>(y)[t] = m;
+#pragma unroll
+    for (int k = 0; k < kPoolPerThread; ++k) {
+      if (r0 + k * THREADS >= ow * nb) break;
+      const Blk* a = v[k];
+      if constexpr (DT == OIDN_F32) {
+        float4 m;
+        m.x = fmaxf(fmaxf(a[0].x, a[1].x), fmaxf(a[2].x, a[3].x));
+        m.y = fmaxf(fmaxf(a[0].y, a[1].y), fmaxf(a[2].y, a[3].y));
+        m.z = fmaxf(fmaxf(a[0].z, a[1].z), fmaxf(a[2].z, a[3].z));
+        m.w = fmaxf(fmaxf(a[0].w, a[1].w), fmaxf(a[2].w, a[3].w));
+        st_stream(out + t[k], m);
+      } else if constexpr (DT == OIDN_F16) {
+        half4 m;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float mv = fmaxf(fmaxf((float)a[0][i], (float)a[1][i]), fmaxf((float)a[2][i], (float)a[3][i]));
+          m[i] = (_Float16)mv;   // exact: mv is one of the fp16 inputs
+        }
+        __builtin_nontemporal_store(m, out + t[k]);
+      } else {
+        // bf16 -> fp32 is exact (the high half of the fp32 bits); the maximum
+        // is one of the inputs, so converting it back is exact too
+        auto lo = [](uint32_t u) { return __uint_as_float(u << 16); };
+        auto hi = [](uint32_t u) { return __uint_as_float(u & 0xffff0000u); };
+        float m[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint32_t w0 = i ? a[0].y : a[0].x, w1 = i ? a[1].y : a[1].x;
+          const uint32_t w2 = i ? a[2].y : a[2].x, w3 = i ? a[3].y : a[3].x;
+          m[2 * i] = fmaxf(fmaxf(lo(w0), lo(w1)), fmaxf(lo(w2), lo(w3)));
+          m[2 * i + 1] = fmaxf(fmaxf(hi(w0), hi(w1)), fmaxf(hi(w2), hi(w3)));
+        }
+        st_stream(out + t[k], make_uint2(pack_bf2(m[0], m[1]), pack_bf2(m[2], m[3])));
+      }
+    }
   }
 }
 
 // Materialised [up(low) | skip]: one thread per (pixel, 4-channel block of
-// the concat); a block is 8 bytes (fp16) or 16 bytes (fp32).
+// the concat) of an output row pair 2 Y, 2 Y + 1 (blockIdx.y = Y, 32-bit
+// index arithmetic within the row); a block is 8 bytes (fp16) or 16 bytes
+// (fp32).  Both rows' blocks are in flight at once: the upsampled block is
+// read once and stored twice, the skip's two blocks are read together.
 template <typename Block>
 __global__ __launch_bounds__(THREADS) void upcat_kernel(const Block* low, int nb_low,
                                                         const Block* skip, int nb_skip, int h,
                                                         int w, Block* z) {
   const int nb = nb_low + nb_skip;
-  const size_t t = (size_t)blockIdx.x * THREADS + threadIdx.x;
-  if (t >= (size_t)h * w * nb) return;
-  const int b = (int)(t % nb);
-  const size_t pix = t / nb;
-  const int x = (int)(pix % w), y = (int)(pix / w);
-  Block v;
-  if (b < nb_low)
-    v = low[((size_t)(y >> 1) * (w >> 1) + (x >> 1)) * nb_low + b];
-  else
-    v = skip[pix * nb_skip + (b - nb_low)];
-  z[t] = v;
+  const int r = blockIdx.x * THREADS + threadIdx.x;   // (pixel, block) within the row
+  if (r >= w * nb) return;
+  const int x = r / nb, b = r - x * nb;
+  const size_t zrow = (size_t)w * nb;
+  for (int ly = blockIdx.y; ly < (h >> 1); ly += gridDim.y) {
+    Block* const z0 = z + (size_t)(2 * ly) * zrow + r;
+    if (b < nb_low) {   // the same low-resolution block for both rows (and both columns)
+      const Block v = low[((size_t)ly * (w >> 1) + (x >> 1)) * nb_low + b];
+      st_stream(z0, v);
+      st_stream(z0 + zrow, v);
+    } else {
+      const Block* const s0 = skip + ((size_t)(2 * ly) * w + x) * nb_skip + (b - nb_low);
+      const Block v0 = s0[0], v1 = s0[(size_t)w * nb_skip];
+      st_stream(z0, v0);
+      st_stream(z0 + zrow, v1);
+    }
+  }
 }
 
 inline dim3 grid_for(size_t n) { return dim3((unsigned)((n + THREADS - 1) / THREADS)); }
+// Rows per launch of the row-indexed kernels (grid y); they step over the rest.
+constexpr int kMaxGridRows = 32768;
+inline unsigned grid_rows(int rows) { return (unsigned)(rows < kMaxGridRows ? rows : kMaxGridRows); }
 
 }  // namespace
 
@@ -188,33 +274,36 @@ hipError_t launch_pack(const PackArgs& a, int dtype, hipStream_t stream) {
 hipError_t launch_unpack(const UnpackArgs& a, hipStream_t stream) {
   const size_t n = (size_t)a.o.out_w * a.o.out_h;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(unpack_output_kernel, grid_for(n), dim3(THREADS), 0, stream, a);
+  hipLaunchKernelGGL(unpack_output_kernel, grid_for((n + kUnpackPerThread - 1) / kUnpackPerThread),
+                     dim3(THREADS), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_pool(const void* x, int h, int w, int cs, void* y, int dtype, hipStream_t stream) {
-  const size_t n = (size_t)(w / 2) * (h / 2) * (cs / 4);
-  if (n == 0) return hipSuccess;
+  const size_t row = (size_t)(w / 2) * (cs / 4);   // items per output row
+  if (row == 0 || h / 2 == 0) return hipSuccess;
+  const dim3 grid(grid_for((row + kPoolPerThread - 1) / kPoolPerThread).x, grid_rows(h / 2));
   if (dtype == OIDN_BF16)
-    hipLaunchKernelGGL(pool2x2_kernel<OIDN_BF16>, grid_for(n), dim3(THREADS), 0, stream, x, h, w, cs, y);
+    hipLaunchKernelGGL(pool2x2_kernel<OIDN_BF16>, grid, dim3(THREADS), 0, stream, x, h, w, cs, y);
   else if (dtype == OIDN_F16)
-    hipLaunchKernelGGL(pool2x2_kernel<OIDN_F16>, grid_for(n), dim3(THREADS), 0, stream, x, h, w, cs, y);
+    hipLaunchKernelGGL(pool2x2_kernel<OIDN_F16>, grid, dim3(THREADS), 0, stream, x, h, w, cs, y);
   else
-    hipLaunchKernelGGL(pool2x2_kernel<OIDN_F32>, grid_for(n), dim3(THREADS), 0, stream, x, h, w, cs, y);
+    hipLaunchKernelGGL(pool2x2_kernel<OIDN_F32>, grid, dim3(THREADS), 0, stream, x, h, w, cs, y);
   return hipGetLastError();
 }
 
 hipError_t launch_upcat(const void* low, int cs_low, const void* skip, int cs_skip, int h, int w,
                         void* z, bool b16, hipStream_t stream) {
   const int nb = (cs_low + cs_skip) / 4;
-  const size_t n = (size_t)h * w * nb;
-  if (n == 0) return hipSuccess;
+  const size_t row = (size_t)w * nb;                 // threads per row (of a row pair)
+  if (row == 0 || h / 2 == 0) return hipSuccess;
+  const dim3 grid(grid_for(row).x, grid_rows(h / 2));
   if (b16)
-    hipLaunchKernelGGL(upcat_kernel<uint2>, grid_for(n), dim3(THREADS), 0, stream,
+    hipLaunchKernelGGL(upcat_kernel<uint2>, grid, dim3(THREADS), 0, stream,
                        static_cast<const uint2*>(low), cs_low / 4, static_cast<const uint2*>(skip),
                        cs_skip / 4, h, w, static_cast<uint2*>(z));
   else
-    hipLaunchKernelGGL(upcat_kernel<float4>, grid_for(n), dim3(THREADS), 0, stream,
+    hipLaunchKernelGGL(upcat_kernel<float4>, grid, dim3(THREADS), 0, stream,
                        static_cast<const float4*>(low), cs_low / 4, static_cast<const float4*>(skip),
                        cs_skip / 4, h, w, static_cast<float4*>(z));
   return hipGetLastError();
