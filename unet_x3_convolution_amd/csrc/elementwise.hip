@@ -224,10 +224,12 @@ __global__ __launch_bounds__(THREADS) void pool2x2_kernel(const void* x, int h, 
 }
 
 // Materialised [up(low) | skip]: one thread per (pixel, 4-channel block of
-// the concat) of an output row pair 2 Y, 2 Y + 1 (blockIdx.y = Y, 32-bit
-// index arithmetic within the row); a block is 8 bytes (fp16) or 16 bytes
-// (fp32).  Both rows' blocks are in flight at once: the upsampled block is
-// read once and stored twice, the skip's two blocks are read together.
+// the concat) of two low-resolution rows, i.e. output rows 4 Y .. 4 Y + 3
+// (blockIdx.y = Y, 32-bit index arithmetic within the row); a block is 8
+// bytes (fp16) or 16 bytes (fp32).  All of a thread's loads are in flight
+// before its stores: an upsampled block is read once per low-resolution row
+// and stored twice, the skip's blocks are read row by row.
+constexpr int kUpcatLowRows = 2;
 template <typename Block>
 __global__ __launch_bounds__(THREADS) void upcat_kernel(const Block* low, int nb_low,
                                                         const Block* skip, int nb_skip, int h,
@@ -237,17 +239,28 @@ __global__ __launch_bounds__(THREADS) void upcat_kernel(const Block* low, int nb
   if (r >= w * nb) return;
   const int x = r / nb, b = r - x * nb;
   const size_t zrow = (size_t)w * nb;
-  for (int ly = blockIdx.y; ly < (h >> 1); ly += gridDim.y) {
-    Block* const z0 = z + (size_t)(2 * ly) * zrow + r;
-    if (b < nb_low) {   // the same low-resolution block for both rows (and both columns)
-      const Block v = low[((size_t)ly * (w >> 1) + (x >> 1)) * nb_low + b];
-      st_stream(z0, v);
-      st_stream(z0 + zrow, v);
-    } else {
-      const Block* const s0 = skip + ((size_t)(2 * ly) * w + x) * nb_skip + (b - nb_low);
-      const Block v0 = s0[0], v1 = s0[(size_t)w * nb_skip];
-      st_stream(z0, v0);
-      st_stream(z0 + zrow, v1);
+  const int nly = h >> 1;
+  for (int ly0 = kUpcatLowRows * blockIdx.y; ly0 < nly; ly0 += kUpcatLowRows * gridDim.y) {
+    Block v[kUpcatLowRows][2];
+#pragma unroll
+    for (int j = 0; j < kUpcatLowRows; ++j) {
+      const int ly = ly0 + j;
+      if (ly >= nly) break;
+      if (b < nb_low) {   // the same low-resolution block for both rows (and both columns)
+        v[j][0] = v[j][1] = low[((size_t)ly * (w >> 1) + (x >> 1)) * nb_low + b];
+      } else {
+        const Block* const s0 = skip + ((size_t)(2 * ly) * w + x) * nb_skip + (b - nb_low);
+        v[j][0] = s0[0];
+        v[j][1] = s0[(size_t)w * nb_skip];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kUpcatLowRows; ++j) {
+      const int ly = ly0 + j;
+      if (ly >= nly) break;
+      Block* const z0 = z + (size_t)(2 * ly) * zrow + r;
+      st_stream(z0, v[j][0]);
+      st_stream(z0 + zrow, v[j][1]);
     }
   }
 }
@@ -297,7 +310,7 @@ hipError_t launch_upcat(const void* low, int cs_low, const void* skip, int cs_sk
   const int nb = (cs_low + cs_skip) / 4;
   const size_t row = (size_t)w * nb;                 // threads per row (of a row pair)
   if (row == 0 || h / 2 == 0) return hipSuccess;
-  const dim3 grid(grid_for(row).x, grid_rows(h / 2));
+  const dim3 grid(grid_for(row).x, grid_rows((h / 2 + kUpcatLowRows - 1) / kUpcatLowRows));
   if (b16)
     hipLaunchKernelGGL(upcat_kernel<uint2>, grid, dim3(THREADS), 0, stream,
                        static_cast<const uint2*>(low), cs_low / 4, static_cast<const uint2*>(skip),
