@@ -93,10 +93,38 @@ __global__ __launch_bounds__(THREADS) void pack_input_kernel(PackArgs a) {
     ch[9] = c8;
     ch[10] = tx + 1 < a.tile_w ? right : 0.f;
   }
-  if (t0 >= n) return;
   const int nblk = a.lanes / 4;   // blocks past the data (lanes 12..15) are zero
   if constexpr (DT != OIDN_F32) {
     constexpr bool BF = DT == OIDN_BF16;
+    // A wave's 64 pixels are one contiguous run of 64 nblk 8-byte blocks:
+    // when all of them are in the tile they go through LDS and out as
+    // lane-contiguous 16-byte streaming stores (whole lines) instead of
+    // nblk 8-byte stores per lane at a pixel stride.
+    __shared__ __attribute__((aligned(16))) uint2 stage[THREADS * 4];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wbase = t0 - lane;                    // the wave's first pixel
+    const bool whole = wbase + 64 <= n;             // wave-uniform
+    uint2* wst = stage + wave * 64 * 4;
+    if (whole) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        if (b < nblk)
+          wst[lane * nblk + b] = b < 3 ? make_uint2(pack2<BF>(ch[4 * b], ch[4 * b + 1]),
+                                                    pack2<BF>(ch[4 * b + 2], ch[4 * b + 3]))
+                                       : make_uint2(0u, 0u);
+    }
+    __syncthreads();
+    if (whole) {
+      // 64 nblk blocks = 32 nblk 16-byte units; nblk is 3 or 4
+      const uint4* src4 = reinterpret_cast<const uint4*>(wst);
+      uint2* out = static_cast<uint2*>(a.packed) + (size_t)wbase * nblk;
+      for (int u = lane; u < 32 * nblk; u += 64) {
+        const uint4 v = src4[u];
+        __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(out) + u);
+      }
+      return;
+    }
+    if (t0 >= n) return;
     uint2* out = static_cast<uint2*>(a.packed) + (size_t)t * nblk;
 #pragma unroll
     for (int b = 0; b < 4; ++b)
@@ -105,6 +133,7 @@ __global__ __launch_bounds__(THREADS) void pack_input_kernel(PackArgs a) {
                                     pack2<BF>(ch[4 * b + 2], ch[4 * b + 3]))
                        : make_uint2(0u, 0u);
   } else {
+    if (t0 >= n) return;
     float4* out = static_cast<float4*>(a.packed) + (size_t)t * nblk;
 #pragma unroll
     for (int b = 0; b < 4; ++b)
