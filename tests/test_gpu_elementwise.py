@@ -33,7 +33,7 @@ def test_pool_bit_exact(h, w, c, precision):
                                                         (4, 2, 4, 3, "f32"),
                                                         (6, 10, 8, 9, "bf16"),
                                                         # rows past one launch's grid
-                                                        (70000, 4, 4, 3, "f16"),
+                                                        (140004, 4, 4, 3, "f16"),
                                                         (140002, 2, 8, 9, "f32")])
 def test_upsample_concat_bit_exact(h, w, c_low, c_skip, precision):
     r = np.random.default_rng(h + c_low)
