@@ -183,7 +183,8 @@ int oidn_upsample_concat(const void* low, int c_low, const void* skip, int c_ski
  * albedo: sanitize(rgb, 0, 1); normal: sanitize(rgb, -1, 1) * 0.5 + 0.5,
  * where sanitize maps NaN to 0 and clamps.  The 3/6/9 channels are packed
  * densely into 4-lane blocks (lane l of block b is channel 4b + l), unused
- * lanes 0.  packed: tile_h x tile_w x C_store(channels) of dtype. */
+ * lanes 0.  packed: tile_h x tile_w x C_store(channels) of dtype.
+ * tile_w * tile_h above 2^31 - 1025 pixels: OIDN_E_UNSUPPORTED. */
 int oidn_pack_input(const float* color, const float* albedo, const float* normal,
                     int img_w, int img_h, int tile_x, int tile_y, int tile_w, int tile_h,
                     int hdr, int transfer, float input_scale, void* packed, int dtype,
@@ -195,7 +196,8 @@ int oidn_pack_input(const float* color, const float* albedo, const float* normal
  *   d = sanitize(net[y + in_off_y][x + in_off_x].rgb, 0, hdr ? FLT_MAX : 1)
  *   out[out_y + y][out_x + x] = (hdr ? F^-1(d) / input_scale : d,
  *                                color[out_y + y][out_x + x].a)
- * out_rgba: img_h x img_w RGBA float32; only the rectangle is written. */
+ * out_rgba: img_h x img_w RGBA float32; only the rectangle is written.
+ * out_w * out_h above 2^31 - 1025 pixels: OIDN_E_UNSUPPORTED. */
 int oidn_unpack_output(const float* net_rgba, int tile_w, int tile_h, int in_off_x,
                        int in_off_y, const float* color, int img_w, int img_h, int out_x,
                        int out_y, int out_w, int out_h, int hdr, int transfer,
@@ -292,6 +294,18 @@ int oidn_unet_workspace_bytes(int in_channels, int w, int h, int max_tile, int o
  * oidn_unet_forward_timed cover the first such batch.  Host only. */
 int oidn_unet_tile_batch(int in_channels, int w, int h, int max_tile, int overlap, int dtype,
                          int* batch);
+
+/* Where oidn_unet_forward keeps the packed network input of a tile inside
+ * its workspace (host only; for inspection and tests): tile k of the last
+ * tile batch of the call (oidn_unet_tile_batch) at workspace + *offset +
+ * k * *tile_stride (stride 0 when tiles run one by one), tile_h x tile_w
+ * pixels of *lanes values of dtype.  With *taps (16-bit storage, nine
+ * channels) lanes 0..7 hold channels 0..7, lanes 8, 9, 10 channel 8 of the
+ * pixels in tile columns x - 1, x, x + 1 (zero past the tile's edge), the
+ * rest zero; else the oidn_pack_input layout padded with zero lanes.  The
+ * values stay there after the call until the workspace is reused. */
+int oidn_unet_input_layout(int in_channels, int w, int h, int max_tile, int overlap, int dtype,
+                           size_t* offset, size_t* tile_stride, int* lanes, int* taps);
 
 /* End-to-end denoise ([webgpu-0.6] recordDenoiseExecution): plan the tile
  * grid, then for each tile in order: input pass, network, output pass into

@@ -379,3 +379,38 @@ def test_unet_1080p_launch_plans():
         inst, nb = UNET_1080P_PLANS[name]
         want = ("conv3x3_pair_f16" + inst[4:]) if inst.startswith("pair") else "conv3x3_f16_mfma" + inst
         assert (sym, blocks) == (want, nb), name
+
+
+def test_input_layout_in_the_workspace():
+    """Where the end-to-end path leaves the packed input: 16 tap lanes for
+    nine channels on the 16-bit paths, 8 lanes for six, 12 fp32 lanes on
+    the fp32 path; one per-tile plan per batched tile, inside the workspace."""
+    F, B, F32 = U.OIDN_F16, U.OIDN_BF16, U.OIDN_F32
+    for dt in (F, B):
+        off, stride, lanes, taps = U.oidn_unet_input_layout(9, 203, 141, 128, 32, dt)
+        ws = U.oidn_unet_workspace_bytes(9, 203, 141, 128, 32, dt)
+        assert (lanes, taps) == (16, True) and stride == ws // 12 and off % 256 == 0
+        assert off + 128 * 112 * 16 * 2 <= stride
+        off, stride, lanes, taps = U.oidn_unet_input_layout(6, 203, 141, 128, 32, dt)
+        assert (lanes, taps) == (8, False)
+        off, stride, lanes, taps = U.oidn_unet_input_layout(9, 1920, 1080, 0, 32, dt)
+        assert stride == 0 and off + 1920 * 1088 * 32 <= U.oidn_unet_workspace_bytes(9, 1920, 1080, 0, 32, dt)
+    off, stride, lanes, taps = U.oidn_unet_input_layout(9, 203, 141, 128, 32, F32)
+    assert (stride, lanes, taps) == (0, 12, False)
+    with pytest.raises(U.OidnError) as e:
+        U.oidn_unet_input_layout(7, 64, 64, 0, 32, F)
+    assert e.value.code == U.OIDN_E_INVALID
+
+
+def test_image_passes_reject_pixel_counts_past_32_bits():
+    """The input and output passes index pixels in 32 bits: larger
+    rectangles are refused before any device work."""
+    N = U.OIDN_E_UNSUPPORTED
+    p = U.oidn_pack_input
+    assert _code(p, FAKE, None, None, 64, 64, 0, 0, 65536, 65536, 1, 1, 1.0, FAKE, U.OIDN_F16, 0) == N
+    assert _code(p, FAKE, None, None, 64, 64, 0, 0, 65536, 32768, 1, 1, 1.0, FAKE, U.OIDN_F16, 0) == N
+    assert "32-bit" in U.last_error()
+    q = U.oidn_unpack_output
+    assert _code(q, FAKE, 65536, 65536, 0, 0, FAKE, 65536, 65536, 0, 0, 65536, 32768, 1, 1, 1.0,
+                 FAKE, 0) == N
+    assert "32-bit" in U.last_error()

@@ -1,12 +1,13 @@
 """GPU parity of the whole UNet denoise against the CPU oracle: the network on
-packed tiles, the end-to-end tiled path, the 1080p and 4K workloads on
-sampled output rectangles, and tiled == untiled."""
+packed tiles, the end-to-end tiled path, the whole 1080p frame and every tile
+of the 4K tiled frame, edge values through the fused input pass, and tiled ==
+untiled."""
 import numpy as np
 import pytest
 
 import synthetic as S
 import unet_x3_convolution_amd as U
-from helpers import DT, TOL, dev, empty, host, packed_unet, rel_err, say, to_dev
+from helpers import DT, TOL, dev, empty, host, packed_unet, rel_err, say, to_dev, ulp_diff
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -212,43 +213,153 @@ def _oracle_rect(ws, bs, color, albedo, normal, out_rect, precision):
 
 
 @pytest.mark.parametrize("precision", ["f16", "bf16"])
-def test_config4_1080p_end_to_end_sampled(precision):
-    """1920x1080, one 1920x1088 tile, HDR log with input scale 1: the whole
-    frame on the GPU; the oracle on sampled output rectangles."""
+def test_config4_1080p_whole_frame(precision):
+    """1920x1080, one 1920x1088 tile, HDR log with input scale 1: every pixel
+    of the frame against the oracle on the same single-tile plan."""
     color, albedo, normal, ws, bs = make_case(1920, 1080)
     got = gpu_denoise(ws, bs, color, albedo, normal, precision, 0, 32)
     assert not np.any(np.isnan(got))
     assert np.array_equal(got[..., 3], color[..., 3])
-    for rect in [(0, 0, 48, 48), (1872, 1032, 48, 48), (944, 520, 32, 40), (1900, 300, 20, 16)]:
-        ref = _oracle_rect(ws, bs, color, albedo, normal, rect, precision)
-        ox, oy, ow, oh = rect
-        err = rel_err(got[oy:oy + oh, ox:ox + ow], ref)
-        say(f"config4 {precision} rect {rect}: max_rel_err={err:.3e}")
-        assert err <= TOL[precision]
+    ref = O.unet_forward(ws, bs, color, albedo, normal, True, 1.0, 0, 32, precision)
+    err = rel_err(got, ref)
+    say(f"config4 1920x1080 {precision}, whole frame: max_rel_err={err:.3e}")
+    assert err <= TOL[precision]
 
 
-def test_config5_4k_tiled_sampled():
-    """3840x2160 fp16, max tile 1024, overlap 32 (12 tiles of 1024x784): the
-    oracle runs one whole tile of the same plan; another tile's interior is
-    checked against its own oracle window; the overlap-32 seam error against
-    a full-context reference is reported."""
+def test_config5_4k_tiled_every_tile():
+    """3840x2160 fp16, max tile 1024, overlap 32 (12 tiles of 1024x784 in one
+    batch): every tile's output rectangle, i.e. the whole frame, against the
+    oracle on the same plan; the overlap-32 seam error against a
+    full-context reference is reported."""
     color, albedo, normal, ws, bs = make_case(3840, 2160)
     got = gpu_denoise(ws, bs, color, albedo, normal, "f16", 1024, 32)
     assert not np.any(np.isnan(got))
     tiles = U.oidn_plan_tiles(3840, 2160, 1024, 32)
     assert len(tiles) == 12 and all(t[2:4] == (1024, 784) for t in tiles)
-    ix, iy, iw, ih, ox, oy, ow, oh = tiles[5]        # an interior tile
-    packed = O.pack_input(color, albedo, normal, ix, iy, iw, ih, True, 1.0, "f16")
-    net = O.unet_forward_packed(ws, bs, packed, 9, "f16")
-    ref = np.full((2160, 3840, 4), np.nan, np.float32)
-    O.unpack_output(net, ox - ix, oy - iy, color, ox, oy, ow, oh, True, 1.0, ref)
-    err = rel_err(got[oy:oy + oh, ox:ox + ow], ref[oy:oy + oh, ox:ox + ow])
-    say(f"config5 tile 5 (oracle, same plan): max_rel_err={err:.3e}")
-    assert err <= TOL["f16"]
-    # seam: the untiled answer near the tile border differs (overlap 32 < reach 94)
+    ref = O.unet_forward(ws, bs, color, albedo, normal, True, 1.0, 1024, 32, "f16")
+    for k, (ix, iy, iw, ih, ox, oy, ow, oh) in enumerate(tiles):
+        err = rel_err(got[oy:oy + oh, ox:ox + ow], ref[oy:oy + oh, ox:ox + ow])
+        say(f"config5 tile {k} out ({ox},{oy},{ow}x{oh}): max_rel_err={err:.3e}")
+        assert err <= TOL["f16"]
+    assert np.array_equal(got[..., 3], color[..., 3])
+    # seam: the untiled answer near a tile border differs (overlap 32 < reach 94)
+    ox, oy = tiles[5][4:6]
     seam = _oracle_rect(ws, bs, color, albedo, normal, (ox, oy, 32, 32), "f16")
     seam_err = rel_err(got[oy:oy + 32, ox:ox + 32], seam)
     say(f"config5 overlap-32 seam error vs full context (reported, not a pass/fail): {seam_err:.3e}")
+
+
+def _expand_taps(p):
+    """The oracle's 9-channel packed tile (12 lanes) in the 16-lane layout the
+    end-to-end path keeps: lanes 0..7 channels 0..7; lanes 8, 9, 10 channel 8
+    of the pixels in columns x - 1, x, x + 1 of the tile (zero past its
+    edges); lanes 11..15 zero."""
+    th, tw = p.shape[:2]
+    out = np.zeros((th, tw, 16), p.dtype)
+    out[..., :8] = p[..., :8]
+    out[:, 1:, 8] = p[:, :-1, 8]
+    out[..., 9] = p[..., 8]
+    out[:, :-1, 10] = p[:, 1:, 8]
+    return out
+
+
+def _plant_edge_values(color, albedo, normal, tiles, seed):
+    """NaN, +-Inf, negatives, albedo > 1 and normals outside [-1, 1] at the
+    image's corners and borders, the tiles' input edges, the first convs'
+    16 x 30 workgroup tile edges and 64-pixel wave edges, plus 3% of the
+    pixels at random.  Alpha stays finite (it is copied through)."""
+    r = np.random.default_rng(seed)
+    h, w = color.shape[:2]
+    xs = {0, 1, w - 2, w - 1}
+    ys = {0, 1, h - 2, h - 1}
+    for ix, iy, iw, ih, *_ in tiles:
+        xs |= {ix, ix + 1, ix + iw - 2, ix + iw - 1}
+        ys |= {iy, iy + 1, iy + ih - 2, iy + ih - 1}
+    xs |= {x for x in range(w) if x % 30 in (0, 29) or x % 64 in (0, 63)}
+    ys |= {y for y in range(h) if y % 16 in (0, 15)}
+    xs = np.array(sorted(x for x in xs if 0 <= x < w))
+    ys = np.array(sorted(y for y in ys if 0 <= y < h))
+    mask = np.zeros((h, w), bool)
+    mask[np.ix_(ys, xs[::3])] = True
+    mask[np.ix_(ys[::2], xs)] = True
+    mask |= r.random((h, w)) < 0.03
+    n = int(mask.sum())
+    specials = {
+        "color": np.array([np.nan, np.inf, -np.inf, -1.0, -1e-3, 1e30, 0.0, 65504.0, 1e5], np.float32),
+        "albedo": np.array([np.nan, np.inf, -np.inf, -3.0, 1.5, 2.0, 0.0, 1.0], np.float32),
+        "normal": np.array([np.nan, np.inf, -np.inf, -5.0, 5.0, -1.5, 1.25, 0.0], np.float32),
+    }
+    for name, img in (("color", color), ("albedo", albedo), ("normal", normal)):
+        vals = r.choice(specials[name], size=(n, 3))
+        keep = r.random((n, 3)) < 0.3        # some channels keep their ordinary value
+        sub = img[mask][:, :3]
+        sub[~keep] = vals[~keep]
+        img[mask, :3] = sub
+    return mask
+
+
+@pytest.mark.parametrize("hdr,precision", [(True, "f16"), (False, "f16"), (True, "bf16")])
+def test_fused_input_pass_edge_values(hdr, precision):
+    """The input pass as the first fused pair runs it in its staging, nine
+    channels with the tap lanes: special and out-of-range values placed at
+    image, tile, workgroup and wave edges of a 203 x 141 image (12 ragged
+    tiles of 128 x 112, one batch, clamp-to-edge past the image).  The packed
+    16-lane tile it leaves in the workspace is compared with the oracle's
+    input pass expanded to that layout -- bit-exact except the HDR colour
+    lanes (device log1p vs float64: <= 1 unit of the stored type) -- and the
+    denoised image with the oracle on the same plan."""
+    w, h = 203, 141
+    tiles = U.oidn_plan_tiles(w, h, 128, 32)
+    assert len(tiles) == 12 and all(t[2:4] == (128, 112) for t in tiles)
+    color, albedo, normal, ws, bs = make_case(w, h, seed=31 + hdr)
+    _plant_edge_values(color, albedo, normal, tiles, seed=7 + hdr)
+    F = DT[precision]
+    off, stride, lanes, taps = U.oidn_unet_input_layout(9, w, h, 128, 32, F)
+    assert lanes == 16 and taps and stride > 0
+    assert U.oidn_unet_tile_batch(9, w, h, 128, 32, F) == 12
+    wd = packed_unet(ws, bs, 9, precision)
+    nbytes = U.oidn_unet_workspace_bytes(9, w, h, 128, 32, F)
+    work = empty((nbytes,), np.uint8)
+    out = empty((h, w, 4), np.float32, fill=float("nan"))
+    scale = 0.6 if hdr else 1.0
+    U.oidn_unet_forward(wd, 9, dev(color), dev(albedo), dev(normal), w, h, hdr,
+                        U.OIDN_TRANSFER_LOG, scale, 128, 32, work, nbytes, out, F)
+    got = host(out)
+    torch = __import__("torch")
+    for k, (ix, iy, iw, ih, *_rest) in enumerate(tiles):
+        raw = work[off + k * stride: off + k * stride + ih * iw * lanes * 2]
+        t16 = raw.view(torch.bfloat16 if precision == "bf16" else torch.float16)
+        gp = host(t16).reshape(ih, iw, lanes)
+        ref = _expand_taps(O.pack_input(color, albedo, normal, ix, iy, iw, ih, hdr, scale,
+                                        precision))
+        exact = gp.copy()
+        if hdr:
+            assert ulp_diff(gp[..., :3], ref[..., :3], precision).max() <= 1, k
+            exact[..., :3] = ref[..., :3]
+        assert np.array_equal(exact.view(np.uint16 if precision == "f16" else np.uint32),
+                              ref.astype(exact.dtype).view(np.uint16 if precision == "f16"
+                                                          else np.uint32)), k
+    assert not np.any(np.isnan(got))
+    assert np.array_equal(got[..., 3], color[..., 3])
+    if not hdr:
+        assert got[..., :3].min() >= 0.0 and got[..., :3].max() <= 1.0
+    ref = O.unet_forward(ws, bs, color, albedo, normal, hdr, scale, 128, 32, precision)
+    err = rel_err(got, ref)
+    if hdr:
+        # Inputs up to FLT_MAX enter as F(FLT_MAX) = 88.7 and drive the
+        # network's output d up to ~30, where the inverse transfer
+        # exp(d) - 1 turns an absolute difference in d into the same relative
+        # difference of the image: the bound is checked on the network's own
+        # output d = F(out * scale), the image error is reported.
+        d = lambda img: np.log1p(np.asarray(img[..., :3], np.float64) * scale)
+        err_d = rel_err(d(got), d(ref))
+        say(f"fused input pass, edge values, hdr {precision}: packed tiles bit-exact, "
+            f"network output max_rel_err={err_d:.3e} (image {err:.3e}, reported)")
+        assert err_d <= TOL[precision]
+    else:
+        say(f"fused input pass, edge values, ldr {precision}: packed tiles bit-exact, "
+            f"max_rel_err={err:.3e}")
+        assert err <= TOL[precision]
 
 
 def test_output_untouched_on_error():

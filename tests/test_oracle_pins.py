@@ -427,3 +427,97 @@ def test_f16_storage_stays_within_tolerance_of_f32(small_unet):
     nb = O.unet_forward_packed(ws, bs, pb, 9, "bf16")
     errb = O.max_rel_error(nb, n32)
     assert err < errb < 0.2      # 3 fewer significand bits than fp16
+
+
+# The network as BASELINE's UNet configuration states it, written out by hand:
+# encoder "32, 32, pool, 48, pool, 64, pool, 80, pool, 96, 96"; decoder
+# "upsample 2x + concat skip -> 112, 112 / 96, 96 / 64, 64 / 64, 32 -> 3";
+# "ReLU except last".  Per conv: (output channels, 2x2 pool after it, ReLU,
+# resolution level of its output before pooling, upsample-concat before it).
+# The skip partners (pool3, pool2, pool1, the packed input) and the
+# [upsampled, skip] order are this build's reading of the missing model
+# description (parity unpinned); everything else is fixed by that text.
+CONFIG_TABLE = [
+    (32, False, True, 0, False),     # enc_conv0
+    (32, True, True, 0, False),      # enc_conv1 -> pool
+    (48, True, True, 1, False),      # enc_conv2 -> pool
+    (64, True, True, 2, False),      # enc_conv3 -> pool
+    (80, True, True, 3, False),      # enc_conv4 -> pool
+    (96, False, True, 4, False),     # enc_conv5a
+    (96, False, True, 4, False),     # enc_conv5b
+    (112, False, True, 3, True),     # dec_conv4a  [up(enc_conv5b), pool3]
+    (112, False, True, 3, False),    # dec_conv4b
+    (96, False, True, 2, True),      # dec_conv3a  [up(dec_conv4b), pool2]
+    (96, False, True, 2, False),     # dec_conv3b
+    (64, False, True, 1, True),      # dec_conv2a  [up(dec_conv3b), pool1]
+    (64, False, True, 1, False),     # dec_conv2b
+    (64, False, True, 0, True),      # dec_conv1a  [up(dec_conv2b), input]
+    (32, False, True, 0, False),     # dec_conv1b
+    (3, False, False, 0, False),     # dec_conv0 (no ReLU, fp32 output)
+]
+
+
+def test_network_table_matches_the_configuration_text():
+    assert len(O.UNET_LAYERS) == len(CONFIG_TABLE) == 16
+    level = 0
+    for (name, _src, skip, cout, pool, relu), (c, p, r, lv, up) in zip(O.UNET_LAYERS, CONFIG_TABLE):
+        if skip is not None:
+            level -= 1
+        assert (cout, pool, relu, level, skip is not None) == (c, p, r, lv, up), name
+        if pool:
+            level += 1
+
+
+def _by_hand(ws, bs, packed, precision):
+    """The configuration's network composed step by step from the oracle's
+    conv, pool and upsample-concat, following CONFIG_TABLE only."""
+    skips = []
+    x, c = packed, 9
+    skips.append((packed, 9))                           # level-0 partner: the input
+    for i in range(7):                                  # encoder
+        cout, pool, relu, _, _ = CONFIG_TABLE[i]
+        x = O.conv3x3(x, c, ws[i], bs[i], relu, precision)
+        c = cout
+        if pool:
+            x = O.pool2x2(x)
+            if i < 4:
+                skips.append((x, c))                    # pool1, pool2, pool3 (pool4 is no skip)
+    skips = skips[:4]
+    for k, i in enumerate(range(7, 16, 2)):             # decoder stages a/b
+        if i == 15:
+            break
+        low, cl = x, c
+        sk, cs = skips[3 - k]
+        cat = O.upsample_concat(low, cl, sk, cs)
+        x = O.conv3x3(cat, cl + cs, ws[i], bs[i], CONFIG_TABLE[i][2], precision)
+        c = CONFIG_TABLE[i][0]
+        x = O.conv3x3(x, c, ws[i + 1], bs[i + 1], CONFIG_TABLE[i + 1][2], precision)
+        c = CONFIG_TABLE[i + 1][0]
+    return O.conv3x3(x, c, ws[15], bs[15], CONFIG_TABLE[15][2], precision, "f32")
+
+
+@pytest.mark.parametrize("precision", ["f32", "f16"])
+def test_network_equals_the_configuration_composed_by_hand(precision):
+    """A dropped ReLU, a moved pool or a miswired skip in the oracle's
+    network changes its result against this independent composition."""
+    r = S.rng(21)
+    color, albedo, normal = S.images(r, 32, 48)
+    ws, bs = S.layer_params(r, O.unet_layer_shapes(9))
+    packed = O.pack_input(color, albedo, normal, 0, 0, 32, 48, True, 1.0, precision)
+    net = O.unet_forward_packed(ws, bs, packed, 9, precision)
+    ref = _by_hand(ws, bs, packed, precision)
+    assert net.dtype == np.float32 and net.shape == (48, 32, 4)
+    assert np.array_equal(net, ref)
+    # the composition is sensitive to each flag: a ReLU dropped from an
+    # encoder, a bottleneck or a decoder layer of the oracle's table changes
+    # the result (planted in a copy of the table, restored afterwards)
+    saved = O.UNET_LAYERS
+    try:
+        for k in (0, 6, 13):
+            layers = list(saved)
+            name, src, skip, cout, pool, _ = layers[k]
+            layers[k] = (name, src, skip, cout, pool, False)
+            O.UNET_LAYERS = tuple(layers)
+            assert not np.array_equal(O.unet_forward_packed(ws, bs, packed, 9, precision), net), k
+    finally:
+        O.UNET_LAYERS = saved

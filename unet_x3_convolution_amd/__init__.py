@@ -41,7 +41,8 @@ EXPORTS = (
     "oidn_conv3x3_pair", "oidn_conv3x3_kernel", "oidn_unet_layer_count", "oidn_unet_layer_info", "oidn_unet_layer_kernel",
     "oidn_unet_weights_bytes",
     "oidn_unet_pack_weights", "oidn_unet_packed_workspace_bytes", "oidn_unet_forward_packed",
-    "oidn_unet_workspace_bytes", "oidn_unet_tile_batch", "oidn_unet_forward",
+    "oidn_unet_workspace_bytes", "oidn_unet_tile_batch", "oidn_unet_input_layout",
+    "oidn_unet_forward",
     "oidn_unet_forward_timed",
     "oidn_event_create", "oidn_event_destroy", "oidn_event_elapsed_ms",
 )
@@ -91,6 +92,8 @@ _SIGS = {
     "oidn_unet_forward_packed": ([_vp, _i, _vp, _i, _i, _vp, _sz, _vp, _i, _vp], _i),
     "oidn_unet_workspace_bytes": ([_i, _i, _i, _i, _i, _i, ctypes.POINTER(_sz)], _i),
     "oidn_unet_tile_batch": ([_i, _i, _i, _i, _i, _i, ctypes.POINTER(_i)], _i),
+    "oidn_unet_input_layout": ([_i, _i, _i, _i, _i, _i, ctypes.POINTER(_sz), ctypes.POINTER(_sz),
+                                ctypes.POINTER(_i), ctypes.POINTER(_i)], _i),
     "oidn_unet_forward": ([_vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp, _i,
                            _vp], _i),
     "oidn_unet_forward_timed": ([_vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp,
@@ -339,6 +342,17 @@ def oidn_unet_tile_batch(in_channels: int, w: int, h: int, max_tile: int, overla
     n = _i()
     _check(lib().oidn_unet_tile_batch(in_channels, w, h, max_tile, overlap, dtype, ctypes.byref(n)))
     return n.value
+
+
+def oidn_unet_input_layout(in_channels: int, w: int, h: int, max_tile: int, overlap: int,
+                           dtype: int):
+    """(offset, tile_stride, lanes, taps) of the packed network input that
+    oidn_unet_forward leaves in its workspace."""
+    off, stride, lanes, taps = _sz(), _sz(), _i(), _i()
+    _check(lib().oidn_unet_input_layout(in_channels, w, h, max_tile, overlap, dtype,
+                                        ctypes.byref(off), ctypes.byref(stride),
+                                        ctypes.byref(lanes), ctypes.byref(taps)))
+    return off.value, stride.value, lanes.value, bool(taps.value)
 
 
 def oidn_unet_forward(d_weights, in_channels: int, color, albedo, normal, w: int, h: int,

@@ -39,6 +39,10 @@ int hip_fail(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The input and output passes index pixels with 32-bit ints (and round the
+// grid up to whole workgroups): rectangles above this many pixels are refused.
+constexpr long long kMaxPassPixels = 2147483647LL - 1024;
+
 int check_dtype(int dtype) {
   if (dtype == OIDN_F32 || dtype == OIDN_F16 || dtype == OIDN_BF16) return OIDN_OK;
   return fail(OIDN_E_INVALID, "unknown dtype %d", dtype);
@@ -955,6 +959,8 @@ int oidn_pack_input(const float* color, const float* albedo, const float* normal
     return fail(OIDN_E_INVALID, "input scale must be positive and finite");
   if (!aligned16(color) || (albedo && !aligned16(albedo)) || (normal && !aligned16(normal)) || !aligned16(packed))
     return fail(OIDN_E_INVALID, "device pointers must be 16-byte aligned");
+  if ((long long)tile_w * tile_h > kMaxPassPixels)
+    return fail(OIDN_E_UNSUPPORTED, "tile of %dx%d pixels exceeds the 32-bit pixel index", tile_w, tile_h);
   PackArgs a{};
   a.color = reinterpret_cast<const float4*>(color);
   a.albedo = reinterpret_cast<const float4*>(albedo);
@@ -994,6 +1000,9 @@ int oidn_unpack_output(const float* net_rgba, int tile_w, int tile_h, int in_off
     return fail(OIDN_E_INVALID, "input scale must be positive and finite");
   if (!aligned16(net_rgba) || !aligned16(color) || !aligned16(out_rgba))
     return fail(OIDN_E_INVALID, "device pointers must be 16-byte aligned");
+  if ((long long)out_w * out_h > kMaxPassPixels)
+    return fail(OIDN_E_UNSUPPORTED, "output rectangle of %dx%d pixels exceeds the 32-bit pixel index",
+                out_w, out_h);
   UnpackArgs a{};
   a.net = reinterpret_cast<const float4*>(net_rgba);
   a.tile_w = tile_w;
@@ -1195,6 +1204,28 @@ int oidn_unet_tile_batch(int in_channels, int w, int h, int max_tile, int overla
   rc = check_dtype(dtype);
   if (rc) return rc;
   *batch = tile_batch(in_channels, dtype, tiles.size());
+  return ok();
+}
+
+int oidn_unet_input_layout(int in_channels, int w, int h, int max_tile, int overlap, int dtype,
+                           size_t* offset, size_t* tile_stride, int* lanes, int* taps) {
+  if (!offset || !tile_stride || !lanes || !taps) return fail(OIDN_E_INVALID, "null pointer");
+  std::vector<oidn_tile> tiles;
+  int rc = plan(w, h, max_tile, overlap, tiles);
+  if (rc) return rc;
+  int tw = 0, th = 0;
+  for (const oidn_tile& t : tiles) {
+    tw = t.in_w > tw ? t.in_w : tw;
+    th = t.in_h > th ? t.in_h : th;
+  }
+  rc = check_network_tile(in_channels, tw, th, dtype);
+  if (rc) return rc;
+  Plan P;
+  plan_workspace(in_channels, tw, th, dtype, true, &P);
+  *offset = P.offset[0];
+  *tile_stride = tile_batch(in_channels, dtype, tiles.size()) > 1 ? P.bytes : 0;
+  *lanes = internal_input_lanes(in_channels, dtype);
+  *taps = unet_taps(in_channels, dtype) && *lanes == 16;
   return ok();
 }
 

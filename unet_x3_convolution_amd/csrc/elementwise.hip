@@ -16,10 +16,12 @@ constexpr int THREADS = 256;
 // nothing reads again are loaded non-temporally, and outputs written in
 // whole lines are stored non-temporally: cold reads of a just-written cache
 // then do not have to evict its dirty lines first (a 150 MB copy moves
-// 5.6 TB/s instead of 3.5 on one MI355X).  Partial-line accesses (the input
-// pass's 8-byte channel blocks at a 24-byte pixel stride, the skip blocks of
-// the concat) stay cached, so that the neighbouring lanes' and waves' pieces
-// of a line meet in L2.
+// 5.6 TB/s instead of 3.5 on one MI355X).  The input pass's 16-bit packed
+// pixels of a whole wave leave through LDS as lane-contiguous 16-byte
+// streaming stores.  Partial-line accesses (the per-lane 8-byte channel
+// blocks at a 24-byte pixel stride of a wave that reaches past the tile and
+// of the fp32 input pass, the skip blocks of the concat) stay cached, so that
+// the neighbouring lanes' and waves' pieces of a line meet in L2.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
