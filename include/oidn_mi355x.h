@@ -319,6 +319,29 @@ int oidn_unet_forward(const void* d_weights, int in_channels, const float* color
                       void* workspace, size_t ws_bytes, float* out_rgba, int dtype,
                       hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * denoise as oidn_unet_forward, with no workspace argument.  Its workspace is
+ * a static device array of OIDN_NOALLOC_SCRATCH_MB MiB inside the library,
+ * one per GPU, held until the process ends; the call allocates and frees
+ * nothing.  As many tiles run per launch as that array holds (the results
+ * are the same bits as oidn_unet_forward's).  A plan whose single tile needs
+ * more (oidn_unet_workspace_bytes / oidn_unet_tile_batch) is refused with
+ * OIDN_E_WORKSPACE before any device work: 1920x1080 in one tile needs about
+ * 400 MB, so such images need max_tile (512 fits).  Nothing in the array
+ * needs to start at zero (every value is written before it is read).  All
+ * calls on one GPU share the array: calls that overlap in time on one GPU
+ * (other streams, other host threads) race and must be ordered by the
+ * caller. */
+#define OIDN_NOALLOC_SCRATCH_MB 64
+int oidn_unet_forward_noalloc(const void* d_weights, int in_channels, const float* color,
+                              const float* albedo, const float* normal, int w, int h, int hdr,
+                              int transfer, float input_scale, int max_tile, int overlap,
+                              float* out_rgba, int dtype, hipStream_t stream);
+
+/* Size in bytes of the array oidn_unet_forward_noalloc uses.  Host only. */
+int oidn_unet_noalloc_scratch_bytes(size_t* bytes);
+
 /* Same as oidn_unet_forward, and records events[k] on the stream before the
  * k-th kernel of the FIRST tile or tile batch (k = 0: input pass, 1..16: layers, 17: output
  * pass) and events[18] after it, for per-kernel timing.  Where the first

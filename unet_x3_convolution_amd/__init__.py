@@ -33,6 +33,7 @@ OIDN_TRANSFER_LOG = 1
 
 OIDN_TILE_ALIGN = 16
 OIDN_DEFAULT_OVERLAP = 96
+OIDN_NOALLOC_SCRATCH_MB = 64
 
 EXPORTS = (
     "oidn_last_error", "oidn_version", "oidn_conv3x3_weights_bytes",
@@ -43,7 +44,7 @@ EXPORTS = (
     "oidn_unet_pack_weights", "oidn_unet_packed_workspace_bytes", "oidn_unet_forward_packed",
     "oidn_unet_workspace_bytes", "oidn_unet_tile_batch", "oidn_unet_input_layout",
     "oidn_unet_forward",
-    "oidn_unet_forward_timed",
+    "oidn_unet_forward_timed", "oidn_unet_forward_noalloc", "oidn_unet_noalloc_scratch_bytes",
     "oidn_event_create", "oidn_event_destroy", "oidn_event_elapsed_ms",
 )
 
@@ -98,6 +99,9 @@ _SIGS = {
                            _vp], _i),
     "oidn_unet_forward_timed": ([_vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp,
                                  _i, _vp, ctypes.POINTER(_vp), _i], _i),
+    "oidn_unet_forward_noalloc": ([_vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _i, _vp, _i,
+                                   _vp], _i),
+    "oidn_unet_noalloc_scratch_bytes": ([ctypes.POINTER(_sz)], _i),
     "oidn_event_create": ([ctypes.POINTER(_vp)], _i),
     "oidn_event_destroy": ([_vp], _i),
     "oidn_event_elapsed_ms": ([_vp, _vp, ctypes.POINTER(_f)], _i),
@@ -372,6 +376,20 @@ def oidn_unet_forward_timed(d_weights, in_channels: int, color, albedo, normal, 
                                          _p(normal), w, h, int(hdr), transfer, input_scale,
                                          max_tile, overlap, _p(workspace), ws_bytes,
                                          _p(out_rgba), dtype, _s(stream), ev, len(events)))
+
+
+def oidn_unet_forward_noalloc(d_weights, in_channels: int, color, albedo, normal, w: int, h: int,
+                              hdr: bool, transfer: int, input_scale: float, max_tile: int,
+                              overlap: int, out_rgba, dtype: int, stream=None):
+    _check(lib().oidn_unet_forward_noalloc(_p(d_weights), in_channels, _p(color), _p(albedo),
+                                           _p(normal), w, h, int(hdr), transfer, input_scale,
+                                           max_tile, overlap, _p(out_rgba), dtype, _s(stream)))
+
+
+def oidn_unet_noalloc_scratch_bytes() -> int:
+    n = _sz()
+    _check(lib().oidn_unet_noalloc_scratch_bytes(ctypes.byref(n)))
+    return n.value
 
 
 def oidn_event_create() -> int:

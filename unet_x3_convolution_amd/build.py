@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liboidn_mi355x.so")
-SOURCES = ["api.cpp", "conv_f16.hip", "conv_f32.hip", "elementwise.hip"]
+SOURCES = ["api.cpp", "conv_f16.hip", "conv_f32.hip", "elementwise.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-fp32 ops are turned off for the device code: plain fp32 arithmetic only.

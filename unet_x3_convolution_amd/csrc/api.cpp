@@ -656,7 +656,8 @@ int check_network_tile(int in_channels, int tw, int th, int dtype) {
 int denoise(const void* d_weights, int in_channels, const float* color, const float* albedo,
             const float* normal, int w, int h, int hdr, int transfer, float input_scale,
             int max_tile, int overlap, void* workspace, size_t ws_bytes, float* out_rgba,
-            int dtype, hipStream_t stream, void* const* events, int n_events) {
+            int dtype, hipStream_t stream, void* const* events, int n_events,
+            bool fit_batch = false) {
   if (!d_weights || !color || !workspace || !out_rgba)
     return fail(OIDN_E_INVALID, "null weights, color, workspace or output pointer");
   const int sources = 1 + (albedo != nullptr) + (normal != nullptr);
@@ -686,7 +687,10 @@ int denoise(const void* d_weights, int in_channels, const float* color, const fl
   if (rc) return rc;
   Plan P;
   plan_workspace(in_channels, tw, th, dtype, true, &P);
-  const int nb = tile_batch(in_channels, dtype, tiles.size());
+  int nb = tile_batch(in_channels, dtype, tiles.size());
+  // fit_batch: as many tiles per launch as the workspace holds (at least one)
+  if (fit_batch && P.bytes > 0 && ws_bytes / P.bytes < (size_t)nb)
+    nb = ws_bytes / P.bytes > 0 ? (int)(ws_bytes / P.bytes) : 1;
   if (ws_bytes < P.bytes * nb)
     return fail(OIDN_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
                 P.bytes * nb);
@@ -795,6 +799,40 @@ int upload(const std::vector<unsigned char>& host, void* dst, hipStream_t stream
 }
 
 }  // namespace
+
+namespace oidn {
+
+int denoise_fit(const void* d_weights, int in_channels, const float* color, const float* albedo,
+                const float* normal, int w, int h, int hdr, int transfer, float input_scale,
+                int max_tile, int overlap, void* workspace, size_t ws_bytes, float* out_rgba,
+                int dtype, hipStream_t stream) {
+  return denoise(d_weights, in_channels, color, albedo, normal, w, h, hdr, transfer, input_scale,
+                 max_tile, overlap, workspace, ws_bytes, out_rgba, dtype, stream, nullptr, 0, true);
+}
+
+int tile_workspace_bytes(int in_channels, int w, int h, int max_tile, int overlap, int dtype,
+                         size_t* bytes) {
+  std::vector<oidn_tile> tiles;
+  int rc = plan(w, h, max_tile, overlap, tiles);
+  if (rc) return rc;
+  int tw = 0, th = 0;
+  for (const oidn_tile& t : tiles) {
+    tw = t.in_w > tw ? t.in_w : tw;
+    th = t.in_h > th ? t.in_h : th;
+  }
+  rc = check_network_tile(in_channels, tw, th, dtype);
+  if (rc) return rc;
+  Plan P;
+  plan_workspace(in_channels, tw, th, dtype, true, &P);
+  *bytes = P.bytes;
+  return OIDN_OK;
+}
+
+int set_error(int code, const char* what) { return fail(code, "%s", what); }
+
+int clear_error() { return ok(); }
+
+}  // namespace oidn
 
 extern "C" {
 

@@ -235,4 +235,16 @@ hipError_t launch_pool(const void* x, int h, int w, int cs, void* y, int dtype, 
 hipError_t launch_upcat(const void* low, int cs_low, const void* skip, int cs_skip, int h, int w,
                         void* z, bool b16, hipStream_t stream);
 
+// The end-to-end denoise (oidn_unet_forward's body) with as many tiles per
+// launch as `ws_bytes` holds, at least one; bytes of one tile's workspace
+// plan for that image.  Both set the thread-local error on failure.
+int denoise_fit(const void* d_weights, int in_channels, const float* color, const float* albedo,
+                const float* normal, int w, int h, int hdr, int transfer, float input_scale,
+                int max_tile, int overlap, void* workspace, size_t ws_bytes, float* out_rgba,
+                int dtype, hipStream_t stream);
+int tile_workspace_bytes(int in_channels, int w, int h, int max_tile, int overlap, int dtype,
+                         size_t* bytes);
+int set_error(int code, const char* what);   // returns code
+int clear_error();                            // returns OIDN_OK
+
 }  // namespace oidn
