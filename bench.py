@@ -2,11 +2,16 @@
 3x3 convs -> output pass) on one MI355X, fp16 storage / fp32 accumulate.
 
 Prints one JSON line.  `value` is megapixels of image per second over the
-timed steps (inputs resident in HBM).  Per-kernel times come from HIP events
-recorded between the launches of every N-th timed step (markers between
-launches slow a step by ~10%, so the other steps run without them); the
-roofline entry is the kernel symbol with the largest total time.  `cpu_baseline` times the CPU
-oracle on one frame of the same workload.
+timed steps (inputs resident in HBM).  Per-launch times come from two HIP
+events recorded around ONE launch of every second timed step, rotating over
+the frame's launches (two markers per instrumented step, so the frame is not
+slowed by a marker between every pair of launches); the roofline entry is the
+kernel symbol with the largest total time.  `measured_peaks` times the
+matrix cores on an MFMA-only stream and HBM on a device copy, for fractions
+of measured next to published peaks.  `other_configs` times the single
+fp32 conv, the fp16 conv ladder, the network on a 512 x 512 tile and the
+3840 x 2160 frame in 1024-pixel tiles.  `cpu_baseline` times the CPU oracle
+on one frame of the same workload.
 """
 import argparse
 import json
@@ -173,11 +178,317 @@ def standalone_passes(U, torch, W, H, tw, th, dtype, d_color, d_albedo, d_normal
     return res
 
 
+PEAK_F32_TFLOPS = 157.3   # MI355X fp32 (matrix) peak, the fp32 path's roof
+
+
+def cpu_info():
+    """Model name, sockets x cores per socket, and the logical CPUs this
+    process may run on (lscpu's fields, read from /proc/cpuinfo and the
+    scheduler affinity)."""
+    model, phys = None, set()
+    try:
+        cur = {}
+        for line in open("/proc/cpuinfo"):
+            if ":" not in line:
+                if cur.get("physical id") is not None and cur.get("core id") is not None:
+                    phys.add((cur["physical id"], cur["core id"]))
+                cur = {}
+                continue
+            k, v = (t.strip() for t in line.split(":", 1))
+            cur[k] = v
+            if k == "model name" and model is None:
+                model = v
+        if cur.get("physical id") is not None and cur.get("core id") is not None:
+            phys.add((cur["physical id"], cur["core id"]))
+    except OSError:
+        pass
+    try:
+        logical = len(os.sched_getaffinity(0))
+    except AttributeError:
+        logical = os.cpu_count()
+    return {"model": model, "physical_cores": len(phys) or None, "logical_cpus_allowed": logical}
+
+
+def blas_threads():
+    import threadpoolctl
+    return max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
+
+
+def measured_peaks(U, torch):
+    """What this device sustains: an MFMA-only stream (fp16, 16 waves per CU,
+    no memory traffic), a 1 GiB device copy (read + write) and a 1 GiB
+    streaming read, each the median of 5 timed runs."""
+    import numpy as np
+    sink = torch.empty(256, dtype=torch.float32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n=5):
+        fn()
+        ts = []
+        for _ in range(n):
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    blocks, iters = 256 * 4, 4096
+    flops = U.oidn_calibrate_mfma(U.OIDN_F16, iters, blocks, sink)
+    ms = timed(lambda: U.oidn_calibrate_mfma(U.OIDN_F16, iters, blocks, sink))
+    mfma = flops / ms / 1e9
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    ms_copy = timed(lambda: b.copy_(a))
+    ms_read = timed(lambda: U.oidn_calibrate_read(a, COPY_BYTES, sink))
+    del a, b
+    return {"mfma_f16_tflops": round(mfma, 1), "mfma_f16_frac_of_published": round(mfma / PEAK_F16_TFLOPS, 4),
+            "hbm_copy_gbs": round(2 * COPY_BYTES / ms_copy / 1e6, 1),
+            "hbm_read_gbs": round(COPY_BYTES / ms_read / 1e6, 1),
+            "method": f"MFMA stream: {blocks} workgroups x 4 waves x {iters} x 8 independent "
+                      "v_mfma_f32_16x16x32_f16 (oidn_calibrate_mfma); HBM: 1 GiB device copy "
+                      "(read + write bytes) and a 1 GiB streaming read (oidn_calibrate_read); medians of 5"}
+
+
+def unet_flops(U, w, h):
+    """Algorithmic FLOPs of the network on a w x h tile, from the library's
+    layer table (decoder convs' upsampled channels at 6 taps, as above)."""
+    fl = 0.0
+    for i in range(U.oidn_unet_layer_count()):
+        _, c0, c1, co, level, _ = U.oidn_unet_layer_info(9, i)
+        fl += 2.0 * (w >> level) * (h >> level) * co * ((6 * c0 + 9 * c1) if c1 else 9 * c0)
+    return fl
+
+
+def other_configs(U, torch, S, dtype_name):
+    """The other workloads, timed on the GPU with events around repeated
+    launches (inputs resident): the single fp32 conv (64 x 64, 9 -> 32), the
+    fp16 conv ladder at 256 x 256 (five conv + pool stages), the network on
+    one packed 512 x 512 tile, and the 3840 x 2160 frame in 1024-pixel tiles
+    (overlap 32, 12 tiles, batched)."""
+    import numpy as np
+    out = {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    # config 1: fp32 conv
+    r = S.rng(0)
+    x = S.uniform_activation(r, 64, 64, 9, 12)
+    w, b = S.he_normal(r, 32, 9), S.bias(r, 32)
+    pk = torch.empty(U.oidn_conv3x3_weights_bytes(9, 0, 32, U.OIDN_F32), dtype=torch.uint8, device="cuda")
+    U.oidn_conv3x3_pack_weights(w, b, 9, 0, 32, U.OIDN_F32, pk)
+    dx = torch.from_numpy(x).cuda()
+    dy = torch.empty((64, 64, 32), dtype=torch.float32, device="cuda")
+    ms = timed(lambda: U.oidn_conv3x3(dx, 64, 64, 9, pk, dy, 32, U.OIDN_F32, U.OIDN_F32, U.OIDN_RELU), 200)
+    fl = 2.0 * 64 * 64 * 32 * 81
+    out["conv_fp32_64x64_9to32"] = {"us": round(ms * 1e3, 2), "tflops": round(fl / ms / 1e9, 3),
+                                    "frac_of_fp32_peak": round(fl / ms / 1e9 / PEAK_F32_TFLOPS, 5),
+                                    "kernel": U.oidn_conv3x3_kernel(64, 64, 9, 0, 32, U.OIDN_F32,
+                                                                    U.OIDN_F32, U.OIDN_RELU)[0]}
+    # config 2: fp16 ladder
+    r = S.rng(0)
+    x = S.relu_normal_activation(r, 256, 256, 32, 32).astype(np.float16)   # round to nearest even
+    chans = [32, 48, 64, 80, 96, 96]
+    flags = U.OIDN_RELU | U.OIDN_POOL2X2
+    bufs = [torch.from_numpy(x).cuda()]
+    packs, fl = [], 0.0
+    hw = 256
+    for i in range(5):
+        cin, cout = chans[i], chans[i + 1]
+        wt, bb = S.he_normal(r, cout, cin), S.bias(r, cout)
+        pkb = torch.empty(U.oidn_conv3x3_weights_bytes(cin, 0, cout, U.OIDN_F16), dtype=torch.uint8,
+                          device="cuda")
+        U.oidn_conv3x3_pack_weights(wt, bb, cin, 0, cout, U.OIDN_F16, pkb)
+        packs.append(pkb)
+        bufs.append(torch.empty((hw // 2, hw // 2, cout), dtype=torch.float16, device="cuda"))
+        fl += 2.0 * hw * hw * cout * 9 * cin
+        hw //= 2
+
+    def ladder():
+        s = 256
+        for i in range(5):
+            U.oidn_conv3x3(bufs[i], s, s, chans[i], packs[i], bufs[i + 1], chans[i + 1], U.OIDN_F16,
+                           U.OIDN_F16, flags)
+            s //= 2
+    ms = timed(ladder, 50)
+    out["conv_ladder_f16_256"] = {"us": round(ms * 1e3, 2), "tflops": round(fl / ms / 1e9, 1),
+                                  "frac_of_f16_peak": round(fl / ms / 1e9 / PEAK_F16_TFLOPS, 4),
+                                  "launches": 5}
+    # config 3: network on one packed 512 x 512 tile
+    DT = {"f16": U.OIDN_F16, "bf16": U.OIDN_BF16}[dtype_name]
+    r = S.rng(0)
+    color, albedo, normal = S.images(r, 512, 512)
+    ws, bs = S.layer_params(r, U.unet_layer_shapes(9))
+    wbuf = torch.empty(U.oidn_unet_weights_bytes(9, DT), dtype=torch.uint8, device="cuda")
+    U.oidn_unet_pack_weights(ws, bs, 9, DT, wbuf)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    packed = torch.empty((512, 512, 12), dtype=torch.float16, device="cuda")
+    U.oidn_pack_input(dev(color), dev(albedo), dev(normal), 512, 512, 0, 0, 512, 512, True,
+                      U.OIDN_TRANSFER_LOG, 1.0, packed, DT)
+    nb = U.oidn_unet_packed_workspace_bytes(9, 512, 512, DT)
+    work = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    net = torch.empty((512, 512, 4), dtype=torch.float32, device="cuda")
+    ms = timed(lambda: U.oidn_unet_forward_packed(wbuf, 9, packed, 512, 512, work, nb, net, DT), 50)
+    fl = unet_flops(U, 512, 512)
+    out["unet_512_packed"] = {"us": round(ms * 1e3, 2), "mp_s": round(512 * 512 / 1e6 / (ms / 1e3), 1),
+                              "conv_tflops": round(fl / ms / 1e9, 1),
+                              "frac_of_f16_peak": round(fl / ms / 1e9 / PEAK_F16_TFLOPS, 4)}
+    del work
+    # config 5: 3840 x 2160 in 1024-pixel tiles
+    W5, H5 = 3840, 2160
+    r = S.rng(0)
+    color, albedo, normal = S.images(r, W5, H5)
+    ws, bs = S.layer_params(r, U.unet_layer_shapes(9))
+    U.oidn_unet_pack_weights(ws, bs, 9, DT, wbuf)
+    nb = U.oidn_unet_workspace_bytes(9, W5, H5, 1024, 32, DT)
+    work = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    o5 = torch.empty((H5, W5, 4), dtype=torch.float32, device="cuda")
+    dc, da, dn = dev(color), dev(albedo), dev(normal)
+    ms = timed(lambda: U.oidn_unet_forward(wbuf, 9, dc, da, dn, W5, H5, True, U.OIDN_TRANSFER_LOG,
+                                           1.0, 1024, 32, work, nb, o5, DT), 10)
+    tiles = U.oidn_plan_tiles(W5, H5, 1024, 32)
+    fl = unet_flops(U, tiles[0][2], tiles[0][3]) * len(tiles)
+    out["unet_3840x2160_tiled"] = {"ms": round(ms, 4), "mp_s": round(W5 * H5 / 1e6 / (ms / 1e3), 1),
+                                   "conv_tflops": round(fl / ms / 1e9, 1),
+                                   "tiles": len(tiles), "tile": list(tiles[0][2:4]),
+                                   "tiles_per_launch": U.oidn_unet_tile_batch(9, W5, H5, 1024, 32, DT)}
+    del work, o5
+    return out
+
+
+def oracle_configs(out_path):
+    """The CPU oracle on the other workloads (a reported baseline, not a
+    target): wall time and rates on all host threads and, for the single
+    conv and the ladder, on one thread.  Writes a markdown summary."""
+    import numpy as np
+    import threadpoolctl
+
+    import synthetic as S
+    from oracle import oracle as O
+    rows = []
+
+    def run(name, fn, work, unit, threads=None):
+        if threads is None:
+            t = time.perf_counter()
+            fn()
+            dt = time.perf_counter() - t
+            used = blas_threads()
+        else:
+            with threadpoolctl.threadpool_limits(threads):
+                t = time.perf_counter()
+                fn()
+                dt = time.perf_counter() - t
+            used = threads
+        rows.append((name, used, dt, work / dt, unit))
+        print(f"  {name:42s} threads={used:3d} {dt:8.3f} s  {work / dt:10.4g} {unit}", flush=True)
+
+    r = S.rng(0)
+    x = S.uniform_activation(r, 64, 64, 9, 12)
+    w, b = S.he_normal(r, 32, 9), S.bias(r, 32)
+    c1 = lambda: O.conv3x3(x, 9, w, b, True, "f32")
+    run("config 1: conv 64x64 9->32 fp32", c1, 2.0 * 64 * 64 * 32 * 81 / 1e9, "GFLOP/s")
+    run("config 1: conv 64x64 9->32 fp32", c1, 2.0 * 64 * 64 * 32 * 81 / 1e9, "GFLOP/s", threads=1)
+    r = S.rng(0)
+    x2 = O.round_to(S.relu_normal_activation(r, 256, 256, 32, 32), "f16")
+    chans = [32, 48, 64, 80, 96, 96]
+    wl = []
+    for i in range(5):
+        wt = S.he_normal(r, chans[i + 1], chans[i])
+        wl.append((wt, S.bias(r, chans[i + 1])))
+    fl2 = sum(2.0 * (256 >> i) ** 2 * chans[i + 1] * 9 * chans[i] for i in range(5))
+
+    def ladder():
+        y = x2
+        for i in range(5):
+            y = O.pool2x2(O.conv3x3(y, chans[i], wl[i][0], wl[i][1], True, "f16"))
+    run("config 2: conv ladder 256^2 fp16 storage", ladder, fl2 / 1e9, "GFLOP/s")
+    run("config 2: conv ladder 256^2 fp16 storage", ladder, fl2 / 1e9, "GFLOP/s", threads=1)
+    r = S.rng(0)
+    color, albedo, normal = S.images(r, 512, 512)
+    ws, bs = S.layer_params(r, O.unet_layer_shapes(9))
+    packed = O.pack_input(color, albedo, normal, 0, 0, 512, 512, True, 1.0, "f16")
+    run("config 3: network 512x512 fp16 storage", lambda: O.unet_forward_packed(ws, bs, packed, 9, "f16"),
+        512 * 512 / 1e6, "MP/s")
+    r = S.rng(0)
+    color, albedo, normal = S.images(r, 3840, 2160)
+    ws, bs = S.layer_params(r, O.unet_layer_shapes(9))
+    run("config 5: 3840x2160, 12 tiles of 1024x784", lambda: O.unet_forward(
+        ws, bs, color, albedo, normal, True, 1.0, 1024, 32, "f16"), 3840 * 2160 / 1e6, "MP/s")
+    info = cpu_info()
+    lines = ["# CPU oracle timings (reported baseline, not a target)", "",
+             "Command (repository root, on the GPU box's host):", "", "```",
+             f"python bench.py --oracle-configs {os.path.relpath(out_path, ROOT)}", "```", "",
+             f"Host: {info['model']}; {info['physical_cores']} physical cores, "
+             f"{info['logical_cpus_allowed']} logical CPUs allowed to the process. The oracle is "
+             "numpy with float64 sums; `threads` is the BLAS thread count it ran with.", "",
+             "| workload | threads | wall s | rate |", "|---|---|---|---|"]
+    for name, used, dt, rate, unit in rows:
+        lines.append(f"| {name} | {used} | {dt:.3f} | {rate:.4g} {unit} |")
+    open(out_path, "w").write("\n".join(lines) + "\n")
+
+
+def mfma_summary(pmc_dir, out_path):
+    """Per-launch MFMA busy fraction and LDS bank-conflict share of the
+    frame's kernels from one rocprofv3 --pmc run (SQ_VALU_MFMA_BUSY_CYCLES,
+    GRBM_GUI_ACTIVE, SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE,
+    SQ_INSTS_VALU_MFMA_MOPS_F16): MFMA busy = busy cycles / (GPU active
+    cycles per XCD x 1024 SIMDs)."""
+    import csv
+    import glob
+    import statistics
+    rows = []
+    for f in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    by, names = {}, {}
+    for r in rows:
+        if "oidn::" not in r["Kernel_Name"]:
+            continue
+        d = int(r["Dispatch_Id"])
+        by.setdefault(d, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        names[d] = kernel_symbol(r["Kernel_Name"])
+    order = sorted(by)
+    first = names[order[0]]
+    starts = [i for i, d in enumerate(order) if names[d] == first]
+    period = starts[1] - starts[0] if len(starts) > 1 else len(order)
+    frames = [order[s:s + period] for s in starts if s + period <= len(order)]
+    lines = ["# MFMA utilisation and LDS bank conflicts per launch: UNet denoise 1920x1080, fp16", "",
+             "Command (repository root, one MI355X):", "", "```",
+             "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_LDS_BANK_CONFLICT "
+             "SQ_LDS_IDX_ACTIVE SQ_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F16 --output-format csv "
+             "-d gpurun_out/pmc_mfma -o run -- python -u bench.py --steps 3 --warmup 1 "
+             "--no-cpu-baseline --pass-launches 0 --cold-frames 0 --no-peaks --no-other-configs",
+             f"python bench.py --mfma-summary gpurun_out/pmc_mfma", "```", "",
+             "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
+             "LDS conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (share of the LDS's "
+             "active cycles lost to bank conflicts); MFMA work = SQ_INSTS_VALU_MFMA_MOPS_F16 x 512 "
+             f"FLOP. Medians over {len(frames)} frames (counters serialise the kernels).", "",
+             "| launch | kernel | MFMA busy | LDS conflict | MFMA GFLOP |", "|---|---|---|---|---|"]
+    for j in range(period):
+        ds = [fr[j] for fr in frames]
+        util = statistics.median(by[d]["SQ_VALU_MFMA_BUSY_CYCLES"] / (by[d]["GRBM_GUI_ACTIVE"] / 8 * 1024)
+                                 for d in ds)
+        conf = statistics.median(by[d]["SQ_LDS_BANK_CONFLICT"] / max(1.0, by[d]["SQ_LDS_IDX_ACTIVE"])
+                                 for d in ds)
+        gf = statistics.median(by[d]["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512 / 1e9 for d in ds)
+        lines.append(f"| {j} | `{names[frames[0][j]]}` | {util:.3f} | {conf:.3f} | {gf:.2f} |")
+    open(out_path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=60)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=140)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--width", type=int, default=1920)
     ap.add_argument("--height", type=int, default=1080)
     ap.add_argument("--max-tile", type=int, default=0)
@@ -187,18 +498,31 @@ def main():
     ap.add_argument("--dtype", choices=["f16", "bf16"], default="f16",
                     help="16-bit storage of the network (the metric is quoted on f16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured MFMA / HBM ceilings")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the single conv, ladder, 512^2 and 4K tiled timings")
     ap.add_argument("--pass-launches", type=int, default=10,
                     help="cold-cache launches of each standalone bandwidth-bound pass (0: skip)")
-    ap.add_argument("--events-every", type=int, default=10,
-                    help="record per-kernel HIP events on every N-th timed step (event markers "
-                         "between launches cost ~4 us each, so they are kept off the other steps)")
+    ap.add_argument("--events-every", type=int, default=2,
+                    help="every N-th timed step records two HIP events around one of the frame's "
+                         "launches (rotating over them)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for HBM counter calibration)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the HBM traffic summary from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--mfma-summary", metavar="PMC_DIR",
+                    help="write the MFMA-busy / LDS-conflict summary from a rocprofv3 --pmc run and exit")
+    ap.add_argument("--oracle-configs", metavar="OUT_MD",
+                    help="time the CPU oracle on the other workloads, write OUT_MD and exit")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
+        return
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary, os.path.join(ROOT, "profiles", "conv_kernels_1080p_mfma_util.md"))
+        return
+    if args.oracle_configs:
+        oracle_configs(args.oracle_configs)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -227,8 +551,16 @@ def main():
     out = torch.empty((H, W, 4), dtype=torch.float32, device="cuda")
     tiles = U.oidn_plan_tiles(W, H, args.max_tile, args.overlap)
     tw, th = tiles[0][2], tiles[0][3]
-    # tiles per launch: the per-kernel events cover the first batch
+    # tiles per launch: the per-launch events cover the first batch
     nbatch = U.oidn_unet_tile_batch(9, W, H, args.max_tile, args.overlap, DTYPE)
+    nlayers = U.oidn_unet_layer_count()
+    syms = [U.oidn_unet_layer_kernel(9, i, tw, th, DTYPE, nbatch) for i in range(nlayers)]
+    # the frame's launches: a fused pair's second layer runs in the first's launch
+    launches, i = [], 0
+    while i < nlayers:
+        launches.append(i)
+        i += 2 if syms[i][0].startswith("conv3x3_pair") else 1
+    nk = nlayers + 2   # events: input pass, layers, output pass
 
     def step(events=None):
         if events is None:
@@ -240,10 +572,15 @@ def main():
                                       U.OIDN_TRANSFER_LOG, 1.0, args.max_tile, args.overlap, work,
                                       nbytes, out, DTYPE, events)
 
-    nk = 18  # input pass, 16 convs, output pass
     every = max(1, args.events_every)
-    inst = [k for k in range(args.steps) if k % every == every - 1] or [args.steps - 1]
-    events = {k: [U.oidn_event_create() for _ in range(nk + 1)] for k in inst}
+    inst = [k for k in range(args.steps) if k % every == every - 1]
+    ev_pool = [U.oidn_event_create() for _ in range(2 * len(inst))]
+    plan = {}   # step -> (launch layer, events array)
+    for n, k in enumerate(inst):
+        li = launches[n % len(launches)]
+        arr = [0] * (nk + 1)
+        arr[1 + li], arr[2 + li] = ev_pool[2 * n], ev_pool[2 * n + 1]
+        plan[k] = (li, arr)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -254,7 +591,7 @@ def main():
     torch.cuda.synchronize()
     t0.record()
     for k in range(args.steps):
-        step(events.get(k))
+        step(plan[k][1] if k in plan else None)
     t1.record()
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
@@ -278,24 +615,27 @@ def main():
                                 args.pass_launches)
               if args.pass_launches > 0 and len(tiles) == 1 else [])
 
-    # per-kernel durations (first tile of each instrumented step)
-    dur = np.zeros((len(inst), nk))
-    for n, k in enumerate(inst):
-        for j in range(nk):
-            dur[n, j] = U.oidn_event_elapsed_ms(events[k][j], events[k][j + 1])
-    for evs in events.values():
-        for e in evs:
-            U.oidn_event_destroy(e)
-    avg_ms = dur.mean(axis=0)
+    # per-launch durations: median over the steps that timed that launch
+    samples = {li: [] for li in launches}
+    for k, (li, arr) in plan.items():
+        samples[li].append(U.oidn_event_elapsed_ms(arr[1 + li], arr[2 + li]))
+    for e in ev_pool:
+        U.oidn_event_destroy(e)
+    launch_ms_events = {li: float(np.median(v)) if v else float("nan") for li, v in samples.items()}
+    # Each event interval also holds its launch's dispatch gap, which the
+    # unmarked frame overlaps with the previous kernel: scale the medians so
+    # that they sum to the unmarked step (never up).
+    scale = min(1.0, ms_per_step / sum(launch_ms_events.values()))
+    launch_ms = {li: v * scale for li, v in launch_ms_events.items()}
 
     # the first pair may run the input pass in its staging (input bit 1), the
     # last the output pass in its epilogue (output field 2)
     def pair_fields(layer):
-        sym = U.oidn_unet_layer_kernel(9, layer, tw, th, DTYPE, nbatch)[0]
+        sym = syms[layer][0]
         if not sym.startswith("conv3x3_pair_"):
             return None
         return [int(f) for f in sym[sym.index("<") + 1:-1].split(", ")]
-    first, last = pair_fields(0), pair_fields(U.oidn_unet_layer_count() - 1)
+    first, last = pair_fields(0), pair_fields(nlayers - 1)
     in_fused = first is not None and (first[3] & 2) != 0
     out_fused = last is not None and last[2] == 2
 
@@ -315,7 +655,7 @@ def main():
         if c1:
             b_in += px * 2 * lanes(c1)
         px_out = px / 4 if flags & U.OIDN_POOL2X2 else px
-        if i == U.oidn_unet_layer_count() - 1:
+        if i == nlayers - 1:
             b_out = px_out * (32 if out_fused else 16)
         else:
             b_out = px_out * 2 * st(co)
@@ -328,56 +668,49 @@ def main():
     layers = []
     groups = {}
     conv_flops = conv_ms = 0.0
-    prev_sym = None
-    for i in range(U.oidn_unet_layer_count()):
+    for i in range(nlayers):
         name, c0, c1, co, level, flags = U.oidn_unet_layer_info(9, i)
         px = (tw >> level) * (th >> level) * nbatch
         # algorithmic work of the method: a decoder conv reads its nearest-2x
         # upsampled source through 2 low-resolution rows per output row (the 3
         # ky taps pre-summed per row parity), so 6 taps for those c0 channels
         flops = 2.0 * px * co * ((6 * c0 + 9 * c1) if c1 else 9 * c0)
-        ms = float(avg_ms[i + 1])
-        sym, nblocks = U.oidn_unet_layer_kernel(9, i, tw, th, DTYPE, nbatch)
+        sym, nblocks = syms[i]
         b_in, b_out = layer_bytes(i, c0, c1, co, level, flags, px)
         conv_flops += flops
-        conv_ms += ms
-        g = groups.setdefault(sym, {"flops": 0.0, "ms": 0.0, "launches": 0})
-        g["flops"] += flops
-        g["ms"] += ms
-        if sym.startswith("conv3x3_pair") and sym == prev_sym:
+        if i not in launch_ms:
             # second layer of a fused pair: its work ran in the previous launch
             prev = layers[-1]
             prev["layer"] += "+" + name
             prev["flops"] += flops
-            prev["us"] = round(prev["us"] + ms * 1e3, 2)
             prev["tflops"] = round(prev["flops"] / (prev["us"] / 1e3) / 1e9, 1)
             prev["bytes"] = prev["b_in"] + b_out     # the intermediate stays on chip
             prev["roof_frac"], prev["roof"] = roof_frac(prev["flops"], prev["bytes"],
                                                         prev["us"] / 1e3)
+            groups[sym]["flops"] += flops
             print(f"  {name:11s}  (fused into the previous launch)", file=sys.stderr)
-            prev_sym = None
             continue
+        ms = launch_ms[i]
+        conv_ms += ms
+        g = groups.setdefault(sym, {"flops": 0.0, "ms": 0.0, "launches": 0})
+        g["flops"] += flops
+        g["ms"] += ms
         g["launches"] += 1
-        prev_sym = sym
         fr, bound = roof_frac(flops, b_in + b_out, ms)
-        layers.append({"layer": name, "us": round(ms * 1e3, 2), "flops": flops,
+        layers.append({"layer": name, "us": round(ms * 1e3, 2),
+                       "us_events": round(launch_ms_events[i] * 1e3, 2), "flops": flops,
                        "tflops": round(flops / ms / 1e9, 1), "roof": bound, "roof_frac": fr,
-                       "bytes": b_in + b_out, "b_in": b_in, "kernel": sym, "blocks": nblocks})
+                       "bytes": b_in + b_out, "b_in": b_in, "kernel": sym, "blocks": nblocks,
+                       "samples": len(samples[i])})
         print(f"  {name:11s} {ms * 1e3:8.1f} us  {flops / ms / 1e9:7.1f} TFLOP/s  {sym} x{nblocks}",
               file=sys.stderr)
     for L in layers:
         L["mb"] = round(L.pop("bytes") / 1e6, 1)
         del L["flops"], L["b_in"]
-    px0 = tw * th
-    pack_bytes = W * H * 48 + px0 * 16 * 2 if len(tiles) == 1 else None   # 16 lanes fp16 out
-    unpack_bytes = W * H * (32 + 16)
-    for j, nm, fused, where in ((0, "input pass", in_fused, "first conv's staging"),
-                                (nk - 1, "output pass", out_fused, "last conv's epilogue")):
-        note = f"  (in the {where})" if fused else ""
-        print(f"  {nm:11s} {avg_ms[j] * 1e3:8.1f} us{note}", file=sys.stderr)
     sym, g = max(groups.items(), key=lambda kv: kv[1]["ms"])
     achieved = g["flops"] / g["ms"] / 1e9  # TFLOP/s
     mp = W * H / 1e6
+    peaks = None if args.no_peaks else measured_peaks(U, torch)
     result = {
         "metric": METRIC,
         "value": round(mp / (ms_per_step / 1e3), 2),
@@ -391,9 +724,15 @@ def main():
         "vs_baseline": None,
         "dtype": args.dtype,
         "data": "synthetic",
-        "kernel_timing": {"instrumented_steps": len(inst), "of_steps": args.steps,
-                          "note": "HIP events between the launches of every "
-                                  f"{every}-th timed step; the other steps run without markers"},
+        "kernel_timing": {"method": f"two HIP events around one launch of every {every}-th timed "
+                                    "step, rotating over the frame's launches (median per launch, "
+                                    "`us_events`); the other steps run without markers. Each "
+                                    "interval also holds its launch's dispatch gap, so the medians "
+                                    "are scaled to sum to ms_per_step (`us`, used for every rate)",
+                          "instrumented_steps": len(inst), "of_steps": args.steps,
+                          "launches_per_frame": len(launches),
+                          "sum_of_event_medians_ms": round(sum(launch_ms_events.values()), 4),
+                          "scale": round(scale, 4)},
         "config": {"workload": f"UNet denoise {W}x{H}, {len(tiles)} tile(s) of {tw}x{th}, HDR log "
                                f"transfer, 9-channel input, {args.dtype} storage / fp32 accumulate",
                    "width": W, "height": H, "tiles": len(tiles), "tiles_per_launch": nbatch,
@@ -406,24 +745,25 @@ def main():
                      "frac": round(achieved / PEAK_F16_TFLOPS, 4),
                      "traffic": recorded_traffic(sym)},
         "elementwise": {
-            "input_pass_fused": in_fused,
-            "input_pass_us": round(float(avg_ms[0]) * 1e3, 2),
-            "input_pass_gbs": (round(pack_bytes / avg_ms[0] / 1e6, 1)
-                               if pack_bytes and not in_fused else None),
-            "output_pass_fused": out_fused,
-            "output_pass_us": round(float(avg_ms[nk - 1]) * 1e3, 2),
-            "output_pass_gbs": (round(unpack_bytes / avg_ms[nk - 1] / 1e6, 1)
-                                if len(tiles) == 1 and not out_fused else None),
-            "peak_gbs": PEAK_HBM_GBS,
-            "standalone": passes},
+            "input_pass_fused": in_fused, "output_pass_fused": out_fused,
+            "peak_gbs": PEAK_HBM_GBS, "standalone": passes},
         "layers": layers,
     }
+    if peaks:
+        result["measured_peaks"] = peaks
+        result["roofline"]["frac_of_measured"] = round(achieved / peaks["mfma_f16_tflops"], 4)
+        result["conv_mfma_frac_of_measured"] = round(conv_flops / conv_ms / 1e9 / peaks["mfma_f16_tflops"], 4)
+        for p in passes:
+            p["frac_of_measured_copy"] = round(p["gbs"] / peaks["hbm_copy_gbs"], 4)
     if cold:
         result["cold_cache"] = {"frames": len(cold), "flush_mb": 512,
                                 "ms_median": round(float(np.median(cold)), 4),
                                 "ms_p10": round(float(np.percentile(cold, 10)), 4),
                                 "ms_p90": round(float(np.percentile(cold, 90)), 4),
                                 "note": "each frame timed alone after writing 512 MB; not value"}
+    if not args.no_other_configs:
+        del work
+        result["other_configs"] = other_configs(U, torch, S, args.dtype)
 
     if args.copy_calibration:
         a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -435,18 +775,22 @@ def main():
 
     if not args.no_cpu_baseline:
         from oracle import oracle as O
-        import threadpoolctl
         t = time.perf_counter()
         O.unet_forward(ws, bs, color, albedo, normal, True, 1.0, args.max_tile, args.overlap,
                        args.dtype)
         dt = time.perf_counter() - t
-        threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
+        info = cpu_info()
         result["cpu_baseline"] = {"value": round(W * H / 1e6 / dt, 4), "unit": "MP/s",
-                                  "cores": threads, "kind": "oracle",
+                                  "cores": blas_threads(), "kind": "oracle",
+                                  "cpu_model": info["model"],
+                                  "physical_cores": info["physical_cores"],
+                                  "logical_cpus_allowed": info["logical_cpus_allowed"],
                                   "sample": f"the same {W}x{H} frame once, end to end (pack, "
                                             f"network, unpack), {args.dtype} storage emulated, float64 "
-                                            f"sums; {dt:.1f} s"}
+                                            f"sums on {blas_threads()} BLAS threads; {dt:.1f} s"}
     print(json.dumps(result), flush=True)
+
+
 
 
 if __name__ == "__main__":

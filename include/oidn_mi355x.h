@@ -355,6 +355,21 @@ int oidn_unet_forward_timed(const void* d_weights, int in_channels, const float*
                             void* workspace, size_t ws_bytes, float* out_rgba, int dtype,
                             hipStream_t stream, void* const* events, int n_events);
 
+/* Measurement helper, not part of the denoise path: `blocks` workgroups of
+ * 4 waves, each wave issuing iters x 8 independent 16x16x32 MFMAs (fp16, or
+ * bf16 with dtype OIDN_BF16) with no memory traffic, to measure the matrix
+ * rate the device sustains.  *flops receives the launch's work (2 per
+ * multiply-add).  sink: a device buffer of at least 256 floats (written
+ * only in a case the operands never produce).  Enqueued on `stream`. */
+int oidn_calibrate_mfma(int dtype, long iters, int blocks, float* sink, long long* flops,
+                        hipStream_t stream);
+
+/* Measurement helper, not part of the denoise path: reads the `bytes` of
+ * device buffer `buf` once (16-byte streaming loads, 2048 workgroups), to
+ * measure the HBM read rate.  bytes: a multiple of 16; sink: a device buffer
+ * of at least 256 floats (written only in a case the data never produces). */
+int oidn_calibrate_read(const void* buf, size_t bytes, float* sink, hipStream_t stream);
+
 /* Timing helpers: a hipEvent_t with timing enabled, its destruction, and the
  * milliseconds between two completed events (synchronises on `end`). */
 int oidn_event_create(void** event);

@@ -414,3 +414,13 @@ def test_image_passes_reject_pixel_counts_past_32_bits():
     assert _code(q, FAKE, 65536, 65536, 0, 0, FAKE, 65536, 65536, 0, 0, 65536, 32768, 1, 1, 1.0,
                  FAKE, 0) == N
     assert "32-bit" in U.last_error()
+
+
+def test_calibration_helpers_reject_bad_arguments():
+    """The measurement helpers check their arguments before any launch."""
+    E = U.OIDN_E_INVALID
+    assert _code(U.oidn_calibrate_mfma, U.OIDN_F32, 16, 8, FAKE) == E        # fp32 has no MFMA stream
+    assert _code(U.oidn_calibrate_mfma, U.OIDN_F16, 0, 8, FAKE) == E         # no iterations
+    assert _code(U.oidn_calibrate_mfma, U.OIDN_F16, 16, 8, 0) == E           # null sink
+    assert _code(U.oidn_calibrate_read, FAKE, 24, FAKE) == E                 # not 16-byte words
+    assert _code(U.oidn_calibrate_read, FAKE + 4, 1024, FAKE) == E           # misaligned

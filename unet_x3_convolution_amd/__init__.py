@@ -45,7 +45,7 @@ EXPORTS = (
     "oidn_unet_workspace_bytes", "oidn_unet_tile_batch", "oidn_unet_input_layout",
     "oidn_unet_forward",
     "oidn_unet_forward_timed", "oidn_unet_forward_noalloc", "oidn_unet_noalloc_scratch_bytes",
-    "oidn_event_create", "oidn_event_destroy", "oidn_event_elapsed_ms",
+    "oidn_calibrate_mfma", "oidn_calibrate_read", "oidn_event_create", "oidn_event_destroy", "oidn_event_elapsed_ms",
 )
 
 
@@ -102,6 +102,8 @@ _SIGS = {
     "oidn_unet_forward_noalloc": ([_vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _i, _vp, _i,
                                    _vp], _i),
     "oidn_unet_noalloc_scratch_bytes": ([ctypes.POINTER(_sz)], _i),
+    "oidn_calibrate_mfma": ([_i, ctypes.c_long, _i, _vp, ctypes.POINTER(ctypes.c_longlong), _vp], _i),
+    "oidn_calibrate_read": ([_vp, _sz, _vp, _vp], _i),
     "oidn_event_create": ([ctypes.POINTER(_vp)], _i),
     "oidn_event_destroy": ([_vp], _i),
     "oidn_event_elapsed_ms": ([_vp, _vp, ctypes.POINTER(_f)], _i),
@@ -390,6 +392,17 @@ def oidn_unet_noalloc_scratch_bytes() -> int:
     n = _sz()
     _check(lib().oidn_unet_noalloc_scratch_bytes(ctypes.byref(n)))
     return n.value
+
+
+def oidn_calibrate_mfma(dtype: int, iters: int, blocks: int, sink, stream=None) -> int:
+    """Launches the MFMA stream; returns its FLOPs."""
+    n = ctypes.c_longlong()
+    _check(lib().oidn_calibrate_mfma(dtype, iters, blocks, _p(sink), ctypes.byref(n), _s(stream)))
+    return n.value
+
+
+def oidn_calibrate_read(buf, nbytes: int, sink, stream=None):
+    _check(lib().oidn_calibrate_read(_p(buf), nbytes, _p(sink), _s(stream)))
 
 
 def oidn_event_create() -> int:

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liboidn_mi355x.so")
-SOURCES = ["api.cpp", "conv_f16.hip", "conv_f32.hip", "elementwise.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "conv_f16.hip", "conv_f32.hip", "elementwise.hip", "noalloc.hip",
+           "calibrate.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-fp32 ops are turned off for the device code: plain fp32 arithmetic only.
@@ -23,8 +24,10 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-I", os.path.join(ROOT, "include")]
 
 
-# Per-source compiler options (none at present).
-SOURCE_FLAGS: dict = {}
+# Per-source options: the MFMA calibration stream keeps its accumulators in
+# arch VGPRs (in accumulation registers the compiler shuffled them between
+# loop iterations).
+SOURCE_FLAGS = {"calibrate.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:

@@ -1285,6 +1285,28 @@ int oidn_unet_forward_timed(const void* d_weights, int in_channels, const float*
                  max_tile, overlap, workspace, ws_bytes, out_rgba, dtype, stream, events, n_events);
 }
 
+int oidn_calibrate_mfma(int dtype, long iters, int blocks, float* sink, long long* flops,
+                        hipStream_t stream) {
+  if (!sink || !flops) return fail(OIDN_E_INVALID, "null sink or flops pointer");
+  if (dtype != OIDN_F16 && dtype != OIDN_BF16)
+    return fail(OIDN_E_INVALID, "the MFMA stream is fp16 or bf16 (got dtype %d)", dtype);
+  if (iters <= 0 || iters > (1L << 30) || blocks <= 0 || blocks > (1 << 20))
+    return fail(OIDN_E_INVALID, "iterations or workgroups out of range");
+  hipError_t e = launch_mfma_stream(dtype == OIDN_BF16, iters, blocks, sink, stream);
+  if (e != hipSuccess) return hip_fail(e, "MFMA stream launch");
+  *flops = mfma_stream_flops(iters, blocks);
+  return ok();
+}
+
+int oidn_calibrate_read(const void* buf, size_t bytes, float* sink, hipStream_t stream) {
+  if (!buf || !sink) return fail(OIDN_E_INVALID, "null buffer or sink pointer");
+  if (bytes == 0 || bytes % 16 || !aligned16(buf))
+    return fail(OIDN_E_INVALID, "the read stream needs a 16-byte aligned buffer of 16-byte words");
+  hipError_t e = launch_read_stream(buf, bytes, sink, stream);
+  if (e != hipSuccess) return hip_fail(e, "read stream launch");
+  return ok();
+}
+
 int oidn_event_create(void** event) {
   if (!event) return fail(OIDN_E_INVALID, "null event pointer");
   hipEvent_t e;

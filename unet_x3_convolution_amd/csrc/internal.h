@@ -235,6 +235,13 @@ hipError_t launch_pool(const void* x, int h, int w, int cs, void* y, int dtype, 
 hipError_t launch_upcat(const void* low, int cs_low, const void* skip, int cs_skip, int h, int w,
                         void* z, bool b16, hipStream_t stream);
 
+// Measurement helper: independent MFMA streams with no memory traffic
+// (calibrate.hip).  Work of a launch in FLOPs (2 per multiply-add).
+hipError_t launch_mfma_stream(int bf16, long iters, int blocks, float* sink, hipStream_t stream);
+long mfma_stream_flops(long iters, int blocks);
+// Measurement helper: reads `bytes` (a multiple of 16) once.
+hipError_t launch_read_stream(const void* p, size_t bytes, float* sink, hipStream_t stream);
+
 // The end-to-end denoise (oidn_unet_forward's body) with as many tiles per
 // launch as `ws_bytes` holds, at least one; bytes of one tile's workspace
 // plan for that image.  Both set the thread-local error on failure.
