@@ -419,8 +419,8 @@ def test_image_passes_reject_pixel_counts_past_32_bits():
 def test_calibration_helpers_reject_bad_arguments():
     """The measurement helpers check their arguments before any launch."""
     E = U.OIDN_E_INVALID
-    assert _code(U.oidn_calibrate_mfma, U.OIDN_F32, 16, 8, FAKE) == E        # fp32 has no MFMA stream
-    assert _code(U.oidn_calibrate_mfma, U.OIDN_F16, 0, 8, FAKE) == E         # no iterations
-    assert _code(U.oidn_calibrate_mfma, U.OIDN_F16, 16, 8, 0) == E           # null sink
-    assert _code(U.oidn_calibrate_read, FAKE, 24, FAKE) == E                 # not 16-byte words
-    assert _code(U.oidn_calibrate_read, FAKE + 4, 1024, FAKE) == E           # misaligned
+    assert _code(U.oidn_calibrate_mfma, U.OIDN_F32, 16, 8, FAKE, 0) == E     # fp32 has no MFMA stream
+    assert _code(U.oidn_calibrate_mfma, U.OIDN_F16, 0, 8, FAKE, 0) == E      # no iterations
+    assert _code(U.oidn_calibrate_mfma, U.OIDN_F16, 16, 8, 0, 0) == E        # null sink
+    assert _code(U.oidn_calibrate_read, FAKE, 24, FAKE, 0) == E              # not 16-byte words
+    assert _code(U.oidn_calibrate_read, FAKE + 4, 1024, FAKE, 0) == E        # misaligned
