@@ -668,9 +668,9 @@ __device__ __forceinline__ void stage_pair_images(uint4* slots, const PackArgs& 
     float ch[12];
 #pragma unroll
     for (int k = 0; k < 12; ++k) ch[k] = 0.f;
-    ch[0] = in_color(col[i].x, in.hdr, in.input_scale);
-    ch[1] = in_color(col[i].y, in.hdr, in.input_scale);
-    ch[2] = in_color(col[i].z, in.hdr, in.input_scale);
+    ch[0] = in_color<true>(col[i].x, in.hdr, in.input_scale);
+    ch[1] = in_color<true>(col[i].y, in.hdr, in.input_scale);
+    ch[2] = in_color<true>(col[i].z, in.hdr, in.input_scale);
     if (in.sources > 1) {
       ch[3] = in_albedo(alb[i].x);
       ch[4] = in_albedo(alb[i].y);

@@ -64,9 +64,9 @@ __global__ __launch_bounds__(THREADS) void pack_input_kernel(PackArgs a) {
 #pragma unroll
   for (int i = 0; i < 12; ++i) ch[i] = 0.f;
   const float4 col = ld_stream(a.color + src);
-  ch[0] = in_color(col.x, a.hdr, a.input_scale);
-  ch[1] = in_color(col.y, a.hdr, a.input_scale);
-  ch[2] = in_color(col.z, a.hdr, a.input_scale);
+  ch[0] = in_color<DT != OIDN_F32>(col.x, a.hdr, a.input_scale);
+  ch[1] = in_color<DT != OIDN_F32>(col.y, a.hdr, a.input_scale);
+  ch[2] = in_color<DT != OIDN_F32>(col.z, a.hdr, a.input_scale);
   if (a.sources > 1) {
     const float4 al = ld_stream(a.albedo + src);
     ch[3] = in_albedo(al.x);
