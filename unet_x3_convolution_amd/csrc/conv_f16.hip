@@ -35,6 +35,7 @@
 // the pixel position or the image size, so tiled and untiled runs agree bit
 // for bit wherever their inputs agree.
 #include <cstdio>
+#include <type_traits>
 
 #include "internal.h"
 #include "image_io.h"
@@ -323,7 +324,9 @@ __device__ __forceinline__ void store_tile(const floatx4 (&acc)[R][NFW], const C
 #pragma unroll
     for (int i = 0; i < 4; ++i) bv[q][i] = a.bias[chan[q] + i];
   }
-  if (!pool) {
+  // relu is uniform: each branch gets its own copy of the loops (a select
+  // per value otherwise)
+  auto plain = [&](auto with_relu) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int yy = yb + r;
@@ -332,12 +335,19 @@ __device__ __forceinline__ void store_tile(const floatx4 (&acc)[R][NFW], const C
 #pragma unroll
         for (int q = 0; q < NFW; ++q)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[q][i] = act(acc[r][q][i] + bv[q][i], relu);
+          for (int i = 0; i < 4; ++i) {
+            v[q][i] = acc[r][q][i] + bv[q][i];
+            if constexpr (decltype(with_relu)::value) v[q][i] = fmaxf(v[q][i], 0.f);
+          }
         store_pixel<NFW, OUTF32, BF>(y, ((size_t)yy * a.w + x) * a.cout_stored, chan, lead, tail,
                                  a.cout_stored, v);
       }
     }
-  } else {
+  };
+  // 2x2 max of the biased values (adding the bias commutes with the max:
+  // rounding is monotone).  After ReLU the values are +0 or positive, whose
+  // bit patterns order like the values: integer maxima, no NaN quieting.
+  auto pooled = [&](auto with_relu) {
     const int ow = a.w >> 1;
 #pragma unroll
     for (int rp = 0; rp < R / 2; ++rp) {
@@ -346,14 +356,26 @@ __device__ __forceinline__ void store_tile(const floatx4 (&acc)[R][NFW], const C
       for (int q = 0; q < NFW; ++q)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float v = act(fmaxf(acc[2 * rp][q][i], acc[2 * rp + 1][q][i]) + bv[q][i], relu);
-          m[q][i] = fmaxf(v, swap_pair(v));
+          if constexpr (decltype(with_relu)::value) {
+            const int v0 = __float_as_int(fmaxf(acc[2 * rp][q][i] + bv[q][i], 0.f));
+            const int v1 = __float_as_int(fmaxf(acc[2 * rp + 1][q][i] + bv[q][i], 0.f));
+            const int v = max(v0, v1);
+            m[q][i] = __int_as_float(max(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false)));
+          } else {
+            const float v = fmaxf(acc[2 * rp][q][i], acc[2 * rp + 1][q][i]) + bv[q][i];
+            m[q][i] = fmaxf(v, swap_pair(v));
+          }
         }
       const int yy = yb + 2 * rp;
       if ((c & 1) == 0 && yy < a.h && x < xend)
         store_pixel<NFW, OUTF32, BF>(y, ((size_t)(yy >> 1) * ow + (x >> 1)) * a.cout_stored, chan,
                                  lead, tail, a.cout_stored, m);
     }
+  };
+  if (!pool) {
+    if (relu) plain(std::true_type{}); else plain(std::false_type{});
+  } else {
+    if (relu) pooled(std::true_type{}); else pooled(std::false_type{});
   }
 }
 
@@ -639,23 +661,24 @@ __device__ __forceinline__ void stage_pair_images(uint4* slots, const PackArgs& 
   float3 col[NIT], alb[NIT], nrm[NIT];
   float zl[NIT], zr[NIT];
   auto rgb = [](const float4* img, size_t i) { return *reinterpret_cast<const float3*>(img + i); };
+  // Clamp-to-edge coordinates are always inside the image, so every lane
+  // loads, with no branches: what lies outside the tile (or past the
+  // patch, in the last round) is zeroed or dropped below.
 #pragma unroll
   for (int i = 0; i < NIT; ++i) {
     const int pp = tid + THREADS * i;
     const int py = pp / PAIR_PW, px = pp - py * PAIR_PW;
     const int y = y0 - 2 + py, x = x0 - 2 + px;
-    col[i] = alb[i] = nrm[i] = make_float3(0.f, 0.f, 0.f);
+    const size_t row = (size_t)min(max(y + in.tile_y, 0), in.img_h - 1) * in.img_w;
+    const size_t src = row + min(max(x + in.tile_x, 0), in.img_w - 1);
+    col[i] = rgb(in.color, src);
+    alb[i] = nrm[i] = make_float3(0.f, 0.f, 0.f);
     zl[i] = zr[i] = 0.f;
-    if (pp < NPIX && y >= 0 && y < h && x >= 0 && x < w) {
-      const size_t row = (size_t)min(max(y + in.tile_y, 0), in.img_h - 1) * in.img_w;
-      const size_t src = row + min(max(x + in.tile_x, 0), in.img_w - 1);
-      col[i] = rgb(in.color, src);
-      if (in.sources > 1) alb[i] = rgb(in.albedo, src);
-      if (in.sources > 2) nrm[i] = rgb(in.normal, src);
-      if (TAPS) {
-        if (x > 0) zl[i] = in.normal[row + min(max(x - 1 + in.tile_x, 0), in.img_w - 1)].z;
-        if (x + 1 < w) zr[i] = in.normal[row + min(max(x + 1 + in.tile_x, 0), in.img_w - 1)].z;
-      }
+    if (in.sources > 1) alb[i] = rgb(in.albedo, src);
+    if (in.sources > 2) nrm[i] = rgb(in.normal, src);
+    if (TAPS) {
+      zl[i] = in.normal[row + min(max(x - 1 + in.tile_x, 0), in.img_w - 1)].z;
+      zr[i] = in.normal[row + min(max(x + 1 + in.tile_x, 0), in.img_w - 1)].z;
     }
   }
 #pragma unroll

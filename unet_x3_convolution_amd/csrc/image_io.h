@@ -10,7 +10,10 @@ namespace oidn {
 constexpr float kFltMax = 3.402823466e+38f;
 
 // NaN -> 0, otherwise clamp to [lo, hi] (reading of the pages' sanitize()).
+// fmaxf returns the other operand for a NaN, so with lo = 0 the clamp alone
+// maps NaN to 0; other bounds test for it.
 __device__ __forceinline__ float sanitize(float v, float lo, float hi) {
+  if (lo == 0.f) return fminf(fmaxf(v, 0.f), hi);
   if (v != v) return 0.f;
   return fminf(fmaxf(v, lo), hi);
 }
@@ -47,16 +50,19 @@ __device__ __forceinline__ float in_color(float v, int hdr, float input_scale) {
 __device__ __forceinline__ float in_albedo(float v) { return sanitize(v, 0.f, 1.f); }
 __device__ __forceinline__ float in_normal(float v) { return sanitize(v, -1.f, 1.f) * 0.5f + 0.5f; }
 
-// Two channels as fp16 (round to nearest even), the first in the low half.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two channels as fp16 (round to nearest even), the first in the low half:
+// one packed conversion instruction.
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
-  const _Float16 ha = (_Float16)a, hb = (_Float16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, f16x2_t));
 }
 
 // Two channels as bf16 (round to nearest even), the first in the low half.
 __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
 // ... in the 16-bit storage type: fp16, or bf16 (BF).
