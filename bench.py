@@ -294,6 +294,20 @@ def other_configs(U, torch, S, dtype_name):
                                     "frac_of_fp32_peak": round(fl / ms / 1e9 / PEAK_F32_TFLOPS, 5),
                                     "kernel": U.oidn_conv3x3_kernel(64, 64, 9, 0, 32, U.OIDN_F32,
                                                                     U.OIDN_F32, U.OIDN_RELU)[0]}
+    # the same fp32 kernel at a size that fills the GPU: 32 -> 32 at 1920 x 1088
+    xb = torch.rand((1088, 1920, 32), dtype=torch.float32, device="cuda")
+    wb, bb = S.he_normal(r, 32, 32), S.bias(r, 32)
+    pkb = torch.empty(U.oidn_conv3x3_weights_bytes(32, 0, 32, U.OIDN_F32), dtype=torch.uint8, device="cuda")
+    U.oidn_conv3x3_pack_weights(wb, bb, 32, 0, 32, U.OIDN_F32, pkb)
+    yb = torch.empty((1088, 1920, 32), dtype=torch.float32, device="cuda")
+    ms = timed(lambda: U.oidn_conv3x3(xb, 1088, 1920, 32, pkb, yb, 32, U.OIDN_F32, U.OIDN_F32,
+                                      U.OIDN_RELU), 20)
+    fl = 2.0 * 1088 * 1920 * 32 * 9 * 32
+    out["conv_fp32_1088x1920_32to32"] = {"us": round(ms * 1e3, 2), "tflops": round(fl / ms / 1e9, 2),
+                                         "frac_of_fp32_peak": round(fl / ms / 1e9 / PEAK_F32_TFLOPS, 4),
+                                         "kernel": U.oidn_conv3x3_kernel(1088, 1920, 32, 0, 32, U.OIDN_F32,
+                                                                         U.OIDN_F32, U.OIDN_RELU)[0]}
+    del xb, yb
     # config 2: fp16 ladder
     r = S.rng(0)
     x = S.relu_normal_activation(r, 256, 256, 32, 32).astype(np.float16)   # round to nearest even

@@ -180,13 +180,22 @@ def test_f32_weight_layout_round_trip():
     packed = U.oidn_conv3x3_pack_weights_host(w, b, cin0, cin1, cout, U.OIDN_F32).view(np.float32)
     cs, cst = O.stored(cout), O.stored(cin0) + O.stored(cin1)
     assert np.array_equal(packed[:cout], b) and np.all(packed[cout:cs] == 0)
-    wt = packed[64:].reshape(cs // 4, 9, cst, 4)
-    for o in range(cs):
+    # per 16-channel output fragment, tap and 32-channel input chunk: the
+    # MFMA A operand of 64 lanes x 8 K steps, lane 16 g + (o mod 16) and step
+    # j holding input channel 32 k + 8 g + j
+    nfrag, nck = -(-cs // 16), -(-cst // 32)
+    wt = packed[64:].reshape(nfrag, 9, nck, 4, 16, 8)
+    assert packed[64:].size == nfrag * 9 * nck * 64 * 8
+    for o in range(16 * nfrag):
         for tap in range(9):
-            for c in range(cst):
-                li = c if c < cin0 else (cin0 + c - O.stored(cin0) if c - O.stored(cin0) < cin1 else -1)
+            for c in range(32 * nck):
+                if c < cst:
+                    li = c if c < cin0 else (cin0 + c - O.stored(cin0) if c - O.stored(cin0) < cin1 else -1)
+                else:
+                    li = -1
                 expected = w[o, tap // 3, tap % 3, li] if (o < cout and li >= 0) else 0.0
-                assert wt[o // 4, tap, c, o % 4] == expected
+                k, cc = divmod(c, 32)
+                assert wt[o // 16, tap, k, cc // 8, o % 16, cc % 8] == expected
 
 
 def test_workspace_plan_is_liveness_bounded():
@@ -345,7 +354,12 @@ def test_conv_kernel_selection():
     assert U.oidn_conv3x3_kernel(1088, 1920, 32, 0, 3, F, F32, 0) == ("conv3x3_f16_mfma<1, 4, 4, true>", 8160)
     assert U.oidn_conv3x3_kernel(136, 240, 160, 0, 112, F, F, R) == ("conv3x3_f16_mfma<1, 4, 4, false>", 952)
     assert U.oidn_conv3x3_kernel(40, 52, 32, 0, 64, F, F, R) == ("conv3x3_f16_mfma<1, 2, 4, false>", 96)
-    assert U.oidn_conv3x3_kernel(8, 8, 9, 0, 32, F32, F32, R)[0] == "conv3x3_f32_direct"
+    # fp32: 8 x 16 tiles, one fragment per workgroup, below 512 workgroups of
+    # the 16 x 16 four-fragment shape
+    assert U.oidn_conv3x3_kernel(8, 8, 9, 0, 32, F32, F32, R) == ("conv3x3_f32_mfma<2, 1>", 2)
+    assert U.oidn_conv3x3_kernel(64, 64, 9, 0, 32, F32, F32, R) == ("conv3x3_f32_mfma<2, 1>", 64)
+    assert U.oidn_conv3x3_kernel(40, 52, 64, 64, 112, F32, F32, R) == ("conv3x3_f32_mfma<2, 1>", 4 * 5 * 7)
+    assert U.oidn_conv3x3_kernel(1088, 1920, 32, 0, 32, F32, F32, R) == ("conv3x3_f32_mfma<4, 4>", 120 * 68)
     with pytest.raises(U.OidnError):
         U.oidn_conv3x3_kernel(8, 8, 300, 0, 32, F, F, R)
 

@@ -123,7 +123,12 @@ def test_conv_bf16_matches_oracle(h, w, cin, cout, flags, outp):
 
 @pytest.mark.parametrize("h,w,cin,cout,flags", [(20, 18, 12, 8, U.OIDN_RELU),
                                                 (10, 14, 40, 20, U.OIDN_RELU | U.OIDN_POOL2X2),
-                                                (9, 5, 3, 3, 0)])
+                                                (9, 5, 3, 3, 0),
+                                                # three input chunks, two fragment groups
+                                                # (7 fragments), ragged 16 x 16 tiles
+                                                (37, 41, 72, 112, U.OIDN_RELU),
+                                                (34, 50, 96, 96, U.OIDN_RELU | U.OIDN_POOL2X2),
+                                                (64, 64, 9, 32, 0)])
 def test_conv_f32_matches_oracle(h, w, cin, cout, flags):
     r = np.random.default_rng(h + cin)
     x = S.relu_normal_activation(r, h, w, cin, O.stored(cin))
@@ -178,6 +183,8 @@ UPCAT_CASES = [
     (20, 12, 8, 5, 16, "f16"),
     (18, 26, 112, 48, 96, "f16"),
     (12, 10, 16, 9, 8, "f32"),
+    (34, 46, 96, 64, 112, "f32"),                               # 6 input chunks, 2 fragment groups
+    (30, 18, 64, 9, 64, "f32"),
     (512, 1024, 64, 9, 64, "f16"),                              # 32-row tiles
     (544, 960, 64, 16, 64, "f16"),                              # <4, 8, 4>: 16-channel skip, 3 chunks
     (546, 1002, 96, 32, 64, "f16"),                             # <4, 8, 4>, ragged, 4 chunks

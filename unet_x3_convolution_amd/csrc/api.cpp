@@ -228,7 +228,7 @@ void pack_conv_host(const float* w, const float* b, int cin0, int cin1, int cout
         for (int c = 0; c < cst; ++c) {
           const int li = c < cs0 ? logical(0, c) : logical(1, c - cs0);
           if (li < 0) continue;
-          wt[(((size_t)(o / 4) * 9 + tap) * cst + c) * 4 + (o % 4)] = wat(o, tap, li);
+          wt[conv_f32_weight_index(o, tap, c, cst)] = wat(o, tap, li);
         }
   }
 }
@@ -941,9 +941,8 @@ int oidn_conv3x3_kernel(int h, int w, int cin0, int cin1, int cout, int in_dtype
     const ConvF16Args a = f16_args(cin0, cin1, cout, h, w, 0, 0, &L);
     conv_f16_describe(a, L.nf, out_dtype == OIDN_F32, in_dtype == OIDN_BF16, buf, cap, &nb);
   } else {
-    snprintf(buf, cap, "conv3x3_f32_direct");
-    const bool pool = flags & OIDN_POOL2X2;
-    nb = (int)cdiv((pool ? w / 2 : w) * (pool ? h / 2 : h) * (stored_channels(cout) / 4), 256);
+    snprintf(buf, cap, "%s", conv_f32_kernel_name(h, w, cout));
+    nb = conv_f32_blocks(h, w, cout);
   }
   if (blocks) *blocks = nb;
   return ok();
@@ -1115,9 +1114,8 @@ int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int batch
     a.batch = batch;
     conv_f16_describe(a, lay.nf, final_layer, dtype == OIDN_BF16, buf, cap, &nb);
   } else {
-    snprintf(buf, cap, "conv3x3_f32_direct");
-    const int oh = kUNet[layer].pool ? h / 2 : h, ow = kUNet[layer].pool ? w / 2 : w;
-    nb = (int)cdiv(ow * oh * (stored_channels(s[layer].cout) / 4), 256) * batch;
+    snprintf(buf, cap, "%s", conv_f32_kernel_name(h, w, s[layer].cout));
+    nb = conv_f32_blocks(h, w, s[layer].cout) * batch;
   }
   if (blocks) *blocks = nb;
   return ok();

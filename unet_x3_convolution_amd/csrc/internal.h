@@ -197,9 +197,10 @@ hipError_t launch_conv_pair_f16(const PairArgs& p, int cga, int nfb, int in, boo
 int conv_pair_blocks(int h, int w);
 
 // ---------------------------------------------------------------------------
-// fp32 direct conv (VALU FMA).  Packed weights: bias (cout_stored floats,
-// 256-aligned) then [out block][tap][stored input channel over both
-// sources][4 output lanes].
+// fp32 conv on the matrix cores.  Packed weights: bias (cout_stored floats,
+// 256-aligned) then, per 16-channel output fragment, tap and 32-channel
+// input chunk (stored channels over both sources), the 64 lanes' 8 values of
+// the MFMA A operand (conv_f32_weight_index).
 // ---------------------------------------------------------------------------
 struct ConvF32Args {
   const float* src0;
@@ -213,6 +214,13 @@ struct ConvF32Args {
 };
 
 size_t conv_f32_bytes(int cin_stored_total, int cout);
+int conv_f32_chunks(int cin_stored_total);
+// Workgroups and kernel instance of the launch for an h x w conv input.
+int conv_f32_blocks(int h, int w, int cout);
+const char* conv_f32_kernel_name(int h, int w, int cout);
+// Float index (after the bias) of the weight of output channel o, tap
+// (3 ky + kx) and stored input channel c.
+size_t conv_f32_weight_index(int o, int tap, int c, int cin_stored_total);
 hipError_t launch_conv_f32(const ConvF32Args& a, bool upcat, bool pool, bool relu,
                            hipStream_t stream);
 
