@@ -13,15 +13,19 @@ namespace {
 constexpr int THREADS = 256;
 
 // Streaming accesses.  Inputs that a wave reads in whole 64-byte lines and
-// nothing reads again are loaded non-temporally, and outputs written in
-// whole lines are stored non-temporally: cold reads of a just-written cache
-// then do not have to evict its dirty lines first (a 150 MB copy moves
-// 5.6 TB/s instead of 3.5 on one MI355X).  The input pass's 16-bit packed
-// pixels of a whole wave leave through LDS as lane-contiguous 16-byte
-// streaming stores.  Partial-line accesses (the per-lane 8-byte channel
-// blocks at a 24-byte pixel stride of a wave that reaches past the tile and
-// of the fp32 input pass, the skip blocks of the concat) stay cached, so that
-// the neighbouring lanes' and waves' pieces of a line meet in L2.
+// nothing reads again are loaded non-temporally, and the input pass, output
+// pass and pool store whole-line outputs non-temporally: cold reads of a
+// just-written cache then do not have to evict its dirty lines first.
+// Measured on one MI355X after other work left dirty lines: the input pass
+// 29.5 us instead of 44.6 with plain accesses, the pool 32.0 instead of
+// 53.4, the output pass 20.1 instead of 31.2 (with clean caches plain
+// accesses are 3-6% faster).  The materialised concat stores plainly, which
+// is faster either way.  The input pass's 16-bit packed pixels of a whole
+// wave leave through LDS as lane-contiguous 16-byte streaming stores.
+// Partial-line accesses (the per-lane 8-byte channel blocks at a 24-byte
+// pixel stride of a wave that reaches past the tile and of the fp32 input
+// pass) stay cached, so that the neighbouring lanes' and waves' pieces of a
+// line meet in L2.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -254,45 +258,56 @@ __global__ __launch_bounds__(THREADS) void pool2x2_kernel(const void* x, int h, 
   }
 }
 
-// Materialised [up(low) | skip]: one thread per (pixel, 4-channel block of
-// the concat) of two low-resolution rows, i.e. output rows 4 Y .. 4 Y + 3
-// (blockIdx.y = Y, 32-bit index arithmetic within the row); a block is 8
-// bytes (fp16) or 16 bytes (fp32).  All of a thread's loads are in flight
-// before its stores: an upsampled block is read once per low-resolution row
-// and stored twice, the skip's blocks are read row by row.
-constexpr int kUpcatLowRows = 2;
-template <typename Block>
-__global__ __launch_bounds__(THREADS) void upcat_kernel(const Block* low, int nb_low,
-                                                        const Block* skip, int nb_skip, int h,
-                                                        int w, Block* z) {
-  const int nb = nb_low + nb_skip;
-  const int r = blockIdx.x * THREADS + threadIdx.x;   // (pixel, block) within the row
-  if (r >= w * nb) return;
-  const int x = r / nb, b = r - x * nb;
-  const size_t zrow = (size_t)w * nb;
-  const int nly = h >> 1;
-  for (int ly0 = kUpcatLowRows * blockIdx.y; ly0 < nly; ly0 += kUpcatLowRows * gridDim.y) {
-    Block v[kUpcatLowRows][2];
+// Materialised [up(low) | skip] in 8-byte words (a 4-channel block of fp16
+// or bf16, half a block of fp32): lw / sw words per pixel of the
+// low-resolution and skip sources, pw = lw + sw per output pixel.  A
+// workgroup writes output rows 2 ly and 2 ly + 1 over the pixel span
+// [x0, x0 + n) (x0 and n even): it copies the low-resolution span and both
+// skip-row spans into LDS with consecutive-lane loads, then writes each
+// output row span as consecutive 16-byte units gathered from LDS (a unit
+// may straddle the low/skip boundary or two pixels).  `magic` is
+// ceil(2^32 / pw): floor(word / pw) = umulhi(word, magic) for the span's
+// word indices (below 2^16).
+__global__ __launch_bounds__(THREADS) void upcat_kernel(const uint2* __restrict__ low, int lw,
+                                                        const uint2* __restrict__ skip, int sw,
+                                                        int h, int w, int seg, unsigned magic,
+                                                        uint4* __restrict__ z) {
+  extern __shared__ uint2 sm[];
+  const int tid = threadIdx.x;
+  const int pw = lw + sw;
+  const int x0 = blockIdx.x * seg;
+  const int n = min(seg, w - x0);
+  uint2* const slow = sm;
+  uint2* const sskip = sm + (n >> 1) * lw;
+  const int nlow = (n >> 1) * lw, nskip = n * sw;
+  const int units = (n * pw) >> 1;                 // 16-byte units per output row span
+  for (int ly = blockIdx.y; ly < (h >> 1); ly += gridDim.y) {
+    const size_t lbase = ((size_t)ly * (w >> 1) + (x0 >> 1)) * lw;
+    for (int i = tid; i < nlow; i += THREADS) slow[i] = ld_stream(low + lbase + i);
 #pragma unroll
-    for (int j = 0; j < kUpcatLowRows; ++j) {
-      const int ly = ly0 + j;
-      if (ly >= nly) break;
-      if (b < nb_low) {   // the same low-resolution block for both rows (and both columns)
-        v[j][0] = v[j][1] = low[((size_t)ly * (w >> 1) + (x >> 1)) * nb_low + b];
-      } else {
-        const Block* const s0 = skip + ((size_t)(2 * ly) * w + x) * nb_skip + (b - nb_low);
-        v[j][0] = s0[0];
-        v[j][1] = s0[(size_t)w * nb_skip];
+    for (int r = 0; r < 2; ++r) {
+      const size_t sbase = ((size_t)(2 * ly + r) * w + x0) * sw;
+      for (int i = tid; i < nskip; i += THREADS) sskip[r * nskip + i] = ld_stream(skip + sbase + i);
+    }
+    __syncthreads();
+    for (int u = tid; u < 2 * units; u += THREADS) {
+      const int r = u >= units ? 1 : 0;
+      const int uu = u - r * units;
+      uint2 v[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const unsigned word = 2 * uu + k;
+        const int p = (int)__umulhi(word, magic);
+        const int off = (int)word - p * pw;
+        v[k] = off < lw ? slow[(p >> 1) * lw + off] : sskip[r * nskip + p * sw + (off - lw)];
       }
+      // a plain store: kept in the caches, the concat's lines are written
+      // back whole (streaming stores measured 10% slower here, with the
+      // caches clean or dirty)
+      const size_t zo = (((size_t)(2 * ly + r) * w + x0) * pw >> 1) + uu;
+      z[zo] = make_uint4(v[0].x, v[0].y, v[1].x, v[1].y);
     }
-#pragma unroll
-    for (int j = 0; j < kUpcatLowRows; ++j) {
-      const int ly = ly0 + j;
-      if (ly >= nly) break;
-      Block* const z0 = z + (size_t)(2 * ly) * zrow + r;
-      st_stream(z0, v[j][0]);
-      st_stream(z0 + zrow, v[j][1]);
-    }
+    __syncthreads();
   }
 }
 
@@ -338,18 +353,24 @@ hipError_t launch_pool(const void* x, int h, int w, int cs, void* y, int dtype, 
 
 hipError_t launch_upcat(const void* low, int cs_low, const void* skip, int cs_skip, int h, int w,
                         void* z, bool b16, hipStream_t stream) {
-  const int nb = (cs_low + cs_skip) / 4;
-  const size_t row = (size_t)w * nb;                 // threads per row (of a row pair)
-  if (row == 0 || h / 2 == 0) return hipSuccess;
-  const dim3 grid(grid_for(row).x, grid_rows((h / 2 + kUpcatLowRows - 1) / kUpcatLowRows));
-  if (b16)
-    hipLaunchKernelGGL(upcat_kernel<uint2>, grid, dim3(THREADS), 0, stream,
-                       static_cast<const uint2*>(low), cs_low / 4, static_cast<const uint2*>(skip),
-                       cs_skip / 4, h, w, static_cast<uint2*>(z));
-  else
-    hipLaunchKernelGGL(upcat_kernel<float4>, grid, dim3(THREADS), 0, stream,
-                       static_cast<const float4*>(low), cs_low / 4, static_cast<const float4*>(skip),
-                       cs_skip / 4, h, w, static_cast<float4*>(z));
+  // 8-byte words per pixel: a 4-channel block is one word in 16 bits, two in fp32
+  const int lw = (cs_low / 4) * (b16 ? 1 : 2), sw = (cs_skip / 4) * (b16 ? 1 : 2);
+  if (w < 2 || h < 2) return hipSuccess;
+  // span: even, at most 256 pixels, LDS (half a span of low pixels and two
+  // rows of skip pixels) within 16 KB.  Measured at 960x544x64 + 1920x1088x12
+  // fp16 (event-timed, clean / dirty caches): 16 KB 76 / 89 us, 14 KB
+  // 81 / 83, 20 KB 83 / 86, 24 KB 88 / 91.
+  const int per_px = 4 * lw + 16 * sw;             // bytes of LDS per span pixel
+  int seg = 16 * 1024 / per_px;
+  seg = seg > 256 ? 256 : seg < 2 ? 2 : seg;
+  seg &= ~1;
+  if (seg > w) seg = w;
+  const int pw = lw + sw;
+  const unsigned magic = (unsigned)((0x100000000ull + pw - 1) / pw);
+  const size_t lds = (size_t)((seg >> 1) * lw + 2 * seg * sw) * 8;
+  const dim3 grid(cdiv(w, seg), grid_rows(h / 2));
+  hipLaunchKernelGGL(upcat_kernel, grid, dim3(THREADS), lds, stream, static_cast<const uint2*>(low),
+                     lw, static_cast<const uint2*>(skip), sw, h, w, seg, magic, static_cast<uint4*>(z));
   return hipGetLastError();
 }
 
