@@ -450,15 +450,11 @@ def oracle_configs(out_path):
     open(out_path, "w").write("\n".join(lines) + "\n")
 
 
-def mfma_summary(pmc_dir, out_path):
-    """Per-launch MFMA busy fraction and LDS bank-conflict share of the
-    frame's kernels from one rocprofv3 --pmc run (SQ_VALU_MFMA_BUSY_CYCLES,
-    GRBM_GUI_ACTIVE, SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE,
-    SQ_INSTS_VALU_MFMA_MOPS_F16): MFMA busy = busy cycles / (GPU active
-    cycles per XCD x 1024 SIMDs)."""
+def mfma_frames(pmc_dir):
+    """Per-dispatch counters of one rocprofv3 --pmc run, cut into frames
+    (the launch sequence that starts with the frame's first kernel)."""
     import csv
     import glob
-    import statistics
     rows = []
     for f in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
         rows += list(csv.DictReader(open(f)))
@@ -474,18 +470,15 @@ def mfma_summary(pmc_dir, out_path):
     starts = [i for i, d in enumerate(order) if names[d] == first]
     period = starts[1] - starts[0] if len(starts) > 1 else len(order)
     frames = [order[s:s + period] for s in starts if s + period <= len(order)]
-    lines = ["# MFMA utilisation and LDS bank conflicts per launch: UNet denoise 1920x1080, fp16", "",
-             "Command (repository root, one MI355X):", "", "```",
-             "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_LDS_BANK_CONFLICT "
-             "SQ_LDS_IDX_ACTIVE SQ_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F16 --output-format csv "
-             "-d gpurun_out/pmc_mfma -o run -- python -u bench.py --steps 3 --warmup 1 "
-             "--no-cpu-baseline --pass-launches 0 --cold-frames 0 --no-peaks --no-other-configs",
-             f"python bench.py --mfma-summary gpurun_out/pmc_mfma", "```", "",
-             "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
-             "LDS conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (share of the LDS's "
-             "active cycles lost to bank conflicts); MFMA work = SQ_INSTS_VALU_MFMA_MOPS_F16 x 512 "
-             f"FLOP. Medians over {len(frames)} frames (counters serialise the kernels).", "",
-             "| launch | kernel | MFMA busy | LDS conflict | MFMA GFLOP |", "|---|---|---|---|---|"]
+    return by, names, frames, period
+
+
+def mfma_rows(pmc_dir):
+    """(kernel, MFMA busy, LDS conflict, MFMA GFLOP) per launch of the frame:
+    medians over the run's frames."""
+    import statistics
+    by, names, frames, period = mfma_frames(pmc_dir)
+    out = []
     for j in range(period):
         ds = [fr[j] for fr in frames]
         util = statistics.median(by[d]["SQ_VALU_MFMA_BUSY_CYCLES"] / (by[d]["GRBM_GUI_ACTIVE"] / 8 * 1024)
@@ -493,7 +486,53 @@ def mfma_summary(pmc_dir, out_path):
         conf = statistics.median(by[d]["SQ_LDS_BANK_CONFLICT"] / max(1.0, by[d]["SQ_LDS_IDX_ACTIVE"])
                                  for d in ds)
         gf = statistics.median(by[d]["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512 / 1e9 for d in ds)
-        lines.append(f"| {j} | `{names[frames[0][j]]}` | {util:.3f} | {conf:.3f} | {gf:.2f} |")
+        out.append((names[frames[0][j]], util, conf, gf))
+    return out, len(frames)
+
+
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE "
+                 "SQ_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F16")
+
+
+def mfma_summary(pmc_dir, out_path, base_dir=None, base_rev=None):
+    """Per-launch MFMA busy fraction and LDS bank-conflict share of the
+    frame's kernels from one rocprofv3 --pmc run (SQ_VALU_MFMA_BUSY_CYCLES,
+    GRBM_GUI_ACTIVE, SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE,
+    SQ_INSTS_VALU_MFMA_MOPS_F16): MFMA busy = busy cycles / (GPU active
+    cycles per XCD x 1024 SIMDs).  With base_dir, the same counters of an
+    earlier revision's run (base_rev) in columns beside them."""
+    rows, nframes = mfma_rows(pmc_dir)
+    base = mfma_rows(base_dir)[0] if base_dir else None
+    cmd = (f"rocprofv3 --pmc {MFMA_COUNTERS} --output-format csv -d gpurun_out/pmc_mfma -o run -- "
+           "python -u bench.py --steps 3 --warmup 1 --no-cpu-baseline --pass-launches 0 --cold-frames 0 "
+           "--no-peaks --no-other-configs")
+    lines = ["# MFMA utilisation and LDS bank conflicts per launch: UNet denoise 1920x1080, fp16", "",
+             "Commands (repository root, one MI355X):", "", "```", cmd]
+    if base_dir:
+        lines += [f"# the earlier revision, in a checkout of commit {base_rev} (its bench.py has no "
+                  "--no-peaks / --no-other-configs):",
+                  f"rocprofv3 --pmc {MFMA_COUNTERS} --output-format csv -d {base_dir} -o run -- "
+                  "python -u bench.py --steps 3 --warmup 1 --no-cpu-baseline --pass-launches 0 --cold-frames 0",
+                  f"python bench.py --mfma-summary gpurun_out/pmc_mfma {base_dir} {base_rev}"]
+    else:
+        lines.append("python bench.py --mfma-summary gpurun_out/pmc_mfma")
+    lines += ["```", "",
+              "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
+              "LDS conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (share of the LDS's "
+              "active cycles lost to bank conflicts); MFMA work = SQ_INSTS_VALU_MFMA_MOPS_F16 x 512 "
+              f"FLOP. Medians over {nframes} frames (counters serialise the kernels).", ""]
+    if base:
+        lines += [f"| launch | kernel | MFMA busy | LDS conflict | MFMA GFLOP | MFMA busy at {base_rev} "
+                  f"| LDS conflict at {base_rev} |", "|---|---|---|---|---|---|---|"]
+    else:
+        lines += ["| launch | kernel | MFMA busy | LDS conflict | MFMA GFLOP |", "|---|---|---|---|---|"]
+    for j, (name, util, conf, gf) in enumerate(rows):
+        line = f"| {j} | `{name}` | {util:.3f} | {conf:.3f} | {gf:.2f} |"
+        if base and j < len(base) and base[j][0] == name:
+            line += f" {base[j][1]:.3f} | {base[j][2]:.3f} |"
+        elif base:
+            line += " - | - |"
+        lines.append(line)
     open(out_path, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -524,8 +563,10 @@ def main():
                     help="also run a 1 GiB device copy (for HBM counter calibration)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the HBM traffic summary from two rocprofv3 --pmc runs and exit")
-    ap.add_argument("--mfma-summary", metavar="PMC_DIR",
-                    help="write the MFMA-busy / LDS-conflict summary from a rocprofv3 --pmc run and exit")
+    ap.add_argument("--mfma-summary", nargs="+", metavar="PMC_DIR",
+                    help="write the MFMA-busy / LDS-conflict summary from a rocprofv3 --pmc run "
+                         "(optionally followed by an earlier revision's run directory and its "
+                         "commit) and exit")
     ap.add_argument("--oracle-configs", metavar="OUT_MD",
                     help="time the CPU oracle on the other workloads, write OUT_MD and exit")
     args = ap.parse_args()
@@ -533,7 +574,9 @@ def main():
         traffic_summary(*args.traffic_summary)
         return
     if args.mfma_summary:
-        mfma_summary(args.mfma_summary, os.path.join(ROOT, "profiles", "conv_kernels_1080p_mfma_util.md"))
+        base = args.mfma_summary[1:3]
+        mfma_summary(args.mfma_summary[0], os.path.join(ROOT, "profiles", "conv_kernels_1080p_mfma_util.md"),
+                     *(base if len(base) == 2 else []))
         return
     if args.oracle_configs:
         oracle_configs(args.oracle_configs)
