@@ -81,9 +81,11 @@ def traffic_summary(fetch_dir, write_dir):
         rows = []
         for f in glob.glob(os.path.join(d, "*counter_collection.csv")):
             rows += [r for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
+        # the 1 GiB calibration copy is the largest device copy of the run
         copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
-        if len(copy) != 1:
-            raise SystemExit(f"{d}: expected one device copy dispatch, found {len(copy)}")
+        if not copy:
+            raise SystemExit(f"{d}: no device copy dispatch (run with --copy-calibration)")
+        copy = [max(copy)]
         scale = COPY_BYTES / 1024.0 / copy[0]
         for r in rows:
             if "oidn::" not in r["Kernel_Name"]:
@@ -96,7 +98,8 @@ def traffic_summary(fetch_dir, write_dir):
              "Commands (repository root, one MI355X):", "", "```"]
     for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         lines.append(f"rocprofv3 --pmc {c} --output-format csv -d {d} -o run -- python -u bench.py "
-                     "--steps 3 --warmup 1 --no-cpu-baseline --copy-calibration")
+                     "--steps 3 --warmup 1 --no-cpu-baseline --no-peaks --no-other-configs "
+                     "--pass-launches 0 --cold-frames 0 --copy-calibration")
     lines += [f"python bench.py --traffic-summary {fetch_dir} {write_dir}", "```", ""]
     any_e = next(iter(per.values()))
     fs, ws = any_e["FETCH_SIZE_scale"], any_e["WRITE_SIZE_scale"]
