@@ -34,6 +34,7 @@
 // The per-pixel reduction order depends only on the channel layout, never on
 // the pixel position or the image size, so tiled and untiled runs agree bit
 // for bit wherever their inputs agree.
+#include <atomic>
 #include <cstdio>
 #include <type_traits>
 
@@ -61,7 +62,7 @@ namespace {
 // that follows drains them.  Slots with no data (channel groups past the
 // source, pixels outside the image) load the zero block.
 // TH: tile height; NW: waves sharing the work; CAP: buffer capacity in slots.
-template <int TH, int NW, int CAP, int CG, bool UP, bool SW = false>
+template <int TH, int NW, int CAP, int CG, bool UP, bool SW = false, bool ASM = false>
 __device__ __forceinline__ void stage_patch_direct(uint4* slots, const _Float16* src, int cs,
                                                    int coff, int h, int w, int y0, int x0,
                                                    int wave, int lane) {
@@ -89,7 +90,7 @@ __device__ __forceinline__ void stage_patch_direct(uint4* slots, const _Float16*
       const void* gp = g_zero16;
       if (iy >= 0 && iy < sh && ix >= 0 && ix < sw && c < cs)
         gp = src + ((size_t)iy * sw + ix) * cs + c;
-      __builtin_amdgcn_global_load_lds(gp, slots + k * 64, 16, 0, 0);
+      dma16<ASM>(gp, slots + k * 64);
     }
   }
 }
@@ -306,24 +307,38 @@ __device__ __forceinline__ void store_pixel(void* y, size_t pix, const int (&cha
 // acc[r][q] holds, for this lane (16-lane group g), rows 4 g .. 4 g + 3 of
 // fragment q0 + q for pixel (yb + r, x); c is the pixel column in the tile.
 // Pixels at or past column xend (<= the image width) are not stored.
-template <int NFW, int R, bool OUTF32, bool BF>
-__device__ __forceinline__ void store_tile(const floatx4 (&acc)[R][NFW], const ConvF16Args& a,
-                                           void* y, int q0, int g, int yb, int x, int c, int pool,
-                                           int relu, int xend) {
-  const int nf = a.nf;
+// EpiChan holds this lane's output channels and biases.
+template <int NFW>
+struct EpiChan {
   int chan[NFW];
   bool lead[NFW], tail[NFW];   // first / second fragment of a pair this lane holds both of
   float bv[NFW][4];
+};
+
+template <int NFW>
+__device__ __forceinline__ EpiChan<NFW> epi_chan(const float* bias, int nf, int q0, int g) {
+  EpiChan<NFW> e;
 #pragma unroll
   for (int q = 0; q < NFW; ++q) {
     const int f = q0 + q;
     const bool paired = (f | 1) < nf;
-    chan[q] = 32 * (f >> 1) + (paired ? 8 * g + 4 * (f & 1) : 4 * g);
-    lead[q] = paired && (f & 1) == 0 && q + 1 < NFW;
-    tail[q] = paired && (f & 1) == 1 && q >= 1;
+    e.chan[q] = 32 * (f >> 1) + (paired ? 8 * g + 4 * (f & 1) : 4 * g);
+    e.lead[q] = paired && (f & 1) == 0 && q + 1 < NFW;
+    e.tail[q] = paired && (f & 1) == 1 && q >= 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bv[q][i] = a.bias[chan[q] + i];
+    for (int i = 0; i < 4; ++i) e.bv[q][i] = bias[e.chan[q] + i];
   }
+  return e;
+}
+
+template <int NFW, int R, bool OUTF32, bool BF>
+__device__ __forceinline__ void store_tile_chan(const floatx4 (&acc)[R][NFW], const EpiChan<NFW>& e,
+                                                const ConvF16Args& a, void* y, int yb, int x, int c,
+                                                int pool, int relu, int xend) {
+  const int (&chan)[NFW] = e.chan;
+  const bool (&lead)[NFW] = e.lead;
+  const bool (&tail)[NFW] = e.tail;
+  const float (&bv)[NFW][4] = e.bv;
   // relu is uniform: each branch gets its own copy of the loops (a select
   // per value otherwise)
   auto plain = [&](auto with_relu) {
@@ -377,6 +392,14 @@ __device__ __forceinline__ void store_tile(const floatx4 (&acc)[R][NFW], const C
   } else {
     if (relu) pooled(std::true_type{}); else pooled(std::false_type{});
   }
+}
+
+template <int NFW, int R, bool OUTF32, bool BF>
+__device__ __forceinline__ void store_tile(const floatx4 (&acc)[R][NFW], const ConvF16Args& a,
+                                           void* y, int q0, int g, int yb, int x, int c, int pool,
+                                           int relu, int xend) {
+  store_tile_chan<NFW, R, OUTF32, BF>(acc, epi_chan<NFW>(a.bias, a.nf, q0, g), a, y, yb, x, c, pool,
+                                      relu, xend);
 }
 
 // Direct global -> LDS copy of a chunk's weight rows for the workgroup's FB
@@ -541,6 +564,245 @@ __device__ __forceinline__ void conv3x3_body(const ConvF16Args& __restrict__ a, 
   store_tile<NFW, R, OUTF32, BF>(acc, a, ydst, q0, g, y0 + R * rg, x0 + c, c, pool, relu, a.w);
 }
 
+// ---------------------------------------------------------------------------
+// Weight-stationary producer / consumer form, for layers whose whole weight
+// set (the workgroup's FB fragments of every chunk) fits in LDS next to two
+// patch slots.  In the form above every tile re-copies its chunks' weight
+// rows (108 KB per tile at dec_conv1a against 43 KB of patches), and the
+// CU's LDS fill rate bounds the layer.  Here a persistent workgroup of eight
+// waves copies the weights once and walks its tiles' chunks as one stream
+// of steps: waves 0-3 (one per SIMD) multiply step s from patch slot s & 1
+// and, after a tile's last chunk, run its epilogue and stores; waves 4-7
+// copy the patch of step s + 1 into the other slot and wait for it; one
+// barrier per step.  The matrix waves read nothing from global memory after
+// the biases (kept in LDS), so no wait of theirs covers a store, and the
+// copy waves store nothing, so their waits cover their copies only.
+// LDS (halves): [slot 0 | slot 1 | weights of chunk 0, 1, ... | biases | zero].
+// Tiles of a workgroup: bx = blockIdx.x + k gridDim.x (gridDim.x a multiple
+// of kXcds, so all of them map to one XCD).
+// ---------------------------------------------------------------------------
+constexpr int WS_THREADS = 512;
+#ifndef OIDN_WS_ENABLE
+#define OIDN_WS_ENABLE 1
+#endif
+template <int NFW, int R, int WR>
+constexpr bool kWsCandidate = NFW == 4 && R == 8 && WR == 4;
+
+// Halves of weights a chunk kind occupies for FB fragments.
+__host__ __device__ constexpr int ws_chunk_weights(int ncg, bool up, int fb) {
+  return ncg * (up ? 4 : 3) * fb * 512;
+}
+
+template <int NFW, int R, int WR, bool OUTF32, bool BF>
+__device__ __forceinline__ void conv3x3_ws_body(const ConvF16Args& __restrict__ a, int pool, int relu) {
+  constexpr bool SW = true;
+  constexpr int FB = NFW * (4 / WR);
+  using T = Tile<WR * R, SW>;
+  extern __shared__ __attribute__((aligned(16))) _Float16 lds[];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int nf = a.nf;
+  const int nch = a.nchunks;
+  const int pslot = a.ws_pslot;
+  const int wbase = 2 * pslot;
+  int wtot = 0;
+  for (int ci = 0; ci < nch; ++ci) wtot += ws_chunk_weights(a.chunk[ci].ncg, ci < a.nup, FB);
+  float* const bias_lds = reinterpret_cast<float*>(lds + wbase + wtot);
+  const int zero = wbase + wtot + 2 * 16 * nf;
+  if (tid < 2) reinterpret_cast<uint2*>(lds + zero)[tid] = make_uint2(0u, 0u);
+  // the slots of every batched tile in one sequence: slot t is tile slot
+  // t mod grid_x of batch entry t / grid_x (grid_x is a multiple of kXcds)
+  const int nslots = (a.batch > 1 ? a.batch : 1) * a.grid_x;
+  const int ntile = (nslots - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int nsteps = ntile * nch;
+  const int bounds[6] = {0, a.nup4, a.nup, a.nup + a.npl4, a.nchunks - a.ntap, a.nchunks};
+  // tile k of this workgroup: its origin and batch byte offset; a padding
+  // slot past the last tile becomes a tile below the image (zero patches,
+  // nothing stored)
+  auto tile = [&](int k, int& y0, int& x0, size_t& boff) {
+    const int t = (int)blockIdx.x + k * (int)gridDim.x;
+    const int z = t / a.grid_x;
+    boff = (size_t)z * a.bstride;
+    int tx, ty;
+    if (tile_of_block(t - z * a.grid_x, a.tiles_x, a.tiles_y, tx, ty)) {
+      y0 = ty * T::TH;
+      x0 = tx * TW;
+    } else {
+      y0 = a.h + 2;
+      x0 = 0;
+    }
+  };
+
+  if (wave >= 4) {
+    // copy waves: the weights once, then one patch per step
+    const int cw = wave - 4;
+    const uint4* const wblk = static_cast<const uint4*>(a.wfrag) + lane + blockIdx.y * FB * 64;
+    {
+      int woff = wbase;
+      for (int ci = 0; ci < nch; ++ci) {
+        const ConvChunk ch = a.chunk[ci];
+        const uint4* const w = wblk + (size_t)ch.wfrag * 64;
+        _Float16* const dst = lds + woff;
+        const int K = ci < bounds[1] ? 0 : ci < bounds[2] ? 1 : ci < bounds[3] ? 2 : ci < bounds[4] ? 3 : 4;
+        if (K == 0) stage_weights<3 * 4 * FB, true>(dst, w, nf, FB, cw);
+        else if (K == 1) stage_weights<2 * 4 * FB, true>(dst, w, nf, FB, cw);
+        else if (K == 2) stage_weights<3 * 3 * FB, true>(dst, w, nf, FB, cw);
+        else if (K == 3) stage_weights<2 * 3 * FB, true>(dst, w, nf, FB, cw);
+        else stage_weights<1 * 3 * FB, true>(dst, w, nf, FB, cw);
+        woff += ws_chunk_weights(ch.ncg, ci < a.nup, FB);
+      }
+    }
+    auto copy = [&](int s) {
+      int ln = lane, ct = tid - 256;
+      asm volatile("" : "+v"(ln), "+v"(ct));
+      const int k = s / nch, ci = s - k * nch;
+      int y0, x0;
+      size_t boff;
+      tile(k, y0, x0, boff);
+      const _Float16* const src0 =
+          reinterpret_cast<const _Float16*>(static_cast<const char*>(a.src0) + boff);
+      const _Float16* const src1 =
+          a.src1 ? reinterpret_cast<const _Float16*>(static_cast<const char*>(a.src1) + boff) : nullptr;
+      const ConvChunk ch = a.chunk[ci];
+      _Float16* const base = lds + (s & 1) * pslot;
+      uint4* const slots = reinterpret_cast<uint4*>(base);
+      const int K = ci < bounds[1] ? 0 : ci < bounds[2] ? 1 : ci < bounds[3] ? 2 : ci < bounds[4] ? 3 : 4;
+      if (K <= 1) {
+        if ((a.cs0 & 7) != 0) {
+          if (K == 0) stage_patch<T::TH, 4, false, true, SW>(base, src0, a.cs0, ch.coff, a.h, a.w, y0, x0, ct);
+          else stage_patch<T::TH, 2, false, true, SW>(base, src0, a.cs0, ch.coff, a.h, a.w, y0, x0, ct);
+        } else if (K == 0) {
+          stage_patch_direct<T::TH, 4, T::PATCH / 8, 4, true, SW, true>(slots, src0, a.cs0, ch.coff, a.h,
+                                                                        a.w, y0, x0, cw, ln);
+        } else {
+          stage_patch_direct<T::TH, 4, T::PATCH / 8, 2, true, SW, true>(slots, src0, a.cs0, ch.coff, a.h,
+                                                                        a.w, y0, x0, cw, ln);
+        }
+        return;
+      }
+      const _Float16* src = ch.src ? src1 : src0;
+      const int cs = ch.src ? a.cs1 : a.cs0;
+      if ((cs & 7) != 0) {
+        if (K == 2) stage_patch<T::TH, 4, false, false, SW>(base, src, cs, ch.coff, a.h, a.w, y0, x0, ct);
+        else stage_patch<T::TH, 2, false, false, SW>(base, src, cs, ch.coff, a.h, a.w, y0, x0, ct);
+      } else if (K == 2) {
+        stage_patch_direct<T::TH, 4, T::PATCH / 8, 4, false, SW, true>(slots, src, cs, ch.coff, a.h, a.w,
+                                                                       y0, x0, cw, ln);
+      } else {
+        stage_patch_direct<T::TH, 4, T::PATCH / 8, 2, false, SW, true>(slots, src, cs, ch.coff, a.h, a.w,
+                                                                       y0, x0, cw, ln);
+      }
+    };
+    if (nsteps > 0) copy(0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+#pragma unroll 1
+    for (int s = 0; s < nsteps; ++s) {
+      __builtin_amdgcn_s_barrier();
+      if (s + 1 < nsteps) copy(s + 1);
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    }
+    return;
+  }
+
+  // matrix waves
+  const int g = lane >> 4, c = lane & 15;
+  const int rg = wave % WR;
+  const int q0 = (blockIdx.y * (4 / WR) + wave / WR) * NFW;
+  for (int i = tid; i < 16 * nf; i += 256) bias_lds[i] = a.bias[i];
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  const uint4* const wl = reinterpret_cast<const uint4*>(lds) + lane + (wave / WR) * NFW * 64;
+  floatx4 acc[R][NFW];
+  uint4 acur[3][NFW];
+  int s = 0;
+#pragma unroll 1
+  for (int k = 0; k < ntile; ++k) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int q = 0; q < NFW; ++q) acc[r][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+    int woff = wbase;
+#define OIDN_WS_UP(K, CG)                                                                       \
+    _Pragma("unroll 1") for (int ci = bounds[K]; ci < bounds[K + 1]; ++ci, ++s) {               \
+      __builtin_amdgcn_s_barrier();                                                             \
+      mma_chunk_up<NFW, R, CG, SW, BF>(acc, lds, (s & 1) * pslot, zero, wl + woff / 8, FB, R * rg, 0, g, c); \
+      woff += ws_chunk_weights(a.chunk[ci].ncg, true, FB);                                      \
+    }
+#define OIDN_WS_PL(K, CG, TAP)                                                                  \
+    _Pragma("unroll 1") for (int ci = bounds[K]; ci < bounds[K + 1]; ++ci, ++s) {               \
+      __builtin_amdgcn_s_barrier();                                                             \
+      mma_chunk<NFW, R, CG, false, PW, SW, TAP, BF>(acc, acur, lds, (s & 1) * pslot, zero, wl + woff / 8, \
+                                                    nullptr, FB, R * rg, 0, g, c, [] {});       \
+      woff += ws_chunk_weights(a.chunk[ci].ncg, false, FB);                                     \
+    }
+    OIDN_WS_UP(0, 4)
+    OIDN_WS_UP(1, 2)
+    OIDN_WS_PL(2, 4, false)
+    OIDN_WS_PL(3, 2, false)
+    OIDN_WS_PL(4, 2, true)
+#undef OIDN_WS_UP
+#undef OIDN_WS_PL
+    int y0, x0;
+    size_t boff;
+    tile(k, y0, x0, boff);
+    store_tile_chan<NFW, R, OUTF32, BF>(acc, epi_chan<NFW>(bias_lds, nf, q0, g), a,
+                                        static_cast<char*>(a.y) + boff, y0 + R * rg, x0 + c, c, pool,
+                                        relu, a.w);
+  }
+}
+
+template <int NFW, int R, int WR, bool OUTF32>
+__global__ __launch_bounds__(WS_THREADS, 1) void conv3x3_ws_f16(ConvF16Args a, int pool, int relu) {
+  if constexpr (kWsCandidate<NFW, R, WR>) conv3x3_ws_body<NFW, R, WR, OUTF32, false>(a, pool, relu);
+}
+template <int NFW, int R, int WR, bool OUTF32>
+__global__ __launch_bounds__(WS_THREADS, 1) void conv3x3_ws_bf16(ConvF16Args a, int pool, int relu) {
+  if constexpr (kWsCandidate<NFW, R, WR>) conv3x3_ws_body<NFW, R, WR, OUTF32, true>(a, pool, relu);
+}
+
+// LDS bytes of the weight-stationary form for a's chunks (0 if it does not
+// fit in a CU's 160 KB), and the patch slot size it sets in a.ws_pslot.
+template <int NFW, int R, int WR>
+size_t ws_lds_bytes(ConvF16Args& a) {
+  constexpr int FB = NFW * (4 / WR);
+  using T = Tile<WR * R, true>;
+  const int tap_patch = ((WR * R + 2) * PW * 16 + 511) / 512 * 512;
+  int pslot = 0, wtot = 0;
+  for (int ci = 0; ci < a.nchunks; ++ci) {
+    const ConvChunk& ch = a.chunk[ci];
+    const bool up = ci < a.nup;
+    const int patch = up ? kUpPatch<WR * R> : ch.cg == 4 ? T::PATCH : tap_patch;
+    pslot = patch > pslot ? patch : pslot;
+    wtot += ws_chunk_weights(ch.ncg, up, FB);
+  }
+  a.ws_pslot = pslot;
+  const size_t bytes = (size_t)(2 * pslot + wtot) * 2 + 16 * 4 * (size_t)a.nf + 16;
+  return bytes <= 160 * 1024 ? bytes : 0;
+}
+
+int device_cus();
+
+// Workgroups along x of the weight-stationary launch: one per CU (shared by
+// the nsplit y slices), a multiple of kXcds, at most the batch's tile slots.
+int ws_grid_x(int grid_x, int batch, int nsplit) {
+  const int nslots = (batch > 1 ? batch : 1) * grid_x;
+  int gx = device_cus() / nsplit / kXcds * kXcds;
+  return gx < kXcds ? kXcds : gx > nslots ? nslots : gx;
+}
+
+// Compute units of the current device (looked up once per device).
+int device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 // The kernels: fp16 and bf16 storage.
 template <int NFW, int R, int WR, bool OUTF32>
 __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(ConvF16Args a, int upcat, int pool,
@@ -559,6 +821,29 @@ hipError_t launch_shape(ConvF16Args a, int nsplit, bool upcat, bool pool, bool r
   a.tiles_x = cdiv(a.w, TW);
   a.tiles_y = cdiv(a.h, WR * R);
   const int ntiles = a.tiles_x * a.tiles_y;
+  a.grid_x = cdiv(ntiles, kXcds) * kXcds;
+  if constexpr (kWsCandidate<NFW, R, WR>) {
+    const size_t lds = OIDN_WS_ENABLE ? ws_lds_bytes<NFW, R, WR>(a) : 0;
+    if (lds > 0) {
+      const int gx = ws_grid_x(a.grid_x, a.batch, nsplit);
+      const void* fn = bf16 ? (out_f32 ? (const void*)conv3x3_ws_bf16<NFW, R, WR, true>
+                                       : (const void*)conv3x3_ws_bf16<NFW, R, WR, false>)
+                            : (out_f32 ? (const void*)conv3x3_ws_f16<NFW, R, WR, true>
+                                       : (const void*)conv3x3_ws_f16<NFW, R, WR, false>);
+      hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      const dim3 wgrid(gx, nsplit, 1), wblock(WS_THREADS);
+      if (bf16 && out_f32)
+        hipLaunchKernelGGL((conv3x3_ws_bf16<NFW, R, WR, true>), wgrid, wblock, lds, stream, a, (int)pool, (int)relu);
+      else if (bf16)
+        hipLaunchKernelGGL((conv3x3_ws_bf16<NFW, R, WR, false>), wgrid, wblock, lds, stream, a, (int)pool, (int)relu);
+      else if (out_f32)
+        hipLaunchKernelGGL((conv3x3_ws_f16<NFW, R, WR, true>), wgrid, wblock, lds, stream, a, (int)pool, (int)relu);
+      else
+        hipLaunchKernelGGL((conv3x3_ws_f16<NFW, R, WR, false>), wgrid, wblock, lds, stream, a, (int)pool, (int)relu);
+      return hipGetLastError();
+    }
+  }
   const dim3 grid(cdiv(ntiles, kXcds) * kXcds, nsplit, a.batch > 1 ? a.batch : 1), block(THREADS);
   if (bf16 && out_f32)
     hipLaunchKernelGGL((conv3x3_bf16_mfma<NFW, R, WR, true>), grid, block, 0, stream, a,
@@ -1162,6 +1447,16 @@ void conv_f16_describe(const ConvF16Args& a, int nf, bool out_f32, bool bf16, ch
                        int* blocks) {
   const int h = a.h, w = a.w;
   const ConvPlan P = conv_f16_plan(h, w, nf, a.nchunks, a.nup, a.batch);
+  if (OIDN_WS_ENABLE && P.nfw == 4 && P.rows == 8 && P.wr == 4) {
+    ConvF16Args b = a;
+    b.nf = nf;
+    if (ws_lds_bytes<4, 8, 4>(b) > 0) {
+      const int nsplit = nf / plan_block_frags(P);
+      snprintf(buf, cap, "conv3x3_ws_%s<4, 8, 4, %s>", bf16 ? "bf16" : "f16", out_f32 ? "true" : "false");
+      *blocks = ws_grid_x(cdiv(cdiv(w, TW) * cdiv(h, 4 * 8), kXcds) * kXcds, a.batch, nsplit) * nsplit;
+      return;
+    }
+  }
   snprintf(buf, cap, "conv3x3_%s_mfma<%d, %d, %d, %s>", bf16 ? "bf16" : "f16", P.nfw, P.rows, P.wr,
            out_f32 ? "true" : "false");
   *blocks = conv_f16_blocks(h, w, nf, a.nchunks, a.nup, a.batch);

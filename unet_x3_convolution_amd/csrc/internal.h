@@ -94,6 +94,8 @@ struct ConvF16Args {
   int cout_stored;
   int nf;             // output fragments of the whole conv
   int tiles_x, tiles_y;
+  int grid_x;         // tile slots along grid x (tiles rounded up to a multiple of 8)
+  int ws_pslot;       // patch slot (halves) of the weight-stationary form
   int nchunks;
   int nup4, nup, npl4;   // chunk ranges of the kernel's loops (see ConvLayout)
   int ntap;
