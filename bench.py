@@ -529,13 +529,19 @@ def mfma_summary(pmc_dir, out_path, base_dir=None, base_rev=None):
                   f"| LDS conflict at {base_rev} |", "|---|---|---|---|---|---|---|"]
     else:
         lines += ["| launch | kernel | MFMA busy | LDS conflict | MFMA GFLOP |", "|---|---|---|---|---|"]
+    changed = []
     for j, (name, util, conf, gf) in enumerate(rows):
         line = f"| {j} | `{name}` | {util:.3f} | {conf:.3f} | {gf:.2f} |"
-        if base and j < len(base) and base[j][0] == name:
+        if base and j < len(base):
+            # the same launch of the frame, whichever kernel served it then
             line += f" {base[j][1]:.3f} | {base[j][2]:.3f} |"
+            if base[j][0] != name:
+                changed.append(f"launch {j} ran `{base[j][0]}` at {base_rev}")
         elif base:
             line += " - | - |"
         lines.append(line)
+    if changed:
+        lines += ["", "Kernels that changed between the two columns: " + "; ".join(changed) + "."]
     open(out_path, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 

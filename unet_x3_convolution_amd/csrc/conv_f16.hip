@@ -823,22 +823,17 @@ hipError_t launch_shape(ConvF16Args a, int nsplit, bool upcat, bool pool, bool r
   const int ntiles = a.tiles_x * a.tiles_y;
   a.grid_x = cdiv(ntiles, kXcds) * kXcds;
   if constexpr (kWsCandidate<NFW, R, WR>) {
-    const size_t lds = OIDN_WS_ENABLE ? ws_lds_bytes<NFW, R, WR>(a) : 0;
+    // (fp16 / bf16 outputs only: no network layer with an fp32 output fits)
+    const size_t lds = OIDN_WS_ENABLE && !out_f32 ? ws_lds_bytes<NFW, R, WR>(a) : 0;
     if (lds > 0) {
       const int gx = ws_grid_x(a.grid_x, a.batch, nsplit);
-      const void* fn = bf16 ? (out_f32 ? (const void*)conv3x3_ws_bf16<NFW, R, WR, true>
-                                       : (const void*)conv3x3_ws_bf16<NFW, R, WR, false>)
-                            : (out_f32 ? (const void*)conv3x3_ws_f16<NFW, R, WR, true>
-                                       : (const void*)conv3x3_ws_f16<NFW, R, WR, false>);
+      const void* fn = bf16 ? (const void*)conv3x3_ws_bf16<NFW, R, WR, false>
+                            : (const void*)conv3x3_ws_f16<NFW, R, WR, false>;
       hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
       const dim3 wgrid(gx, nsplit, 1), wblock(WS_THREADS);
-      if (bf16 && out_f32)
-        hipLaunchKernelGGL((conv3x3_ws_bf16<NFW, R, WR, true>), wgrid, wblock, lds, stream, a, (int)pool, (int)relu);
-      else if (bf16)
+      if (bf16)
         hipLaunchKernelGGL((conv3x3_ws_bf16<NFW, R, WR, false>), wgrid, wblock, lds, stream, a, (int)pool, (int)relu);
-      else if (out_f32)
-        hipLaunchKernelGGL((conv3x3_ws_f16<NFW, R, WR, true>), wgrid, wblock, lds, stream, a, (int)pool, (int)relu);
       else
         hipLaunchKernelGGL((conv3x3_ws_f16<NFW, R, WR, false>), wgrid, wblock, lds, stream, a, (int)pool, (int)relu);
       return hipGetLastError();
@@ -1447,7 +1442,7 @@ void conv_f16_describe(const ConvF16Args& a, int nf, bool out_f32, bool bf16, ch
                        int* blocks) {
   const int h = a.h, w = a.w;
   const ConvPlan P = conv_f16_plan(h, w, nf, a.nchunks, a.nup, a.batch);
-  if (OIDN_WS_ENABLE && P.nfw == 4 && P.rows == 8 && P.wr == 4) {
+  if (OIDN_WS_ENABLE && !out_f32 && P.nfw == 4 && P.rows == 8 && P.wr == 4) {
     ConvF16Args b = a;
     b.nf = nf;
     if (ws_lds_bytes<4, 8, 4>(b) > 0) {
