@@ -159,6 +159,30 @@ def test_tiled_equals_untiled_at_default_overlap():
 
 
 @pytest.mark.parametrize("precision", ["f16", "bf16"])
+def test_batched_weight_stationary_layer_with_padded_slots_bit_exact(precision):
+    """1280x720 in three 624x720 tiles, one batch: dec_conv1a takes the
+    persistent weight-stationary form on both runs, and at the tile size its
+    897 tiles leave 7 padding slots after every batch entry's tiles in the
+    workgroups' shared tile sequence.  At overlap 96 the tiled result must
+    equal the untiled one bit for bit."""
+    F = DT[precision]
+    tiles = U.oidn_plan_tiles(1280, 720, 768, 96)
+    tw, th = tiles[0][2], tiles[0][3]
+    assert len(tiles) == 3 and all((t[2], t[3]) == (tw, th) for t in tiles)
+    nb = U.oidn_unet_tile_batch(9, 1280, 720, 768, 96, F)
+    assert nb == 3
+    assert U.oidn_unet_layer_kernel(9, 13, tw, th, F, nb)[0].startswith(f"conv3x3_ws_{precision}<")
+    assert U.oidn_unet_layer_kernel(9, 13, 1280, 720, F)[0].startswith(f"conv3x3_ws_{precision}<")
+    assert (-(-tw // 16) * -(-th // 32)) % 8 != 0
+    color, albedo, normal, ws, bs = make_case(1280, 720, seed=21)
+    untiled = gpu_denoise(ws, bs, color, albedo, normal, precision, 0, 96)
+    tiled = gpu_denoise(ws, bs, color, albedo, normal, precision, 768, 96)
+    assert not np.any(np.isnan(untiled))
+    assert np.array_equal(tiled, untiled)
+    say(f"weight-stationary dec_conv1a, 3 batched tiles with padded slots, {precision}: bit-exact")
+
+
+@pytest.mark.parametrize("precision", ["f16", "bf16"])
 def test_fused_io_passes_equal_separate_passes_bit_exact(precision):
     """On the 16-bit paths the first fused pair reads the images through the
     input pass and the last writes the image through the output pass.  With 6
