@@ -803,6 +803,24 @@ int device_cus() {
   return n;
 }
 
+// Raises kernel `fn`'s dynamic LDS limit to at least `bytes` on the current
+// device: once per device and kernel (slot 0 / 1: the fp16 / bf16 form),
+// again only for a larger size.
+hipError_t allow_dynamic_lds(const void* fn, int slot, int bytes) {
+  static std::atomic<int> granted[64][2];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (granted[dev][slot].load(std::memory_order_acquire) >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  int cur = granted[dev][slot].load(std::memory_order_relaxed);
+  while (cur < bytes && !granted[dev][slot].compare_exchange_weak(cur, bytes)) {
+  }
+  return hipSuccess;
+}
+
 // The kernels: fp16 and bf16 storage.
 template <int NFW, int R, int WR, bool OUTF32>
 __global__ __launch_bounds__(THREADS, 2) void conv3x3_f16_mfma(ConvF16Args a, int upcat, int pool,
@@ -829,7 +847,7 @@ hipError_t launch_shape(ConvF16Args a, int nsplit, bool upcat, bool pool, bool r
       const int gx = ws_grid_x(a.grid_x, a.batch, nsplit);
       const void* fn = bf16 ? (const void*)conv3x3_ws_bf16<NFW, R, WR, false>
                             : (const void*)conv3x3_ws_f16<NFW, R, WR, false>;
-      hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      hipError_t e = allow_dynamic_lds(fn, bf16 ? 1 : 0, (int)lds);
       if (e != hipSuccess) return e;
       const dim3 wgrid(gx, nsplit, 1), wblock(WS_THREADS);
       if (bf16)
