@@ -506,7 +506,7 @@ def mfma_summary(pmc_dir, out_path, base_dir=None, base_rev=None):
     earlier revision's run (base_rev) in columns beside them."""
     rows, nframes = mfma_rows(pmc_dir)
     base = mfma_rows(base_dir)[0] if base_dir else None
-    cmd = (f"rocprofv3 --pmc {MFMA_COUNTERS} --output-format csv -d gpurun_out/pmc_mfma -o run -- "
+    cmd = (f"rocprofv3 --pmc {MFMA_COUNTERS} --output-format csv -d {pmc_dir} -o run -- "
            "python -u bench.py --steps 3 --warmup 1 --no-cpu-baseline --pass-launches 0 --cold-frames 0 "
            "--no-peaks --no-other-configs")
     lines = ["# MFMA utilisation and LDS bank conflicts per launch: UNet denoise 1920x1080, fp16", "",
@@ -516,9 +516,9 @@ def mfma_summary(pmc_dir, out_path, base_dir=None, base_rev=None):
                   "--no-peaks / --no-other-configs):",
                   f"rocprofv3 --pmc {MFMA_COUNTERS} --output-format csv -d {base_dir} -o run -- "
                   "python -u bench.py --steps 3 --warmup 1 --no-cpu-baseline --pass-launches 0 --cold-frames 0",
-                  f"python bench.py --mfma-summary gpurun_out/pmc_mfma {base_dir} {base_rev}"]
+                  f"python bench.py --mfma-summary {pmc_dir} {base_dir} {base_rev}"]
     else:
-        lines.append("python bench.py --mfma-summary gpurun_out/pmc_mfma")
+        lines.append(f"python bench.py --mfma-summary {pmc_dir}")
     lines += ["```", "",
               "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
               "LDS conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (share of the LDS's "
