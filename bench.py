@@ -42,7 +42,7 @@ def conv_source_hash():
 
 
 def kernel_symbol(name):
-    """'void oidn::(anonymous namespace)::conv3x3_f16_mfma<4, 8, false>(...)' -> 'conv3x3_f16_mfma<4, 8, false>'."""
+    """'void oidn::(anonymous namespace)::conv3x3_f16_mfma<4, 8, 4, false>(...)' -> 'conv3x3_f16_mfma<4, 8, 4, false>'."""
     name = name.replace("(anonymous namespace)::", "").replace("oidn::", "").replace("void ", "")
     depth = 0
     for i, ch in enumerate(name):

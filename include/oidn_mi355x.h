@@ -154,7 +154,7 @@ int oidn_conv3x3_pair(const void* x, int h, int w, int cin, const void* wa_packe
 /* Name of the kernel instance that oidn_conv3x3 (cin1 == 0) or
  * oidn_conv3x3_upcat (cin0 = c_low, cin1 = c_skip) runs for this shape,
  * written NUL-terminated into buf (cap bytes), e.g.
- * "conv3x3_f16_mfma<4, 8, false>"; *blocks (may be null) receives the
+ * "conv3x3_f16_mfma<4, 8, 4, false>"; *blocks (may be null) receives the
  * launch's workgroup count.  Same validation as those calls; host only. */
 int oidn_conv3x3_kernel(int h, int w, int cin0, int cin1, int cout, int in_dtype,
                         int out_dtype, unsigned flags, char* buf, int cap, int* blocks);
@@ -247,9 +247,13 @@ int oidn_unet_layer_info(int in_channels, int layer, int* cin0, int* cin1, int* 
  * rows per wave, row groups, fp32 output) or, for both layers of a fused
  * pair, "conv3x3_pair_f16<2, 2, 0, 3>" (convA channel groups, convB
  * fragments, output: 0 16-bit, 1 fp32, 2 straight through the output pass;
- * input: bit 0 tap-packed, bit 1 the caller's images through the input pass);
- * with bf16 storage "conv3x3_bf16_mfma" and "conv3x3_pair_bf16".  *blocks
- * receives the launch's workgroup count.  Host only. */
+ * input: bit 0 tap-packed, bit 1 the caller's images through the input pass),
+ * or "conv3x3_ws_f16<4, 8, 4, false>" for a layer whose whole weight set fits
+ * in LDS (dec_conv1a with the tap-packed skip): one persistent workgroup per
+ * compute unit that walks the launch's tiles, so *blocks is that grid;
+ * with bf16 storage "conv3x3_bf16_mfma", "conv3x3_pair_bf16" and
+ * "conv3x3_ws_bf16".  *blocks receives the launch's workgroup count.  Host
+ * only. */
 int oidn_unet_layer_kernel(int in_channels, int layer, int tw, int th, int batch, int dtype,
                            char* buf, int cap, int* blocks);
 
@@ -290,7 +294,8 @@ int oidn_unet_workspace_bytes(int in_channels, int w, int h, int max_tile, int o
 /* Tiles of this plan that oidn_unet_forward runs through the network
  * together: on the 16-bit paths, where both image passes run inside the first
  * and last convs, up to 16 consecutive tiles of one size share one launch
- * per layer (tile index in grid z); else 1.  The per-kernel events of
+ * per layer (tile index in grid z, or one tile sequence for the persistent
+ * weight-stationary layer); else 1.  The per-kernel events of
  * oidn_unet_forward_timed cover the first such batch.  Host only. */
 int oidn_unet_tile_batch(int in_channels, int w, int h, int max_tile, int overlap, int dtype,
                          int* batch);
