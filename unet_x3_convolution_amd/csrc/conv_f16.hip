@@ -1097,14 +1097,21 @@ __device__ __forceinline__ void conv3x3_pair_body(const PairArgs& __restrict__ p
   const int g = lane >> 4, c = lane & 15;
   const int cf = wave & 1, rh = wave >> 1;        // column fragment, row half
 
+  // A packed source was written by the previous launch in ascending tile
+  // (and batch) order; walking the tiles in descending order reads the most
+  // recently written lines first, while the memory-side cache still holds
+  // them (dec_conv1a's 267 MB output at 1080p exceeds that cache).  Block b
+  // still runs on XCD b mod 8 and walks one contiguous band of tiles.
+  constexpr bool REV = !IMG;
+  const int bx = REV ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
   int tx, ty;
-  if (!tile_of_block(blockIdx.x, p.tiles_x, p.tiles_y, tx, ty)) return;
+  if (!tile_of_block(bx, p.tiles_x, p.tiles_y, tx, ty)) return;
   const int y0 = ty * PAIR_TH, x0 = tx * PAIR_TW;
   if (tid < 2) reinterpret_cast<uint2*>(lds + L::ZERO)[tid] = make_uint2(0u, 0u);
   constexpr int RB = PAIR_TH / 2;                 // convB rows per wave
   const int xend = x0 + PAIR_TW < p.w ? x0 + PAIR_TW : p.w;
   // this tile of the batch: activations at its offset, its image rectangle
-  const int bt = blockIdx.z;
+  const int bt = REV ? (int)gridDim.z - 1 - (int)blockIdx.z : (int)blockIdx.z;
   const size_t boff = (size_t)bt * p.bstride;
   OutputPass img = p.img;
   if constexpr (OUT == kPairImage) {
